@@ -1,0 +1,21 @@
+"""float64 CPU oracle of the Mamba-3 forward path.
+
+Test infrastructure: only the tests, the smoke check and the benchmark's CPU
+baseline import this package.  It shares no code with the HIP library.
+"""
+
+from .m3_oracle import (  # noqa: F401
+    MIMO_NORM_EPS,
+    PreprocessConfig,
+    SsmConfig,
+    mimo_scan,
+    parity_error,
+    preprocess,
+    preprocess_width,
+    rotate,
+    sigmoid,
+    silu,
+    siso_scan,
+    siso_step,
+    softplus,
+)

@@ -1,0 +1,157 @@
+"""Seeded synthetic inputs shaped like the Mamba-3 SsmConfig workloads.
+
+This module is shared by the tests, the smoke check and the benchmark.  It
+draws random numbers and shapes their distributions; it computes none of the
+scan's steps.  Every array it returns is float32 and C-contiguous, in the
+operand layouts of the ``mamba3_siso`` / ``mamba3_mimo`` / ``mamba3_siso_step``
+docs (mamba3.rs, oarust 0.8.6):
+
+  c, b      [B, L, R*G, N]   standard normal rows rescaled to unit RMS
+  x, z      [B, L, H, P]     standard normal
+  dt        [B, L, H]        uniform on [dt_lo, dt_hi]
+  adt       [B, L, H]        -A * dt with A uniform on [1, 16] per element
+  trap      [B, L, H]        logistic of a standard normal
+  angle     [B, L, A]        normal, standard deviation 0.1
+  d         [H]              standard normal
+  c_bias, b_bias [H, (R,) N] normal, standard deviation 0.02
+  mimo_x/z/o [H, R, P]       normal, standard deviation 0.5 (variance 1/4)
+  norm_weight [H, P]         1 + normal(0, 0.02)
+
+Draw order is fixed (x, z, B, C, dt, A, trap, angle, D, c_bias, b_bias, MIMO
+weights, states) so that one seed fixes every value.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+RMS_EPS = 1.0e-5
+
+
+@dataclass(frozen=True)
+class Dims:
+    """Scan geometry: batch, length, heads, groups (0 => heads), head_dim, state, angles, rank."""
+
+    B: int
+    L: int
+    H: int
+    G: int
+    P: int
+    N: int
+    A: int
+    R: int = 1
+    has_z: bool = True
+    has_d: bool = True
+    has_output_norm: bool = False
+
+    @property
+    def groups(self) -> int:
+        return self.H if self.G == 0 else self.G
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str  # "siso" | "mimo" | "step"
+    dims: Dims
+    dt_range: tuple = (1e-3, 0.1)
+    seed: int = 0
+    steps: int = 1
+    extra: dict = field(default_factory=dict)
+
+
+# The five workloads: a tiny parity case, the 1.3B-class mixer layer, a long
+# sequence, a rank-4 MIMO layer, and batched single-token decode.
+WORKLOADS = {
+    "siso_tiny": Workload("siso_tiny", "siso", Dims(1, 64, 2, 1, 16, 16, 8), seed=1000),
+    "siso_b4_l2048": Workload("siso_b4_l2048", "siso", Dims(4, 2048, 24, 1, 64, 128, 32), seed=1001),
+    "siso_long_l65536": Workload("siso_long_l65536", "siso", Dims(1, 65536, 32, 1, 64, 128, 32),
+                                 dt_range=(1e-3, 0.01), seed=1002),
+    "mimo_b8_l4096_r4": Workload("mimo_b8_l4096_r4", "mimo",
+                                 Dims(8, 4096, 32, 1, 64, 128, 32, R=4, has_output_norm=True), seed=1003),
+    "decode_b256": Workload("decode_b256", "step", Dims(256, 1, 32, 1, 64, 128, 32), seed=1004, steps=1024),
+}
+
+
+def _unit_rms_rows(raw: np.ndarray) -> np.ndarray:
+    """Rescale each last-axis row to unit root-mean-square (input shaping)."""
+    r64 = raw.astype(np.float64)
+    scale = np.sqrt(np.mean(r64 * r64, axis=-1, keepdims=True) + RMS_EPS)
+    return (r64 / scale).astype(np.float32)
+
+
+def _logistic(v: np.ndarray) -> np.ndarray:
+    return (1.0 / (1.0 + np.exp(-v.astype(np.float64)))).astype(np.float32)
+
+
+def ssm_inputs(d: Dims, seed: int, dt_range=(1e-3, 0.1), mimo: bool | None = None,
+               overrides: dict | None = None) -> dict:
+    """Seeded operands for one SISO or MIMO scan call."""
+    rng = np.random.default_rng(seed)
+    B, L, H, G, P, N, A, R = d.B, d.L, d.H, d.groups, d.P, d.N, d.A, d.R
+    mimo = (R > 1 or d.has_output_norm) if mimo is None else mimo
+    f32 = np.float32
+    out = {}
+    out["x"] = rng.standard_normal((B, L, H, P), dtype=f32)
+    out["z"] = rng.standard_normal((B, L, H, P), dtype=f32)
+    out["b"] = _unit_rms_rows(rng.standard_normal((B, L, R * G, N), dtype=f32))
+    out["c"] = _unit_rms_rows(rng.standard_normal((B, L, R * G, N), dtype=f32))
+    lo, hi = dt_range
+    dt = (f32(lo) + f32(hi - lo) * rng.random((B, L, H), dtype=f32)).astype(f32)
+    out["dt"] = dt
+    a_mag = (f32(1.0) + f32(15.0) * rng.random((B, L, H), dtype=f32)).astype(f32)
+    out["adt"] = (-a_mag * dt).astype(f32)
+    out["trap"] = _logistic(rng.standard_normal((B, L, H), dtype=f32))
+    out["angle"] = (f32(0.1) * rng.standard_normal((B, L, A), dtype=f32)).astype(f32)
+    out["d"] = rng.standard_normal((H,), dtype=f32)
+    bias_shape = (H, R, N) if mimo else (H, N)
+    out["c_bias"] = (f32(0.02) * rng.standard_normal(bias_shape, dtype=f32)).astype(f32)
+    out["b_bias"] = (f32(0.02) * rng.standard_normal(bias_shape, dtype=f32)).astype(f32)
+    if mimo:
+        out["mimo_x"] = (f32(0.5) * rng.standard_normal((H, R, P), dtype=f32)).astype(f32)
+        out["mimo_z"] = (f32(0.5) * rng.standard_normal((H, R, P), dtype=f32)).astype(f32)
+        out["mimo_o"] = (f32(0.5) * rng.standard_normal((H, R, P), dtype=f32)).astype(f32)
+        out["norm_weight"] = (f32(1.0) + f32(0.02) * rng.standard_normal((H, P), dtype=f32)).astype(f32)
+    if overrides:
+        for k, v in overrides.items():
+            out[k] = np.ascontiguousarray(np.broadcast_to(np.asarray(v, dtype=f32), out[k].shape))
+    return {k: np.ascontiguousarray(v) for k, v in out.items()}
+
+
+def decode_states(d: Dims, seed: int) -> dict:
+    """Seeded recurrent states for ``mamba3_siso_step``.
+
+    ssm_state ~ N(0,1) [B,H,P,N]; angle_state ~ U[-pi, pi] [B,H,A];
+    k_state holds a unit-RMS B-like row [B,H,N] and v_state an x-like row
+    [B,H,P], standing for the previous token's stored key and value.
+    """
+    rng = np.random.default_rng([seed, 0x5747])
+    B, H, P, N, A = d.B, d.H, d.P, d.N, d.A
+    f32 = np.float32
+    st = {
+        "ssm_state": rng.standard_normal((B, H, P, N), dtype=f32),
+        "angle_state": (f32(-np.pi) + f32(2 * np.pi) * rng.random((B, H, A), dtype=f32)).astype(f32),
+        "k_state": _unit_rms_rows(rng.standard_normal((B, H, N), dtype=f32)),
+        "v_state": rng.standard_normal((B, H, P), dtype=f32),
+    }
+    return {k: np.ascontiguousarray(v) for k, v in st.items()}
+
+
+def step_inputs(d: Dims, seed: int, step: int, dt_range=(1e-3, 0.1)) -> dict:
+    """Fresh seeded L == 1 operands for decode step ``step``."""
+    d1 = Dims(d.B, 1, d.H, d.G, d.P, d.N, d.A, d.R, d.has_z, d.has_d, d.has_output_norm)
+    return ssm_inputs(d1, seed=np.random.SeedSequence([seed, step]).generate_state(1)[0],
+                      dt_range=dt_range, mimo=False)
+
+
+def preprocess_inputs(rows: int, width: int, heads: int, seed: int,
+                      dt_lo: float = 1e-3, dt_hi: float = 0.1) -> dict:
+    """Packed projections ~ N(0,1) [rows, width]; dt_bias [H] such that
+    softplus(dt_bias) is log-uniform on [dt_lo, dt_hi]."""
+    rng = np.random.default_rng(seed)
+    projected = rng.standard_normal((rows, width), dtype=np.float32)
+    target = np.exp(rng.uniform(np.log(dt_lo), np.log(dt_hi), size=heads))
+    dt_bias = np.log(np.expm1(target)).astype(np.float32)  # inverse of log(1 + e^u)
+    return {"projected": np.ascontiguousarray(projected), "dt_bias": dt_bias}
