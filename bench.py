@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of the Mamba-3 SISO forward path on MI355X.
+
+A step is one pass of the whole SISO hot path over one batch of the
+B4 L2048 H24 P64 N128 A32 layer: m3_preprocess on the packed projection
+[8192, 3432], then m3_siso_fwd on its outputs.  Inputs for three
+independent batches are resident in HBM before timing and are rotated so
+the 256 MB last-level cache cannot hold a whole step's working set.
+
+Prints one JSON line: tokens/s of the step, the scan kernel's roofline
+(algorithmic bytes / live HIP-event duration against 8 TB/s), and the float64
+CPU oracle timed on a bounded sample on the host cores.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, GB/s
+FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 (vector and matrix)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=3, help="input sets rotated through the timed loop")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the oracle's timed sample")
+    ap.add_argument("--no-parity", action="store_true")
+    return ap.parse_args()
+
+
+def scan_algorithmic_bytes(B, L, H, G, P, N, A) -> int:
+    """Each scan operand read once, out written once (fp32)."""
+    elems = 3 * B * L * H * P + 2 * B * L * G * N + 3 * B * L * H + B * L * A + 2 * H * N + H
+    return 4 * elems
+
+
+def preprocess_algorithmic_bytes(rows, W, I, M, H, A) -> int:
+    """Packed row and dt_bias read once, the eight outputs written once."""
+    return 4 * (rows * W + H + rows * (2 * I + 2 * M + 3 * H + A))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: every (batch, head) "
+              "chain is independent, so more GPUs would shard batch/heads with no communication.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import selective_state_space_mamba3_amd as m3
+    from selective_state_space_mamba3_amd import _binding as bd
+    from workloads import WORKLOADS, packed_projection
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 3
+    lib = m3.lib()  # raises if libm3.so is missing: there is no CPU fallback
+    dev = torch.device("cuda:0")
+    w = WORKLOADS["siso_b4_l2048"]
+    d = w.dims
+    B, L, H, G, P, N, A = d.B, d.L, d.H, d.groups, d.P, d.N, d.A
+    rows, I, M = B * L, H * P, G * N
+    pcfg = m3.PreprocessConfig(inner_size=I, state_size=N, num_heads=H, num_rope_angles=A, num_groups=G,
+                               mimo_rank=1, epsilon=1e-5, dt_min=1e-3, dt_max=0.1, a_floor=1e-4)
+    scfg = m3.SsmConfig(B, L, H, G, P, N, A, 1, True, True, False)
+    W = pcfg.width
+
+    # ---- inputs resident in HBM -------------------------------------------
+    host_sets, sets = [], []
+    for k in range(args.sets):
+        hs = packed_projection(d, seed=w.seed + 100 * k, dt_range=w.dt_range)
+        host_sets.append(hs if k == 0 else None)
+        ds = {key: torch.from_numpy(v).to(dev) for key, v in hs.items()}
+        outs = {"x": torch.empty(rows, I, device=dev), "z": torch.empty(rows, I, device=dev),
+                "bh": torch.empty(rows, M, device=dev), "ch": torch.empty(rows, M, device=dev),
+                "dt": torch.empty(rows, H, device=dev), "adt": torch.empty(rows, H, device=dev),
+                "trap": torch.empty(rows, H, device=dev), "angle": torch.empty(rows, A, device=dev)}
+        ds["pre"] = outs
+        ds["out"] = torch.empty(B, L, H, P, device=dev)
+        sets.append(ds)
+    ws = torch.empty(max(1, m3.siso_fwd_workspace_bytes(scfg)), dtype=torch.uint8, device=dev)
+
+    def scan_operands(s):
+        o = s["pre"]
+        return (o["ch"].view(B, L, G, N), o["bh"].view(B, L, G, N), o["x"].view(B, L, H, P),
+                o["z"].view(B, L, H, P), o["adt"].view(B, L, H), o["dt"].view(B, L, H),
+                o["trap"].view(B, L, H), o["angle"].view(B, L, A), s["c_bias"], s["b_bias"], s["d"])
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record()
+        m3.m3_preprocess(s["projected"], s["dt_bias"], pcfg, outs=s["pre"])
+        if ev is not None:
+            ev[1].record()
+        m3.m3_siso_fwd(*scan_operands(s), scfg, out=s["out"], workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    # ---- parity in the same run, before timing ----------------------------
+    parity = None
+    if not args.no_parity:
+        import oracle as O
+        s0 = sets[0]
+        step(s0)
+        torch.cuda.synchronize()
+        hs = host_sets[0]
+        ocfg = O.PreprocessConfig(I, N, H, A, G, 1, 1e-5, 1e-3, 0.1, 1e-4)
+        pre = O.preprocess(hs["projected"], hs["dt_bias"], ocfg)
+        heads = [0, H - 1]
+        shp = {"x": (B, L, H, P), "z": (B, L, H, P), "bh": (B, L, G, N), "ch": (B, L, G, N),
+               "dt": (B, L, H), "adt": (B, L, H), "trap": (B, L, H), "angle": (B, L, A)}
+        oi = {k: pre[k].reshape(shp[k]) for k in shp}
+        ref = O.siso_scan(oi["ch"], oi["bh"], oi["x"], oi["z"], oi["adt"], oi["dt"], oi["trap"], oi["angle"],
+                          hs["c_bias"], hs["b_bias"], hs["d"], O.SsmConfig(B, L, H, G, P, N, A), heads=heads)
+        got = s0["out"].cpu().numpy()[:, :, heads]
+        e = O.parity_error(got, ref)
+        parity = {"e": e["e"], "tol": 1e-4, "sample": f"all batch rows of heads {heads}, full sequence",
+                  "pass": bool(e["e"] <= 1e-4 and e["nonfinite"] == 0)}
+        if not parity["pass"]:
+            print(json.dumps({"parity_failed": parity}), file=sys.stderr)
+            return 4
+
+    # ---- warmup ------------------------------------------------------------
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    # ---- timed region ------------------------------------------------------
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    lib.m3_set_profile_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def new_event():
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    K = args.steps
+    kern_ev = [(new_event(), new_event()) for _ in range(K)]
+    step_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record()
+    for i in range(K):
+        lib.m3_set_profile_events(kern_ev[i][0], kern_ev[i][1])
+        step(sets[i % len(sets)], step_ev[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    lib.m3_set_profile_events(None, None)
+
+    ms_total = t_begin.elapsed_time(t_end)
+    ms_step = ms_total / K
+    f = ctypes.c_float()
+    kern_ms = []
+    for a, b in kern_ev:
+        hip.hipEventElapsedTime(ctypes.byref(f), a, b)
+        kern_ms.append(f.value)
+        hip.hipEventDestroy(a)
+        hip.hipEventDestroy(b)
+    pre_ms = [ev[0].elapsed_time(ev[1]) for ev in step_ev]
+    scan_ms = [ev[1].elapsed_time(ev[2]) for ev in step_ev]
+    kern_avg = float(np.mean(kern_ms))
+    tokens = B * L
+    scan_bytes = scan_algorithmic_bytes(B, L, H, G, P, N, A)
+    pre_bytes = preprocess_algorithmic_bytes(rows, W, I, M, H, A)
+    min_flops = 4 * N * P * B * L * H  # state read-out and state update, per token-head
+    kern_gbs = scan_bytes / (kern_avg * 1e-3) / 1e9
+    scan_call_ms = float(np.mean(scan_ms))
+    pre_avg = float(np.mean(pre_ms))
+
+    # ---- CPU baseline: the oracle on a bounded sample ---------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        hs = host_sets[0]
+        ocfg = O.PreprocessConfig(I, N, H, A, G, 1, 1e-5, 1e-3, 0.1, 1e-4)
+        c0 = time.perf_counter()
+        pre = O.preprocess(hs["projected"], hs["dt_bias"], ocfg)
+        t_pre = time.perf_counter() - c0
+        shp = {"x": (B, L, H, P), "z": (B, L, H, P), "bh": (B, L, G, N), "ch": (B, L, G, N),
+               "dt": (B, L, H), "adt": (B, L, H), "trap": (B, L, H), "angle": (B, L, A)}
+        oi = {k: pre[k].reshape(shp[k]) for k in shp}
+        hsel = list(range(min(args.cpu_heads, H)))
+        c0 = time.perf_counter()
+        O.siso_scan(oi["ch"], oi["bh"], oi["x"], oi["z"], oi["adt"], oi["dt"], oi["trap"], oi["angle"],
+                    hs["c_bias"], hs["b_bias"], hs["d"], O.SsmConfig(B, L, H, G, P, N, A), heads=hsel)
+        t_scan = time.perf_counter() - c0
+        est = t_pre + t_scan * H / len(hsel)
+        cpu = {"value": tokens / est, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": (f"float64 oracle, one thread: preprocess of all {rows} packed rows "
+                          f"({t_pre:.2f} s) + scan of {len(hsel)} of {H} heads over all {B} batch rows "
+                          f"and {L} tokens ({t_scan:.2f} s), scan time scaled by {H}/{len(hsel)}"),
+               "host_cpus": os.cpu_count()}
+
+    result = {
+        "metric": "scan fwd tokens/s + HBM GB/s (% roofline), SISO B4 L2048 H24 P64 N128",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "siso_b4_l2048: m3_preprocess [8192 x 3432] -> m3_siso_fwd",
+                   "batch": B, "seq_len": L, "heads": H, "groups": G, "head_dim": P, "state": N,
+                   "rope_angles": A, "has_z": True, "has_d": True, "input_sets": args.sets},
+        "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": kern_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "scan_chunk_kernel<32, true> (main scan pass)",
+                     "kernel_ms": kern_avg, "algorithmic_bytes": scan_bytes,
+                     "fp32_tflops_min_work": min_flops / (kern_avg * 1e-3) / 1e12,
+                     "fp32_frac": min_flops / (kern_avg * 1e-3) / 1e12 / FP32_PEAK_TFLOPS},
+        "scan": {"call_ms": scan_call_ms, "tokens_per_s": tokens / (scan_call_ms * 1e-3),
+                 "gbs": scan_bytes / (scan_call_ms * 1e-3) / 1e9,
+                 "hbm_frac": scan_bytes / (scan_call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "workspace_bytes": m3.siso_fwd_workspace_bytes(scfg)},
+        "preprocess": {"ms": pre_avg, "algorithmic_bytes": pre_bytes,
+                       "gbs": pre_bytes / (pre_avg * 1e-3) / 1e9,
+                       "hbm_frac": pre_bytes / (pre_avg * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "wall_s_timed": wall,
+        "parity": parity,
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

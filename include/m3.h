@@ -1,0 +1,219 @@
+/*
+ * m3.h -- C ABI of the MI355X (gfx950) Mamba-3 selective-state forward path.
+ *
+ * Four operations, named after the public functions of the oarust 0.8.6
+ * source page src/rs/ml/matrix/mamba3.rs ("Public API" section) and the
+ * ml::matrix API index:
+ *
+ *   m3_preprocess   mamba3_preprocess   split + transform one packed projection
+ *   m3_siso_fwd     mamba3_siso         SISO selective-state scan, forward
+ *   m3_mimo_fwd     mamba3_mimo         shared-state MIMO scan, forward
+ *   m3_siso_step    mamba3_siso_step    one SISO decode token, states in place
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers:   every tensor argument is a DEVICE pointer to contiguous,
+ *             row-major float32 memory on the current HIP device, in exactly
+ *             the layout the comment of that entry point gives.  Only the
+ *             angle operand may be NULL, and only when num_rope_angles == 0.
+ * Ownership:  the caller allocates every input, output, state and workspace
+ *             buffer.  The library allocates no device memory on these paths
+ *             and keeps no pointer after the call returns.
+ * Streams:    `stream` is a hipStream_t (NULL = the legacy default stream).
+ *             All work is enqueued on it; no call synchronises the host.
+ *             Outputs are valid once the stream reaches the call.
+ * Errors:     each call returns an m3_status.  Geometry and shape rules are
+ *             checked on the host before anything is enqueued, so on
+ *             M3_ERR_INVALID_ARGUMENT or M3_ERR_UNSUPPORTED no device memory
+ *             is touched (decode states stay as they were).  M3_ERR_HIP
+ *             reports a failed kernel launch.  m3_last_error() returns a
+ *             thread-local message naming the operation and the broken rule.
+ * Threads:    calls are thread-safe; calls on different streams may overlap.
+ * Precision:  float32 storage and arithmetic, accurate exp/sin/cos.
+ */
+#ifndef M3_H
+#define M3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum m3_status {
+    M3_OK = 0,
+    M3_ERR_INVALID_ARGUMENT = 1, /* a geometry/shape rule of the operation is broken */
+    M3_ERR_UNSUPPORTED = 2,      /* valid geometry beyond what the kernels implement */
+    M3_ERR_HIP = 3               /* the HIP runtime rejected a launch */
+} m3_status;
+
+/*
+ * Scan geometry and flags: mirror of SsmConfig (mamba3.rs, "Explicit tensor
+ * geometry and optional paths for a selective-state scan").  Passed by value.
+ *   batch_size B, sequence_length L, num_heads H,
+ *   num_groups G  (0 means G = H: one Q/K group per head),
+ *   head_dim P, state_size N, num_rope_angles A (rotary pairs in the state
+ *   axis), mimo_rank R (1 for SISO), and three 0/1 flags: has_z (SiLU z
+ *   gate), has_d (D skip), has_output_norm (MIMO output RMS norm; SISO
+ *   requires 0).
+ * Head h reads B/C group g = h / (H / G).
+ */
+typedef struct m3_ssm_config {
+    uint32_t batch_size;
+    uint32_t sequence_length;
+    uint32_t num_heads;
+    uint32_t num_groups;
+    uint32_t head_dim;
+    uint32_t state_size;
+    uint32_t num_rope_angles;
+    uint32_t mimo_rank;
+    uint32_t has_z;
+    uint32_t has_d;
+    uint32_t has_output_norm;
+} m3_ssm_config;
+
+/*
+ * Preprocess geometry and bounds: mirror of Mamba3PreprocessConfig
+ * (mamba3.rs, "Geometry and numerical bounds for the fused Mamba-3
+ * projection preprocess").  inner_size I (width of the z and x slices),
+ * state_size N, num_heads H, num_rope_angles A, num_groups G (>= 1 here),
+ * mimo_rank R, RMS epsilon, inclusive dt bounds [dt_min, dt_max], and
+ * a_floor, the positive floor of the A magnitude.
+ */
+typedef struct m3_preprocess_config {
+    uint32_t inner_size;
+    uint32_t state_size;
+    uint32_t num_heads;
+    uint32_t num_rope_angles;
+    uint32_t num_groups;
+    uint32_t mimo_rank;
+    float epsilon;
+    float dt_min;
+    float dt_max;
+    float a_floor;
+} m3_preprocess_config;
+
+/*
+ * m3_preprocess -- mamba3_preprocess ("Split and transform one packed
+ * Mamba-3 input projection"; PreprocessGeometry::resolve for the rules;
+ * Mamba3PreprocessResult for the outputs).
+ *
+ * In:  projected [rows, W] with W = 2I + 2*G*R*N + 3H + A, columns in the
+ *      order z | x | B | C | dt | A | trap | angle;  dt_bias [H].
+ * Out: x, z [rows, I]  copies of their slices;
+ *      bh, ch [rows, G*R*N]  each N-wide row v scaled by 1/sqrt(mean(v^2)+eps);
+ *      dt [rows, H]   = clamp(softplus(dt_raw + dt_bias[h]), dt_min, dt_max);
+ *      adt [rows, H]  = -max(softplus(A_raw), a_floor) * dt;
+ *      trap [rows, H], angle [rows, A]  copies (raw gate, raw angular velocity).
+ * Rules (M3_ERR_INVALID_ARGUMENT): rows, I, N, H, G, R > 0; 2A <= N;
+ *      epsilon, dt_min, dt_max, a_floor finite; epsilon, dt_min, a_floor > 0;
+ *      dt_min <= dt_max; every element count and W fit in uint32.
+ * `angle` may be NULL when A == 0.  Outputs must not alias the inputs.
+ */
+int m3_preprocess(const float* projected, const float* dt_bias, uint32_t rows,
+                  m3_preprocess_config cfg,
+                  float* x, float* z, float* bh, float* ch,
+                  float* dt, float* adt, float* trap, float* angle,
+                  void* stream);
+
+/*
+ * m3_siso_fwd -- mamba3_siso ("Run the Mamba-3 SISO selective-state
+ * recurrence"; Geometry::resolve for the rules).  Operands in the pages'
+ * order, C before B:
+ *   c, b [B,L,G,N];  x, z [B,L,H,P];  adt, dt, trap [B,L,H];  angle [B,L,A];
+ *   c_bias, b_bias [H,N];  d [H]   ->   out [B,L,H,P].
+ * Per (batch, head), from a zero state, for t = 0..L-1:
+ *   theta_t = theta_{t-1} + dt_t * angle_t;  lam_t = sigmoid(trap_t);
+ *   K_t = rot(B_t + b_bias, theta_t);  Q_t = rot(C_t + c_bias, theta_t);
+ *   h_t = e^{adt_t} h_{t-1} + (1-lam_t) dt_t e^{adt_t} x_{t-1} K_{t-1}^T
+ *         + lam_t dt_t x_t K_t^T;
+ *   out_t = (h_t Q_t + has_d * D x_t) * (has_z ? silu(z_t) : 1)
+ * where rot() turns split-half pairs (a, a+A) of the state axis by theta_a.
+ * z and d are read only when their flag is set but must be valid pointers.
+ * Rules (M3_ERR_INVALID_ARGUMENT): B, L, H, G, P, N > 0; H % G == 0;
+ *   P <= 128; N <= 128; A <= 64; 2A <= N; mimo_rank == 1;
+ *   has_output_norm == 0; flags 0 or 1; element counts and B*H fit uint32.
+ * workspace: at least m3_siso_fwd_workspace_bytes(cfg) bytes of device
+ *   memory (may be NULL when that is 0); its contents on entry are ignored.
+ * `out` must not alias any input.
+ */
+size_t m3_siso_fwd_workspace_bytes(m3_ssm_config cfg);
+int m3_siso_fwd(const float* c, const float* b, const float* x, const float* z,
+                const float* adt, const float* dt, const float* trap, const float* angle,
+                const float* c_bias, const float* b_bias, const float* d,
+                m3_ssm_config cfg, float* out,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * m3_mimo_fwd -- mamba3_mimo ("Run the shared-state Mamba-3 MIMO selective
+ * scan"; MimoGeometry::resolve for the rules).  Operands:
+ *   c, b [B,L,R*G,N] (row r*G + g is rank r of group g);  x, z [B,L,H,P];
+ *   adt, dt, trap [B,L,H];  angle [B,L,A];  c_bias, b_bias [H,R,N];  d [H];
+ *   mimo_x, mimo_z, mimo_o [H,R,P];  norm_weight [H,P]  ->  out [B,L,H,P].
+ * One state per (batch, head) fed by every rank: with X_r = x * mimo_x[h,r]
+ * and K_r, Q_r as in m3_siso_fwd from row r*G+g and biases [h,r],
+ *   h_t = e^{adt_t} h_{t-1} + (1-lam_t) dt_t e^{adt_t} sum_r X_r,{t-1} K_r,{t-1}^T
+ *         + lam_t dt_t sum_r X_r,t K_r,t^T;
+ *   Y_r = (h_t Q_r,t + has_d * D X_r,t) * (has_z ? silu(z_t * mimo_z[h,r]) : 1);
+ *   if has_output_norm: Y_r = Y_r / sqrt(mean_p(Y_r^2) + 1e-5) * norm_weight[h];
+ *   out_t = sum_r mimo_o[h,r] * Y_r.
+ * norm_weight is read only when has_output_norm == 1 but must be valid.
+ * Rules: as m3_siso_fwd with 1 <= mimo_rank <= 8 and has_output_norm 0/1.
+ *   The pages' cap P*N <= 4096 is a capacity limit of their kernel and is
+ *   not applied: P, N <= 128 each.
+ * workspace: at least m3_mimo_fwd_workspace_bytes(cfg) bytes (NULL if 0).
+ */
+size_t m3_mimo_fwd_workspace_bytes(m3_ssm_config cfg);
+int m3_mimo_fwd(const float* c, const float* b, const float* x, const float* z,
+                const float* adt, const float* dt, const float* trap, const float* angle,
+                const float* c_bias, const float* b_bias, const float* d,
+                const float* mimo_x, const float* mimo_z, const float* mimo_o,
+                const float* norm_weight,
+                m3_ssm_config cfg, float* out,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * m3_siso_step -- mamba3_siso_step ("Advance one Mamba-3 SISO token and
+ * update four explicit recurrent states"; dispatch_mamba3_siso_step for the
+ * state shapes).  The eleven operands take their L == 1 shapes
+ * (c, b [B,1,G,N]; x, z [B,1,H,P]; adt, dt, trap [B,1,H]; angle [B,1,A];
+ * biases [H,N]; d [H]).  States, read and written in place:
+ *   ssm_state   [B,H,P,N]  h
+ *   angle_state [B,H,A]    cumulative angle theta
+ *   k_state     [B,H,N]    previous key (rotated, bias added)
+ *   v_state     [B,H,P]    previous value (the previous token's x)
+ * One token of the m3_siso_fwd recurrence, continuing from these states;
+ * afterwards angle_state = theta_t, k_state = K_t, v_state = x_t.  A
+ * sequence of L steps from zero states equals m3_siso_fwd over L tokens.
+ * Rules: as m3_siso_fwd plus sequence_length == 1.  States are modified
+ * only by a call that returns M3_OK.  States must not alias each other or
+ * the operands; out [B,1,H,P] must not alias anything.
+ */
+int m3_siso_step(const float* c, const float* b, const float* x, const float* z,
+                 const float* adt, const float* dt, const float* trap, const float* angle,
+                 const float* c_bias, const float* b_bias, const float* d,
+                 float* ssm_state, float* angle_state, float* k_state, float* v_state,
+                 m3_ssm_config cfg, float* out, void* stream);
+
+/*
+ * Measurement hook.  After m3_set_profile_events(start, stop) with two
+ * hipEvent_t handles, later m3_siso_fwd / m3_mimo_fwd calls on this thread
+ * record `start` just before and `stop` just after their main scan kernel,
+ * on the call's stream, so hipEventElapsedTime(start, stop) is that
+ * kernel's duration.  Passing NULL, NULL turns the hook off.  The caller
+ * owns the events.
+ */
+void m3_set_profile_events(void* start_event, void* stop_event);
+
+/* Thread-local message of the last failed call on this thread ("" if none). */
+const char* m3_last_error(void);
+
+/* Library version string. */
+const char* m3_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* M3_H */

@@ -1,0 +1,23 @@
+"""MI355X (gfx950) Mamba-3 selective-state forward path.
+
+The compute lives in libm3.so (hand-written HIP kernels behind a C ABI, see
+include/m3.h); this package is its thin ctypes binding, with torch used for
+device memory and streams only.  Entry points carry the C names:
+m3_preprocess, m3_siso_fwd, m3_mimo_fwd, m3_siso_step.
+"""
+
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    M3Error,
+    PreprocessConfig,
+    SsmConfig,
+    header_functions,
+    last_error,
+    lib,
+    m3_mimo_fwd,
+    m3_preprocess,
+    m3_siso_fwd,
+    m3_siso_step,
+    mimo_fwd_workspace_bytes,
+    siso_fwd_workspace_bytes,
+)

@@ -1,0 +1,243 @@
+// C ABI of the Mamba-3 forward path: validation and dispatch.
+//
+// Validation mirrors the rules of the oarust 0.8.6 page
+// src/rs/ml/matrix/mamba3.rs: Geometry::resolve (SISO), MimoGeometry::resolve
+// (MIMO, without its P*N <= 4096 capacity cap), PreprocessGeometry::resolve
+// and the sequence_length == 1 rule of dispatch_mamba3_siso_step, plus the
+// u32 element-count limits those functions apply.  Every rule is checked on
+// the host before any HIP call, so a rejected call touches no device memory
+// and does not initialise the HIP runtime.
+#include "../../include/m3.h"
+#include "launch.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <initializer_list>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+constexpr uint64_t kU32 = 0xffffffffull;
+
+// Product of extents, false on overflow of uint32 (the stable shader ABI width).
+bool count_u32(std::initializer_list<uint64_t> ext) {
+  uint64_t c = 1;
+  for (uint64_t e : ext) {
+    if (e != 0 && c > kU32 / e) return false;
+    c *= e;
+  }
+  return c <= kU32;
+}
+
+struct Resolved {
+  m3::ScanGeom g;
+};
+
+// Shared rule set of the scan geometry.  `mimo` selects the MIMO rules.
+int resolve_scan(const char* op, const m3_ssm_config& cfg, bool mimo, m3::ScanGeom* out) {
+  const uint32_t G = cfg.num_groups == 0 ? cfg.num_heads : cfg.num_groups;
+  const bool flags_ok = cfg.has_z <= 1 && cfg.has_d <= 1 && cfg.has_output_norm <= 1;
+  if (!flags_ok)
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: has_z, has_d and has_output_norm must be 0 or 1", op);
+  bool bad = cfg.batch_size == 0 || cfg.sequence_length == 0 || cfg.num_heads == 0 || G == 0 ||
+             cfg.num_heads % G != 0 || cfg.head_dim == 0 || cfg.head_dim > 128 ||
+             cfg.state_size == 0 || cfg.state_size > 128 || cfg.num_rope_angles > 64 ||
+             2ull * cfg.num_rope_angles > cfg.state_size;
+  if (mimo) {
+    bad = bad || cfg.mimo_rank < 1 || cfg.mimo_rank > 8;
+    if (bad)
+      return fail(M3_ERR_INVALID_ARGUMENT,
+                  "%s requires B/L/H/G/P/N > 0, H divisible by G, P/N <= 128, A <= 64, 2A <= N, "
+                  "and MIMO rank in 1..=8",
+                  op);
+  } else {
+    bad = bad || cfg.mimo_rank != 1 || cfg.has_output_norm != 0;
+    if (bad)
+      return fail(M3_ERR_INVALID_ARGUMENT,
+                  "%s requires B/L/H/G/P/N > 0, H divisible by G, P/N <= 128, A <= 64, 2A <= N, "
+                  "MIMO rank one, and no MIMO output normalization",
+                  op);
+  }
+  const uint64_t B = cfg.batch_size, L = cfg.sequence_length, H = cfg.num_heads, P = cfg.head_dim,
+                 N = cfg.state_size, A = cfg.num_rope_angles, R = mimo ? cfg.mimo_rank : 1;
+  const bool counts_ok = count_u32({B, L, R * G, N}) && count_u32({B, L, H, P}) &&
+                         count_u32({B, L, H}) && count_u32({B, L, A}) && count_u32({H, R, N}) &&
+                         count_u32({H, R, P}) && count_u32({B, H});
+  if (!counts_ok)
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: a tensor element count or the batch-head count exceeds u32",
+                op);
+  out->B = cfg.batch_size;
+  out->L = cfg.sequence_length;
+  out->H = cfg.num_heads;
+  out->G = G;
+  out->P = cfg.head_dim;
+  out->N = cfg.state_size;
+  out->A = cfg.num_rope_angles;
+  out->R = (uint32_t)R;
+  out->has_z = cfg.has_z;
+  out->has_d = cfg.has_d;
+  out->has_norm = mimo ? cfg.has_output_norm : 0;
+  return M3_OK;
+}
+
+int check_ptrs(const char* op, std::initializer_list<std::pair<const char*, const void*>> ptrs) {
+  for (const auto& pr : ptrs)
+    if (pr.second == nullptr) return fail(M3_ERR_INVALID_ARGUMENT, "%s: operand %s is NULL", op, pr.first);
+  return M3_OK;
+}
+
+int hip_status(const char* op, hipError_t e) {
+  if (e == hipSuccess) return M3_OK;
+  return fail(M3_ERR_HIP, "%s: HIP error %d (%s)", op, (int)e, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* m3_last_error(void) { return g_err; }
+
+void m3_set_profile_events(void* start_event, void* stop_event) {
+  m3::ProfileEvents& pe = m3::profile_events();
+  const bool on = start_event != nullptr && stop_event != nullptr;
+  pe.start = on ? static_cast<hipEvent_t>(start_event) : nullptr;
+  pe.stop = on ? static_cast<hipEvent_t>(stop_event) : nullptr;
+}
+
+const char* m3_version(void) { return "m3 0.1.0 gfx950"; }
+
+int m3_preprocess(const float* projected, const float* dt_bias, uint32_t rows,
+                  m3_preprocess_config cfg, float* x, float* z, float* bh, float* ch, float* dt,
+                  float* adt, float* trap, float* angle, void* stream) {
+  const char* op = "m3_preprocess";
+  clear_error();
+  if (rows == 0 || cfg.inner_size == 0 || cfg.state_size == 0 || cfg.num_heads == 0 ||
+      cfg.num_groups == 0 || cfg.mimo_rank == 0 ||
+      2ull * cfg.num_rope_angles > cfg.state_size || !std::isfinite(cfg.epsilon) ||
+      cfg.epsilon <= 0.f || !std::isfinite(cfg.dt_min) || !std::isfinite(cfg.dt_max) ||
+      cfg.dt_min <= 0.f || cfg.dt_min > cfg.dt_max || !std::isfinite(cfg.a_floor) ||
+      cfg.a_floor <= 0.f)
+    return fail(M3_ERR_INVALID_ARGUMENT,
+                "%s requires positive geometry, 2*rope_angles <= state_size, finite epsilon/dt/A bounds, "
+                "epsilon/dt_min/A floor > 0, and dt_min <= dt_max",
+                op);
+  const uint64_t I = cfg.inner_size, N = cfg.state_size, H = cfg.num_heads,
+                 A = cfg.num_rope_angles, GR = (uint64_t)cfg.num_groups * cfg.mimo_rank;
+  const uint64_t M = GR * N;
+  const uint64_t W = 2 * I + 2 * M + 3 * H + A;
+  if (GR > kU32 || M > kU32 || W > kU32 || !count_u32({rows, W}) || !count_u32({rows, I}) ||
+      !count_u32({rows, M}) || !count_u32({rows, H}) || !count_u32({rows, A}))
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: projected width or an element count exceeds u32", op);
+  int st = check_ptrs(op, {{"projected", projected}, {"dt_bias", dt_bias}, {"x", x}, {"z", z},
+                           {"bh", bh}, {"ch", ch}, {"dt", dt}, {"adt", adt}, {"trap", trap}});
+  if (st) return st;
+  if (A > 0 && angle == nullptr) return fail(M3_ERR_INVALID_ARGUMENT, "%s: operand angle is NULL", op);
+  m3::PreGeom g{rows, cfg.inner_size, cfg.state_size, cfg.num_heads, cfg.num_rope_angles,
+                cfg.num_groups, cfg.mimo_rank, cfg.epsilon, cfg.dt_min, cfg.dt_max, cfg.a_floor};
+  m3::PreOperands o{projected, dt_bias, x, z, bh, ch, dt, adt, trap, angle};
+  return hip_status(op, m3::launch_preprocess(g, o, static_cast<hipStream_t>(stream)));
+}
+
+size_t m3_siso_fwd_workspace_bytes(m3_ssm_config cfg) {
+  m3::ScanGeom g{};
+  if (resolve_scan("m3_siso_fwd_workspace_bytes", cfg, false, &g) != M3_OK) return 0;
+  return m3::plan_workspace_bytes(m3::plan_siso(g));
+}
+
+size_t m3_mimo_fwd_workspace_bytes(m3_ssm_config cfg) {
+  m3::ScanGeom g{};
+  if (resolve_scan("m3_mimo_fwd_workspace_bytes", cfg, true, &g) != M3_OK) return 0;
+  return m3::plan_workspace_bytes(m3::plan_mimo(g));
+}
+
+int m3_siso_fwd(const float* c, const float* b, const float* x, const float* z, const float* adt,
+                const float* dt, const float* trap, const float* angle, const float* c_bias,
+                const float* b_bias, const float* d, m3_ssm_config cfg, float* out, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const char* op = "m3_siso_fwd";
+  clear_error();
+  m3::ScanGeom g{};
+  int st = resolve_scan(op, cfg, false, &g);
+  if (st) return st;
+  st = check_ptrs(op, {{"c", c}, {"b", b}, {"x", x}, {"z", z}, {"adt", adt}, {"dt", dt},
+                       {"trap", trap}, {"c_bias", c_bias}, {"b_bias", b_bias}, {"d", d}, {"out", out}});
+  if (st) return st;
+  if (g.A > 0 && angle == nullptr) return fail(M3_ERR_INVALID_ARGUMENT, "%s: operand angle is NULL", op);
+  const m3::ScanPlan plan = m3::plan_siso(g);
+  const size_t need = m3::plan_workspace_bytes(plan);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: workspace of %zu bytes required, %zu given", op, need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  m3::ScanOperands o{c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d,
+                     nullptr, nullptr, nullptr, nullptr, out};
+  return hip_status(op, m3::launch_siso_fwd(g, o, plan, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int m3_mimo_fwd(const float* c, const float* b, const float* x, const float* z, const float* adt,
+                const float* dt, const float* trap, const float* angle, const float* c_bias,
+                const float* b_bias, const float* d, const float* mimo_x, const float* mimo_z,
+                const float* mimo_o, const float* norm_weight, m3_ssm_config cfg, float* out,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  const char* op = "m3_mimo_fwd";
+  clear_error();
+  m3::ScanGeom g{};
+  int st = resolve_scan(op, cfg, true, &g);
+  if (st) return st;
+  st = check_ptrs(op, {{"c", c}, {"b", b}, {"x", x}, {"z", z}, {"adt", adt}, {"dt", dt},
+                       {"trap", trap}, {"c_bias", c_bias}, {"b_bias", b_bias}, {"d", d},
+                       {"mimo_x", mimo_x}, {"mimo_z", mimo_z}, {"mimo_o", mimo_o},
+                       {"norm_weight", norm_weight}, {"out", out}});
+  if (st) return st;
+  if (g.A > 0 && angle == nullptr) return fail(M3_ERR_INVALID_ARGUMENT, "%s: operand angle is NULL", op);
+  const m3::ScanPlan plan = m3::plan_mimo(g);
+  const size_t need = m3::plan_workspace_bytes(plan);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: workspace of %zu bytes required, %zu given", op, need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  m3::ScanOperands o{c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d,
+                     mimo_x, mimo_z, mimo_o, norm_weight, out};
+  return hip_status(op, m3::launch_mimo_fwd(g, o, plan, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int m3_siso_step(const float* c, const float* b, const float* x, const float* z, const float* adt,
+                 const float* dt, const float* trap, const float* angle, const float* c_bias,
+                 const float* b_bias, const float* d, float* ssm_state, float* angle_state,
+                 float* k_state, float* v_state, m3_ssm_config cfg, float* out, void* stream) {
+  const char* op = "m3_siso_step";
+  clear_error();
+  m3::ScanGeom g{};
+  int st = resolve_scan(op, cfg, false, &g);
+  if (st) return st;
+  if (cfg.sequence_length != 1)
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s requires sequence_length == 1", op);
+  if (!count_u32({g.B, g.H, g.P, g.N}))
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: state element count exceeds u32", op);
+  st = check_ptrs(op, {{"c", c}, {"b", b}, {"x", x}, {"z", z}, {"adt", adt}, {"dt", dt},
+                       {"trap", trap}, {"c_bias", c_bias}, {"b_bias", b_bias}, {"d", d},
+                       {"ssm_state", ssm_state}, {"k_state", k_state}, {"v_state", v_state},
+                       {"out", out}});
+  if (st) return st;
+  if (g.A > 0 && (angle == nullptr || angle_state == nullptr))
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: operand angle or angle_state is NULL", op);
+  m3::ScanOperands o{c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d,
+                     nullptr, nullptr, nullptr, nullptr, out};
+  m3::StepStates s{ssm_state, angle_state, k_state, v_state};
+  return hip_status(op, m3::launch_siso_step(g, o, s, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal launch interface between the C ABI (abi.cpp) and the HIP kernels.
+// Geometry arriving here has already been validated by abi.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace m3 {
+
+struct ScanGeom {
+  uint32_t B, L, H, G, P, N, A, R;
+  uint32_t has_z, has_d, has_norm;
+};
+
+struct ScanOperands {
+  const float *c, *b, *x, *z, *adt, *dt, *trap, *angle, *c_bias, *b_bias, *d;
+  const float *mimo_x, *mimo_z, *mimo_o, *norm_weight;  // MIMO only
+  float* out;
+};
+
+struct StepStates {
+  float *ssm, *angle, *k, *v;
+};
+
+struct PreGeom {
+  uint32_t rows, I, N, H, A, G, R;
+  float eps, dt_min, dt_max, a_floor;
+};
+
+struct PreOperands {
+  const float *projected, *dt_bias;
+  float *x, *z, *bh, *ch, *dt, *adt, *trap, *angle;
+};
+
+// Chunked scan plan: chunk length, number of sequence segments.
+struct ScanPlan {
+  int chunk;
+  int nseg;
+  int seg_len;
+  size_t ws_state_floats;
+  size_t ws_aux_floats;
+};
+
+// Events recorded around the main scan kernel (measurement hook; may be null).
+struct ProfileEvents {
+  hipEvent_t start, stop;
+};
+ProfileEvents& profile_events();
+
+ScanPlan plan_siso(const ScanGeom& g);
+ScanPlan plan_mimo(const ScanGeom& g);
+inline size_t plan_workspace_bytes(const ScanPlan& p) {
+  return (p.ws_state_floats + p.ws_aux_floats) * sizeof(float);
+}
+
+hipError_t launch_siso_fwd(const ScanGeom& g, const ScanOperands& o, const ScanPlan& plan,
+                           void* workspace, hipStream_t stream);
+hipError_t launch_mimo_fwd(const ScanGeom& g, const ScanOperands& o, const ScanPlan& plan,
+                           void* workspace, hipStream_t stream);
+hipError_t launch_siso_step(const ScanGeom& g, const ScanOperands& o, const StepStates& s,
+                            hipStream_t stream);
+hipError_t launch_preprocess(const PreGeom& g, const PreOperands& o, hipStream_t stream);
+
+}  // namespace m3

@@ -1,0 +1,95 @@
+"""GPU parity of m3_siso_fwd against the float64 oracle on seeded inputs."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from _gpu import assert_parity, gpu_siso, oracle_siso, to_dev
+from workloads import WORKLOADS, Dims, ssm_inputs
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # (name, dims, seed, dt_range)
+    ("siso_tiny_B1_L64_H2_P16_N16_A8", WORKLOADS["siso_tiny"].dims, 1000, (1e-3, 0.1)),
+    ("X1_B2_L67_H4_G2_P24_N48_A8", Dims(2, 67, 4, 2, 24, 48, 8), 2001, (1e-3, 0.1)),
+    ("X2_G0_H3_A0_noz", Dims(2, 45, 3, 0, 16, 32, 0, has_z=False), 2002, (1e-3, 0.1)),
+    ("X3_N32_A16_nod", Dims(1, 99, 2, 1, 32, 32, 16, has_d=False), 2003, (1e-3, 0.1)),
+    ("X4_P128_N128_L130", Dims(2, 130, 2, 1, 128, 128, 32), 2004, (1e-3, 0.1)),
+    ("odd_P5_N6_A3_L33", Dims(1, 33, 2, 2, 5, 6, 3), 2005, (1e-3, 0.1)),
+    ("P64_N128_L1", Dims(3, 1, 5, 1, 64, 128, 32), 2006, (1e-3, 0.1)),
+    ("P64_N128_L257_ragged", Dims(2, 257, 6, 3, 64, 128, 32), 2007, (1e-3, 0.1)),
+    ("P48_N80_A40_L100", Dims(1, 100, 4, 4, 48, 80, 40), 2008, (1e-3, 0.1)),
+    ("P16_N128_A64_L70_flags_off", Dims(2, 70, 2, 1, 16, 128, 64, has_z=False, has_d=False), 2009,
+     (1e-3, 0.1)),
+]
+
+
+@pytest.mark.parametrize("name,d,seed,dtr", SMALL, ids=[s[0] for s in SMALL])
+def test_siso_small(name, d, seed, dtr):
+    inp = ssm_inputs(d, seed=seed, dt_range=dtr)
+    got = gpu_siso(to_dev(inp), d).cpu().numpy()
+    assert_parity(got, oracle_siso(inp, d), name)
+
+
+@pytest.mark.parametrize("sign", [+1, -1])
+def test_siso_trap_extremes(sign):
+    d = Dims(2, 90, 3, 1, 32, 64, 16)
+    inp = ssm_inputs(d, seed=2010 + sign)
+    inp["trap"][:] = 40.0 * sign
+    got = gpu_siso(to_dev(inp), d).cpu().numpy()
+    assert_parity(got, oracle_siso(inp, d), f"X6_trap_{sign * 40}")
+
+
+@pytest.mark.parametrize("nseg", [1, 2, 3, 7])
+def test_siso_forced_segments(nseg, monkeypatch):
+    # the same answer whatever the number of sequence segments
+    monkeypatch.setenv("M3_SCAN_NSEG", str(nseg))
+    d = Dims(2, 300, 3, 1, 64, 128, 32)
+    inp = ssm_inputs(d, seed=2020)
+    got = gpu_siso(to_dev(inp), d).cpu().numpy()
+    assert_parity(got, oracle_siso(inp, d), f"segments_{nseg}")
+
+
+def test_siso_deterministic():
+    d = Dims(2, 200, 4, 1, 64, 128, 32)
+    inp = to_dev(ssm_inputs(d, seed=2030))
+    a = gpu_siso(inp, d).cpu().numpy()
+    b = gpu_siso(inp, d).cpu().numpy()
+    np.testing.assert_array_equal(a, b)
+
+
+def test_siso_does_not_touch_inputs():
+    d = Dims(1, 50, 2, 1, 16, 32, 8)
+    inp = ssm_inputs(d, seed=2040)
+    di = to_dev(inp)
+    gpu_siso(di, d)
+    for k, v in inp.items():
+        np.testing.assert_array_equal(di[k].cpu().numpy(), v)
+
+
+def test_siso_full_b4_l2048_sampled():
+    """The 1.3B-class layer B4 L2048 H24 P64 N128 A32, every batch row of three heads."""
+    w = WORKLOADS["siso_b4_l2048"]
+    d = w.dims
+    inp = ssm_inputs(d, seed=w.seed, dt_range=w.dt_range)
+    got = gpu_siso(to_dev(inp), d).cpu().numpy()
+    assert got.shape == (4, 2048, 24, 64)
+    assert np.isfinite(got).all()
+    heads = [0, 11, 23]
+    ref = oracle_siso(inp, d, heads=heads)
+    assert_parity(got[:, :, heads], ref, "siso_b4_l2048 heads 0,11,23")
+
+
+def test_siso_full_long_l65536_sampled():
+    """B1 L65536 H32 with dt in [1e-3, 0.01]: two heads over the whole sequence."""
+    w = WORKLOADS["siso_long_l65536"]
+    d = w.dims
+    inp = ssm_inputs(d, seed=w.seed, dt_range=w.dt_range)
+    got = gpu_siso(to_dev(inp), d).cpu().numpy()
+    assert np.isfinite(got).all()
+    heads = [0, 31]
+    ref = oracle_siso(inp, d, heads=heads)
+    assert_parity(got[:, :, heads], ref, "siso_long_l65536 heads 0,31")

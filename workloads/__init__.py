@@ -155,3 +155,42 @@ def preprocess_inputs(rows: int, width: int, heads: int, seed: int,
     target = np.exp(rng.uniform(np.log(dt_lo), np.log(dt_hi), size=heads))
     dt_bias = np.log(np.expm1(target)).astype(np.float32)  # inverse of log(1 + e^u)
     return {"projected": np.ascontiguousarray(projected), "dt_bias": dt_bias}
+
+
+def _inverse_softplus(y: np.ndarray) -> np.ndarray:
+    """u with log(1 + e^u) = y (input shaping for the packed projection)."""
+    y64 = np.asarray(y, dtype=np.float64)
+    return np.log(np.expm1(y64))
+
+
+def packed_projection(d: Dims, seed: int, dt_range=(1e-3, 0.1)) -> dict:
+    """A packed projection [B*L, 2I + 2GN + 3H + A] (I = H*P, rank one) whose
+    preprocess outputs follow the scan-input recipe of this module: z, x ~ N(0,1);
+    B, C standard normal (the preprocess RMS-normalises them); dt_raw such that
+    softplus(dt_raw) is uniform on dt_range (dt_bias = 0); A_raw such that
+    softplus(A_raw) is uniform on [1, 16]; trap = logistic(N(0,1)); angle ~ N(0, 0.1).
+    Also returns dt_bias (zeros) and the scan parameters c_bias, b_bias, d."""
+    rng = np.random.default_rng(seed)
+    B, L, H, G, P, N, A = d.B, d.L, d.H, d.groups, d.P, d.N, d.A
+    rows, I, M = B * L, H * P, G * N
+    f32 = np.float32
+    W = 2 * I + 2 * M + 3 * H + A
+    proj = np.empty((rows, W), dtype=f32)
+    off = 0
+    proj[:, off:off + I] = rng.standard_normal((rows, I), dtype=f32); off += I      # z
+    proj[:, off:off + I] = rng.standard_normal((rows, I), dtype=f32); off += I      # x
+    proj[:, off:off + M] = rng.standard_normal((rows, M), dtype=f32); off += M      # B
+    proj[:, off:off + M] = rng.standard_normal((rows, M), dtype=f32); off += M      # C
+    lo, hi = dt_range
+    proj[:, off:off + H] = _inverse_softplus(lo + (hi - lo) * rng.random((rows, H))); off += H
+    proj[:, off:off + H] = _inverse_softplus(1.0 + 15.0 * rng.random((rows, H))); off += H
+    proj[:, off:off + H] = _logistic(rng.standard_normal((rows, H), dtype=f32)); off += H
+    proj[:, off:off + A] = f32(0.1) * rng.standard_normal((rows, A), dtype=f32); off += A
+    assert off == W
+    return {
+        "projected": proj,
+        "dt_bias": np.zeros(H, dtype=f32),
+        "c_bias": (f32(0.02) * rng.standard_normal((H, N), dtype=f32)).astype(f32),
+        "b_bias": (f32(0.02) * rng.standard_normal((H, N), dtype=f32)).astype(f32),
+        "d": rng.standard_normal((H,), dtype=f32),
+    }
