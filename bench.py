@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated through the timed loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the oracle's timed sample")
+    ap.add_argument("--cpu-heads", type=int, default=24, help="heads in the oracle's timed sample")
     ap.add_argument("--no-parity", action="store_true")
     return ap.parse_args()
 

@@ -17,6 +17,43 @@ __device__ __forceinline__ floatx4 mfma16(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// exp(x) through the hardware exp2 (v_exp_f32): relative error about
+// |x| * 2^-23 from the log2(e) scaling, used where the result multiplies
+// terms that are themselves negligible once |x| is large.
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+
+// u * sigmoid(u) with the hardware exp2 and reciprocal (about 2 ulp).
+__device__ __forceinline__ float silu_fast(float u) {
+  return u * __builtin_amdgcn_rcpf(1.f + exp_fast(-u));
+}
+
+// Cross-lane helpers on DPP (register-to-register lane shifts; no LDS).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+// Inclusive prefix sum within each 32-lane half of the wave: shifts by
+// 1, 2, 4, 8 inside 16-lane rows, then lane 15 of rows 0 / 2 into rows 1 / 3.
+__device__ __forceinline__ float scan32_f(float v) {
+  v += dpp_f<0x111>(v);
+  v += dpp_f<0x112>(v);
+  v += dpp_f<0x114>(v);
+  v += dpp_f<0x118>(v);
+  v += dpp_f<0x142, 0xa>(v);
+  return v;
+}
+// Inclusive prefix sum over the whole wave (adds lane 31 into rows 2 and 3).
+__device__ __forceinline__ float scan64_f(float v) {
+  v = scan32_f(v);
+  v += dpp_f<0x143, 0xc>(v);
+  return v;
+}
+// Value of lane i + 1 (zero in lane 63).
+__device__ __forceinline__ float next_lane_f(float v) { return dpp_f<0x130>(v); }
+__device__ __forceinline__ float read_lane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 __device__ __forceinline__ float sigmoidf_acc(float u) {
   // 1 / (1 + e^-u) without overflow for large |u|.
   if (u >= 0.f) return 1.f / (1.f + expf(-u));
@@ -29,6 +66,59 @@ __device__ __forceinline__ float siluf_acc(float u) { return u * sigmoidf_acc(u)
 __device__ __forceinline__ float softplusf_acc(float u) {
   // max(u, 0) + log1p(e^-|u|): exact for large |u|, no overflow.
   return fmaxf(u, 0.f) + log1pf(expf(-fabsf(u)));
+}
+
+// sin and cos of x, accurate to a few ulp.  The argument is reduced by pi/2
+// (k = rint(x 2/pi), r = x - k pi/2) with pi/2 split into three float32
+// pieces applied by fused multiply-adds (Cody-Waite), or in float64 for
+// |x| >= 8192; then Taylor polynomials on |r| <= pi/4, whose truncation error
+// (below 1e-12) is far under float32 rounding.  The pieces of pi/2 come from
+// Machin's formula evaluated to 60 digits.
+__device__ __forceinline__ void sincos_acc(float x, float* s_out, float* c_out) {
+  float r;
+  int q;
+  if (fabsf(x) < 8192.f) {
+    const float k = rintf(x * 0x1.45f306p-1f);
+    r = fmaf(-k, 0x1.921fb6p+0f, x);
+    r = fmaf(-k, -0x1.777a5cp-25f, r);
+    r = fmaf(-k, -0x1.ee59dap-50f, r);
+    q = (int)k;
+  } else {
+    const double xd = (double)x;
+    const double kd = rint(xd * 0x1.45f306dc9c883p-1);
+    double rd = fma(-kd, 0x1.921fb54442d18p+0, xd);
+    rd = fma(-kd, 0x1.1a62633145c07p-54, rd);
+    r = (float)rd;
+    q = (int)(kd - 4.0 * floor(kd * 0.25));  // k mod 4 without integer overflow
+  }
+  const float r2 = r * r;
+  // sin r = r - r^3/3! + r^5/5! - ... ; cos r = 1 - r^2/2! + r^4/4! - ...
+  float sp = fmaf(r2, -1.f / 39916800.f, 1.f / 362880.f);
+  sp = fmaf(r2, sp, -1.f / 5040.f);
+  sp = fmaf(r2, sp, 1.f / 120.f);
+  sp = fmaf(r2, sp, -1.f / 6.f);
+  const float sn = fmaf(r * r2, sp, r);
+  float cp = fmaf(r2, 1.f / 479001600.f, -1.f / 3628800.f);
+  cp = fmaf(r2, cp, 1.f / 40320.f);
+  cp = fmaf(r2, cp, -1.f / 720.f);
+  cp = fmaf(r2, cp, 1.f / 24.f);
+  cp = fmaf(r2, cp, -0.5f);
+  const float cs = fmaf(r2, cp, 1.f);
+  switch (q & 3) {
+    case 0: *s_out = sn; *c_out = cs; break;
+    case 1: *s_out = cs; *c_out = -sn; break;
+    case 2: *s_out = -sn; *c_out = -cs; break;
+    default: *s_out = -cs; *c_out = sn; break;
+  }
+}
+
+// Workgroup barrier for hand-offs through LDS only.  It waits for this wave's
+// LDS operations (lgkmcnt) and then meets the other waves, but unlike
+// __syncthreads() it does not wait for outstanding global loads (vmcnt), so
+// prefetches issued before it stay in flight.  The memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ floatx4 lds_read4(const float* p) {

@@ -16,17 +16,20 @@
 // h_previous), here computed in registers and LDS instead of memory.
 //
 // Work decomposition
-//   * A chunk holds QV "virtual rows" v = t * RS + r (token t, rank r < R,
-//     RS = R rounded up to a power of two so that no token's rows straddle a
-//     16-row MFMA tile; rows with r >= R stay zero).  SISO has R = RS = 1,
-//     MIMO stacks its ranks inside the chunk.
-//   * One workgroup runs one (batch, head, sequence segment); one wave per
-//     16-wide slice of head_dim.  The state h'^T [N x P] lives in MFMA
-//     accumulator registers for the whole segment: wave w keeps the 16x16
-//     tiles (n-block, p-block w).
+//   * A chunk holds QV = 32 "virtual rows" v = t * RS + r (token t, rank
+//     r < R, RS = R rounded up to a power of two so that no token's rows
+//     straddle a 16-row MFMA tile; rows with r >= R stay zero).  SISO has
+//     R = RS = 1, MIMO stacks its ranks inside the chunk.
+//   * One workgroup runs one (batch, head, sequence segment).  Wave w < PT
+//     owns the 16 head_dim columns [16w, 16w+16) and keeps the state
+//     h'^T [N x 16] of those columns in MFMA accumulator registers for the
+//     whole segment; at least four waves share the loads and VALU work.
 //   * Intra-chunk S = Q K^T, the decay/trapezoid mask, M X, the carried-state
 //     read Q h'^T and the state update K^T (w X) all run on
 //     v_mfma_f32_16x16x4_f32.
+//   * The next chunk's x, B, C, angle and scalars are loaded into registers
+//     while the current chunk's MFMA work runs; z is loaded at the start of
+//     the chunk that uses it.  The cumulative angle is a 32-lane scan.
 //   * Sequence segments: a first pass computes each segment's end state
 //     from a zero entry (plus its decay product and angle increment) into
 //     the workspace; the main pass folds the earlier segments' summaries
@@ -42,6 +45,7 @@ namespace {
 constexpr int kAux = 68;        // per segment summary: angle increment [<=64], decay at 64
 constexpr int kAuxDecay = 64;
 constexpr float kNormEps = 1.0e-5f;  // MIMO output-norm epsilon of the MIMO push constants
+constexpr int kQV = 32;         // virtual rows per chunk
 
 struct ScanKParams {
   const float *c, *b, *x, *z, *adt, *dt, *trap, *angle, *c_bias, *b_bias, *d;
@@ -50,18 +54,55 @@ struct ScanKParams {
   float* ws_state;  // [B*H][nseg-1][PT*NT tiles][64 lanes][4]
   float* ws_aux;    // [B*H][nseg-1][kAux]
   int B, L, H, G, P, N, A, R;
-  int has_z, has_d, has_norm, mimo;
+  int has_z, has_d, has_norm;
   int NT, PT;       // 16-wide blocks of N and P
   int RS, rs_log2;  // rank stride of the virtual rows (power of two >= R)
   int Qt;           // tokens per chunk (QV / RS)
   int seg_len, nseg;
   // LDS layout (float offsets) and row strides
-  int o_ql, o_kt, o_xt, o_ml, o_yl, o_cs, o_sc, o_run, lds_floats;
-  int ks, ts, ys;
+  int o_ql, o_kl, o_xl, o_ml, o_yl, o_cs, o_bias, o_mimo, o_sc, o_run, lds_floats;
+  int ks, xs, ms, ys;
 };
 
-template <int QV, bool FULL>
+template <int VEC>
+struct VecOf;
+template <>
+struct VecOf<4> {
+  using T = floatx4;
+};
+template <>
+struct VecOf<1> {
+  using T = float;
+};
+
+template <int VEC>
+__device__ __forceinline__ typename VecOf<VEC>::T vload(const float* p) {
+  if constexpr (VEC == 4)
+    return *reinterpret_cast<const floatx4*>(p);
+  else
+    return *p;
+}
+template <int VEC>
+__device__ __forceinline__ void vstore(float* p, const typename VecOf<VEC>::T& v) {
+  if constexpr (VEC == 4)
+    *reinterpret_cast<floatx4*>(p) = v;
+  else
+    *p = v;
+}
+__device__ __forceinline__ float comp(const floatx4& v, int e) { return v[e]; }
+__device__ __forceinline__ float comp(const float& v, int) { return v; }
+__device__ __forceinline__ void set_comp(floatx4& v, int e, float x) { v[e] = x; }
+__device__ __forceinline__ void set_comp(float& v, int, float x) { v = x; }
+
+template <int VEC, bool FULL, bool MIMO>
 __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
+  using vec_t = typename VecOf<VEC>::T;
+  constexpr int QV = kQV;
+  constexpr int TB = QV / 16;
+  constexpr int KX = 8 / VEC;   // x / z items per thread (Qt*P/VEC <= 8/VEC * threads)
+  constexpr int KB = 16 / VEC;  // B / C row items per thread (QV*N/VEC <= 16/VEC * threads)
+  constexpr int KA = 4;         // angle values per lane (launch gives >= A/8 waves)
+  constexpr int KZM = 8;        // tokens per wave in the MIMO epilogue
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -84,15 +125,24 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
   const int R = p.R;
   const int RG = R * p.G;
   const int Qt = p.Qt;
-  const int RS = p.RS, rsl = p.rs_log2;
+  const int rsl = p.rs_log2;
+  const int N = p.N, P = p.P, A = p.A;
+  const int ks = p.ks, xs = p.xs, ms = p.ms, ys = p.ys;
+  const bool mma_wave = wave < p.PT;
 
-  float* Ql = lds + p.o_ql;   // [QV][ks]   rotated C (+bias)
-  float* Kt = lds + p.o_kt;   // [NT*16][ts] rotated B (+bias), transposed
-  float* Xt = lds + p.o_xt;   // [PT*16][ts] per-rank x, transposed
-  float* Ml = lds + p.o_ml;   // [QV][ts]   masked S
-  float* Yl = lds + p.o_yl;   // [QV][ys]   raw y
-  float* CS = lds + p.o_cs;   // [Qt][64] theta, then cos; [Qt][64] sin after it
-  float* SN = CS + QV * 64;
+  float* Ql = lds + p.o_ql;   // [QV][ks] C (+bias), pairs rotated in place   (main pass)
+  float* Kl = lds + p.o_kl;   // [QV][ks] B (+bias), pairs rotated in place
+  float* Xl = lds + p.o_xl;   // [QV][xs] per-rank x
+  float* Ml = lds + p.o_ml;   // [QV][ms] masked S                             (main pass)
+  float* Yl = lds + p.o_yl;   // [QV][ys] raw y                                (main pass)
+  float* CS = lds + p.o_cs;   // [64] cos / [64] sin for the entry-state fold
+  float* SN = CS + 64;
+  float* bbL = lds + p.o_bias;  // [R][N] b_bias of this head; cbL follows
+  float* cbL = bbL + R * N;
+  float* mxL = lds + p.o_mimo;  // [R][P] mimo_x, mimo_z, mimo_o, then norm_weight [P]
+  float* mzL = mxL + R * P;
+  float* moL = mzL + R * P;
+  float* nwL = moL + R * P;
   float* sc_cum = lds + p.o_sc;
   float* sc_ecum = sc_cum + QV;
   float* sc_gam = sc_ecum + QV;
@@ -103,6 +153,20 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
 
   for (int i = tid; i < p.lds_floats; i += nthreads) lds[i] = 0.f;
   __syncthreads();
+  for (int i = tid; i < R * N; i += nthreads) {
+    bbL[i] = p.b_bias[(size_t)h * R * N + i];
+    if (FULL) cbL[i] = p.c_bias[(size_t)h * R * N + i];
+  }
+  if constexpr (FULL && MIMO) {
+    for (int i = tid; i < R * P; i += nthreads) {
+      mxL[i] = p.mimo_x[(size_t)h * R * P + i];
+      mzL[i] = p.mimo_z[(size_t)h * R * P + i];
+      moL[i] = p.mimo_o[(size_t)h * R * P + i];
+    }
+    for (int i = tid; i < P; i += nthreads) nwL[i] = p.norm_weight[(size_t)h * P + i];
+  } else if constexpr (MIMO) {
+    for (int i = tid; i < R * P; i += nthreads) mxL[i] = p.mimo_x[(size_t)h * R * P + i];
+  }
 
   const int p0 = wave * 16;
   floatx4 Hacc[8];
@@ -116,84 +180,135 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
   // before i (the keys it holds are rot(theta_i + local) = rot(theta_i) rot(local)).
   // U_i passes through LDS in [p][n] layout for the pair rotation.
   if (FULL && seg > 0) {
+    __syncthreads();
     float* Ub = lds;  // [PT*16][NT*16 + 4], overlays the chunk buffers (unused yet)
     const int us = p.NT * 16 + 4;
     for (int i = 0; i < seg; ++i) {
       const size_t si = (size_t)bh * (p.nseg - 1) + i;
       const float* aux = p.ws_aux + si * kAux;
       const float* st = p.ws_state + si * (size_t)(p.PT * p.NT) * 256;
+      if (mma_wave) {
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        if (nb < p.NT) {
-          const floatx4 u = *reinterpret_cast<const floatx4*>(st + ((wave * p.NT + nb) * 64 + lane) * 4);
+        for (int nb = 0; nb < 8; ++nb) {
+          if (nb < p.NT) {
+            const floatx4 u = *reinterpret_cast<const floatx4*>(st + ((wave * p.NT + nb) * 64 + lane) * 4);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) Ub[(p0 + l16) * us + nb * 16 + 4 * lq + r] = u[r];
+            for (int r = 0; r < 4; ++r) Ub[(p0 + l16) * us + nb * 16 + 4 * lq + r] = u[r];
+          }
         }
       }
-      if (tid < p.A) {
+      if (tid < A) {
         float sn, cs;
-        sincosf(run[tid], &sn, &cs);
+        sincos_acc(run[tid], &sn, &cs);
         CS[tid] = cs;
         SN[tid] = sn;
       }
       __syncthreads();
-      for (int e = tid; e < p.PT * 16 * p.A; e += nthreads) {
-        const int pp = e / p.A, a = e - pp * p.A;
-        const float u0 = Ub[pp * us + a], u1 = Ub[pp * us + a + p.A];
+      for (int e = tid; e < p.PT * 16 * A; e += nthreads) {
+        const int pp = e / A, a = e - pp * A;
+        const float u0 = Ub[pp * us + a], u1 = Ub[pp * us + a + A];
         Ub[pp * us + a] = u0 * CS[a] - u1 * SN[a];
-        Ub[pp * us + a + p.A] = u0 * SN[a] + u1 * CS[a];
+        Ub[pp * us + a + A] = u0 * SN[a] + u1 * CS[a];
       }
       __syncthreads();
       const float dec = aux[kAuxDecay];
+      if (mma_wave) {
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        if (nb < p.NT) {
+        for (int nb = 0; nb < 8; ++nb) {
+          if (nb < p.NT) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            Hacc[nb][r] = fmaf(dec, Hacc[nb][r], Ub[(p0 + l16) * us + nb * 16 + 4 * lq + r]);
+            for (int r = 0; r < 4; ++r)
+              Hacc[nb][r] = fmaf(dec, Hacc[nb][r], Ub[(p0 + l16) * us + nb * 16 + 4 * lq + r]);
+          }
         }
       }
-      if (tid < p.A) run[tid] += aux[tid];
+      if (tid < A) run[tid] += aux[tid];
       __syncthreads();
     }
     for (int i = tid; i < p.PT * 16 * us; i += nthreads) Ub[i] = 0.f;  // restore the zero padding
   }
   float seg_decay = 1.f;  // thread 0: product of chunk decays (summary pass)
-  __syncthreads();
 
-  const int items_row = p.N - p.A;  // A rotated pairs + (N - 2A) plain coordinates per row
+  // ---- register prefetch of one chunk's global operands -------------------
+  // Addresses are a wave-uniform chunk base (scalar registers) plus a 32-bit
+  // per-lane offset, so loads use the scalar-base + vector-offset form.
+  const int xrow = P / VEC;   // x items per token
+  const int brow = N / VEC;   // B / C items per virtual row
+  const int tokx = p.H * P;   // x / z / out elements per token
+  const int tokb = RG * N;    // B / C elements per token
+  vec_t xr[KX], br[KB], cr[KB];
+  float angr[KA];
+  float s_dt = 0.f, s_adt = 0.f, s_trap = 0.f;
+
+  auto prefetch = [&](int cs) {
+    const int nv = min(Qt, t_end - cs);
+    const float* xbase = p.x + (((size_t)b * p.L + cs) * p.H + h) * P;
+    const float* bbase = p.b + ((size_t)b * p.L + cs) * tokb;
+    const float* cbase = p.c + ((size_t)b * p.L + cs) * tokb;
+    const float* abase = p.angle + ((size_t)b * p.L + cs) * A;
+#pragma unroll
+    for (int k = 0; k < KX; ++k) {
+      const int idx = tid + k * nthreads;
+      const int t = idx / xrow, pv = idx - t * xrow;
+      vec_t v{};
+      if (idx < Qt * xrow && t < nv) v = vload<VEC>(xbase + (uint32_t)(t * tokx + pv * VEC));
+      xr[k] = v;
+    }
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int idx = tid + k * nthreads;
+      const int u = idx / brow, j = idx - u * brow;
+      const int t = u / R, r = u - t * R;
+      vec_t v0{}, w0{};
+      if (idx < Qt * R * brow && t < nv) {
+        const uint32_t off = (uint32_t)(t * tokb + (r * p.G + g) * N + j * VEC);
+        v0 = vload<VEC>(bbase + off);
+        if (FULL) w0 = vload<VEC>(cbase + off);
+      }
+      br[k] = v0;
+      cr[k] = w0;
+    }
+#pragma unroll
+    for (int i = 0; i < KA; ++i) {
+      const int a = 2 * (i * nwaves + wave) + (lane >> 5);
+      const int t = lane & 31;
+      angr[i] = (a < A && t < nv) ? abase[(uint32_t)(t * A + a)] : 0.f;
+    }
+    if (wave == 0) {
+      const bool okl = lane <= Qt && cs + lane < p.L;
+      const size_t sbase = ((size_t)b * p.L + cs) * p.H + h;
+      const uint32_t so = (uint32_t)(lane * p.H);
+      s_dt = okl ? p.dt[sbase + so] : 0.f;
+      s_trap = okl ? p.trap[sbase + so] : 0.f;
+      s_adt = lane < nv ? p.adt[sbase + so] : 0.f;
+    }
+  };
+
+  prefetch(t_begin);
+  __syncthreads();
 
   for (int c0 = t_begin; c0 < t_end; c0 += Qt) {
     const int nvalid = min(Qt, t_end - c0);
 
-    // ---- per-token scalars (wave 0; lane = token) -------------------------
+    // ---- P0: scalars (wave 0, lane = token); x, B, C rows into LDS; z loads --
     if (wave == 0) {
       const int t = lane;
-      float adt_v = 0.f, dt_v = 0.f, gam = 0.f, scl = 0.f;
-      if (t < nvalid) {
-        const size_t idx = ((size_t)b * p.L + c0 + t) * p.H + h;
-        dt_v = p.dt[idx];
-        adt_v = p.adt[idx];
-        gam = sigmoidf_acc(p.trap[idx]) * dt_v;
-        scl = gam;
-        if (c0 + t + 1 < p.L) {
-          const size_t idn = idx + p.H;
-          scl = gam + (1.f - sigmoidf_acc(p.trap[idn])) * p.dt[idn];
-        }
-      }
-      float cum = adt_v;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float v = __shfl_up(cum, off, 64);
-        if (lane >= off) cum += v;
-      }
-      const float cum_last = __shfl(cum, 63, 64);  // padding lanes add zero
+      const float dt_n = next_lane_f(s_dt);
+      const float tr_n = next_lane_f(s_trap);
+      const bool ok = t < nvalid;
+      const float dt_v = ok ? s_dt : 0.f;
+      const float adt_v = ok ? s_adt : 0.f;
+      const float gam = ok ? sigmoidf_acc(s_trap) * dt_v : 0.f;
+      float scl = gam;
+      if (ok && c0 + t + 1 < p.L) scl = gam + (1.f - sigmoidf_acc(tr_n)) * dt_n;
+      const float cum = scan64_f(adt_v);
+      const float cum_last = read_lane_f(cum, 63);  // padding lanes add zero
       if (t < Qt) {
         sc_cum[t] = cum;
         sc_ecum[t] = expf(cum);
         sc_gam[t] = gam;
         sc_scl[t] = scl;
-        sc_w[t] = t < nvalid ? expf(cum_last - cum) * scl : 0.f;
+        sc_w[t] = ok ? expf(cum_last - cum) * scl : 0.f;
         sc_dt[t] = dt_v;
       }
       if (lane == 0) {
@@ -202,101 +317,118 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
         seg_decay *= dec;
       }
     }
-    __syncthreads();
-
-    // ---- cumulative angle per token (thread a < A walks the chunk) ---------
-    if (tid < p.A) {
-      float th = run[tid];
-      for (int t = 0; t < nvalid; ++t) {
-        th = fmaf(sc_dt[t], p.angle[((size_t)b * p.L + c0 + t) * p.A + tid], th);
-        CS[t * 64 + tid] = th;
+#pragma unroll
+    for (int k = 0; k < KX; ++k) {
+      const int idx = tid + k * nthreads;
+      if (idx < Qt * xrow) {
+        const int t = idx / xrow, pv = idx - t * xrow;
+        if constexpr (MIMO) {
+          for (int r = 0; r < R; ++r) {
+            vec_t v = xr[k];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) set_comp(v, e, comp(v, e) * mxL[r * P + pv * VEC + e]);
+            vstore<VEC>(Xl + ((t << rsl) + r) * xs + pv * VEC, v);
+          }
+        } else {
+          vstore<VEC>(Xl + t * xs + pv * VEC, xr[k]);
+        }
       }
-      run[tid] = th;
     }
-    __syncthreads();
-    for (int e = tid; e < nvalid * p.A; e += nthreads) {
-      const int t = e / p.A, a = e - t * p.A;
-      float s, co;
-      sincosf(CS[t * 64 + a], &s, &co);
-      CS[t * 64 + a] = co;
-      SN[t * 64 + a] = s;
-    }
-    // ---- x rows (per rank) into Xt[p][v] ----------------------------------
-    for (int e = tid; e < Qt * R * p.P; e += nthreads) {
-      const int u = e / p.P, pp = e - u * p.P;
-      const int t = u / R, r = u - t * R;
-      const int v = (t << rsl) + r;
-      float val = 0.f;
-      if (t < nvalid) {
-        val = p.x[(((size_t)b * p.L + c0 + t) * p.H + h) * p.P + pp];
-        if (p.mimo) val *= p.mimo_x[((size_t)h * R + r) * p.P + pp];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int idx = tid + k * nthreads;
+      if (idx < Qt * R * brow) {
+        const int u = idx / brow, j = idx - u * brow;
+        const int t = u / R, r = u - t * R;
+        const int v = (t << rsl) + r;
+        const bool ok = t < nvalid;
+        vec_t kv = br[k], qv = cr[k];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          set_comp(kv, e, ok ? comp(kv, e) + bbL[r * N + j * VEC + e] : 0.f);
+          if (FULL) set_comp(qv, e, ok ? comp(qv, e) + cbL[r * N + j * VEC + e] : 0.f);
+        }
+        vstore<VEC>(Kl + v * ks + j * VEC, kv);
+        if (FULL) vstore<VEC>(Ql + v * ks + j * VEC, qv);
       }
-      Xt[pp * p.ts + v] = val;
     }
-    __syncthreads();
+    vec_t zr[KX];
+    float zm[KZM][2];
+    const size_t cbase_tok = (((size_t)b * p.L + c0) * p.H + h) * P;  // x / z / out at token c0
+    const float* zbase = p.z + cbase_tok;
+    if constexpr (FULL && !MIMO) {
+#pragma unroll
+      for (int k = 0; k < KX; ++k) {
+        const int idx = tid + k * nthreads;
+        const int t = idx / xrow, pv = idx - t * xrow;
+        vec_t v{};
+        if (p.has_z && idx < Qt * xrow && t < nvalid) v = vload<VEC>(zbase + (uint32_t)(t * tokx + pv * VEC));
+        zr[k] = v;
+      }
+    }
+    if constexpr (FULL && MIMO) {
+#pragma unroll
+      for (int i = 0; i < KZM; ++i) {
+        const int t = wave + i * nwaves;
+        const uint32_t ob = (uint32_t)(t * tokx);
+        const bool ok = p.has_z && t < nvalid;
+        zm[i][0] = (ok && lane < P) ? zbase[ob + lane] : 0.f;
+        zm[i][1] = (ok && lane + 64 < P) ? zbase[ob + lane + 64] : 0.f;
+      }
+    }
+    lds_barrier();
 
-    // ---- rotated keys / queries -------------------------------------------
-    for (int e = tid; e < Qt * R * items_row; e += nthreads) {
-      const int u = e / items_row, j = e - u * items_row;
-      const int t = u / R, r = u - t * R;
-      const int v = (t << rsl) + r;
-      const bool ok = t < nvalid;
-      const size_t row = (((size_t)b * p.L + c0 + t) * RG + r * p.G + g) * p.N;
-      const size_t brow = ((size_t)h * R + r) * p.N;
-      if (j < p.A) {
-        const int a = j;
-        float k0 = 0.f, k1 = 0.f, q0 = 0.f, q1 = 0.f;
-        if (ok) {
-          const float co = CS[t * 64 + a], s = SN[t * 64 + a];
-          const float b0 = p.b[row + a] + p.b_bias[brow + a];
-          const float b1 = p.b[row + a + p.A] + p.b_bias[brow + a + p.A];
-          k0 = b0 * co - b1 * s;
-          k1 = b0 * s + b1 * co;
+    // ---- P2: cumulative angle (32-lane scans), cos / sin, and the rotation of
+    //      the pairs (a, a + A) of every rank's key and query row, in place -----
+#pragma unroll
+    for (int i = 0; i < KA; ++i) {
+      const int am = 2 * (i * nwaves + wave);
+      if (am >= A) break;  // wave-uniform
+      const int a = am + (lane >> 5);
+      const int t = lane & 31;
+      const bool ok = a < A && t < nvalid;
+      const float phi = scan32_f(ok ? sc_dt[t] * angr[i] : 0.f);
+      if (ok) {
+        const float th = run[a] + phi;
+        float sn, co;
+        sincos_acc(th, &sn, &co);
+        for (int r = 0; r < R; ++r) {
+          float* kr = Kl + ((t << rsl) + r) * ks;
+          const float k0 = kr[a], k1 = kr[a + A];
+          kr[a] = k0 * co - k1 * sn;
+          kr[a + A] = k0 * sn + k1 * co;
           if (FULL) {
-            const float e0 = p.c[row + a] + p.c_bias[brow + a];
-            const float e1 = p.c[row + a + p.A] + p.c_bias[brow + a + p.A];
-            q0 = e0 * co - e1 * s;
-            q1 = e0 * s + e1 * co;
+            float* qr = Ql + ((t << rsl) + r) * ks;
+            const float q0 = qr[a], q1 = qr[a + A];
+            qr[a] = q0 * co - q1 * sn;
+            qr[a + A] = q0 * sn + q1 * co;
           }
         }
-        Kt[a * p.ts + v] = k0;
-        Kt[(a + p.A) * p.ts + v] = k1;
-        if (FULL) {
-          Ql[v * p.ks + a] = q0;
-          Ql[v * p.ks + a + p.A] = q1;
-        }
-      } else {
-        const int n = j + p.A;
-        float k = 0.f, q = 0.f;
-        if (ok) {
-          k = p.b[row + n] + p.b_bias[brow + n];
-          if (FULL) q = p.c[row + n] + p.c_bias[brow + n];
-        }
-        Kt[n * p.ts + v] = k;
-        if (FULL) Ql[v * p.ks + n] = q;
+        if (t == nvalid - 1) run[a] = th;
       }
     }
-    __syncthreads();
+    // The next chunk's loads go out now and land during this chunk's MFMA work.
+    if (c0 + Qt < t_end) prefetch(c0 + Qt);
+    lds_barrier();
 
-    constexpr int TB = QV / 16;
     if constexpr (FULL) {
-      // ---- S = Q K^T on lower 16x16 tiles, masked -------------------------
+      // ---- P4: S = Q K^T on lower 16x16 tiles, masked ------------------------
       constexpr int NPAIRS = TB * (TB + 1) / 2;
       for (int pr = wave; pr < NPAIRS; pr += nwaves) {
         int tb = 0, sb = pr;
         while (sb > tb) { sb -= tb + 1; ++tb; }
         floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-        const float* qa = Ql + (tb * 16 + l16) * p.ks + 4 * lq;
-        const float* kb = Kt + (4 * lq) * p.ts + sb * 16 + l16;
+        const float* qa = Ql + (tb * 16 + l16) * ks + 4 * lq;
+        const float* kb = Kl + (sb * 16 + l16) * ks + 4 * lq;
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
           if (nb < p.NT) {
             const floatx4 a4 = lds_read4(qa + nb * 16);
-            const float* kbn = kb + nb * 16 * p.ts;
-            acc = mfma16(a4.x, kbn[0], acc);
-            acc = mfma16(a4.y, kbn[p.ts], acc);
-            acc = mfma16(a4.z, kbn[2 * p.ts], acc);
-            acc = mfma16(a4.w, kbn[3 * p.ts], acc);
+            const floatx4 b4 = lds_read4(kb + nb * 16);
+            acc = mfma16(a4.x, b4.x, acc);
+            acc = mfma16(a4.y, b4.y, acc);
+            acc = mfma16(a4.z, b4.z, acc);
+            acc = mfma16(a4.w, b4.w, acc);
           }
         }
         const int vs = sb * 16 + l16;
@@ -307,120 +439,141 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
           const int vt = tb * 16 + 4 * lq + r;
           const int tt = vt >> rsl;
           float m = 0.f;
-          if (ts_ < tt) m = acc[r] * (expf(sc_cum[tt] - cum_s) * scl_s);
+          if (ts_ < tt) m = acc[r] * (exp_fast(sc_cum[tt] - cum_s) * scl_s);
           else if (ts_ == tt) m = acc[r] * sc_gam[tt];
-          Ml[vt * p.ts + vs] = m;
+          Ml[vt * ms + vs] = m;
         }
       }
-      __syncthreads();
-
-      // ---- Y = M X + diag(exp(cum)) Q h'^T  (this wave's 16 columns) -------
-      for (int tb = 0; tb < TB; ++tb) {
-        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-        for (int sb = 0; sb <= tb; ++sb) {
-          const floatx4 a4 = lds_read4(Ml + (tb * 16 + l16) * p.ts + sb * 16 + 4 * lq);
-          const floatx4 b4 = lds_read4(Xt + (p0 + l16) * p.ts + sb * 16 + 4 * lq);
-          acc = mfma16(a4.x, b4.x, acc);
-          acc = mfma16(a4.y, b4.y, acc);
-          acc = mfma16(a4.z, b4.z, acc);
-          acc = mfma16(a4.w, b4.w, acc);
-        }
-        const float ec = sc_ecum[(tb * 16 + l16) >> rsl];
-        const float* qa = Ql + (tb * 16 + l16) * p.ks + 4 * lq;
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          if (nb < p.NT) {
-            const floatx4 a4 = lds_read4(qa + nb * 16) * ec;
-            acc = mfma16(a4.x, Hacc[nb].x, acc);
-            acc = mfma16(a4.y, Hacc[nb].y, acc);
-            acc = mfma16(a4.z, Hacc[nb].z, acc);
-            acc = mfma16(a4.w, Hacc[nb].w, acc);
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Yl[(tb * 16 + 4 * lq + r) * p.ys + p0 + l16] = acc[r];
-      }
+      lds_barrier();
     }
 
-    // ---- state update h' = decay h' + K^T (w X) ---------------------------
-    {
+    if (mma_wave) {
+      if constexpr (FULL) {
+        // ---- P5a: Y = M X + diag(exp(cum)) Q h'^T (this wave's 16 columns) ---
+        for (int tb = 0; tb < TB; ++tb) {
+          floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+          for (int sb = 0; sb <= tb; ++sb) {
+            const floatx4 a4 = lds_read4(Ml + (tb * 16 + l16) * ms + sb * 16 + 4 * lq);
+            const float* xc = Xl + (sb * 16 + 4 * lq) * xs + p0 + l16;
+            acc = mfma16(a4.x, xc[0], acc);
+            acc = mfma16(a4.y, xc[xs], acc);
+            acc = mfma16(a4.z, xc[2 * xs], acc);
+            acc = mfma16(a4.w, xc[3 * xs], acc);
+          }
+          const float ec = sc_ecum[(tb * 16 + l16) >> rsl];
+          const float* qa = Ql + (tb * 16 + l16) * ks + 4 * lq;
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            if (nb < p.NT) {
+              const floatx4 a4 = lds_read4(qa + nb * 16) * ec;
+              acc = mfma16(a4.x, Hacc[nb].x, acc);
+              acc = mfma16(a4.y, Hacc[nb].y, acc);
+              acc = mfma16(a4.z, Hacc[nb].z, acc);
+              acc = mfma16(a4.w, Hacc[nb].w, acc);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Yl[(tb * 16 + 4 * lq + r) * ys + p0 + l16] = acc[r];
+        }
+      }
+      // ---- P5b: state update h' = decay h' + K^T (w X) ------------------------
       const float dec = run[64];
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) Hacc[nb] *= dec;
       for (int sb = 0; sb < TB; ++sb) {
-        floatx4 xw = lds_read4(Xt + (p0 + l16) * p.ts + sb * 16 + 4 * lq);
         const int v0 = sb * 16 + 4 * lq;
-        xw.x *= sc_w[(v0 + 0) >> rsl];
-        xw.y *= sc_w[(v0 + 1) >> rsl];
-        xw.z *= sc_w[(v0 + 2) >> rsl];
-        xw.w *= sc_w[(v0 + 3) >> rsl];
+        const float* xc = Xl + v0 * xs + p0 + l16;
+        const float xw0 = xc[0] * sc_w[(v0 + 0) >> rsl];
+        const float xw1 = xc[xs] * sc_w[(v0 + 1) >> rsl];
+        const float xw2 = xc[2 * xs] * sc_w[(v0 + 2) >> rsl];
+        const float xw3 = xc[3 * xs] * sc_w[(v0 + 3) >> rsl];
+        const float* kc = Kl + v0 * ks + l16;
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
           if (nb < p.NT) {
-            const floatx4 a4 = lds_read4(Kt + (nb * 16 + l16) * p.ts + sb * 16 + 4 * lq);
-            Hacc[nb] = mfma16(a4.x, xw.x, Hacc[nb]);
-            Hacc[nb] = mfma16(a4.y, xw.y, Hacc[nb]);
-            Hacc[nb] = mfma16(a4.z, xw.z, Hacc[nb]);
-            Hacc[nb] = mfma16(a4.w, xw.w, Hacc[nb]);
+            Hacc[nb] = mfma16(kc[nb * 16], xw0, Hacc[nb]);
+            Hacc[nb] = mfma16(kc[ks + nb * 16], xw1, Hacc[nb]);
+            Hacc[nb] = mfma16(kc[2 * ks + nb * 16], xw2, Hacc[nb]);
+            Hacc[nb] = mfma16(kc[3 * ks + nb * 16], xw3, Hacc[nb]);
           }
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- epilogue: D skip, gate, MIMO norm and rank mix; one wave per token
-    if constexpr (FULL) {
+    // ---- P6: epilogue ---------------------------------------------------------
+    if constexpr (FULL && !MIMO) {
+      // out = (y + D x) * silu(z), VEC-wide and coalesced along head_dim
       const float dh = p.has_d ? p.d[h] : 0.f;
-      for (int t = wave; t < nvalid; t += nwaves) {
-        const size_t ob = (((size_t)b * p.L + c0 + t) * p.H + h) * p.P;
+#pragma unroll
+      for (int k = 0; k < KX; ++k) {
+        const int idx = tid + k * nthreads;
+        const int t = idx / xrow, pv = idx - t * xrow;
+        if (idx < Qt * xrow && t < nvalid) {
+          vec_t y = vload<VEC>(Yl + t * ys + pv * VEC);
+          const vec_t xv = vload<VEC>(Xl + t * xs + pv * VEC);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            float v = comp(y, e);
+            if (p.has_d) v = fmaf(dh, comp(xv, e), v);
+            if (p.has_z) v *= silu_fast(comp(zr[k], e));
+            set_comp(y, e, v);
+          }
+          vstore<VEC>(p.out + cbase_tok + (uint32_t)(t * tokx + pv * VEC), y);
+        }
+      }
+      lds_barrier();
+    }
+    if constexpr (FULL && MIMO) {
+      // per rank: D skip, gate silu(z * mimo_z), optional RMS norm over P,
+      // then the mimo_o-weighted sum over ranks; one wave per token
+      const float dh = p.has_d ? p.d[h] : 0.f;
+      const int pa = lane, pb = lane + 64;
+#pragma unroll
+      for (int i = 0; i < KZM; ++i) {
+        const int t = wave + i * nwaves;
+        if (t >= nvalid) break;  // wave-uniform
         float o0 = 0.f, o1 = 0.f;
-        const int pa = lane, pb = lane + 64;
-        const float z0 = (p.has_z && pa < p.P) ? p.z[ob + pa] : 0.f;
-        const float z1 = (p.has_z && pb < p.P) ? p.z[ob + pb] : 0.f;
         for (int r = 0; r < R; ++r) {
           const int v = (t << rsl) + r;
           float y0 = 0.f, y1 = 0.f;
-          if (pa < p.P) {
-            y0 = Yl[v * p.ys + pa];
-            if (p.has_d) y0 = fmaf(dh, Xt[pa * p.ts + v], y0);
-            if (p.has_z) y0 *= siluf_acc(p.mimo ? z0 * p.mimo_z[((size_t)h * R + r) * p.P + pa] : z0);
+          if (pa < P) {
+            y0 = Yl[v * ys + pa];
+            if (p.has_d) y0 = fmaf(dh, Xl[v * xs + pa], y0);
+            if (p.has_z) y0 *= silu_fast(zm[i][0] * mzL[r * P + pa]);
           }
-          if (pb < p.P) {
-            y1 = Yl[v * p.ys + pb];
-            if (p.has_d) y1 = fmaf(dh, Xt[pb * p.ts + v], y1);
-            if (p.has_z) y1 *= siluf_acc(p.mimo ? z1 * p.mimo_z[((size_t)h * R + r) * p.P + pb] : z1);
+          if (pb < P) {
+            y1 = Yl[v * ys + pb];
+            if (p.has_d) y1 = fmaf(dh, Xl[v * xs + pb], y1);
+            if (p.has_z) y1 *= silu_fast(zm[i][1] * mzL[r * P + pb]);
           }
           if (p.has_norm) {
-            float ss = y0 * y0 + y1 * y1;
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-            const float inv = 1.f / sqrtf(ss / (float)p.P + kNormEps);
-            if (pa < p.P) y0 = y0 * inv * p.norm_weight[(size_t)h * p.P + pa];
-            if (pb < p.P) y1 = y1 * inv * p.norm_weight[(size_t)h * p.P + pb];
+            const float ss = read_lane_f(scan64_f(y0 * y0 + y1 * y1), 63);
+            const float inv = 1.f / sqrtf(ss / (float)P + kNormEps);
+            if (pa < P) y0 = y0 * inv * nwL[pa];
+            if (pb < P) y1 = y1 * inv * nwL[pb];
           }
-          if (p.mimo) {
-            if (pa < p.P) o0 = fmaf(p.mimo_o[((size_t)h * R + r) * p.P + pa], y0, o0);
-            if (pb < p.P) o1 = fmaf(p.mimo_o[((size_t)h * R + r) * p.P + pb], y1, o1);
-          } else {
-            o0 = y0;
-            o1 = y1;
-          }
+          if (pa < P) o0 = fmaf(moL[r * P + pa], y0, o0);
+          if (pb < P) o1 = fmaf(moL[r * P + pb], y1, o1);
         }
-        if (pa < p.P) p.out[ob + pa] = o0;
-        if (pb < p.P) p.out[ob + pb] = o1;
+        float* ob = p.out + cbase_tok + (uint32_t)(t * tokx);
+        if (pa < P) ob[pa] = o0;
+        if (pb < P) ob[pb] = o1;
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
 
   if constexpr (!FULL) {
     const size_t si = (size_t)bh * (p.nseg - 1) + seg;
     float* st = p.ws_state + si * (size_t)(p.PT * p.NT) * 256;
+    if (mma_wave) {
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-      if (nb < p.NT) *reinterpret_cast<floatx4*>(st + ((wave * p.NT + nb) * 64 + lane) * 4) = Hacc[nb];
+      for (int nb = 0; nb < 8; ++nb)
+        if (nb < p.NT) *reinterpret_cast<floatx4*>(st + ((wave * p.NT + nb) * 64 + lane) * 4) = Hacc[nb];
+    }
     float* aux = p.ws_aux + si * kAux;
-    if (tid < p.A) aux[tid] = run[tid];
+    if (tid < A) aux[tid] = run[tid];
     if (tid == 0) aux[kAuxDecay] = seg_decay;
   }
 }
@@ -431,22 +584,24 @@ int env_int(const char* name, int dflt) {
   return atoi(s);
 }
 
-constexpr int kQV = 32;
+int rank_stride(int R) {
+  int RS = 1;
+  while (RS < R) RS <<= 1;
+  return RS;
+}
 
 ScanPlan make_plan(const ScanGeom& g) {
   ScanPlan pl{};
   pl.chunk = kQV;
-  const int R = (int)g.R;
-  int RS = 1;
-  while (RS < R) RS <<= 1;
-  const int Qt = kQV / RS;
+  const int Qt = kQV / rank_stride((int)g.R);
   const int NT = ((int)g.N + 15) / 16, PT = ((int)g.P + 15) / 16;
   const long bhn = (long)g.B * g.H;
-  // Split the sequence into segments until there are enough workgroups to
-  // cover the chip; each segment keeps at least a few chunks.
-  int target = env_int("M3_SCAN_TARGET_WG", 256);
+  // Split the sequence into as many segments as keep every workgroup resident
+  // at once (two per CU on 256 CUs), so no CU runs a second round; each
+  // segment keeps at least four chunks.
+  const int target = env_int("M3_SCAN_TARGET_WG", 512);
   long nseg = 1;
-  if (bhn < target) nseg = (target + bhn - 1) / bhn;
+  if (bhn < target) nseg = target / bhn;
   const long max_seg = ((long)g.L + 4L * Qt - 1) / (4L * Qt);
   if (nseg > max_seg) nseg = max_seg;
   const int forced = env_int("M3_SCAN_NSEG", 0);
@@ -462,21 +617,69 @@ ScanPlan make_plan(const ScanGeom& g) {
   return pl;
 }
 
-template <int QV, bool FULL>
-hipError_t launch_one(const ScanKParams& kp, unsigned grid, unsigned block, size_t lds_bytes,
-                      hipStream_t stream) {
+// LDS layout of one pass; the summary pass needs no Q, M or Y buffers.  Rows
+// are padded by four floats so that rows 4 apart start 16 banks apart.
+void layout(ScanKParams& kp, bool full, bool mimo) {
+  const int QV = kQV;
+  kp.ks = kp.NT * 16 + 4;
+  kp.xs = kp.PT * 16 + 4;
+  kp.ms = QV + 4;
+  kp.ys = kp.PT * 16 + 4;
+  int off = 0;
+  kp.o_ql = off; off += full ? QV * kp.ks : 0;
+  kp.o_kl = off; off += QV * kp.ks;
+  kp.o_xl = off; off += QV * kp.xs;
+  kp.o_ml = off; off += full ? QV * kp.ms : 0;
+  kp.o_yl = off; off += full ? QV * kp.ys : 0;
+  // the entry-state fold overlays [PT*16][NT*16+4] floats on the chunk buffers
+  if (full && off < kp.PT * 16 * (kp.NT * 16 + 4)) off = kp.PT * 16 * (kp.NT * 16 + 4);
+  kp.o_cs = off; off += 2 * 64;
+  kp.o_bias = off; off += 2 * kp.R * kp.N;
+  kp.o_mimo = off; off += mimo ? 3 * kp.R * kp.P + kp.P : 0;
+  off = (off + 3) / 4 * 4;
+  kp.o_sc = off; off += 6 * QV;
+  kp.o_run = off; off += 68;
+  kp.lds_floats = off;
+}
+
+template <int VEC, bool FULL, bool MIMO>
+hipError_t launch_one(const ScanKParams& kp, unsigned grid, unsigned block, hipStream_t stream) {
+  const size_t lds_bytes = (size_t)kp.lds_floats * sizeof(float);
   // Dynamic LDS above 64 KiB needs the opt-in attribute on some runtimes;
-  // set it once and keep going if the runtime does not know it.
-  static bool attr_set = false;
-  if (!attr_set && lds_bytes > 64 * 1024) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_chunk_kernel<QV, FULL>),
+  // raise it when a larger layout first appears, and keep going if the
+  // runtime does not know the attribute.
+  static size_t attr_bytes = 64 * 1024;
+  if (lds_bytes > attr_bytes) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_chunk_kernel<VEC, FULL, MIMO>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) != hipSuccess)
       (void)hipGetLastError();
-    attr_set = true;
+    attr_bytes = lds_bytes;
   }
-  hipLaunchKernelGGL((scan_chunk_kernel<QV, FULL>), dim3(grid), dim3(block), lds_bytes, stream, kp);
+  hipLaunchKernelGGL((scan_chunk_kernel<VEC, FULL, MIMO>), dim3(grid), dim3(block), lds_bytes, stream, kp);
   return hipGetLastError();
 }
+
+template <int VEC, bool MIMO>
+hipError_t launch_passes(ScanKParams kp, const ScanPlan& plan, unsigned bhn, unsigned block,
+                         hipStream_t stream) {
+  if (plan.nseg > 1) {
+    ScanKParams ka = kp;
+    layout(ka, false, MIMO);
+    hipError_t e = launch_one<VEC, false, MIMO>(ka, bhn * (unsigned)(plan.nseg - 1), block, stream);
+    if (e != hipSuccess) return e;
+  }
+  layout(kp, true, MIMO);
+  const ProfileEvents& pe = profile_events();
+  if (pe.start) {
+    hipError_t e = hipEventRecord(pe.start, stream);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch_one<VEC, true, MIMO>(kp, bhn * (unsigned)plan.nseg, block, stream);
+  if (e == hipSuccess && pe.stop) e = hipEventRecord(pe.stop, stream);
+  return e;
+}
+
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0u; }
 
 hipError_t launch_scan(const ScanGeom& g, const ScanOperands& o, const ScanPlan& plan,
                        void* workspace, hipStream_t stream) {
@@ -487,50 +690,32 @@ hipError_t launch_scan(const ScanGeom& g, const ScanOperands& o, const ScanPlan&
   kp.out = o.out;
   kp.B = g.B; kp.L = g.L; kp.H = g.H; kp.G = g.G; kp.P = g.P; kp.N = g.N; kp.A = g.A; kp.R = g.R;
   kp.has_z = g.has_z; kp.has_d = g.has_d; kp.has_norm = g.has_norm;
-  kp.mimo = o.mimo_x != nullptr;
+  const bool mimo = o.mimo_x != nullptr;
   kp.NT = ((int)g.N + 15) / 16;
   kp.PT = ((int)g.P + 15) / 16;
-  kp.RS = 1;
+  kp.RS = rank_stride((int)g.R);
   kp.rs_log2 = 0;
-  while (kp.RS < (int)g.R) { kp.RS <<= 1; ++kp.rs_log2; }
+  while ((1 << kp.rs_log2) < kp.RS) ++kp.rs_log2;
   kp.Qt = kQV / kp.RS;
   kp.seg_len = plan.seg_len;
   kp.nseg = plan.nseg;
   float* ws = static_cast<float*>(workspace);
   kp.ws_state = ws;
   kp.ws_aux = ws ? ws + plan.ws_state_floats : nullptr;
-
-  const int QV = kQV;
-  kp.ks = kp.NT * 16 + 4;
-  kp.ts = QV + 4;
-  kp.ys = kp.PT * 16 + 4;
-  int off = 0;
-  kp.o_ql = off; off += QV * kp.ks;
-  kp.o_kt = off; off += kp.NT * 16 * kp.ts;
-  kp.o_xt = off; off += kp.PT * 16 * kp.ts;
-  kp.o_ml = off; off += QV * kp.ts;
-  kp.o_yl = off; off += QV * kp.ys;
-  // the entry-state fold overlays [PT*16][NT*16+4] floats on the chunk buffers
-  if (off < kp.PT * 16 * (kp.NT * 16 + 4)) off = kp.PT * 16 * (kp.NT * 16 + 4);
-  kp.o_cs = off; off += 2 * QV * 64;
-  kp.o_sc = off; off += 6 * QV;
-  kp.o_run = off; off += 68;
-  kp.lds_floats = off;
-  const size_t lds_bytes = (size_t)off * sizeof(float);
-  const unsigned block = 64u * (unsigned)kp.PT;
+  // 16-byte vector access needs every row width and row start on a 16-byte boundary.
+  const bool vec4 = g.P % 4 == 0 && g.N % 4 == 0 && aligned16(o.x) && aligned16(o.z) && aligned16(o.b) && aligned16(o.c) &&
+                    aligned16(o.out);
+  // one wave per 16 head_dim columns, at least four, and enough that the
+  // angle scan (two angles per wave and pass, four passes) covers A
+  unsigned nwaves = kp.PT > 4 ? (unsigned)kp.PT : 4u;
+  while (8u * nwaves < g.A) ++nwaves;
+  const unsigned block = 64u * nwaves;
   const unsigned bhn = g.B * g.H;
-  if (plan.nseg > 1) {
-    hipError_t e = launch_one<kQV, false>(kp, bhn * (unsigned)(plan.nseg - 1), block, lds_bytes, stream);
-    if (e != hipSuccess) return e;
-  }
-  const ProfileEvents& pe = profile_events();
-  if (pe.start) {
-    hipError_t e = hipEventRecord(pe.start, stream);
-    if (e != hipSuccess) return e;
-  }
-  hipError_t e = launch_one<kQV, true>(kp, bhn * (unsigned)plan.nseg, block, lds_bytes, stream);
-  if (e == hipSuccess && pe.stop) e = hipEventRecord(pe.stop, stream);
-  return e;
+  if (vec4)
+    return mimo ? launch_passes<4, true>(kp, plan, bhn, block, stream)
+                : launch_passes<4, false>(kp, plan, bhn, block, stream);
+  return mimo ? launch_passes<1, true>(kp, plan, bhn, block, stream)
+              : launch_passes<1, false>(kp, plan, bhn, block, stream);
 }
 
 }  // namespace

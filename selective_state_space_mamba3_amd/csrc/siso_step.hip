@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void siso_step_kernel(StepKParams p) {
     if (j < A) {
       const float th = fmaf(dtv, p.angle[(size_t)b * A + j], p.ang_state[sidx * A + j]);
       float s, co;
-      sincosf(th, &s, &co);
+      sincos_acc(th, &s, &co);
       const float b0 = p.b[row + j] + p.b_bias[brow + j];
       const float b1 = p.b[row + j + A] + p.b_bias[brow + j + A];
       const float c0 = p.c[row + j] + p.c_bias[brow + j];
