@@ -125,6 +125,29 @@ __device__ __forceinline__ floatx4 lds_read4(const float* p) {
   return *reinterpret_cast<const floatx4*>(p);
 }
 
+// Raw buffer access (buffer_load / buffer_store with a scalar resource and a
+// 32-bit per-lane byte offset).  The resource covers [base, base + bytes):
+// loads past the end return zero and stores past the end are dropped, which
+// masks partial chunks without branches.  0x00020000 is the gfx9-family
+// third descriptor word for 32-bit raw data.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ floatx4 buf_load4(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ float buf_load1(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+typedef unsigned int uintx4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t byte_off, floatx4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uintx4, v), r, byte_off, 0, 0);
+}
+__device__ __forceinline__ void buf_store1(rsrc_t r, uint32_t byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, byte_off, 0, 0);
+}
+
 // Map a hardware workgroup id to a logical work unit so that consecutive
 // logical units land on the same XCD: the dispatcher hands workgroup i to
 // XCD i % 8, so logical units are dealt out in eight contiguous runs.

@@ -20,10 +20,13 @@
 //     r < R, RS = R rounded up to a power of two so that no token's rows
 //     straddle a 16-row MFMA tile; rows with r >= R stay zero).  SISO has
 //     R = RS = 1, MIMO stacks its ranks inside the chunk.
-//   * One workgroup runs one (batch, head, sequence segment).  Wave w < PT
-//     owns the 16 head_dim columns [16w, 16w+16) and keeps the state
-//     h'^T [N x 16] of those columns in MFMA accumulator registers for the
-//     whole segment; at least four waves share the loads and VALU work.
+//   * One workgroup runs one (batch, head, sequence segment).  MFMA wave
+//     (pt, nh) owns the 16 head_dim columns [16 pt, 16 pt + 16) and the
+//     state rows of N-part nh (at most 64 of the N state coordinates); it
+//     keeps that slice of h'^T in MFMA accumulator registers for the whole
+//     segment.  The N-parts' partial outputs meet in LDS.  The block has
+//     enough waves that each thread prefetches at most two 16-byte B and C
+//     vectors, so a wave fits in 128 VGPRs and four waves share each SIMD.
 //   * Intra-chunk S = Q K^T, the decay/trapezoid mask, M X, the carried-state
 //     read Q h'^T and the state update K^T (w X) all run on
 //     v_mfma_f32_16x16x4_f32.
@@ -56,11 +59,12 @@ struct ScanKParams {
   int B, L, H, G, P, N, A, R;
   int has_z, has_d, has_norm;
   int NT, PT;       // 16-wide blocks of N and P
+  int NH, NTH;      // N split into NH parts of NTH 16-wide blocks (one part per wave)
   int RS, rs_log2;  // rank stride of the virtual rows (power of two >= R)
   int Qt;           // tokens per chunk (QV / RS)
   int seg_len, nseg;
   // LDS layout (float offsets) and row strides
-  int o_ql, o_kl, o_xl, o_ml, o_yl, o_cs, o_bias, o_mimo, o_sc, o_run, lds_floats;
+  int o_ql, o_kl, o_xl, o_ml, o_yl, o_yl2, o_cs, o_bias, o_mimo, o_sc, o_run, lds_floats;
   int ks, xs, ms, ys;
 };
 
@@ -83,6 +87,20 @@ __device__ __forceinline__ typename VecOf<VEC>::T vload(const float* p) {
     return *p;
 }
 template <int VEC>
+__device__ __forceinline__ typename VecOf<VEC>::T bload(rsrc_t r, uint32_t elem_off) {
+  if constexpr (VEC == 4)
+    return buf_load4(r, elem_off * 4u);
+  else
+    return buf_load1(r, elem_off * 4u);
+}
+template <int VEC>
+__device__ __forceinline__ void bstore(rsrc_t r, uint32_t elem_off, const typename VecOf<VEC>::T& v) {
+  if constexpr (VEC == 4)
+    buf_store4(r, elem_off * 4u, v);
+  else
+    buf_store1(r, elem_off * 4u, v);
+}
+template <int VEC>
 __device__ __forceinline__ void vstore(float* p, const typename VecOf<VEC>::T& v) {
   if constexpr (VEC == 4)
     *reinterpret_cast<floatx4*>(p) = v;
@@ -94,20 +112,26 @@ __device__ __forceinline__ float comp(const float& v, int) { return v; }
 __device__ __forceinline__ void set_comp(floatx4& v, int e, float x) { v[e] = x; }
 __device__ __forceinline__ void set_comp(float& v, int, float x) { v = x; }
 
-template <int VEC, bool FULL, bool MIMO>
-__global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
+// NTC / PTC / NWC fix the 16-wide block counts of N and P and the number of
+// waves at compile time (0 = taken from the parameters), so that LDS row
+// strides are constants and accesses fold into immediate offsets.  Fixed-size
+// SISO variants ask for two resident workgroups per CU (NWC / 2 waves per
+// SIMD, at most 128 VGPRs); MIMO, with R query rows per token, keeps its
+// registers at one workgroup per CU instead of spilling.
+template <int VEC, bool FULL, bool MIMO, int NTC, int PTC, int NWC>
+__global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC / 2) : 1) void scan_chunk_kernel(ScanKParams p) {
   using vec_t = typename VecOf<VEC>::T;
   constexpr int QV = kQV;
   constexpr int TB = QV / 16;
-  constexpr int KX = 8 / VEC;   // x / z items per thread (Qt*P/VEC <= 8/VEC * threads)
-  constexpr int KB = 16 / VEC;  // B / C row items per thread (QV*N/VEC <= 16/VEC * threads)
+  constexpr int KX = VEC == 4 ? 1 : 4;  // x / z items per thread (block >= Qt*P/(VEC*KX) threads)
+  constexpr int KB = VEC == 4 ? 2 : 8;  // B / C row items per thread (block >= QV*N/(VEC*KB) threads)
   constexpr int KA = 4;         // angle values per lane (launch gives >= A/8 waves)
   constexpr int KZM = 8;        // tokens per wave in the MIMO epilogue
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int nthreads = blockDim.x;
+  const int nthreads = NWC ? NWC * 64 : (int)blockDim.x;
   const int nwaves = nthreads >> 6;
   const int l16 = lane & 15;
   const int lq = lane >> 4;
@@ -122,19 +146,26 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
   const int bh = b * p.H + h;
   const int t_begin = seg * p.seg_len;
   const int t_end = min(t_begin + p.seg_len, p.L);
-  const int R = p.R;
+  const int R = MIMO ? p.R : 1;
   const int RG = R * p.G;
-  const int Qt = p.Qt;
-  const int rsl = p.rs_log2;
-  const int N = p.N, P = p.P, A = p.A;
-  const int ks = p.ks, xs = p.xs, ms = p.ms, ys = p.ys;
-  const bool mma_wave = wave < p.PT;
+  const int Qt = MIMO ? p.Qt : QV;
+  const int rsl = MIMO ? p.rs_log2 : 0;
+  const int NT = NTC ? NTC : p.NT, PT = PTC ? PTC : p.PT;
+  const int NH = NTC ? (NTC > 4 ? 2 : 1) : p.NH;
+  const int NTH = NTC ? (NTC + NH - 1) / NH : p.NTH;
+  const int N = NTC ? NTC * 16 : p.N, P = PTC ? PTC * 16 : p.P, A = p.A;
+  const int ks = NT * 16 + 4, xs = PT * 16 + 4, ms = QV + 4, ys = PT * 16 + 4;
+  const bool mma_wave = wave < PT * NH;
+  const int pt = wave % PT;             // head_dim block of this MFMA wave
+  const int nb0 = (wave / PT) * NTH;    // first state block of this MFMA wave
+  const int ntw = mma_wave ? min(NTH, NT - nb0) : 0;
 
   float* Ql = lds + p.o_ql;   // [QV][ks] C (+bias), pairs rotated in place   (main pass)
   float* Kl = lds + p.o_kl;   // [QV][ks] B (+bias), pairs rotated in place
   float* Xl = lds + p.o_xl;   // [QV][xs] per-rank x
   float* Ml = lds + p.o_ml;   // [QV][ms] masked S                             (main pass)
-  float* Yl = lds + p.o_yl;   // [QV][ys] raw y                                (main pass)
+  float* Yl = lds + p.o_yl;   // [QV][ys] raw y, N-part 0 (+ M X)              (main pass)
+  float* Yl2 = lds + p.o_yl2;  // [QV][ys] raw y, N-part 1                      (main pass)
   float* CS = lds + p.o_cs;   // [64] cos / [64] sin for the entry-state fold
   float* SN = CS + 64;
   float* bbL = lds + p.o_bias;  // [R][N] b_bias of this head; cbL follows
@@ -168,10 +199,10 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
     for (int i = tid; i < R * P; i += nthreads) mxL[i] = p.mimo_x[(size_t)h * R * P + i];
   }
 
-  const int p0 = wave * 16;
-  floatx4 Hacc[8];
+  const int p0 = pt * 16;
+  floatx4 Hacc[4];  // state blocks nb0 .. nb0 + ntw - 1 of columns p0 .. p0 + 15
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) Hacc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 4; ++j) Hacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // Entry state: fold the summaries of the earlier segments, in order,
   //   h' <- decay_i h' + rot(theta_i) U_i,
@@ -182,16 +213,17 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
   if (FULL && seg > 0) {
     __syncthreads();
     float* Ub = lds;  // [PT*16][NT*16 + 4], overlays the chunk buffers (unused yet)
-    const int us = p.NT * 16 + 4;
+    const int us = NT * 16 + 4;
     for (int i = 0; i < seg; ++i) {
       const size_t si = (size_t)bh * (p.nseg - 1) + i;
       const float* aux = p.ws_aux + si * kAux;
-      const float* st = p.ws_state + si * (size_t)(p.PT * p.NT) * 256;
+      const float* st = p.ws_state + si * (size_t)(PT * NT) * 256;
       if (mma_wave) {
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          if (nb < p.NT) {
-            const floatx4 u = *reinterpret_cast<const floatx4*>(st + ((wave * p.NT + nb) * 64 + lane) * 4);
+        for (int j = 0; j < 4; ++j) {
+          if (j < ntw) {
+            const int nb = nb0 + j;
+            const floatx4 u = *reinterpret_cast<const floatx4*>(st + ((pt * NT + nb) * 64 + lane) * 4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) Ub[(p0 + l16) * us + nb * 16 + 4 * lq + r] = u[r];
           }
@@ -204,7 +236,7 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
         SN[tid] = sn;
       }
       __syncthreads();
-      for (int e = tid; e < p.PT * 16 * A; e += nthreads) {
+      for (int e = tid; e < PT * 16 * A; e += nthreads) {
         const int pp = e / A, a = e - pp * A;
         const float u0 = Ub[pp * us + a], u1 = Ub[pp * us + a + A];
         Ub[pp * us + a] = u0 * CS[a] - u1 * SN[a];
@@ -214,24 +246,25 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
       const float dec = aux[kAuxDecay];
       if (mma_wave) {
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          if (nb < p.NT) {
+        for (int j = 0; j < 4; ++j) {
+          if (j < ntw) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              Hacc[nb][r] = fmaf(dec, Hacc[nb][r], Ub[(p0 + l16) * us + nb * 16 + 4 * lq + r]);
+              Hacc[j][r] = fmaf(dec, Hacc[j][r], Ub[(p0 + l16) * us + (nb0 + j) * 16 + 4 * lq + r]);
           }
         }
       }
       if (tid < A) run[tid] += aux[tid];
       __syncthreads();
     }
-    for (int i = tid; i < p.PT * 16 * us; i += nthreads) Ub[i] = 0.f;  // restore the zero padding
+    for (int i = tid; i < PT * 16 * us; i += nthreads) Ub[i] = 0.f;  // restore the zero padding
   }
   float seg_decay = 1.f;  // thread 0: product of chunk decays (summary pass)
 
   // ---- register prefetch of one chunk's global operands -------------------
-  // Addresses are a wave-uniform chunk base (scalar registers) plus a 32-bit
-  // per-lane offset, so loads use the scalar-base + vector-offset form.
+  // Each operand is read through a buffer resource that starts at the chunk's
+  // first token and ends after its last valid one, so rows past the end of
+  // the chunk (or past the last item) load as zero without a branch.
   const int xrow = P / VEC;   // x items per token
   const int brow = N / VEC;   // B / C items per virtual row
   const int tokx = p.H * P;   // x / z / out elements per token
@@ -242,45 +275,42 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
 
   auto prefetch = [&](int cs) {
     const int nv = min(Qt, t_end - cs);
-    const float* xbase = p.x + (((size_t)b * p.L + cs) * p.H + h) * P;
-    const float* bbase = p.b + ((size_t)b * p.L + cs) * tokb;
-    const float* cbase = p.c + ((size_t)b * p.L + cs) * tokb;
-    const float* abase = p.angle + ((size_t)b * p.L + cs) * A;
+    const rsrc_t xres = make_rsrc(p.x + (((size_t)b * p.L + cs) * p.H + h) * P, (uint32_t)(nv * tokx * 4));
+    const rsrc_t bres = make_rsrc(p.b + ((size_t)b * p.L + cs) * tokb, (uint32_t)(nv * tokb * 4));
+    const rsrc_t cres = make_rsrc(p.c + ((size_t)b * p.L + cs) * tokb, (uint32_t)(nv * tokb * 4));
+    const rsrc_t ares = make_rsrc(p.angle + ((size_t)b * p.L + cs) * A, (uint32_t)(nv * A * 4));
 #pragma unroll
     for (int k = 0; k < KX; ++k) {
       const int idx = tid + k * nthreads;
       const int t = idx / xrow, pv = idx - t * xrow;
-      vec_t v{};
-      if (idx < Qt * xrow && t < nv) v = vload<VEC>(xbase + (uint32_t)(t * tokx + pv * VEC));
-      xr[k] = v;
+      xr[k] = bload<VEC>(xres, (uint32_t)(t * tokx + pv * VEC));
     }
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
       const int idx = tid + k * nthreads;
       const int u = idx / brow, j = idx - u * brow;
       const int t = u / R, r = u - t * R;
-      vec_t v0{}, w0{};
-      if (idx < Qt * R * brow && t < nv) {
-        const uint32_t off = (uint32_t)(t * tokb + (r * p.G + g) * N + j * VEC);
-        v0 = vload<VEC>(bbase + off);
-        if (FULL) w0 = vload<VEC>(cbase + off);
-      }
-      br[k] = v0;
-      cr[k] = w0;
+      const uint32_t off = (uint32_t)(t * tokb + (r * p.G + g) * N + j * VEC);
+      br[k] = bload<VEC>(bres, off);
+      if (FULL) cr[k] = bload<VEC>(cres, off);
     }
 #pragma unroll
     for (int i = 0; i < KA; ++i) {
       const int a = 2 * (i * nwaves + wave) + (lane >> 5);
       const int t = lane & 31;
-      angr[i] = (a < A && t < nv) ? abase[(uint32_t)(t * A + a)] : 0.f;
+      angr[i] = a < A ? buf_load1(ares, (uint32_t)(t * A + a) * 4u) : 0.f;
     }
     if (wave == 0) {
-      const bool okl = lane <= Qt && cs + lane < p.L;
+      // tokens cs .. cs + Qt (one past the chunk, for the trapezoid look-ahead)
       const size_t sbase = ((size_t)b * p.L + cs) * p.H + h;
-      const uint32_t so = (uint32_t)(lane * p.H);
-      s_dt = okl ? p.dt[sbase + so] : 0.f;
-      s_trap = okl ? p.trap[sbase + so] : 0.f;
-      s_adt = lane < nv ? p.adt[sbase + so] : 0.f;
+      const uint32_t nl = (uint32_t)min(Qt + 1, p.L - cs);
+      const rsrc_t dres = make_rsrc(p.dt + sbase, nl * p.H * 4);
+      const rsrc_t tres = make_rsrc(p.trap + sbase, nl * p.H * 4);
+      const rsrc_t adres = make_rsrc(p.adt + sbase, (uint32_t)(nv * p.H * 4));
+      const uint32_t so = (uint32_t)(lane * p.H) * 4u;
+      s_dt = buf_load1(dres, so);
+      s_trap = buf_load1(tres, so);
+      s_adt = buf_load1(adres, so);
     }
   };
 
@@ -355,15 +385,15 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
     vec_t zr[KX];
     float zm[KZM][2];
     const size_t cbase_tok = (((size_t)b * p.L + c0) * p.H + h) * P;  // x / z / out at token c0
-    const float* zbase = p.z + cbase_tok;
+    // z and out: valid tokens of this chunk only (no z reads when has_z is off)
+    const rsrc_t zres = make_rsrc(p.z + cbase_tok, p.has_z ? (uint32_t)(nvalid * tokx * 4) : 0u);
+    const rsrc_t ores = make_rsrc(p.out + cbase_tok, (uint32_t)(nvalid * tokx * 4));
     if constexpr (FULL && !MIMO) {
 #pragma unroll
       for (int k = 0; k < KX; ++k) {
         const int idx = tid + k * nthreads;
         const int t = idx / xrow, pv = idx - t * xrow;
-        vec_t v{};
-        if (p.has_z && idx < Qt * xrow && t < nvalid) v = vload<VEC>(zbase + (uint32_t)(t * tokx + pv * VEC));
-        zr[k] = v;
+        zr[k] = bload<VEC>(zres, (uint32_t)(t * tokx + pv * VEC));
       }
     }
     if constexpr (FULL && MIMO) {
@@ -371,9 +401,8 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
       for (int i = 0; i < KZM; ++i) {
         const int t = wave + i * nwaves;
         const uint32_t ob = (uint32_t)(t * tokx);
-        const bool ok = p.has_z && t < nvalid;
-        zm[i][0] = (ok && lane < P) ? zbase[ob + lane] : 0.f;
-        zm[i][1] = (ok && lane + 64 < P) ? zbase[ob + lane + 64] : 0.f;
+        zm[i][0] = lane < P ? buf_load1(zres, (ob + lane) * 4u) : 0.f;
+        zm[i][1] = lane + 64 < P ? buf_load1(zres, (ob + lane + 64) * 4u) : 0.f;
       }
     }
     lds_barrier();
@@ -417,20 +446,22 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
       for (int pr = wave; pr < NPAIRS; pr += nwaves) {
         int tb = 0, sb = pr;
         while (sb > tb) { sb -= tb + 1; ++tb; }
-        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+        floatx4 accs[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
         const float* qa = Ql + (tb * 16 + l16) * ks + 4 * lq;
         const float* kb = Kl + (sb * 16 + l16) * ks + 4 * lq;
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
-          if (nb < p.NT) {
+          if (nb < NT) {
             const floatx4 a4 = lds_read4(qa + nb * 16);
             const floatx4 b4 = lds_read4(kb + nb * 16);
+            floatx4& acc = accs[nb & 1];
             acc = mfma16(a4.x, b4.x, acc);
             acc = mfma16(a4.y, b4.y, acc);
             acc = mfma16(a4.z, b4.z, acc);
             acc = mfma16(a4.w, b4.w, acc);
           }
         }
+        const floatx4 acc = accs[0] + accs[1];
         const int vs = sb * 16 + l16;
         const int ts_ = vs >> rsl;
         const float cum_s = sc_cum[ts_], scl_s = sc_scl[ts_];
@@ -449,37 +480,52 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
 
     if (mma_wave) {
       if constexpr (FULL) {
-        // ---- P5a: Y = M X + diag(exp(cum)) Q h'^T (this wave's 16 columns) ---
-        for (int tb = 0; tb < TB; ++tb) {
-          floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-          for (int sb = 0; sb <= tb; ++sb) {
-            const floatx4 a4 = lds_read4(Ml + (tb * 16 + l16) * ms + sb * 16 + 4 * lq);
-            const float* xc = Xl + (sb * 16 + 4 * lq) * xs + p0 + l16;
-            acc = mfma16(a4.x, xc[0], acc);
-            acc = mfma16(a4.y, xc[xs], acc);
-            acc = mfma16(a4.z, xc[2 * xs], acc);
-            acc = mfma16(a4.w, xc[3 * xs], acc);
-          }
-          const float ec = sc_ecum[(tb * 16 + l16) >> rsl];
-          const float* qa = Ql + (tb * 16 + l16) * ks + 4 * lq;
+        // ---- P5a: Y = M X + diag(exp(cum)) Q h'^T over this wave's state
+        //      blocks; N-part 0 adds the intra-chunk M X.  One accumulator per
+        //      16-row block keeps independent MFMA chains in flight.
+        floatx4 acc[TB];
 #pragma unroll
-          for (int nb = 0; nb < 8; ++nb) {
-            if (nb < p.NT) {
-              const floatx4 a4 = lds_read4(qa + nb * 16) * ec;
-              acc = mfma16(a4.x, Hacc[nb].x, acc);
-              acc = mfma16(a4.y, Hacc[nb].y, acc);
-              acc = mfma16(a4.z, Hacc[nb].z, acc);
-              acc = mfma16(a4.w, Hacc[nb].w, acc);
+        for (int tb = 0; tb < TB; ++tb) acc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (nb0 == 0) {
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb) {
+            for (int sb = 0; sb <= tb; ++sb) {
+              const floatx4 a4 = lds_read4(Ml + (tb * 16 + l16) * ms + sb * 16 + 4 * lq);
+              const float* xc = Xl + (sb * 16 + 4 * lq) * xs + p0 + l16;
+              acc[tb] = mfma16(a4.x, xc[0], acc[tb]);
+              acc[tb] = mfma16(a4.y, xc[xs], acc[tb]);
+              acc[tb] = mfma16(a4.z, xc[2 * xs], acc[tb]);
+              acc[tb] = mfma16(a4.w, xc[3 * xs], acc[tb]);
             }
           }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) Yl[(tb * 16 + 4 * lq + r) * ys + p0 + l16] = acc[r];
         }
+        float ec[TB];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) ec[tb] = sc_ecum[(tb * 16 + l16) >> rsl];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (j < ntw) {
+            const int nb = nb0 + j;
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+              const floatx4 a4 = lds_read4(Ql + (tb * 16 + l16) * ks + nb * 16 + 4 * lq) * ec[tb];
+              acc[tb] = mfma16(a4.x, Hacc[j].x, acc[tb]);
+              acc[tb] = mfma16(a4.y, Hacc[j].y, acc[tb]);
+              acc[tb] = mfma16(a4.z, Hacc[j].z, acc[tb]);
+              acc[tb] = mfma16(a4.w, Hacc[j].w, acc[tb]);
+            }
+          }
+        }
+        float* Yd = nb0 == 0 ? Yl : Yl2;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Yd[(tb * 16 + 4 * lq + r) * ys + p0 + l16] = acc[tb][r];
       }
       // ---- P5b: state update h' = decay h' + K^T (w X) ------------------------
       const float dec = run[64];
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) Hacc[nb] *= dec;
+      for (int j = 0; j < 4; ++j) Hacc[j] *= dec;
       for (int sb = 0; sb < TB; ++sb) {
         const int v0 = sb * 16 + 4 * lq;
         const float* xc = Xl + v0 * xs + p0 + l16;
@@ -487,14 +533,14 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
         const float xw1 = xc[xs] * sc_w[(v0 + 1) >> rsl];
         const float xw2 = xc[2 * xs] * sc_w[(v0 + 2) >> rsl];
         const float xw3 = xc[3 * xs] * sc_w[(v0 + 3) >> rsl];
-        const float* kc = Kl + v0 * ks + l16;
+        const float* kc = Kl + v0 * ks + nb0 * 16 + l16;
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          if (nb < p.NT) {
-            Hacc[nb] = mfma16(kc[nb * 16], xw0, Hacc[nb]);
-            Hacc[nb] = mfma16(kc[ks + nb * 16], xw1, Hacc[nb]);
-            Hacc[nb] = mfma16(kc[2 * ks + nb * 16], xw2, Hacc[nb]);
-            Hacc[nb] = mfma16(kc[3 * ks + nb * 16], xw3, Hacc[nb]);
+        for (int j = 0; j < 4; ++j) {
+          if (j < ntw) {
+            Hacc[j] = mfma16(kc[j * 16], xw0, Hacc[j]);
+            Hacc[j] = mfma16(kc[ks + j * 16], xw1, Hacc[j]);
+            Hacc[j] = mfma16(kc[2 * ks + j * 16], xw2, Hacc[j]);
+            Hacc[j] = mfma16(kc[3 * ks + j * 16], xw3, Hacc[j]);
           }
         }
       }
@@ -511,6 +557,7 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
         const int t = idx / xrow, pv = idx - t * xrow;
         if (idx < Qt * xrow && t < nvalid) {
           vec_t y = vload<VEC>(Yl + t * ys + pv * VEC);
+          if (NH > 1) y += vload<VEC>(Yl2 + t * ys + pv * VEC);
           const vec_t xv = vload<VEC>(Xl + t * xs + pv * VEC);
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
@@ -519,7 +566,7 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
             if (p.has_z) v *= silu_fast(comp(zr[k], e));
             set_comp(y, e, v);
           }
-          vstore<VEC>(p.out + cbase_tok + (uint32_t)(t * tokx + pv * VEC), y);
+          bstore<VEC>(ores, (uint32_t)(t * tokx + pv * VEC), y);
         }
       }
       lds_barrier();
@@ -538,12 +585,12 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
           const int v = (t << rsl) + r;
           float y0 = 0.f, y1 = 0.f;
           if (pa < P) {
-            y0 = Yl[v * ys + pa];
+            y0 = Yl[v * ys + pa] + (NH > 1 ? Yl2[v * ys + pa] : 0.f);
             if (p.has_d) y0 = fmaf(dh, Xl[v * xs + pa], y0);
             if (p.has_z) y0 *= silu_fast(zm[i][0] * mzL[r * P + pa]);
           }
           if (pb < P) {
-            y1 = Yl[v * ys + pb];
+            y1 = Yl[v * ys + pb] + (NH > 1 ? Yl2[v * ys + pb] : 0.f);
             if (p.has_d) y1 = fmaf(dh, Xl[v * xs + pb], y1);
             if (p.has_z) y1 *= silu_fast(zm[i][1] * mzL[r * P + pb]);
           }
@@ -556,9 +603,9 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
           if (pa < P) o0 = fmaf(moL[r * P + pa], y0, o0);
           if (pb < P) o1 = fmaf(moL[r * P + pb], y1, o1);
         }
-        float* ob = p.out + cbase_tok + (uint32_t)(t * tokx);
-        if (pa < P) ob[pa] = o0;
-        if (pb < P) ob[pb] = o1;
+        const uint32_t ob = (uint32_t)(t * tokx);
+        if (pa < P) buf_store1(ores, (ob + pa) * 4u, o0);
+        if (pb < P) buf_store1(ores, (ob + pb) * 4u, o1);
       }
       lds_barrier();
     }
@@ -566,11 +613,11 @@ __global__ __launch_bounds__(512) void scan_chunk_kernel(ScanKParams p) {
 
   if constexpr (!FULL) {
     const size_t si = (size_t)bh * (p.nseg - 1) + seg;
-    float* st = p.ws_state + si * (size_t)(p.PT * p.NT) * 256;
+    float* st = p.ws_state + si * (size_t)(PT * NT) * 256;
     if (mma_wave) {
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
-        if (nb < p.NT) *reinterpret_cast<floatx4*>(st + ((wave * p.NT + nb) * 64 + lane) * 4) = Hacc[nb];
+      for (int j = 0; j < 4; ++j)
+        if (j < ntw) *reinterpret_cast<floatx4*>(st + ((pt * NT + nb0 + j) * 64 + lane) * 4) = Hacc[j];
     }
     float* aux = p.ws_aux + si * kAux;
     if (tid < A) aux[tid] = run[tid];
@@ -631,6 +678,7 @@ void layout(ScanKParams& kp, bool full, bool mimo) {
   kp.o_xl = off; off += QV * kp.xs;
   kp.o_ml = off; off += full ? QV * kp.ms : 0;
   kp.o_yl = off; off += full ? QV * kp.ys : 0;
+  kp.o_yl2 = off; off += (full && kp.NH > 1) ? QV * kp.ys : 0;
   // the entry-state fold overlays [PT*16][NT*16+4] floats on the chunk buffers
   if (full && off < kp.PT * 16 * (kp.NT * 16 + 4)) off = kp.PT * 16 * (kp.NT * 16 + 4);
   kp.o_cs = off; off += 2 * 64;
@@ -642,7 +690,7 @@ void layout(ScanKParams& kp, bool full, bool mimo) {
   kp.lds_floats = off;
 }
 
-template <int VEC, bool FULL, bool MIMO>
+template <int VEC, bool FULL, bool MIMO, int NTC, int PTC, int NWC>
 hipError_t launch_one(const ScanKParams& kp, unsigned grid, unsigned block, hipStream_t stream) {
   const size_t lds_bytes = (size_t)kp.lds_floats * sizeof(float);
   // Dynamic LDS above 64 KiB needs the opt-in attribute on some runtimes;
@@ -650,22 +698,22 @@ hipError_t launch_one(const ScanKParams& kp, unsigned grid, unsigned block, hipS
   // runtime does not know the attribute.
   static size_t attr_bytes = 64 * 1024;
   if (lds_bytes > attr_bytes) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_chunk_kernel<VEC, FULL, MIMO>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) != hipSuccess)
       (void)hipGetLastError();
     attr_bytes = lds_bytes;
   }
-  hipLaunchKernelGGL((scan_chunk_kernel<VEC, FULL, MIMO>), dim3(grid), dim3(block), lds_bytes, stream, kp);
+  hipLaunchKernelGGL((scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC>), dim3(grid), dim3(block), lds_bytes, stream, kp);
   return hipGetLastError();
 }
 
-template <int VEC, bool MIMO>
+template <int VEC, bool MIMO, int NTC, int PTC, int NWC>
 hipError_t launch_passes(ScanKParams kp, const ScanPlan& plan, unsigned bhn, unsigned block,
                          hipStream_t stream) {
   if (plan.nseg > 1) {
     ScanKParams ka = kp;
     layout(ka, false, MIMO);
-    hipError_t e = launch_one<VEC, false, MIMO>(ka, bhn * (unsigned)(plan.nseg - 1), block, stream);
+    hipError_t e = launch_one<VEC, false, MIMO, NTC, PTC, NWC>(ka, bhn * (unsigned)(plan.nseg - 1), block, stream);
     if (e != hipSuccess) return e;
   }
   layout(kp, true, MIMO);
@@ -674,7 +722,7 @@ hipError_t launch_passes(ScanKParams kp, const ScanPlan& plan, unsigned bhn, uns
     hipError_t e = hipEventRecord(pe.start, stream);
     if (e != hipSuccess) return e;
   }
-  hipError_t e = launch_one<VEC, true, MIMO>(kp, bhn * (unsigned)plan.nseg, block, stream);
+  hipError_t e = launch_one<VEC, true, MIMO, NTC, PTC, NWC>(kp, bhn * (unsigned)plan.nseg, block, stream);
   if (e == hipSuccess && pe.stop) e = hipEventRecord(pe.stop, stream);
   return e;
 }
@@ -693,6 +741,8 @@ hipError_t launch_scan(const ScanGeom& g, const ScanOperands& o, const ScanPlan&
   const bool mimo = o.mimo_x != nullptr;
   kp.NT = ((int)g.N + 15) / 16;
   kp.PT = ((int)g.P + 15) / 16;
+  kp.NH = kp.NT > 4 ? 2 : 1;
+  kp.NTH = (kp.NT + kp.NH - 1) / kp.NH;
   kp.RS = rank_stride((int)g.R);
   kp.rs_log2 = 0;
   while ((1 << kp.rs_log2) < kp.RS) ++kp.rs_log2;
@@ -705,17 +755,28 @@ hipError_t launch_scan(const ScanGeom& g, const ScanOperands& o, const ScanPlan&
   // 16-byte vector access needs every row width and row start on a 16-byte boundary.
   const bool vec4 = g.P % 4 == 0 && g.N % 4 == 0 && aligned16(o.x) && aligned16(o.z) && aligned16(o.b) && aligned16(o.c) &&
                     aligned16(o.out);
-  // one wave per 16 head_dim columns, at least four, and enough that the
-  // angle scan (two angles per wave and pass, four passes) covers A
-  unsigned nwaves = kp.PT > 4 ? (unsigned)kp.PT : 4u;
+  // One MFMA wave per (16 head_dim columns, N-part of at most four 16-wide
+  // blocks); at least four waves; enough threads that every thread prefetches
+  // at most KX x-vectors and KB B/C vectors (8P and 4N threads for both the
+  // 16-byte and the scalar variant); and enough waves that the angle scan
+  // (two angles per wave and pass, four passes) covers A.
+  unsigned nwaves = (unsigned)(kp.PT * kp.NH);
+  if (nwaves < 4u) nwaves = 4u;
+  while (64u * nwaves < 8u * g.P) ++nwaves;
+  while (64u * nwaves < 4u * g.N) ++nwaves;
   while (8u * nwaves < g.A) ++nwaves;
   const unsigned block = 64u * nwaves;
   const unsigned bhn = g.B * g.H;
+  // The N = 128, P = 64 layers (eight waves) get a variant with compile-time
+  // strides; every other geometry runs the generic variant.
+  if (vec4 && g.N == 128 && g.P == 64 && nwaves == 8)
+    return mimo ? launch_passes<4, true, 8, 4, 8>(kp, plan, bhn, block, stream)
+                : launch_passes<4, false, 8, 4, 8>(kp, plan, bhn, block, stream);
   if (vec4)
-    return mimo ? launch_passes<4, true>(kp, plan, bhn, block, stream)
-                : launch_passes<4, false>(kp, plan, bhn, block, stream);
-  return mimo ? launch_passes<1, true>(kp, plan, bhn, block, stream)
-              : launch_passes<1, false>(kp, plan, bhn, block, stream);
+    return mimo ? launch_passes<4, true, 0, 0, 0>(kp, plan, bhn, block, stream)
+                : launch_passes<4, false, 0, 0, 0>(kp, plan, bhn, block, stream);
+  return mimo ? launch_passes<1, true, 0, 0, 0>(kp, plan, bhn, block, stream)
+              : launch_passes<1, false, 0, 0, 0>(kp, plan, bhn, block, stream);
 }
 
 }  // namespace
