@@ -64,7 +64,7 @@ struct ScanKParams {
   int Qt;           // tokens per chunk (QV / RS)
   int seg_len, nseg;
   // LDS layout (float offsets) and row strides
-  int o_ql, o_kl, o_xl, o_ml, o_yl, o_yl2, o_cs, o_bias, o_mimo, o_sc, o_run, lds_floats;
+  int o_ql, o_kl, o_xl, o_ml, o_ml2, o_yl, o_yl2, o_cs, o_bias, o_mimo, o_sc, o_run, lds_floats;
   int ks, xs, ms, ys;
 };
 
@@ -155,15 +155,28 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
   const int NTH = NTC ? (NTC + NH - 1) / NH : p.NTH;
   const int N = NTC ? NTC * 16 : p.N, P = PTC ? PTC * 16 : p.P, A = p.A;
   const int ks = NT * 16 + 4, xs = PT * 16 + 4, ms = QV + 4, ys = PT * 16 + 4;
-  const bool mma_wave = wave < PT * NH;
+  // In the fixed-size variant every wave is an MFMA wave with NTH state
+  // blocks, known at compile time, so the block loops carry no branches and
+  // the scheduler can overlap LDS reads with MFMAs across them.
+  constexpr bool FIXED = NTC > 0 && PTC > 0 && NWC > 0 && NTC % (NTC > 4 ? 2 : 1) == 0 &&
+                         PTC * (NTC > 4 ? 2 : 1) == NWC;
+  const bool mma_wave = FIXED || wave < PT * NH;
   const int pt = wave % PT;             // head_dim block of this MFMA wave
   const int nb0 = (wave / PT) * NTH;    // first state block of this MFMA wave
-  const int ntw = mma_wave ? min(NTH, NT - nb0) : 0;
+  const int ntw = FIXED ? NTH : (mma_wave ? min(NTH, NT - nb0) : 0);
+  constexpr int JMAX = FIXED ? (NTC > 4 ? NTC / 2 : NTC) : 4;  // state blocks per wave (bound)
+  // Fixed-size SISO: every (wave, half-wave) owns one 8-column group of the
+  // B / C rows (N / 8 == 2 * waves), either a rotated pair group
+  // (a0..a0+3, a0+A..a0+A+3) or a plain group, and rotates it in registers;
+  // S is split over six waves (three tile pairs x two N-halves).
+  constexpr bool MERGED = FIXED && !MIMO && NTC * 16 == 16 * NWC;
+  const int sw = nwaves - 1;  // wave that computes the per-token scalars
 
   float* Ql = lds + p.o_ql;   // [QV][ks] C (+bias), pairs rotated in place   (main pass)
   float* Kl = lds + p.o_kl;   // [QV][ks] B (+bias), pairs rotated in place
   float* Xl = lds + p.o_xl;   // [QV][xs] per-rank x
-  float* Ml = lds + p.o_ml;   // [QV][ms] masked S                             (main pass)
+  float* Ml = lds + p.o_ml;   // [QV][ms] masked S (N-half 0 when S is split)  (main pass)
+  float* Ml2 = lds + p.o_ml2;  // [QV][ms] masked S, N-half 1 (split S only)
   float* Yl = lds + p.o_yl;   // [QV][ys] raw y, N-part 0 (+ M X)              (main pass)
   float* Yl2 = lds + p.o_yl2;  // [QV][ys] raw y, N-part 1                      (main pass)
   float* CS = lds + p.o_cs;   // [64] cos / [64] sin for the entry-state fold
@@ -202,7 +215,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
   const int p0 = pt * 16;
   floatx4 Hacc[4];  // state blocks nb0 .. nb0 + ntw - 1 of columns p0 .. p0 + 15
 #pragma unroll
-  for (int j = 0; j < 4; ++j) Hacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < JMAX; ++j) Hacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // Entry state: fold the summaries of the earlier segments, in order,
   //   h' <- decay_i h' + rot(theta_i) U_i,
@@ -220,8 +233,8 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
       const float* st = p.ws_state + si * (size_t)(PT * NT) * 256;
       if (mma_wave) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j < ntw) {
+        for (int j = 0; j < JMAX; ++j) {
+          if (FIXED || j < ntw) {
             const int nb = nb0 + j;
             const floatx4 u = *reinterpret_cast<const floatx4*>(st + ((pt * NT + nb) * 64 + lane) * 4);
 #pragma unroll
@@ -246,8 +259,8 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
       const float dec = aux[kAuxDecay];
       if (mma_wave) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j < ntw) {
+        for (int j = 0; j < JMAX; ++j) {
+          if (FIXED || j < ntw) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               Hacc[j][r] = fmaf(dec, Hacc[j][r], Ub[(p0 + l16) * us + (nb0 + j) * 16 + 4 * lq + r]);
@@ -259,7 +272,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
     }
     for (int i = tid; i < PT * 16 * us; i += nthreads) Ub[i] = 0.f;  // restore the zero padding
   }
-  float seg_decay = 1.f;  // thread 0: product of chunk decays (summary pass)
+  float seg_decay = 1.f;  // lane 0 of the scalar wave: product of chunk decays (summary pass)
 
   // ---- register prefetch of one chunk's global operands -------------------
   // Each operand is read through a buffer resource that starts at the chunk's
@@ -272,6 +285,13 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
   vec_t xr[KX], br[KB], cr[KB];
   float angr[KA];
   float s_dt = 0.f, s_adt = 0.f, s_trap = 0.f;
+  // merged layout: this lane's token and 8-column group of the B / C rows
+  const int mt = lane & 31;
+  const int mgrp = 2 * wave + (lane >> 5);
+  const bool mpair = MERGED && mgrp < A / 4;
+  const int mc0 = mpair ? 4 * mgrp : 2 * A + 8 * (mgrp - A / 4);
+  const int mc1 = mpair ? mc0 + A : mc0 + 4;
+  float mdt = 0.f;
 
   auto prefetch = [&](int cs) {
     const int nv = min(Qt, t_end - cs);
@@ -285,22 +305,38 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
       const int t = idx / xrow, pv = idx - t * xrow;
       xr[k] = bload<VEC>(xres, (uint32_t)(t * tokx + pv * VEC));
     }
+    if constexpr (MERGED) {
+      const uint32_t row = (uint32_t)(mt * tokb + g * N);
+      br[0] = bload<VEC>(bres, row + mc0);
+      br[1] = bload<VEC>(bres, row + mc1);
+      if (FULL) {
+        cr[0] = bload<VEC>(cres, row + mc0);
+        cr[1] = bload<VEC>(cres, row + mc1);
+      }
+      if (mpair) {
+        const floatx4 a4 = buf_load4(ares, (uint32_t)(mt * A + mc0) * 4u);
+        angr[0] = a4.x; angr[1] = a4.y; angr[2] = a4.z; angr[3] = a4.w;
+      }
+      const size_t sbase = ((size_t)b * p.L + cs) * p.H + h;
+      mdt = buf_load1(make_rsrc(p.dt + sbase, (uint32_t)(nv * p.H * 4)), (uint32_t)(mt * p.H) * 4u);
+    } else {
 #pragma unroll
-    for (int k = 0; k < KB; ++k) {
-      const int idx = tid + k * nthreads;
-      const int u = idx / brow, j = idx - u * brow;
-      const int t = u / R, r = u - t * R;
-      const uint32_t off = (uint32_t)(t * tokb + (r * p.G + g) * N + j * VEC);
-      br[k] = bload<VEC>(bres, off);
-      if (FULL) cr[k] = bload<VEC>(cres, off);
-    }
+      for (int k = 0; k < KB; ++k) {
+        const int idx = tid + k * nthreads;
+        const int u = idx / brow, j = idx - u * brow;
+        const int t = u / R, r = u - t * R;
+        const uint32_t off = (uint32_t)(t * tokb + (r * p.G + g) * N + j * VEC);
+        br[k] = bload<VEC>(bres, off);
+        if (FULL) cr[k] = bload<VEC>(cres, off);
+      }
 #pragma unroll
-    for (int i = 0; i < KA; ++i) {
-      const int a = 2 * (i * nwaves + wave) + (lane >> 5);
-      const int t = lane & 31;
-      angr[i] = a < A ? buf_load1(ares, (uint32_t)(t * A + a) * 4u) : 0.f;
+      for (int i = 0; i < KA; ++i) {
+        const int a = 2 * (i * nwaves + wave) + (lane >> 5);
+        const int t = lane & 31;
+        angr[i] = a < A ? buf_load1(ares, (uint32_t)(t * A + a) * 4u) : 0.f;
+      }
     }
-    if (wave == 0) {
+    if (wave == (MERGED ? sw : 0)) {
       // tokens cs .. cs + Qt (one past the chunk, for the trapezoid look-ahead)
       const size_t sbase = ((size_t)b * p.L + cs) * p.H + h;
       const uint32_t nl = (uint32_t)min(Qt + 1, p.L - cs);
@@ -320,8 +356,8 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
   for (int c0 = t_begin; c0 < t_end; c0 += Qt) {
     const int nvalid = min(Qt, t_end - c0);
 
-    // ---- P0: scalars (wave 0, lane = token); x, B, C rows into LDS; z loads --
-    if (wave == 0) {
+    // ---- P0: scalars (one wave, lane = token); x, B, C rows into LDS; z loads --
+    if (wave == (MERGED ? sw : 0)) {
       const int t = lane;
       const float dt_n = next_lane_f(s_dt);
       const float tr_n = next_lane_f(s_trap);
@@ -364,10 +400,57 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
         }
       }
     }
+    if constexpr (MERGED) {
+      // cumulative angle of this lane's token for four pair angles (DPP scans
+      // over the 32 tokens of the half-wave), then the rotation in registers
+      const bool tok_ok = mt < nvalid;
+      float th[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) th[e] = scan32_f((mpair && tok_ok) ? mdt * angr[e] : 0.f);
+      vec_t k0 = br[0], k1 = br[1], q0 = cr[0], q1 = cr[1];
+      const floatx4 bb0 = lds_read4(bbL + mc0), bb1 = lds_read4(bbL + mc1);
+      k0 += bb0;
+      k1 += bb1;
+      if (FULL) {
+        q0 += lds_read4(cbL + mc0);
+        q1 += lds_read4(cbL + mc1);
+      }
+      if (mpair) {
+        const floatx4 r4 = lds_read4(run + mc0);
+        float thv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          thv[e] = r4[e] + th[e];
+          float sn, co;
+          sincos_acc(thv[e], &sn, &co);
+          const float u0 = k0[e], u1 = k1[e];
+          k0[e] = u0 * co - u1 * sn;
+          k1[e] = u0 * sn + u1 * co;
+          if (FULL) {
+            const float w0 = q0[e], w1 = q1[e];
+            q0[e] = w0 * co - w1 * sn;
+            q1[e] = w0 * sn + w1 * co;
+          }
+        }
+        if (mt == nvalid - 1) *reinterpret_cast<floatx4*>(run + mc0) = floatx4{thv[0], thv[1], thv[2], thv[3]};
+      }
+      if (!tok_ok) {
+        k0 = floatx4{0.f, 0.f, 0.f, 0.f};
+        k1 = k0;
+        q0 = k0;
+        q1 = k0;
+      }
+      vstore<VEC>(Kl + mt * ks + mc0, k0);
+      vstore<VEC>(Kl + mt * ks + mc1, k1);
+      if (FULL) {
+        vstore<VEC>(Ql + mt * ks + mc0, q0);
+        vstore<VEC>(Ql + mt * ks + mc1, q1);
+      }
+    }
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
       const int idx = tid + k * nthreads;
-      if (idx < Qt * R * brow) {
+      if (!MERGED && idx < Qt * R * brow) {
         const int u = idx / brow, j = idx - u * brow;
         const int t = u / R, r = u - t * R;
         const int v = (t << rsl) + r;
@@ -405,12 +488,12 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
         zm[i][1] = lane + 64 < P ? buf_load1(zres, (ob + lane + 64) * 4u) : 0.f;
       }
     }
-    lds_barrier();
+    if constexpr (!MERGED) lds_barrier();
 
     // ---- P2: cumulative angle (32-lane scans), cos / sin, and the rotation of
     //      the pairs (a, a + A) of every rank's key and query row, in place -----
 #pragma unroll
-    for (int i = 0; i < KA; ++i) {
+    for (int i = 0; i < (MERGED ? 0 : KA); ++i) {
       const int am = 2 * (i * nwaves + wave);
       if (am >= A) break;  // wave-uniform
       const int a = am + (lane >> 5);
@@ -443,15 +526,19 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
     if constexpr (FULL) {
       // ---- P4: S = Q K^T on lower 16x16 tiles, masked ------------------------
       constexpr int NPAIRS = TB * (TB + 1) / 2;
-      for (int pr = wave; pr < NPAIRS; pr += nwaves) {
+      // split S: unit = (tile pair, N-half), each masked into its own buffer
+      constexpr int SPL = MERGED ? 2 : 1;
+      for (int un = wave; un < NPAIRS * SPL; un += nwaves) {
+        const int pr = un / SPL, half = un - pr * SPL;
         int tb = 0, sb = pr;
         while (sb > tb) { sb -= tb + 1; ++tb; }
         floatx4 accs[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-        const float* qa = Ql + (tb * 16 + l16) * ks + 4 * lq;
-        const float* kb = Kl + (sb * 16 + l16) * ks + 4 * lq;
+        const float* qa = Ql + (tb * 16 + l16) * ks + 4 * lq + half * (NT / SPL) * 16;
+        const float* kb = Kl + (sb * 16 + l16) * ks + 4 * lq + half * (NT / SPL) * 16;
+        float* Mdst = half ? Ml2 : Ml;
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          if (nb < NT) {
+        for (int nb = 0; nb < 8 / SPL; ++nb) {
+          if (nb < NT / SPL) {
             const floatx4 a4 = lds_read4(qa + nb * 16);
             const floatx4 b4 = lds_read4(kb + nb * 16);
             floatx4& acc = accs[nb & 1];
@@ -472,7 +559,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
           float m = 0.f;
           if (ts_ < tt) m = acc[r] * (exp_fast(sc_cum[tt] - cum_s) * scl_s);
           else if (ts_ == tt) m = acc[r] * sc_gam[tt];
-          Ml[vt * ms + vs] = m;
+          Mdst[vt * ms + vs] = m;
         }
       }
       lds_barrier();
@@ -490,7 +577,8 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
 #pragma unroll
           for (int tb = 0; tb < TB; ++tb) {
             for (int sb = 0; sb <= tb; ++sb) {
-              const floatx4 a4 = lds_read4(Ml + (tb * 16 + l16) * ms + sb * 16 + 4 * lq);
+              floatx4 a4 = lds_read4(Ml + (tb * 16 + l16) * ms + sb * 16 + 4 * lq);
+              if constexpr (MERGED) a4 += lds_read4(Ml2 + (tb * 16 + l16) * ms + sb * 16 + 4 * lq);
               const float* xc = Xl + (sb * 16 + 4 * lq) * xs + p0 + l16;
               acc[tb] = mfma16(a4.x, xc[0], acc[tb]);
               acc[tb] = mfma16(a4.y, xc[xs], acc[tb]);
@@ -503,8 +591,8 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) ec[tb] = sc_ecum[(tb * 16 + l16) >> rsl];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j < ntw) {
+        for (int j = 0; j < JMAX; ++j) {
+          if (FIXED || j < ntw) {
             const int nb = nb0 + j;
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
@@ -525,7 +613,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
       // ---- P5b: state update h' = decay h' + K^T (w X) ------------------------
       const float dec = run[64];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Hacc[j] *= dec;
+      for (int j = 0; j < JMAX; ++j) Hacc[j] *= dec;
       for (int sb = 0; sb < TB; ++sb) {
         const int v0 = sb * 16 + 4 * lq;
         const float* xc = Xl + v0 * xs + p0 + l16;
@@ -535,8 +623,8 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
         const float xw3 = xc[3 * xs] * sc_w[(v0 + 3) >> rsl];
         const float* kc = Kl + v0 * ks + nb0 * 16 + l16;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j < ntw) {
+        for (int j = 0; j < JMAX; ++j) {
+          if (FIXED || j < ntw) {
             Hacc[j] = mfma16(kc[j * 16], xw0, Hacc[j]);
             Hacc[j] = mfma16(kc[ks + j * 16], xw1, Hacc[j]);
             Hacc[j] = mfma16(kc[2 * ks + j * 16], xw2, Hacc[j]);
@@ -616,12 +704,12 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
     float* st = p.ws_state + si * (size_t)(PT * NT) * 256;
     if (mma_wave) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j < ntw) *reinterpret_cast<floatx4*>(st + ((pt * NT + nb0 + j) * 64 + lane) * 4) = Hacc[j];
+      for (int j = 0; j < JMAX; ++j)
+        if (FIXED || j < ntw) *reinterpret_cast<floatx4*>(st + ((pt * NT + nb0 + j) * 64 + lane) * 4) = Hacc[j];
     }
     float* aux = p.ws_aux + si * kAux;
     if (tid < A) aux[tid] = run[tid];
-    if (tid == 0) aux[kAuxDecay] = seg_decay;
+    if (tid == (MERGED ? sw : 0) * 64) aux[kAuxDecay] = seg_decay;  // lane 0 of the scalar wave
   }
 }
 
@@ -677,6 +765,7 @@ void layout(ScanKParams& kp, bool full, bool mimo) {
   kp.o_kl = off; off += QV * kp.ks;
   kp.o_xl = off; off += QV * kp.xs;
   kp.o_ml = off; off += full ? QV * kp.ms : 0;
+  kp.o_ml2 = off; off += (full && !mimo && kp.NH > 1) ? QV * kp.ms : 0;
   kp.o_yl = off; off += full ? QV * kp.ys : 0;
   kp.o_yl2 = off; off += (full && kp.NH > 1) ? QV * kp.ys : 0;
   // the entry-state fold overlays [PT*16][NT*16+4] floats on the chunk buffers
@@ -769,7 +858,7 @@ hipError_t launch_scan(const ScanGeom& g, const ScanOperands& o, const ScanPlan&
   const unsigned bhn = g.B * g.H;
   // The N = 128, P = 64 layers (eight waves) get a variant with compile-time
   // strides; every other geometry runs the generic variant.
-  if (vec4 && g.N == 128 && g.P == 64 && nwaves == 8)
+  if (vec4 && g.N == 128 && g.P == 64 && nwaves == 8 && g.A % 4 == 0)
     return mimo ? launch_passes<4, true, 8, 4, 8>(kp, plan, bhn, block, stream)
                 : launch_passes<4, false, 8, 4, 8>(kp, plan, bhn, block, stream);
   if (vec4)
