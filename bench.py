@@ -17,7 +17,10 @@ CPU oracle timed on a bounded sample on the host cores.
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +30,20 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, GB/s
 FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 (vector and matrix)
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_b4_l2048_traffic.json")
+MAIN_KERNEL = "scan_chunk_kernel<4, true, false"  # main scan pass of the N=128/P=64 SISO variant
+COPY_KERNEL = "neg_kernel"  # torch.neg over a float32 buffer: reads and writes n*4 bytes once
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the sources the scan kernel is compiled from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "selective_state_space_mamba3_amd", "csrc")
+    for name in ("scan_fwd.hip", "common.h", "launch.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def parse():
@@ -38,7 +55,69 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=24, help="heads in the oracle's timed sample")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run plain device copies of this many MiB (counter calibration)")
+    ap.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="summarise rocprofv3 kernel-stats / FETCH_SIZE / WRITE_SIZE output into profiles/")
+    ap.add_argument("--calib-mib", type=int, default=256, help="copy size used in the calibrated runs")
     return ap.parse_args()
+
+
+def _read_csv(pattern):
+    files = glob.glob(pattern, recursive=True)
+    if not files:
+        raise FileNotFoundError(pattern)
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize(stats_dir, fetch_dir, write_dir, calib_mib):
+    """Write the kernel-time summary and the counter-derived traffic of the main
+    scan kernel.  FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by the
+    ratio between the known size of a plain device copy and what the same
+    counter reads for that copy in the same run."""
+    stats = _read_csv(os.path.join(stats_dir, "**", "*kernel_stats.csv"))
+    def counter(d, name):
+        rows = _read_csv(os.path.join(d, "**", "*counter_collection.csv"))
+        main = [float(r["Counter_Value"]) for r in rows
+                if r["Counter_Name"] == name and MAIN_KERNEL in r["Kernel_Name"]]
+        copy = [float(r["Counter_Value"]) for r in rows
+                if r["Counter_Name"] == name and COPY_KERNEL in r["Kernel_Name"]]
+        return sum(main) / len(main), sum(copy) / len(copy)
+    f_main, f_copy = counter(fetch_dir, "FETCH_SIZE")
+    w_main, w_copy = counter(write_dir, "WRITE_SIZE")
+    known = calib_mib * 1024 * 1024
+    fetch_scale = known / (f_copy * 1024.0)
+    write_scale = known / (w_copy * 1024.0)
+    out = {
+        "kernel": MAIN_KERNEL + ", ...> (main scan pass)",
+        "workload": "siso_b4_l2048 (B4 L2048 H24 G1 P64 N128 A32), bench.py default run",
+        "kernel_source_sha256": kernel_source_hash(),
+        "fetch_kib_per_dispatch": f_main, "write_kib_per_dispatch": w_main,
+        "copy_mib": calib_mib, "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
+        "fetch_scale": fetch_scale, "write_scale": write_scale,
+        "fetch_bytes": f_main * 1024.0 * fetch_scale, "write_bytes": w_main * 1024.0 * write_scale,
+        "kernel_stats": [{k: r[k] for k in ("Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage")}
+                         for r in stats],
+    }
+    out["traffic_bytes"] = out["fetch_bytes"] + out["write_bytes"]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps({k: v for k, v in out.items() if k != "kernel_stats"}, indent=1))
+    return 0
+
+
+def recorded_traffic():
+    """Counter-derived HBM bytes of the main kernel, if taken from the current source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes")
 
 
 def scan_algorithmic_bytes(B, L, H, G, P, N, A) -> int:
@@ -54,6 +133,8 @@ def preprocess_algorithmic_bytes(rows, W, I, M, H, A) -> int:
 
 def main():
     args = parse()
+    if args.summarize:
+        return summarize(*args.summarize, args.calib_mib)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: every (batch, head) "
               "chain is independent, so more GPUs would shard batch/heads with no communication.",
@@ -168,6 +249,15 @@ def main():
     wall = time.perf_counter() - wall0
     lib.m3_set_profile_events(None, None)
 
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * 1024 * 1024 // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty(n, device=dev)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     ms_total = t_begin.elapsed_time(t_end)
     ms_step = ms_total / K
     f = ctypes.c_float()
@@ -191,7 +281,10 @@ def main():
     # ---- CPU baseline: the oracle on a bounded sample ---------------------
     cpu = None
     if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
         import oracle as O
+        single = threadpool_limits(limits=1)  # numpy's BLAS on one thread: cores == 1 below
         hs = host_sets[0]
         ocfg = O.PreprocessConfig(I, N, H, A, G, 1, 1e-5, 1e-3, 0.1, 1e-4)
         c0 = time.perf_counter()
@@ -205,6 +298,7 @@ def main():
         O.siso_scan(oi["ch"], oi["bh"], oi["x"], oi["z"], oi["adt"], oi["dt"], oi["trap"], oi["angle"],
                     hs["c_bias"], hs["b_bias"], hs["d"], O.SsmConfig(B, L, H, G, P, N, A), heads=hsel)
         t_scan = time.perf_counter() - c0
+        single.restore_original_limits()
         est = t_pre + t_scan * H / len(hsel)
         cpu = {"value": tokens / est, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                "sample": (f"float64 oracle, one thread: preprocess of all {rows} packed rows "
@@ -229,8 +323,8 @@ def main():
                    "batch": B, "seq_len": L, "heads": H, "groups": G, "head_dim": P, "state": N,
                    "rope_angles": A, "has_z": True, "has_d": True, "input_sets": args.sets},
         "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": kern_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "scan_chunk_kernel<32, true> (main scan pass)",
+                     "frac": kern_gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(),
+                     "kernel": "scan_chunk_kernel<4, true, false, 8, 4, 8> (main scan pass)",
                      "kernel_ms": kern_avg, "algorithmic_bytes": scan_bytes,
                      "fp32_tflops_min_work": min_flops / (kern_avg * 1e-3) / 1e12,
                      "fp32_frac": min_flops / (kern_avg * 1e-3) / 1e12 / FP32_PEAK_TFLOPS},
