@@ -22,10 +22,14 @@ __device__ __forceinline__ floatx4 mfma16(float a, float b, floatx4 c) {
 // terms that are themselves negligible once |x| is large.
 __device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
 
-// u * sigmoid(u) with the hardware exp2 and reciprocal (about 2 ulp).
-__device__ __forceinline__ float silu_fast(float u) {
-  return u * __builtin_amdgcn_rcpf(1.f + exp_fast(-u));
+// sigmoid(u) with the hardware exp2 and reciprocal (a few ulp); saturates
+// cleanly: exp2 of a large argument is +inf and its reciprocal zero.
+__device__ __forceinline__ float sigmoid_fast(float u) {
+  return __builtin_amdgcn_rcpf(1.f + exp_fast(-u));
 }
+
+// u * sigmoid(u) with the hardware exp2 and reciprocal (about 2 ulp).
+__device__ __forceinline__ float silu_fast(float u) { return u * sigmoid_fast(u); }
 
 // Cross-lane helpers on DPP (register-to-register lane shifts; no LDS).
 template <int CTRL, int ROW_MASK = 0xf>
@@ -131,8 +135,11 @@ __device__ __forceinline__ floatx4 lds_read4(const float* p) {
 // masks partial chunks without branches.  0x00020000 is the gfx9-family
 // third descriptor word for 32-bit raw data.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// The size must be wave-uniform; readfirstlane tells the compiler so, which
+// keeps the descriptor in scalar registers.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
 }
 __device__ __forceinline__ floatx4 buf_load4(rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));

@@ -222,8 +222,68 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
   // where U_i was built with the angle restarted at zero inside segment i, so
   // its state axis is turned by theta_i = the summed angle of the segments
   // before i (the keys it holds are rot(theta_i + local) = rot(theta_i) rot(local)).
-  // U_i passes through LDS in [p][n] layout for the pair rotation.
-  if (FULL && seg > 0) {
+  //
+  // With N = 128 split into two halves of 64 state rows per wave and A a
+  // multiple of 16 with 2A <= 64, both members of every rotated pair
+  // (a, a + A) sit in the same lane and register of one wave (blocks a / 16
+  // and a / 16 + A / 16), so the fold rotates in registers, with all
+  // summaries loaded at once and cos / sin of every theta_i from an LDS table.
+  // Otherwise U_i passes through LDS in [p][n] layout for the pair rotation.
+  const bool reg_fold = FIXED && NTC == 8 && !MIMO && (A == 0 || A == 16 || A == 32) && p.nseg <= 64;
+  if (FULL && seg > 0 && reg_fold) {
+    const size_t sbase = (size_t)bh * (p.nseg - 1);
+    float* CSt = lds;  // [seg][A] cos, then [seg][A] sin; overlays the chunk buffers (unused yet)
+    float* SNt = CSt + seg * A;
+    for (int idx = tid; idx < seg * A; idx += nthreads) {
+      const int i = idx / A, a = idx - i * A;
+      float th = 0.f;
+      for (int k = 0; k < i; ++k) th += p.ws_aux[(sbase + k) * kAux + a];
+      float sn, cs;
+      sincos_acc(th, &sn, &cs);
+      CSt[idx] = cs;
+      SNt[idx] = sn;
+    }
+    for (int a = tid; a < A; a += nthreads) {
+      float th = 0.f;
+      for (int k = 0; k < seg; ++k) th += p.ws_aux[(sbase + k) * kAux + a];
+      run[a] = th;
+    }
+    __syncthreads();
+    for (int i = 0; i < seg; ++i) {
+      const float* st = p.ws_state + (sbase + i) * (size_t)(PT * NT) * 256;
+      floatx4 u[JMAX];
+#pragma unroll
+      for (int j = 0; j < JMAX; ++j) u[j] = *reinterpret_cast<const floatx4*>(st + ((pt * NT + nb0 + j) * 64 + lane) * 4);
+      if (nb0 == 0 && A > 0) {
+        const float* ci = CSt + i * A;
+        const float* si = SNt + i * A;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (A == 32) {
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+              const int a = 16 * jb + 4 * lq + r;
+              const float c = ci[a], sv = si[a];
+              const float u0 = u[jb][r], u1 = u[jb + 2][r];
+              u[jb][r] = u0 * c - u1 * sv;
+              u[jb + 2][r] = u0 * sv + u1 * c;
+            }
+          } else {  // A == 16
+            const int a = 4 * lq + r;
+            const float c = ci[a], sv = si[a];
+            const float u0 = u[0][r], u1 = u[1][r];
+            u[0][r] = u0 * c - u1 * sv;
+            u[1][r] = u0 * sv + u1 * c;
+          }
+        }
+      }
+      const float dec = p.ws_aux[(sbase + i) * kAux + kAuxDecay];
+#pragma unroll
+      for (int j = 0; j < JMAX; ++j) Hacc[j] = dec * Hacc[j] + u[j];
+    }
+    __syncthreads();
+    for (int i = tid; i < 2 * seg * A; i += nthreads) CSt[i] = 0.f;  // restore the zeroed chunk buffers
+  } else if (FULL && seg > 0) {
     __syncthreads();
     float* Ub = lds;  // [PT*16][NT*16 + 4], overlays the chunk buffers (unused yet)
     const int us = NT * 16 + 4;
@@ -364,14 +424,14 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
       const bool ok = t < nvalid;
       const float dt_v = ok ? s_dt : 0.f;
       const float adt_v = ok ? s_adt : 0.f;
-      const float gam = ok ? sigmoidf_acc(s_trap) * dt_v : 0.f;
+      const float gam = ok ? sigmoid_fast(s_trap) * dt_v : 0.f;
       float scl = gam;
-      if (ok && c0 + t + 1 < p.L) scl = gam + (1.f - sigmoidf_acc(tr_n)) * dt_n;
+      if (ok && c0 + t + 1 < p.L) scl = gam + (1.f - sigmoid_fast(tr_n)) * dt_n;
       const float cum = scan64_f(adt_v);
       const float cum_last = read_lane_f(cum, 63);  // padding lanes add zero
       if (t < Qt) {
         sc_cum[t] = cum;
-        sc_ecum[t] = expf(cum);
+        sc_ecum[t] = exp_fast(cum);
         sc_gam[t] = gam;
         sc_scl[t] = scl;
         sc_w[t] = ok ? expf(cum_last - cum) * scl : 0.f;

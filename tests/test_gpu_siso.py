@@ -24,6 +24,11 @@ SMALL = [
     ("P48_N80_A40_L100", Dims(1, 100, 4, 4, 48, 80, 40), 2008, (1e-3, 0.1)),
     ("P16_N128_A64_L70_flags_off", Dims(2, 70, 2, 1, 16, 128, 64, has_z=False, has_d=False), 2009,
      (1e-3, 0.1)),
+    ("P64_N128_A16_L150_G2_noz", Dims(2, 150, 4, 2, 64, 128, 16, has_z=False), 2011, (1e-3, 0.1)),
+    ("P64_N128_A0_L97_nod", Dims(1, 97, 3, 1, 64, 128, 0, has_d=False), 2012, (1e-3, 0.1)),
+    ("P64_N128_A16_L31_flags_off", Dims(2, 31, 2, 1, 64, 128, 16, has_z=False, has_d=False), 2013,
+     (1e-3, 0.1)),
+    ("P64_N128_A8_L70", Dims(1, 70, 2, 1, 64, 128, 8), 2014, (1e-3, 0.1)),
 ]
 
 
@@ -51,6 +56,24 @@ def test_siso_forced_segments(nseg, monkeypatch):
     inp = ssm_inputs(d, seed=2020)
     got = gpu_siso(to_dev(inp), d).cpu().numpy()
     assert_parity(got, oracle_siso(inp, d), f"segments_{nseg}")
+
+
+@pytest.mark.parametrize("nseg", [4, 10])
+def test_siso_forced_segments_a16(nseg, monkeypatch):
+    monkeypatch.setenv("M3_SCAN_NSEG", str(nseg))
+    d = Dims(2, 300, 3, 1, 64, 128, 16, has_z=False)
+    inp = ssm_inputs(d, seed=2021)
+    got = gpu_siso(to_dev(inp), d).cpu().numpy()
+    assert_parity(got, oracle_siso(inp, d), f"segments_a16_{nseg}")
+
+
+def test_siso_sixty_four_segments(monkeypatch):
+    # one 32-token chunk per segment: the entry state folds up to 63 summaries
+    monkeypatch.setenv("M3_SCAN_NSEG", "64")
+    d = Dims(1, 2048, 2, 1, 64, 128, 32)
+    inp = ssm_inputs(d, seed=2022)
+    got = gpu_siso(to_dev(inp), d).cpu().numpy()
+    assert_parity(got, oracle_siso(inp, d), "segments_64")
 
 
 def test_siso_deterministic():
