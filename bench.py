@@ -9,7 +9,10 @@ the 256 MB last-level cache cannot hold a whole step's working set.
 
 Prints one JSON line: tokens/s of the step, the scan kernel's roofline
 (algorithmic bytes / live HIP-event duration against 8 TB/s), and the float64
-CPU oracle timed on a bounded sample on the host cores.
+CPU oracle timed on a bounded sample on the host cores.  After the timed
+region it also measures the other rows of the path at their own workloads
+("rows"): the decode step at B256 H32 (1 token per step, HBM-bound) and the
+MIMO scan at B8 L4096 H32 R4 (FP32-matrix-bound).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
 """
@@ -60,7 +63,93 @@ def parse():
     ap.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="summarise rocprofv3 kernel-stats / FETCH_SIZE / WRITE_SIZE output into profiles/")
     ap.add_argument("--calib-mib", type=int, default=256, help="copy size used in the calibrated runs")
+    ap.add_argument("--no-rows", action="store_true", help="skip the decode-step and MIMO measurements")
     return ap.parse_args()
+
+
+def decode_algorithmic_bytes(B, H, G, P, N, A) -> int:
+    """State read and written once, the small states read and written, the
+    token operands read and out written (fp32)."""
+    return 4 * (2 * B * H * P * N + 2 * B * G * N + 3 * B * H * P + 3 * B * H + B * A
+                + 2 * B * H * A + 2 * B * H * N + 2 * B * H * P + 2 * H * N + H)
+
+
+def measure_rows(torch, m3, lib, hip, new_event, dev):
+    """Decode-step and MIMO-scan rows, each at its own workload, timed with HIP
+    events on the stream the kernels run on."""
+    from workloads import WORKLOADS, decode_states, ssm_inputs, step_inputs
+    ops11 = ("c", "b", "x", "z", "adt", "dt", "trap", "angle", "c_bias", "b_bias", "d")
+    rows = {}
+
+    # decode: 256 x 32 heads, state [256, 32, 64, 128]; eight staged token sets
+    w = WORKLOADS["decode_b256"]
+    d = w.dims
+    st = {k: torch.from_numpy(v).to(dev) for k, v in decode_states(d, w.seed).items()}
+    toks = [{k: torch.from_numpy(v).to(dev) for k, v in step_inputs(d, w.seed, s).items()} for s in range(8)]
+    cfg = m3.SsmConfig(d.B, 1, d.H, d.G, d.P, d.N, d.A)
+    out = torch.empty(d.B, 1, d.H, d.P, device=dev)
+
+    def one(i):
+        t = toks[i % len(toks)]
+        m3.m3_siso_step(*[t[k] for k in ops11], st["ssm_state"], st["angle_state"], st["k_state"],
+                        st["v_state"], cfg, out=out)
+    for i in range(20):
+        one(i)
+    torch.cuda.synchronize()
+    n_steps = 256
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n_steps):
+        one(i)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / n_steps
+    byt = decode_algorithmic_bytes(d.B, d.H, d.groups, d.P, d.N, d.A)
+    rows["decode_step"] = {"workload": "decode_b256: B256 H32 P64 N128 A32, one token per step",
+                           "us_per_step": us, "tokens_per_s": d.B / (us * 1e-6),
+                           "algorithmic_bytes": byt, "gbs": byt / (us * 1e-6) / 1e9,
+                           "hbm_frac": byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "bound": "hbm",
+                           "steps_timed": n_steps}
+    del st, toks, out
+
+    # MIMO: B8 L4096 H32 P64 N128 A32 R4 with output norm
+    w = WORKLOADS["mimo_b8_l4096_r4"]
+    d = w.dims
+    inp = {k: torch.from_numpy(v).to(dev) for k, v in ssm_inputs(d, seed=w.seed, dt_range=w.dt_range).items()}
+    cfg = m3.SsmConfig(d.B, d.L, d.H, d.G, d.P, d.N, d.A, d.R, True, True, True)
+    ops = [inp[k] for k in ops11 + ("mimo_x", "mimo_z", "mimo_o", "norm_weight")]
+    ws = torch.empty(max(1, m3.mimo_fwd_workspace_bytes(cfg)), dtype=torch.uint8, device=dev)
+    out = torch.empty(d.B, d.L, d.H, d.P, device=dev)
+    for _ in range(3):
+        m3.m3_mimo_fwd(*ops, cfg, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    kms, cms = [], []
+    f = ctypes.c_float()
+    for _ in range(10):
+        e0, e1 = new_event(), new_event()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        lib.m3_set_profile_events(e0, e1)
+        a.record()
+        m3.m3_mimo_fwd(*ops, cfg, out=out, workspace=ws)
+        b.record()
+        torch.cuda.synchronize()
+        lib.m3_set_profile_events(None, None)
+        hip.hipEventElapsedTime(ctypes.byref(f), e0, e1)
+        kms.append(f.value)
+        cms.append(a.elapsed_time(b))
+        hip.hipEventDestroy(e0)
+        hip.hipEventDestroy(e1)
+    km, cm = float(np.median(kms)), float(np.median(cms))
+    Bm, Lm, Hm, Gm, Pm, Nm, Am, Rm = d.B, d.L, d.H, d.groups, d.P, d.N, d.A, d.R
+    flops = 4 * Rm * Nm * Pm * Bm * Lm * Hm
+    byt = 4 * (3 * Bm * Lm * Hm * Pm + 2 * Bm * Lm * Rm * Gm * Nm + 3 * Bm * Lm * Hm + Bm * Lm * Am
+               + 2 * Hm * Rm * Nm + Hm + 3 * Hm * Rm * Pm + Hm * Pm)
+    rows["mimo_scan"] = {"workload": "mimo_b8_l4096_r4: B8 L4096 H32 P64 N128 A32 R4, output norm",
+                         "call_ms": cm, "main_kernel_ms": km, "tokens_per_s": Bm * Lm / (cm * 1e-3),
+                         "min_flops": flops, "fp32_tflops": flops / (cm * 1e-3) / 1e12,
+                         "fp32_frac": flops / (cm * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, "bound": "fp32 matrix",
+                         "algorithmic_bytes": byt, "gbs": byt / (cm * 1e-3) / 1e9}
+    return rows
 
 
 def _read_csv(pattern):
@@ -258,6 +347,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    rows_out = None
+    if not args.no_rows:
+        del sets, ws
+        torch.cuda.empty_cache()
+        rows_out = measure_rows(torch, m3, lib, hip, new_event, dev)
+
     ms_total = t_begin.elapsed_time(t_end)
     ms_step = ms_total / K
     f = ctypes.c_float()
@@ -337,6 +432,7 @@ def main():
                        "hbm_frac": pre_bytes / (pre_avg * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "wall_s_timed": wall,
         "parity": parity,
+        "rows": rows_out,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),
     }

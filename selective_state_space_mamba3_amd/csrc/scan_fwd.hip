@@ -114,19 +114,20 @@ __device__ __forceinline__ void set_comp(float& v, int, float x) { v = x; }
 
 // NTC / PTC / NWC fix the 16-wide block counts of N and P and the number of
 // waves at compile time (0 = taken from the parameters), so that LDS row
-// strides are constants and accesses fold into immediate offsets.  Fixed-size
-// SISO variants ask for two resident workgroups per CU (NWC / 2 waves per
-// SIMD, at most 128 VGPRs); MIMO, with R query rows per token, keeps its
-// registers at one workgroup per CU instead of spilling.
-template <int VEC, bool FULL, bool MIMO, int NTC, int PTC, int NWC>
-__global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC / 2) : 1) void scan_chunk_kernel(ScanKParams p) {
+// strides are constants and accesses fold into immediate offsets; RSC fixes
+// the rank stride of the virtual rows (0 = from the parameters).  Fixed-size
+// variants ask for two resident workgroups per CU (NWC / 2 waves per SIMD,
+// at most 128 VGPRs).
+template <int VEC, bool FULL, bool MIMO, int NTC, int PTC, int NWC, int RSC>
+__global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan_chunk_kernel(ScanKParams p) {
   using vec_t = typename VecOf<VEC>::T;
   constexpr int QV = kQV;
   constexpr int TB = QV / 16;
   constexpr int KX = VEC == 4 ? 1 : 4;  // x / z items per thread (block >= Qt*P/(VEC*KX) threads)
   constexpr int KB = VEC == 4 ? 2 : 8;  // B / C row items per thread (block >= QV*N/(VEC*KB) threads)
   constexpr int KA = 4;         // angle values per lane (launch gives >= A/8 waves)
-  constexpr int KZM = 8;        // tokens per wave in the MIMO epilogue
+  // tokens per wave in the MIMO epilogue (a chunk holds QV / RS tokens)
+  constexpr int KZM = (RSC > 0 && NWC > 0) ? ((QV / RSC) > NWC ? (QV / RSC) / NWC : 1) : 8;
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -149,7 +150,8 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
   const int R = MIMO ? p.R : 1;
   const int RG = R * p.G;
   const int Qt = MIMO ? p.Qt : QV;
-  const int rsl = MIMO ? p.rs_log2 : 0;
+  constexpr int RSL_C = RSC >= 8 ? 3 : RSC >= 4 ? 2 : RSC >= 2 ? 1 : 0;
+  const int rsl = RSC > 0 ? RSL_C : (MIMO ? p.rs_log2 : 0);
   const int NT = NTC ? NTC : p.NT, PT = PTC ? PTC : p.PT;
   const int NH = NTC ? (NTC > 4 ? 2 : 1) : p.NH;
   const int NTH = NTC ? (NTC + NH - 1) / NH : p.NTH;
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
   // B / C rows (N / 8 == 2 * waves), either a rotated pair group
   // (a0..a0+3, a0+A..a0+A+3) or a plain group, and rotates it in registers;
   // S is split over six waves (three tile pairs x two N-halves).
-  constexpr bool MERGED = FIXED && !MIMO && NTC * 16 == 16 * NWC;
+  constexpr bool MERGED = FIXED && NTC * 16 == 16 * NWC && RSC > 0;
   const int sw = nwaves - 1;  // wave that computes the per-token scalars
 
   float* Ql = lds + p.o_ql;   // [QV][ks] C (+bias), pairs rotated in place   (main pass)
@@ -345,8 +347,12 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
   vec_t xr[KX], br[KB], cr[KB];
   float angr[KA];
   float s_dt = 0.f, s_adt = 0.f, s_trap = 0.f;
-  // merged layout: this lane's token and 8-column group of the B / C rows
+  // merged layout: this lane's virtual row (token mtok, rank mr) and 8-column
+  // group of the B / C rows; rows of padding ranks (mr >= R) stay zero
   const int mt = lane & 31;
+  const int mtok = mt >> rsl;
+  const int mr = mt & ((1 << rsl) - 1);
+  const int mrc = mr < R ? mr : 0;  // a rank that exists, for addressing
   const int mgrp = 2 * wave + (lane >> 5);
   const bool mpair = MERGED && mgrp < A / 4;
   const int mc0 = mpair ? 4 * mgrp : 2 * A + 8 * (mgrp - A / 4);
@@ -366,7 +372,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
       xr[k] = bload<VEC>(xres, (uint32_t)(t * tokx + pv * VEC));
     }
     if constexpr (MERGED) {
-      const uint32_t row = (uint32_t)(mt * tokb + g * N);
+      const uint32_t row = (uint32_t)(mtok * tokb + (mrc * p.G + g) * N);
       br[0] = bload<VEC>(bres, row + mc0);
       br[1] = bload<VEC>(bres, row + mc1);
       if (FULL) {
@@ -374,11 +380,11 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
         cr[1] = bload<VEC>(cres, row + mc1);
       }
       if (mpair) {
-        const floatx4 a4 = buf_load4(ares, (uint32_t)(mt * A + mc0) * 4u);
+        const floatx4 a4 = buf_load4(ares, (uint32_t)(mtok * A + mc0) * 4u);
         angr[0] = a4.x; angr[1] = a4.y; angr[2] = a4.z; angr[3] = a4.w;
       }
       const size_t sbase = ((size_t)b * p.L + cs) * p.H + h;
-      mdt = buf_load1(make_rsrc(p.dt + sbase, (uint32_t)(nv * p.H * 4)), (uint32_t)(mt * p.H) * 4u);
+      mdt = buf_load1(make_rsrc(p.dt + sbase, (uint32_t)(nv * p.H * 4)), (uint32_t)(mtok * p.H) * 4u);
     } else {
 #pragma unroll
       for (int k = 0; k < KB; ++k) {
@@ -462,18 +468,22 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
     }
     if constexpr (MERGED) {
       // cumulative angle of this lane's token for four pair angles (DPP scans
-      // over the 32 tokens of the half-wave), then the rotation in registers
-      const bool tok_ok = mt < nvalid;
+      // over the 32 virtual rows of the half-wave; only rank 0 rows add, so
+      // every rank of a token sees that token's angle), then the rotation in
+      // registers
+      const bool tok_ok = mtok < nvalid && mr < R;
       float th[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) th[e] = scan32_f((mpair && tok_ok) ? mdt * angr[e] : 0.f);
+      for (int e = 0; e < 4; ++e) th[e] = scan32_f((mpair && tok_ok && mr == 0) ? mdt * angr[e] : 0.f);
       vec_t k0 = br[0], k1 = br[1], q0 = cr[0], q1 = cr[1];
-      const floatx4 bb0 = lds_read4(bbL + mc0), bb1 = lds_read4(bbL + mc1);
+      const float* bbr = bbL + mrc * N;
+      const floatx4 bb0 = lds_read4(bbr + mc0), bb1 = lds_read4(bbr + mc1);
       k0 += bb0;
       k1 += bb1;
       if (FULL) {
-        q0 += lds_read4(cbL + mc0);
-        q1 += lds_read4(cbL + mc1);
+        const float* cbr = cbL + mrc * N;
+        q0 += lds_read4(cbr + mc0);
+        q1 += lds_read4(cbr + mc1);
       }
       if (mpair) {
         const floatx4 r4 = lds_read4(run + mc0);
@@ -492,7 +502,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? (MIMO ? NWC / 4 : NWC 
             q1[e] = w0 * sn + w1 * co;
           }
         }
-        if (mt == nvalid - 1) *reinterpret_cast<floatx4*>(run + mc0) = floatx4{thv[0], thv[1], thv[2], thv[3]};
+        if (mt == ((nvalid - 1) << rsl)) *reinterpret_cast<floatx4*>(run + mc0) = floatx4{thv[0], thv[1], thv[2], thv[3]};
       }
       if (!tok_ok) {
         k0 = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -825,7 +835,7 @@ void layout(ScanKParams& kp, bool full, bool mimo) {
   kp.o_kl = off; off += QV * kp.ks;
   kp.o_xl = off; off += QV * kp.xs;
   kp.o_ml = off; off += full ? QV * kp.ms : 0;
-  kp.o_ml2 = off; off += (full && !mimo && kp.NH > 1) ? QV * kp.ms : 0;
+  kp.o_ml2 = off; off += (full && kp.NH > 1) ? QV * kp.ms : 0;
   kp.o_yl = off; off += full ? QV * kp.ys : 0;
   kp.o_yl2 = off; off += (full && kp.NH > 1) ? QV * kp.ys : 0;
   // the entry-state fold overlays [PT*16][NT*16+4] floats on the chunk buffers
@@ -839,7 +849,7 @@ void layout(ScanKParams& kp, bool full, bool mimo) {
   kp.lds_floats = off;
 }
 
-template <int VEC, bool FULL, bool MIMO, int NTC, int PTC, int NWC>
+template <int VEC, bool FULL, bool MIMO, int NTC, int PTC, int NWC, int RSC>
 hipError_t launch_one(const ScanKParams& kp, unsigned grid, unsigned block, hipStream_t stream) {
   const size_t lds_bytes = (size_t)kp.lds_floats * sizeof(float);
   // Dynamic LDS above 64 KiB needs the opt-in attribute on some runtimes;
@@ -847,22 +857,22 @@ hipError_t launch_one(const ScanKParams& kp, unsigned grid, unsigned block, hipS
   // runtime does not know the attribute.
   static size_t attr_bytes = 64 * 1024;
   if (lds_bytes > attr_bytes) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC, RSC>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) != hipSuccess)
       (void)hipGetLastError();
     attr_bytes = lds_bytes;
   }
-  hipLaunchKernelGGL((scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC>), dim3(grid), dim3(block), lds_bytes, stream, kp);
+  hipLaunchKernelGGL((scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC, RSC>), dim3(grid), dim3(block), lds_bytes, stream, kp);
   return hipGetLastError();
 }
 
-template <int VEC, bool MIMO, int NTC, int PTC, int NWC>
+template <int VEC, bool MIMO, int NTC, int PTC, int NWC, int RSC>
 hipError_t launch_passes(ScanKParams kp, const ScanPlan& plan, unsigned bhn, unsigned block,
                          hipStream_t stream) {
   if (plan.nseg > 1) {
     ScanKParams ka = kp;
     layout(ka, false, MIMO);
-    hipError_t e = launch_one<VEC, false, MIMO, NTC, PTC, NWC>(ka, bhn * (unsigned)(plan.nseg - 1), block, stream);
+    hipError_t e = launch_one<VEC, false, MIMO, NTC, PTC, NWC, RSC>(ka, bhn * (unsigned)(plan.nseg - 1), block, stream);
     if (e != hipSuccess) return e;
   }
   layout(kp, true, MIMO);
@@ -871,7 +881,7 @@ hipError_t launch_passes(ScanKParams kp, const ScanPlan& plan, unsigned bhn, uns
     hipError_t e = hipEventRecord(pe.start, stream);
     if (e != hipSuccess) return e;
   }
-  hipError_t e = launch_one<VEC, true, MIMO, NTC, PTC, NWC>(kp, bhn * (unsigned)plan.nseg, block, stream);
+  hipError_t e = launch_one<VEC, true, MIMO, NTC, PTC, NWC, RSC>(kp, bhn * (unsigned)plan.nseg, block, stream);
   if (e == hipSuccess && pe.stop) e = hipEventRecord(pe.stop, stream);
   return e;
 }
@@ -917,15 +927,21 @@ hipError_t launch_scan(const ScanGeom& g, const ScanOperands& o, const ScanPlan&
   const unsigned block = 64u * nwaves;
   const unsigned bhn = g.B * g.H;
   // The N = 128, P = 64 layers (eight waves) get a variant with compile-time
-  // strides; every other geometry runs the generic variant.
-  if (vec4 && g.N == 128 && g.P == 64 && nwaves == 8 && g.A % 4 == 0)
-    return mimo ? launch_passes<4, true, 8, 4, 8>(kp, plan, bhn, block, stream)
-                : launch_passes<4, false, 8, 4, 8>(kp, plan, bhn, block, stream);
+  // strides and rank stride; every other geometry runs the generic variant.
+  if (vec4 && g.N == 128 && g.P == 64 && nwaves == 8 && g.A % 4 == 0) {
+    if (!mimo) return launch_passes<4, false, 8, 4, 8, 1>(kp, plan, bhn, block, stream);
+    switch (kp.RS) {
+      case 1: return launch_passes<4, true, 8, 4, 8, 1>(kp, plan, bhn, block, stream);
+      case 2: return launch_passes<4, true, 8, 4, 8, 2>(kp, plan, bhn, block, stream);
+      case 4: return launch_passes<4, true, 8, 4, 8, 4>(kp, plan, bhn, block, stream);
+      default: return launch_passes<4, true, 8, 4, 8, 8>(kp, plan, bhn, block, stream);
+    }
+  }
   if (vec4)
-    return mimo ? launch_passes<4, true, 0, 0, 0>(kp, plan, bhn, block, stream)
-                : launch_passes<4, false, 0, 0, 0>(kp, plan, bhn, block, stream);
-  return mimo ? launch_passes<1, true, 0, 0, 0>(kp, plan, bhn, block, stream)
-              : launch_passes<1, false, 0, 0, 0>(kp, plan, bhn, block, stream);
+    return mimo ? launch_passes<4, true, 0, 0, 0, 0>(kp, plan, bhn, block, stream)
+                : launch_passes<4, false, 0, 0, 0, 0>(kp, plan, bhn, block, stream);
+  return mimo ? launch_passes<1, true, 0, 0, 0, 0>(kp, plan, bhn, block, stream)
+              : launch_passes<1, false, 0, 0, 0, 0>(kp, plan, bhn, block, stream);
 }
 
 }  // namespace

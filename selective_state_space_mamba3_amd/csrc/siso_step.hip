@@ -136,6 +136,102 @@ __global__ __launch_bounds__(256) void siso_step_kernel(StepKParams p) {
     p.ang_state[sidx * A + a] = fmaf(dtv, p.angle[(size_t)b * A + a], p.ang_state[sidx * A + a]);
 }
 
+// N = 128, P = 64 with a 16-byte aligned state: 256 threads per (batch,
+// head).  Wave w, pass i covers state rows 8 i + 2 w (lanes 0-31) and
+// 8 i + 2 w + 1 (lanes 32-63), one 16-byte item per lane, so each load or
+// store instruction moves 1 KiB of contiguous state.  All eight passes are
+// loaded before anything else happens, so one memory round trip covers the
+// whole 32 KiB state; the row sums of h Q are 32-lane DPP reductions.
+__global__ __launch_bounds__(256) void siso_step_n128p64_kernel(StepKParams p) {
+  constexpr int N = 128, P = 64;
+  __shared__ __attribute__((aligned(16))) float Kv[N];
+  __shared__ __attribute__((aligned(16))) float Qv[N];
+  __shared__ __attribute__((aligned(16))) float kp[N];
+  __shared__ float vp[P], xv[P], yv[P];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int bh = blockIdx.x;
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int g = h / (p.H / p.G);
+  const int A = p.A;
+  const size_t sidx = (size_t)bh;  // scalar index for [B,1,H]
+  float* st = p.ssm + sidx * (size_t)P * N;
+  const int c4 = 4 * (lane & 31);  // this lane's four state columns
+  const int r0 = 2 * wave + (lane >> 5);  // row of pass 0; pass i adds 8 i
+  floatx4 hv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) hv[i] = *reinterpret_cast<const floatx4*>(st + (size_t)(r0 + 8 * i) * N + c4);
+
+  const float dtv = p.dt[sidx];
+  const float alpha = expf(p.adt[sidx]);
+  const float lam = sigmoidf_acc(p.trap[sidx]);
+  const float gam = lam * dtv;
+  const float beta = (1.f - lam) * dtv * alpha;
+  // old previous key / value, the new x, and the rotated key and query
+  if (tid < N) kp[tid] = p.k_state[sidx * N + tid];
+  if (tid < P) {
+    vp[tid] = p.v_state[sidx * P + tid];
+    xv[tid] = p.x[sidx * P + tid];
+  }
+  const size_t row = ((size_t)b * p.G + g) * N;
+  const size_t brow = (size_t)h * N;
+  if (tid < N - A) {
+    const int j = tid;
+    if (j < A) {
+      const float th = fmaf(dtv, p.angle[(size_t)b * A + j], p.ang_state[sidx * A + j]);
+      float s, co;
+      sincos_acc(th, &s, &co);
+      const float b0 = p.b[row + j] + p.b_bias[brow + j];
+      const float b1 = p.b[row + j + A] + p.b_bias[brow + j + A];
+      const float c0 = p.c[row + j] + p.c_bias[brow + j];
+      const float c1 = p.c[row + j + A] + p.c_bias[brow + j + A];
+      Kv[j] = b0 * co - b1 * s;
+      Kv[j + A] = b0 * s + b1 * co;
+      Qv[j] = c0 * co - c1 * s;
+      Qv[j + A] = c0 * s + c1 * co;
+    } else {
+      const int n = j + A;
+      Kv[n] = p.b[row + n] + p.b_bias[brow + n];
+      Qv[n] = p.c[row + n] + p.c_bias[brow + n];
+    }
+  }
+  __syncthreads();
+
+  const floatx4 KK = *reinterpret_cast<const floatx4*>(Kv + c4);
+  const floatx4 QQ = *reinterpret_cast<const floatx4*>(Qv + c4);
+  const floatx4 kk = *reinterpret_cast<const floatx4*>(kp + c4);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = r0 + 8 * i;
+    const float cx = gam * xv[r];
+    const float cv = beta * vp[r];
+    floatx4 v = hv[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = fmaf(cx, KK[e], fmaf(cv, kk[e], alpha * v[e]));
+    *reinterpret_cast<floatx4*>(st + (size_t)r * N + c4) = v;
+    float acc = v[0] * QQ[0];
+    acc = fmaf(v[1], QQ[1], acc);
+    acc = fmaf(v[2], QQ[2], acc);
+    acc = fmaf(v[3], QQ[3], acc);
+    acc = scan32_f(acc);  // lane 31 / 63 hold the row sums
+    if ((lane & 31) == 31) yv[r] = acc;
+  }
+  __syncthreads();
+
+  const float dh = p.has_d ? p.d[h] : 0.f;
+  if (tid < P) {
+    float y = yv[tid];
+    if (p.has_d) y = fmaf(dh, xv[tid], y);
+    if (p.has_z) y *= siluf_acc(p.z[sidx * P + tid]);
+    p.out[sidx * P + tid] = y;
+    p.v_state[sidx * P + tid] = xv[tid];
+  }
+  if (tid < N) p.k_state[sidx * N + tid] = Kv[tid];
+  if (tid < A) p.ang_state[sidx * A + tid] = fmaf(dtv, p.angle[(size_t)b * A + tid], p.ang_state[sidx * A + tid]);
+}
+
 }  // namespace
 
 hipError_t launch_siso_step(const ScanGeom& g, const ScanOperands& o, const StepStates& s,
@@ -147,6 +243,10 @@ hipError_t launch_siso_step(const ScanGeom& g, const ScanOperands& o, const Step
   kp.B = g.B; kp.H = g.H; kp.G = g.G; kp.P = g.P; kp.N = g.N; kp.A = g.A;
   kp.has_z = g.has_z; kp.has_d = g.has_d;
   const bool vec4 = (g.N % 4u) == 0u && (reinterpret_cast<uintptr_t>(s.ssm) % 16u) == 0u;
+  if (vec4 && g.N == 128 && g.P == 64) {
+    hipLaunchKernelGGL(siso_step_n128p64_kernel, dim3(g.B * g.H), dim3(256), 0, stream, kp);
+    return hipGetLastError();
+  }
   const int NV = vec4 ? (int)g.N / 4 : (int)g.N;
   int sg = 1, lg = 0;
   while (sg < NV && sg < 64) { sg <<= 1; ++lg; }

@@ -29,6 +29,8 @@ def _gpu_step(tok_dev, states_dev, d1):
     Dims(2, 1, 3, 0, 24, 48, 8, has_z=False),
     Dims(2, 1, 2, 1, 5, 6, 3),      # odd sizes: scalar state path
     Dims(4, 1, 8, 1, 64, 128, 32),
+    Dims(2, 1, 4, 2, 64, 128, 16, has_z=False),
+    Dims(1, 1, 3, 1, 64, 128, 0, has_d=False),
     Dims(1, 1, 2, 1, 128, 128, 64, has_d=False),
 ], ids=lambda d: f"B{d.B}H{d.H}G{d.G}P{d.P}N{d.N}A{d.A}")
 def test_step_matches_oracle(d):
