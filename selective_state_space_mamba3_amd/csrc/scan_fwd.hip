@@ -657,20 +657,21 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
             }
           }
         }
-        float ec[TB];
+        // Q h'^T in its own accumulators; exp(cum) scales its rows afterwards
+        floatx4 aci[TB];
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) ec[tb] = sc_ecum[(tb * 16 + l16) >> rsl];
+        for (int tb = 0; tb < TB; ++tb) aci[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < JMAX; ++j) {
           if (FIXED || j < ntw) {
             const int nb = nb0 + j;
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
-              const floatx4 a4 = lds_read4(Ql + (tb * 16 + l16) * ks + nb * 16 + 4 * lq) * ec[tb];
-              acc[tb] = mfma16(a4.x, Hacc[j].x, acc[tb]);
-              acc[tb] = mfma16(a4.y, Hacc[j].y, acc[tb]);
-              acc[tb] = mfma16(a4.z, Hacc[j].z, acc[tb]);
-              acc[tb] = mfma16(a4.w, Hacc[j].w, acc[tb]);
+              const floatx4 a4 = lds_read4(Ql + (tb * 16 + l16) * ks + nb * 16 + 4 * lq);
+              aci[tb] = mfma16(a4.x, Hacc[j].x, aci[tb]);
+              aci[tb] = mfma16(a4.y, Hacc[j].y, aci[tb]);
+              aci[tb] = mfma16(a4.z, Hacc[j].z, aci[tb]);
+              aci[tb] = mfma16(a4.w, Hacc[j].w, aci[tb]);
             }
           }
         }
@@ -678,7 +679,10 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) Yd[(tb * 16 + 4 * lq + r) * ys + p0 + l16] = acc[tb][r];
+          for (int r = 0; r < 4; ++r) {
+            const int v = tb * 16 + 4 * lq + r;
+            Yd[v * ys + p0 + l16] = fmaf(sc_ecum[v >> rsl], aci[tb][r], acc[tb][r]);
+          }
       }
       // ---- P5b: state update h' = decay h' + K^T (w X) ------------------------
       const float dec = run[64];
