@@ -9,6 +9,7 @@ from .m3_oracle import (  # noqa: F401
     PreprocessConfig,
     SsmConfig,
     mimo_scan,
+    mimo_step,
     parity_error,
     preprocess,
     preprocess_width,

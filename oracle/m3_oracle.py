@@ -15,6 +15,9 @@ Sources (the oarust 0.8.6 source page ``src/rs/ml/matrix/mamba3.rs`` and the
 * ``mamba3_siso_step`` docs (four recurrent states, their layouts)
   -> :func:`siso_step`.
 * ``MimoGeometry::resolve`` and the ``mamba3_mimo`` docs -> :func:`mimo_scan`.
+* ``mamba3_mimo_step`` docs and ``dispatch_mamba3_mimo_step`` (four states:
+  ssm [B,H,P,N], angle [B,H,A], per-rank keys [B,H,R,N] and values
+  [B,H,R,P]) -> :func:`mimo_step`.
 
 The pages print no formula of the recurrence.  The definition used here is
 read off the docstrings, the operand shapes and the intermediates that the
@@ -294,6 +297,49 @@ def siso_step(c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d,
 # MIMO scan
 # ---------------------------------------------------------------------------
 
+def _mimo_inputs(c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d,
+                 mimo_x, mimo_z, mimo_o, norm_weight, cfg: SsmConfig, heads):
+    """float64 operands of the selected heads; B/C rows r*G + g per rank."""
+    R, G = cfg.mimo_rank, cfg.groups
+    hs, grp = _head_selection(cfg, heads)
+    rows = np.arange(R)[None, :] * G + grp[:, None]  # [Hs, R]
+    return dict(
+        hs=hs, Cm=_f64(c)[:, :, rows, :], Bm=_f64(b)[:, :, rows, :],  # [B,L,Hs,R,N]
+        X=_f64(x)[:, :, hs, :], Z=_f64(z)[:, :, hs, :], ADT=_f64(adt)[:, :, hs], DT=_f64(dt)[:, :, hs],
+        TRAP=_f64(trap)[:, :, hs], ANG=_f64(angle),
+        cb=_f64(c_bias)[hs], bb=_f64(b_bias)[hs], D=_f64(d)[hs],  # biases [Hs,R,N]
+        MX=_f64(mimo_x)[hs], MZ=_f64(mimo_z)[hs], MO=_f64(mimo_o)[hs],  # [Hs,R,P]
+        NW=_f64(norm_weight)[hs])  # [Hs,P]
+
+
+def _mimo_token(m, t, cfg, h, theta, k_prev, v_prev):
+    """One token t of the MIMO recurrence for all selected (batch, head) pairs;
+    returns (out [B,Hs,P], h, theta, K [B,Hs,R,N], X_r [B,Hs,R,P])."""
+    A = cfg.num_rope_angles
+    DT, ADT = m["DT"][:, t], m["ADT"][:, t]
+    theta = theta + DT[..., None] * m["ANG"][:, t, None, :]
+    alpha = np.exp(ADT)
+    lam = sigmoid(m["TRAP"][:, t])
+    gamma = lam * DT
+    beta = (1.0 - lam) * DT * alpha
+    Xr = m["X"][:, t, :, None, :] * m["MX"][None]  # [B,Hs,R,P]
+    K = rotate(m["Bm"][:, t] + m["bb"][None], theta[:, :, None, :], A)  # [B,Hs,R,N]
+    Q = rotate(m["Cm"][:, t] + m["cb"][None], theta[:, :, None, :], A)
+    h = (alpha[..., None, None] * h
+         + beta[..., None, None] * np.einsum("bhrp,bhrn->bhpn", v_prev, k_prev)
+         + gamma[..., None, None] * np.einsum("bhrp,bhrn->bhpn", Xr, K))
+    Y = np.einsum("bhpn,bhrn->bhrp", h, Q)
+    if cfg.has_d:
+        Y = Y + m["D"][None, :, None, None] * Xr
+    if cfg.has_z:
+        Y = Y * silu(m["Z"][:, t, :, None, :] * m["MZ"][None])
+    if cfg.has_output_norm:
+        ms = np.mean(Y * Y, axis=-1, keepdims=True)
+        Y = Y / np.sqrt(ms + MIMO_NORM_EPS) * m["NW"][None, :, None, :]
+    out = np.einsum("hrp,bhrp->bhp", m["MO"], Y)
+    return out, h, theta, K, Xr
+
+
 def mimo_scan(c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d,
               mimo_x, mimo_z, mimo_o, norm_weight, cfg: SsmConfig, heads=None):
     """Shared-state Mamba-3 MIMO scan (``mamba3_mimo``).
@@ -308,55 +354,37 @@ def mimo_scan(c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d,
     """
     Bsz, L = cfg.batch_size, cfg.sequence_length
     P, N, A, R = cfg.head_dim, cfg.state_size, cfg.num_rope_angles, cfg.mimo_rank
-    G = cfg.groups
-    hs, grp = _head_selection(cfg, heads)
-    Hs = len(hs)
-    rows = np.arange(R)[None, :] * G + grp[:, None]  # [Hs, R]
-    Cm = _f64(c)[:, :, rows, :]  # [B,L,Hs,R,N]
-    Bm = _f64(b)[:, :, rows, :]
-    X = _f64(x)[:, :, hs, :]
-    Z = _f64(z)[:, :, hs, :]
-    ADT = _f64(adt)[:, :, hs]
-    DT = _f64(dt)[:, :, hs]
-    TRAP = _f64(trap)[:, :, hs]
-    ANG = _f64(angle)
-    cb = _f64(c_bias)[hs]  # [Hs,R,N]
-    bb = _f64(b_bias)[hs]
-    D = _f64(d)[hs]
-    MX = _f64(mimo_x)[hs]  # [Hs,R,P]
-    MZ = _f64(mimo_z)[hs]
-    MO = _f64(mimo_o)[hs]
-    NW = _f64(norm_weight)[hs]  # [Hs,P]
-
+    m = _mimo_inputs(c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d,
+                     mimo_x, mimo_z, mimo_o, norm_weight, cfg, heads)
+    Hs = len(m["hs"])
     theta = np.zeros((Bsz, Hs, A))
     h = np.zeros((Bsz, Hs, P, N))
     k_prev = np.zeros((Bsz, Hs, R, N))
     v_prev = np.zeros((Bsz, Hs, R, P))
     out = np.zeros((Bsz, L, Hs, P))
     for t in range(L):
-        theta = theta + DT[:, t, :, None] * ANG[:, t, None, :]
-        alpha = np.exp(ADT[:, t])
-        lam = sigmoid(TRAP[:, t])
-        gamma = lam * DT[:, t]
-        beta = (1.0 - lam) * DT[:, t] * alpha
-        Xr = X[:, t, :, None, :] * MX[None]  # [B,Hs,R,P]
-        K = rotate(Bm[:, t] + bb[None], theta[:, :, None, :], A)  # [B,Hs,R,N]
-        Q = rotate(Cm[:, t] + cb[None], theta[:, :, None, :], A)
-        h = (alpha[..., None, None] * h
-             + beta[..., None, None] * np.einsum("bhrp,bhrn->bhpn", v_prev, k_prev)
-             + gamma[..., None, None] * np.einsum("bhrp,bhrn->bhpn", Xr, K))
-        Y = np.einsum("bhpn,bhrn->bhrp", h, Q)
-        if cfg.has_d:
-            Y = Y + D[None, :, None, None] * Xr
-        if cfg.has_z:
-            Y = Y * silu(Z[:, t, :, None, :] * MZ[None])
-        if cfg.has_output_norm:
-            ms = np.mean(Y * Y, axis=-1, keepdims=True)
-            Y = Y / np.sqrt(ms + MIMO_NORM_EPS) * NW[None, :, None, :]
-        out[:, t] = np.einsum("hrp,bhrp->bhp", MO, Y)
-        k_prev = K
-        v_prev = Xr
+        out[:, t], h, theta, k_prev, v_prev = _mimo_token(m, t, cfg, h, theta, k_prev, v_prev)
     return out
+
+
+def mimo_step(c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d,
+              mimo_x, mimo_z, mimo_o, norm_weight,
+              ssm_state, angle_state, k_state, v_state, cfg: SsmConfig, heads=None):
+    """One MIMO decode token (``mamba3_mimo_step``), L == 1.
+
+    States: ssm [B,H,P,N], cumulative angle [B,H,A], previous keys
+    [B,H,R,N] (each rank's rotated, bias-added key of the previous token),
+    previous values [B,H,R,P] (each rank's X_r of the previous token).
+    Returns (out [B,1,H',P], new_states); the inputs are not modified.
+    """
+    if cfg.sequence_length != 1:
+        raise ValueError("mimo_step requires sequence_length == 1")
+    m = _mimo_inputs(c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d,
+                     mimo_x, mimo_z, mimo_o, norm_weight, cfg, heads)
+    hs = m["hs"]
+    y, h, theta, k, v = _mimo_token(m, 0, cfg, _f64(ssm_state)[:, hs], _f64(angle_state)[:, hs],
+                                    _f64(k_state)[:, hs], _f64(v_state)[:, hs])
+    return y[:, None], {"ssm_state": h, "angle_state": theta, "k_state": k, "v_state": v}
 
 
 # ---------------------------------------------------------------------------

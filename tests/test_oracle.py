@@ -21,7 +21,7 @@ import pytest
 from scipy.signal import lfilter
 
 import oracle as O
-from workloads import Dims, ssm_inputs
+from workloads import Dims, decode_states, ssm_inputs
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
@@ -301,6 +301,49 @@ def test_mimo_superposes_siso_over_rank_pairs(R, G, norm):
         Y = Y / np.sqrt(np.mean(Y ** 2, axis=-1, keepdims=True) + 1e-5) * f("norm_weight")[None, None, :, None, :]
     ref = np.sum(f("mimo_o")[None, None] * Y, axis=3)
     np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+MIMO15 = ("c", "b", "x", "z", "adt", "dt", "trap", "angle", "c_bias", "b_bias", "d",
+          "mimo_x", "mimo_z", "mimo_o", "norm_weight")
+
+
+def test_mimo_steps_from_zero_states_equal_the_scan():
+    d = Dims(2, 12, 4, 2, 5, 8, 3, R=3, has_output_norm=True)
+    inp = ssm_inputs(d, seed=53, mimo=True)
+    full = _mimo(inp, _cfg(d))
+    cfg1 = _cfg(d, sequence_length=1)
+    st = {"ssm_state": np.zeros((d.B, d.H, d.P, d.N)), "angle_state": np.zeros((d.B, d.H, d.A)),
+          "k_state": np.zeros((d.B, d.H, d.R, d.N)), "v_state": np.zeros((d.B, d.H, d.R, d.P))}
+    for t in range(d.L):
+        tok = {k: (v[:, t:t + 1] if v.ndim >= 3 and v.shape[1] == d.L else v) for k, v in inp.items()}
+        y, st = O.mimo_step(*[tok[k] for k in MIMO15], st["ssm_state"], st["angle_state"],
+                            st["k_state"], st["v_state"], cfg1)
+        np.testing.assert_allclose(y[:, 0], full[:, t], rtol=1e-12, atol=1e-13)
+    # the stored previous values are the last token's x * mimo_x per rank
+    xr = inp["x"][:, -1, :, None, :].astype(np.float64) * inp["mimo_x"][None].astype(np.float64)
+    np.testing.assert_array_equal(st["v_state"], xr)
+
+
+def test_mimo_step_rank_one_is_siso_step():
+    d = Dims(3, 1, 4, 2, 6, 10, 4, R=1)
+    inp = ssm_inputs(d, seed=54, mimo=True)
+    for k in ("mimo_x", "mimo_z", "mimo_o"):
+        inp[k][:] = 1.0
+    st = decode_states(d, seed=55)
+    cfg = _cfg(d)
+    y_m, st_m = O.mimo_step(*[inp[k] for k in MIMO15], st["ssm_state"], st["angle_state"],
+                            st["k_state"][:, :, None], st["v_state"][:, :, None], cfg)
+    s_inp = dict(inp)
+    s_inp["c_bias"] = inp["c_bias"][:, 0]
+    s_inp["b_bias"] = inp["b_bias"][:, 0]
+    y_s, st_s = O.siso_step(*[s_inp[k] for k in ("c", "b", "x", "z", "adt", "dt", "trap", "angle",
+                                                  "c_bias", "b_bias", "d")],
+                            st["ssm_state"], st["angle_state"], st["k_state"], st["v_state"], cfg)
+    np.testing.assert_allclose(y_m, y_s, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(st_m["ssm_state"], st_s["ssm_state"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(st_m["k_state"][:, :, 0], st_s["k_state"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(st_m["v_state"][:, :, 0], st_s["v_state"])
+    np.testing.assert_array_equal(st_m["angle_state"], st_s["angle_state"])
 
 
 # ---------------------------------------------------------------------------

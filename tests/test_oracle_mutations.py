@@ -47,6 +47,8 @@ MUTATIONS = {
         "return (v / np.sqrt(ms + float(np.float32(cfg.epsilon)))).reshape(rows, M)",
         "return (v / (np.sqrt(ms) + float(np.float32(cfg.epsilon)))).reshape(rows, M)"),
     "preprocess_no_a_floor": ("adt = -a_mag * dt", "adt = -softplus(a_raw) * dt"),
+    "mimo_step_ignores_previous_keys": ("_f64(k_state)[:, hs], _f64(v_state)[:, hs])",
+                                        "0.0 * _f64(k_state)[:, hs], _f64(v_state)[:, hs])"),
     "step_keeps_unrotated_key": ("return y, h, theta, K, Xt.copy()",
                                  "return y, h, theta, Bt + bb[None], Xt.copy()"),
 }
