@@ -11,8 +11,9 @@ Prints one JSON line: tokens/s of the step, the scan kernel's roofline
 (algorithmic bytes / live HIP-event duration against 8 TB/s), and the float64
 CPU oracle timed on a bounded sample on the host cores.  After the timed
 region it also measures the other rows of the path at their own workloads
-("rows"): the decode step at B256 H32 (1 token per step, HBM-bound) and the
-MIMO scan at B8 L4096 H32 R4 (FP32-matrix-bound).
+("rows"): the decode step at B256 H32 (1 token per step, HBM-bound), the
+rank-4 MIMO decode step at the same geometry, and the MIMO scan at
+B8 L4096 H32 R4 (FP32-matrix-bound).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
 """
@@ -77,7 +78,7 @@ def decode_algorithmic_bytes(B, H, G, P, N, A) -> int:
 def measure_rows(torch, m3, lib, hip, new_event, dev):
     """Decode-step and MIMO-scan rows, each at its own workload, timed with HIP
     events on the stream the kernels run on."""
-    from workloads import WORKLOADS, decode_states, ssm_inputs, step_inputs
+    from workloads import WORKLOADS, decode_states, mimo_decode_states, ssm_inputs, step_inputs
     ops11 = ("c", "b", "x", "z", "adt", "dt", "trap", "angle", "c_bias", "b_bias", "d")
     rows = {}
 
@@ -110,6 +111,41 @@ def measure_rows(torch, m3, lib, hip, new_event, dev):
                            "algorithmic_bytes": byt, "gbs": byt / (us * 1e-6) / 1e9,
                            "hbm_frac": byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "bound": "hbm",
                            "steps_timed": n_steps}
+    del st, toks, out
+
+    # MIMO decode: 256 x 32 heads, rank 4, output norm; eight staged token sets
+    w = WORKLOADS["mimo_decode_b256_r4"]
+    d = w.dims
+    st = {k: torch.from_numpy(v).to(dev) for k, v in mimo_decode_states(d, w.seed).items()}
+    toks = [{k: torch.from_numpy(v).to(dev) for k, v in step_inputs(d, w.seed, s, mimo=True).items()}
+            for s in range(8)]
+    cfg = m3.SsmConfig(d.B, 1, d.H, d.G, d.P, d.N, d.A, d.R, True, True, True)
+    out = torch.empty(d.B, 1, d.H, d.P, device=dev)
+    ops15 = ops11 + ("mimo_x", "mimo_z", "mimo_o", "norm_weight")
+
+    def one_m(i):
+        t = toks[i % len(toks)]
+        m3.m3_mimo_step(*[t[k] for k in ops15], st["ssm_state"], st["angle_state"], st["k_state"],
+                        st["v_state"], cfg, out=out)
+    for i in range(20):
+        one_m(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n_steps):
+        one_m(i)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / n_steps
+    Bd, Hd, Gd, Pd, Nd, Ad, Rd = d.B, d.H, d.groups, d.P, d.N, d.A, d.R
+    byt = 4 * (2 * Bd * Hd * Pd * Nd + 2 * Bd * Rd * Gd * Nd + 3 * Bd * Hd * Pd + 3 * Bd * Hd + Bd * Ad
+               + 2 * Bd * Hd * Ad + 2 * Bd * Hd * Rd * Nd + 2 * Bd * Hd * Rd * Pd + 2 * Hd * Rd * Nd + Hd
+               + 3 * Hd * Rd * Pd + Hd * Pd)
+    rows["mimo_decode_step"] = {"workload": "mimo_decode_b256_r4: B256 H32 P64 N128 A32 R4, output norm, one token per step",
+                                "us_per_step": us, "tokens_per_s": Bd / (us * 1e-6),
+                                "algorithmic_bytes": byt, "gbs": byt / (us * 1e-6) / 1e9,
+                                "hbm_frac": byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "bound": "hbm",
+                                "steps_timed": n_steps}
     del st, toks, out
 
     # MIMO: B8 L4096 H32 P64 N128 A32 R4 with output norm

@@ -1,7 +1,7 @@
 /*
  * m3.h -- C ABI of the MI355X (gfx950) Mamba-3 selective-state forward path.
  *
- * Four operations, named after the public functions of the oarust 0.8.6
+ * Five operations, named after the public functions of the oarust 0.8.6
  * source page src/rs/ml/matrix/mamba3.rs ("Public API" section) and the
  * ml::matrix API index:
  *
@@ -9,6 +9,7 @@
  *   m3_siso_fwd     mamba3_siso         SISO selective-state scan, forward
  *   m3_mimo_fwd     mamba3_mimo         shared-state MIMO scan, forward
  *   m3_siso_step    mamba3_siso_step    one SISO decode token, states in place
+ *   m3_mimo_step    mamba3_mimo_step    one MIMO decode token, states in place
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -29,7 +30,10 @@
  *             reports a failed kernel launch.  m3_last_error() returns a
  *             thread-local message naming the operation and the broken rule.
  * Threads:    calls are thread-safe; calls on different streams may overlap.
- * Precision:  float32 storage and arithmetic, accurate exp/sin/cos.
+ * Precision:  float32 storage and arithmetic.  sin / cos are accurate to a
+ *             few ulp; the state decay uses an accurate exp; the
+ *             intra-chunk decay mask, exp(cum) and the SiLU gate use the
+ *             hardware exp2 (relative error about |x| 2^-23).
  */
 #ifndef M3_H
 #define M3_H
@@ -193,6 +197,32 @@ int m3_mimo_fwd(const float* c, const float* b, const float* x, const float* z,
 int m3_siso_step(const float* c, const float* b, const float* x, const float* z,
                  const float* adt, const float* dt, const float* trap, const float* angle,
                  const float* c_bias, const float* b_bias, const float* d,
+                 float* ssm_state, float* angle_state, float* k_state, float* v_state,
+                 m3_ssm_config cfg, float* out, void* stream);
+
+/*
+ * m3_mimo_step -- mamba3_mimo_step ("Advance one Mamba-3 MIMO token";
+ * dispatch_mamba3_mimo_step for the state shapes).  The fifteen operands of
+ * m3_mimo_fwd take their L == 1 shapes (c, b [B,1,R*G,N]; x, z [B,1,H,P];
+ * adt, dt, trap [B,1,H]; angle [B,1,A]; biases [H,R,N]; d [H];
+ * mimo_x, mimo_z, mimo_o [H,R,P]; norm_weight [H,P]).  States, read and
+ * written in place:
+ *   ssm_state   [B,H,P,N]    h (one state per head, fed by every rank)
+ *   angle_state [B,H,A]      cumulative angle theta
+ *   k_state     [B,H,R,N]    previous key of each rank (rotated, bias added)
+ *   v_state     [B,H,R,P]    previous value of each rank (x * mimo_x[h,r])
+ * One token of the m3_mimo_fwd recurrence, continuing from these states;
+ * afterwards angle_state = theta_t, k_state[r] = K_r,t, v_state[r] = X_r,t.
+ * A sequence of L steps from zero states equals m3_mimo_fwd over L tokens.
+ * Rules: as m3_mimo_fwd plus sequence_length == 1.  States are modified
+ * only by a call that returns M3_OK.  States must not alias each other or
+ * the operands; out [B,1,H,P] must not alias anything.
+ */
+int m3_mimo_step(const float* c, const float* b, const float* x, const float* z,
+                 const float* adt, const float* dt, const float* trap, const float* angle,
+                 const float* c_bias, const float* b_bias, const float* d,
+                 const float* mimo_x, const float* mimo_z, const float* mimo_o,
+                 const float* norm_weight,
                  float* ssm_state, float* angle_state, float* k_state, float* v_state,
                  m3_ssm_config cfg, float* out, void* stream);
 

@@ -115,6 +115,8 @@ def lib() -> ctypes.CDLL:
     L.m3_mimo_fwd.argtypes = [_P] * 15 + [_CSsm, _P, _P, ctypes.c_size_t, _P]
     L.m3_siso_step.restype = ctypes.c_int
     L.m3_siso_step.argtypes = [_P] * 15 + [_CSsm, _P, _P]
+    L.m3_mimo_step.restype = ctypes.c_int
+    L.m3_mimo_step.argtypes = [_P] * 19 + [_CSsm, _P, _P]
     _LIB = L
     return L
 
@@ -260,6 +262,36 @@ def m3_siso_step(c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d, ssm_state,
     _expect("out", out, oshape, dev)
     _check(L_.m3_siso_step(*[_ptr(ops[k]) for k in _OPS11], _ptr(ssm_state), _ptr(angle_state),
                            _ptr(k_state), _ptr(v_state), c_ssm(cfg), _ptr(out), _stream(dev, stream)))
+    return out
+
+
+def m3_mimo_step(c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d, mimo_x, mimo_z, mimo_o,
+                 norm_weight, ssm_state, angle_state, k_state, v_state, cfg: SsmConfig, out=None,
+                 stream=None) -> torch.Tensor:
+    """One MIMO decode token; updates the four states in place, returns out [B, 1, H, P]."""
+    L_ = lib()
+    dev = x.device
+    if cfg.sequence_length != 1:
+        raise ValueError("m3_mimo_step requires sequence_length == 1")
+    R = cfg.mimo_rank
+    ops = dict(zip(_OPS11, (c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d)))
+    for k, shp in _scan_shapes(cfg, R * cfg.groups, (cfg.num_heads, R, cfg.state_size)).items():
+        _expect(k, ops[k], shp, dev)
+    for k, t in (("mimo_x", mimo_x), ("mimo_z", mimo_z), ("mimo_o", mimo_o)):
+        _expect(k, t, (cfg.num_heads, R, cfg.head_dim), dev)
+    _expect("norm_weight", norm_weight, (cfg.num_heads, cfg.head_dim), dev)
+    B, H, P, N, A = cfg.batch_size, cfg.num_heads, cfg.head_dim, cfg.state_size, cfg.num_rope_angles
+    _expect("ssm_state", ssm_state, (B, H, P, N), dev)
+    _expect("angle_state", angle_state, (B, H, A), dev)
+    _expect("k_state", k_state, (B, H, R, N), dev)
+    _expect("v_state", v_state, (B, H, R, P), dev)
+    oshape = (B, 1, H, P)
+    if out is None:
+        out = torch.empty(oshape, dtype=torch.float32, device=dev)
+    _expect("out", out, oshape, dev)
+    _check(L_.m3_mimo_step(*[_ptr(ops[k]) for k in _OPS11], _ptr(mimo_x), _ptr(mimo_z), _ptr(mimo_o),
+                           _ptr(norm_weight), _ptr(ssm_state), _ptr(angle_state), _ptr(k_state),
+                           _ptr(v_state), c_ssm(cfg), _ptr(out), _stream(dev, stream)))
     return out
 
 

@@ -240,4 +240,32 @@ int m3_siso_step(const float* c, const float* b, const float* x, const float* z,
   return hip_status(op, m3::launch_siso_step(g, o, s, static_cast<hipStream_t>(stream)));
 }
 
+int m3_mimo_step(const float* c, const float* b, const float* x, const float* z, const float* adt,
+                 const float* dt, const float* trap, const float* angle, const float* c_bias,
+                 const float* b_bias, const float* d, const float* mimo_x, const float* mimo_z,
+                 const float* mimo_o, const float* norm_weight, float* ssm_state, float* angle_state,
+                 float* k_state, float* v_state, m3_ssm_config cfg, float* out, void* stream) {
+  const char* op = "m3_mimo_step";
+  clear_error();
+  m3::ScanGeom g{};
+  int st = resolve_scan(op, cfg, true, &g);
+  if (st) return st;
+  if (cfg.sequence_length != 1)
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s requires sequence_length == 1", op);
+  if (!count_u32({g.B, g.H, g.P, g.N}) || !count_u32({g.B, g.H, g.R, g.N}) || !count_u32({g.B, g.H, g.R, g.P}))
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: state element count exceeds u32", op);
+  st = check_ptrs(op, {{"c", c}, {"b", b}, {"x", x}, {"z", z}, {"adt", adt}, {"dt", dt},
+                       {"trap", trap}, {"c_bias", c_bias}, {"b_bias", b_bias}, {"d", d},
+                       {"mimo_x", mimo_x}, {"mimo_z", mimo_z}, {"mimo_o", mimo_o},
+                       {"norm_weight", norm_weight}, {"ssm_state", ssm_state}, {"k_state", k_state},
+                       {"v_state", v_state}, {"out", out}});
+  if (st) return st;
+  if (g.A > 0 && (angle == nullptr || angle_state == nullptr))
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: operand angle or angle_state is NULL", op);
+  m3::ScanOperands o{c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d,
+                     mimo_x, mimo_z, mimo_o, norm_weight, out};
+  m3::StepStates s{ssm_state, angle_state, k_state, v_state};
+  return hip_status(op, m3::launch_mimo_step(g, o, s, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -60,6 +60,8 @@ hipError_t launch_mimo_fwd(const ScanGeom& g, const ScanOperands& o, const ScanP
                            void* workspace, hipStream_t stream);
 hipError_t launch_siso_step(const ScanGeom& g, const ScanOperands& o, const StepStates& s,
                             hipStream_t stream);
+hipError_t launch_mimo_step(const ScanGeom& g, const ScanOperands& o, const StepStates& s,
+                            hipStream_t stream);
 hipError_t launch_preprocess(const PreGeom& g, const PreOperands& o, hipStream_t stream);
 
 }  // namespace m3

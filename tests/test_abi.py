@@ -25,7 +25,7 @@ def _lib():
 def test_library_exports_every_header_function():
     names = m3.header_functions()
     assert set(names) >= {"m3_preprocess", "m3_siso_fwd", "m3_mimo_fwd", "m3_siso_step",
-                          "m3_last_error", "m3_siso_fwd_workspace_bytes",
+                          "m3_mimo_step", "m3_last_error", "m3_siso_fwd_workspace_bytes",
                           "m3_mimo_fwd_workspace_bytes", "m3_version"}
     L = _lib()
     for n in names:
@@ -140,6 +140,27 @@ def test_step_rules():
     a[12] = None  # angle_state with A > 0
     assert L.m3_siso_step(*a, bd.c_ssm(_ssm(sequence_length=1)), FAKE, None) == INVALID
     assert L.m3_siso_step(*args, bd.c_ssm(_ssm(sequence_length=1, mimo_rank=2)), FAKE, None) == INVALID
+
+
+def test_mimo_step_rules():
+    L = _lib()
+    args = [FAKE] * 19
+    one = _ssm(sequence_length=1, mimo_rank=2)
+    assert L.m3_mimo_step(*args, bd.c_ssm(_ssm(sequence_length=2, mimo_rank=2)), FAKE, None) == INVALID
+    assert "sequence_length == 1" in m3.last_error()
+    for i in (15, 17, 18):  # ssm_state, k_state, v_state
+        a = list(args)
+        a[i] = None
+        assert L.m3_mimo_step(*a, bd.c_ssm(one), FAKE, None) == INVALID
+    a = list(args)
+    a[16] = None  # angle_state with A > 0
+    assert L.m3_mimo_step(*a, bd.c_ssm(one), FAKE, None) == INVALID
+    a = list(args)
+    a[14] = None  # norm_weight must be valid even without the norm
+    assert L.m3_mimo_step(*a, bd.c_ssm(one), FAKE, None) == INVALID
+    for rank in (0, 9):
+        assert L.m3_mimo_step(*args, bd.c_ssm(_ssm(sequence_length=1, mimo_rank=rank)), FAKE, None) == INVALID
+    assert L.m3_mimo_step(*args, bd.c_ssm(one), None, None) == INVALID  # out
 
 
 def _pre(**kw):

@@ -54,7 +54,7 @@ class Dims:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "siso" | "mimo" | "step"
+    kind: str  # "siso" | "mimo" | "step" | "mimo_step"
     dims: Dims
     dt_range: tuple = (1e-3, 0.1)
     seed: int = 0
@@ -62,8 +62,9 @@ class Workload:
     extra: dict = field(default_factory=dict)
 
 
-# The five workloads: a tiny parity case, the 1.3B-class mixer layer, a long
-# sequence, a rank-4 MIMO layer, and batched single-token decode.
+# The workloads: a tiny parity case, the 1.3B-class mixer layer, a long
+# sequence, a rank-4 MIMO layer, batched single-token decode, and batched
+# rank-4 MIMO decode.
 WORKLOADS = {
     "siso_tiny": Workload("siso_tiny", "siso", Dims(1, 64, 2, 1, 16, 16, 8), seed=1000),
     "siso_b4_l2048": Workload("siso_b4_l2048", "siso", Dims(4, 2048, 24, 1, 64, 128, 32), seed=1001),
@@ -72,6 +73,10 @@ WORKLOADS = {
     "mimo_b8_l4096_r4": Workload("mimo_b8_l4096_r4", "mimo",
                                  Dims(8, 4096, 32, 1, 64, 128, 32, R=4, has_output_norm=True), seed=1003),
     "decode_b256": Workload("decode_b256", "step", Dims(256, 1, 32, 1, 64, 128, 32), seed=1004, steps=1024),
+    # MIMO decode at the decode geometry with the MIMO workload's rank and norm
+    "mimo_decode_b256_r4": Workload("mimo_decode_b256_r4", "mimo_step",
+                                    Dims(256, 1, 32, 1, 64, 128, 32, R=4, has_output_norm=True),
+                                    seed=1005, steps=256),
 }
 
 
@@ -139,11 +144,28 @@ def decode_states(d: Dims, seed: int) -> dict:
     return {k: np.ascontiguousarray(v) for k, v in st.items()}
 
 
-def step_inputs(d: Dims, seed: int, step: int, dt_range=(1e-3, 0.1)) -> dict:
-    """Fresh seeded L == 1 operands for decode step ``step``."""
+def mimo_decode_states(d: Dims, seed: int) -> dict:
+    """Seeded recurrent states for ``mamba3_mimo_step``: ssm_state ~ N(0,1)
+    [B,H,P,N]; angle_state ~ U[-pi, pi] [B,H,A]; per rank r a unit-RMS key
+    row k_state [B,H,R,N] and an x-like value row v_state [B,H,R,P]."""
+    rng = np.random.default_rng([seed, 0x4D53])
+    B, H, P, N, A, R = d.B, d.H, d.P, d.N, d.A, d.R
+    f32 = np.float32
+    st = {
+        "ssm_state": rng.standard_normal((B, H, P, N), dtype=f32),
+        "angle_state": (f32(-np.pi) + f32(2 * np.pi) * rng.random((B, H, A), dtype=f32)).astype(f32),
+        "k_state": _unit_rms_rows(rng.standard_normal((B, H, R, N), dtype=f32)),
+        "v_state": rng.standard_normal((B, H, R, P), dtype=f32),
+    }
+    return {k: np.ascontiguousarray(v) for k, v in st.items()}
+
+
+def step_inputs(d: Dims, seed: int, step: int, dt_range=(1e-3, 0.1), mimo: bool = False) -> dict:
+    """Fresh seeded L == 1 operands for decode step ``step`` (MIMO operands
+    and [H,R,N] biases with ``mimo``)."""
     d1 = Dims(d.B, 1, d.H, d.G, d.P, d.N, d.A, d.R, d.has_z, d.has_d, d.has_output_norm)
     return ssm_inputs(d1, seed=np.random.SeedSequence([seed, step]).generate_state(1)[0],
-                      dt_range=dt_range, mimo=False)
+                      dt_range=dt_range, mimo=mimo)
 
 
 def preprocess_inputs(rows: int, width: int, heads: int, seed: int,
