@@ -131,56 +131,202 @@ __device__ __forceinline__ void mimo_step_finish(const MimoStepParams& p, int bh
     p.ang_state[(size_t)bh * A + a] = fmaf(s.dtv, p.angle[(size_t)b * A + a], p.ang_state[(size_t)bh * A + a]);
 }
 
-// N = 128, P = 64, 16-byte aligned state: 256 threads per (batch, head).
-// Wave w, pass i covers state rows 8 i + 2 w (lanes 0-31) and 8 i + 2 w + 1
-// (lanes 32-63), one 16-byte item per lane, so each load or store moves
-// 1 KiB of contiguous state; all eight passes are loaded first.
+// N = 128, P = 64, 16-byte aligned state, rank R fixed at compile time:
+// 256 threads per (batch, head).  Wave w, pass i covers state rows 8 i + 2 w
+// (lanes 0-31) and 8 i + 2 w + 1 (lanes 32-63), one 16-byte item per lane,
+// so each load or store moves 1 KiB of contiguous state.  Every global load
+// of the workgroup (the eight state items, the set-up operands and the
+// epilogue operands) is issued before the first one is used, so one memory
+// round trip covers them all; the loads use clamped in-range indices rather
+// than branches.  A lane's key and query columns are the same in all eight
+// passes, so for R <= 4 they are held in registers.
+template <int R>
 __global__ __launch_bounds__(256) void mimo_step_n128p64_kernel(MimoStepParams p) {
-  constexpr int N = 128, P = 64, RMAX = 8;
-  __shared__ __attribute__((aligned(16))) float Kv[RMAX * N];
-  __shared__ __attribute__((aligned(16))) float Qv[RMAX * N];
-  __shared__ __attribute__((aligned(16))) float kp[RMAX * N];
-  __shared__ float vp[RMAX * P], xr[RMAX * P], yv[RMAX * P];
+  constexpr int N = 128, P = 64;
+  constexpr bool HOIST = R <= 4;
+  constexpr int KPN = (R * N + 255) / 256;  // previous-key items per thread
+  constexpr int VPN = (R * P + 255) / 256;  // previous-value / X_r items per thread
+  constexpr int KR = (R + 3) / 4;           // epilogue ranks per wave
+  __shared__ __attribute__((aligned(16))) float Kv[R * N];
+  __shared__ __attribute__((aligned(16))) float Qv[R * N];
+  __shared__ __attribute__((aligned(16))) float kp[R * N];
+  __shared__ float vp[R * P], xr[R * P], yv[R * P];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int bh = blockIdx.x;
-  const int R = p.R;
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int g = h / (p.H / p.G);
+  const int A = p.A;
   float* st = p.ssm + (size_t)bh * P * N;
   const int c4 = 4 * (lane & 31);
   const int r0 = 2 * wave + (lane >> 5);
+
   floatx4 hv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) hv[i] = *reinterpret_cast<const floatx4*>(st + (size_t)(r0 + 8 * i) * N + c4);
 
-  const StepScalars s = mimo_step_setup(p, bh, Kv, Qv, kp, vp, xr, tid, 256);
+  // set-up operands
+  const float dtv = p.dt[bh];
+  const float adtv = p.adt[bh];
+  const float trv = p.trap[bh];
+  const float dh = p.has_d ? p.d[h] : 0.f;
+  float kpl[KPN], vpl[VPN], xl[VPN], mxl[VPN];
+#pragma unroll
+  for (int k = 0; k < KPN; ++k) kpl[k] = p.k_state[(size_t)bh * R * N + min(tid + 256 * k, R * N - 1)];
+#pragma unroll
+  for (int k = 0; k < VPN; ++k) {
+    const int i = min(tid + 256 * k, R * P - 1);
+    vpl[k] = p.v_state[(size_t)bh * R * P + i];
+    xl[k] = p.x[(size_t)bh * P + (i & (P - 1))];
+    mxl[k] = p.mimo_x[(size_t)h * R * P + i];
+  }
+  // column j < A: the pair (j, j + A); A <= j < N - A: the plain column j + A
+  const int j = min(tid, N - A - 1);
+  const int n0 = j < A ? j : j + A;
+  const int n1 = j < A ? j + A : n0;
+  float bl0[R], bl1[R], bb0[R], bb1[R], cl0[R], cl1[R], cb0[R], cb1[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float* brow = p.b + ((size_t)b * R * p.G + (size_t)r * p.G + g) * N;
+    const float* crow = p.c + ((size_t)b * R * p.G + (size_t)r * p.G + g) * N;
+    const float* bb = p.b_bias + ((size_t)h * R + r) * N;
+    const float* cb = p.c_bias + ((size_t)h * R + r) * N;
+    bl0[r] = brow[n0]; bl1[r] = brow[n1]; bb0[r] = bb[n0]; bb1[r] = bb[n1];
+    cl0[r] = crow[n0]; cl1[r] = crow[n1]; cb0[r] = cb[n0]; cb1[r] = cb[n1];
+  }
+  float ang = 0.f, ast = 0.f;
+  if (A > 0) {
+    const int ja = min(j, A - 1);
+    ang = p.angle[(size_t)b * A + ja];
+    ast = p.ang_state[(size_t)bh * A + ja];
+  }
+  // epilogue operands of this wave's ranks (wave, wave + 4)
+  const float* zp = p.has_z ? p.z : p.x;
+  const float* mzp = p.has_z ? p.mimo_z : p.mimo_o;
+  const float* nwp = p.has_norm ? p.norm_weight : p.mimo_o;
+  const float zl = zp[(size_t)bh * P + lane];
+  const float nwl = nwp[(size_t)h * P + lane];
+  float mzl[KR], mol[KR];
+#pragma unroll
+  for (int k = 0; k < KR; ++k) {
+    const int r = min(wave + 4 * k, R - 1);
+    mzl[k] = mzp[((size_t)h * R + r) * P + lane];
+    mol[k] = p.mimo_o[((size_t)h * R + r) * P + lane];
+  }
+
+  // scalars and the set-up into LDS
+  const float alpha = expf(adtv);
+  const float lam = sigmoidf_acc(trv);
+  const float gam = lam * dtv;
+  const float beta = (1.f - lam) * dtv * alpha;
+#pragma unroll
+  for (int k = 0; k < KPN; ++k)
+    if (tid + 256 * k < R * N) kp[tid + 256 * k] = kpl[k];
+#pragma unroll
+  for (int k = 0; k < VPN; ++k)
+    if (tid + 256 * k < R * P) {
+      vp[tid + 256 * k] = vpl[k];
+      xr[tid + 256 * k] = xl[k] * mxl[k];
+    }
+  const float th = fmaf(dtv, ang, ast);
+  if (tid < N - A) {
+    if (j < A) {
+      float sn, co;
+      sincos_acc(th, &sn, &co);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float k0 = bl0[r] + bb0[r], k1 = bl1[r] + bb1[r];
+        const float q0 = cl0[r] + cb0[r], q1 = cl1[r] + cb1[r];
+        Kv[r * N + j] = k0 * co - k1 * sn;
+        Kv[r * N + j + A] = k0 * sn + k1 * co;
+        Qv[r * N + j] = q0 * co - q1 * sn;
+        Qv[r * N + j + A] = q0 * sn + q1 * co;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        Kv[r * N + n0] = bl0[r] + bb0[r];
+        Qv[r * N + n0] = cl0[r] + cb0[r];
+      }
+    }
+  }
   __syncthreads();
+
+  // the new small states (every read of the old ones is done)
+  if (tid < A) p.ang_state[(size_t)bh * A + tid] = th;
+#pragma unroll
+  for (int k = 0; k < KPN; ++k)
+    if (tid + 256 * k < R * N) p.k_state[(size_t)bh * R * N + tid + 256 * k] = Kv[tid + 256 * k];
+#pragma unroll
+  for (int k = 0; k < VPN; ++k)
+    if (tid + 256 * k < R * P) p.v_state[(size_t)bh * R * P + tid + 256 * k] = xr[tid + 256 * k];
+
+  floatx4 kkr[HOIST ? R : 1], KKr[HOIST ? R : 1], QQr[HOIST ? R : 1];
+  if constexpr (HOIST) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      kkr[r] = *reinterpret_cast<const floatx4*>(kp + r * N + c4);
+      KKr[r] = *reinterpret_cast<const floatx4*>(Kv + r * N + c4);
+      QQr[r] = *reinterpret_cast<const floatx4*>(Qv + r * N + c4);
+    }
+  }
 
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = r0 + 8 * i;
-    floatx4 v = hv[i] * s.alpha;
+    floatx4 v = hv[i] * alpha;
+#pragma unroll
     for (int r = 0; r < R; ++r) {
-      const floatx4 kk = *reinterpret_cast<const floatx4*>(kp + r * N + c4);
-      const floatx4 KK = *reinterpret_cast<const floatx4*>(Kv + r * N + c4);
-      const float cv = s.beta * vp[r * P + row];
-      const float cx = s.gam * xr[r * P + row];
+      const floatx4 kk = HOIST ? kkr[r] : *reinterpret_cast<const floatx4*>(kp + r * N + c4);
+      const floatx4 KK = HOIST ? KKr[r] : *reinterpret_cast<const floatx4*>(Kv + r * N + c4);
+      const float cv = beta * vp[r * P + row];
+      const float cx = gam * xr[r * P + row];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = fmaf(cx, KK[e], fmaf(cv, kk[e], v[e]));
     }
     *reinterpret_cast<floatx4*>(st + (size_t)row * N + c4) = v;
+    float acc[R];
+#pragma unroll
     for (int r = 0; r < R; ++r) {
-      const floatx4 QQ = *reinterpret_cast<const floatx4*>(Qv + r * N + c4);
-      float acc = v[0] * QQ[0];
-      acc = fmaf(v[1], QQ[1], acc);
-      acc = fmaf(v[2], QQ[2], acc);
-      acc = fmaf(v[3], QQ[3], acc);
-      acc = scan32_f(acc);  // lane 31 / 63 hold the row sums
-      if ((lane & 31) == 31) yv[r * P + row] = acc;
+      const floatx4 QQ = HOIST ? QQr[r] : *reinterpret_cast<const floatx4*>(Qv + r * N + c4);
+      float a = v[0] * QQ[0];
+      a = fmaf(v[1], QQ[1], a);
+      a = fmaf(v[2], QQ[2], a);
+      acc[r] = fmaf(v[3], QQ[3], a);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = scan32_f(acc[r]);  // lane 31 / 63 hold the row sums
+    if ((lane & 31) == 31) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) yv[r * P + row] = acc[r];
     }
   }
   __syncthreads();
-  mimo_step_finish(p, bh, s, Kv, xr, yv, tid, 256);
+
+  // epilogue: wave w handles ranks w and w + 4, lane = head_dim index
+#pragma unroll
+  for (int k = 0; k < KR; ++k) {
+    const int r = wave + 4 * k;
+    if (r < R) {
+      float y = yv[r * P + lane];
+      if (p.has_d) y = fmaf(dh, xr[r * P + lane], y);
+      if (p.has_z) y *= siluf_acc(zl * mzl[k]);
+      if (p.has_norm) {
+        const float ss = read_lane_f(scan64_f(y * y), 63);
+        y = y * (1.f / sqrtf(ss / (float)P + kMimoNormEps)) * nwl;
+      }
+      yv[r * P + lane] = y * mol[k];
+    }
+  }
+  __syncthreads();
+  if (tid < P) {
+    float o = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) o += yv[r * P + tid];
+    p.out[(size_t)bh * P + tid] = o;
+  }
 }
 
 // Any N, P (<= 128), R <= 8: a group of sg lanes owns one state row at a
@@ -243,8 +389,17 @@ hipError_t launch_mimo_step(const ScanGeom& g, const ScanOperands& o, const Step
   kp.has_z = g.has_z; kp.has_d = g.has_d; kp.has_norm = g.has_norm;
   const unsigned grid = g.B * g.H;
   const bool al16 = (reinterpret_cast<uintptr_t>(s.ssm) % 16u) == 0u;
-  if (al16 && g.N == 128 && g.P == 64 && g.R <= 8) {
-    hipLaunchKernelGGL(mimo_step_n128p64_kernel, dim3(grid), dim3(256), 0, stream, kp);
+  if (al16 && g.N == 128 && g.P == 64 && g.R >= 1 && g.R <= 8) {
+    switch (g.R) {
+      case 1: hipLaunchKernelGGL(mimo_step_n128p64_kernel<1>, dim3(grid), dim3(256), 0, stream, kp); break;
+      case 2: hipLaunchKernelGGL(mimo_step_n128p64_kernel<2>, dim3(grid), dim3(256), 0, stream, kp); break;
+      case 3: hipLaunchKernelGGL(mimo_step_n128p64_kernel<3>, dim3(grid), dim3(256), 0, stream, kp); break;
+      case 4: hipLaunchKernelGGL(mimo_step_n128p64_kernel<4>, dim3(grid), dim3(256), 0, stream, kp); break;
+      case 5: hipLaunchKernelGGL(mimo_step_n128p64_kernel<5>, dim3(grid), dim3(256), 0, stream, kp); break;
+      case 6: hipLaunchKernelGGL(mimo_step_n128p64_kernel<6>, dim3(grid), dim3(256), 0, stream, kp); break;
+      case 7: hipLaunchKernelGGL(mimo_step_n128p64_kernel<7>, dim3(grid), dim3(256), 0, stream, kp); break;
+      default: hipLaunchKernelGGL(mimo_step_n128p64_kernel<8>, dim3(grid), dim3(256), 0, stream, kp); break;
+    }
     return hipGetLastError();
   }
   int sg = 1, lg = 0;

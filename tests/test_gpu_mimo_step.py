@@ -27,6 +27,11 @@ def _gpu_step(tok_dev, states_dev, cfg):
     Dims(2, 1, 2, 1, 64, 128, 16, R=8, has_d=False),
     Dims(1, 1, 2, 1, 64, 128, 0, R=1, has_output_norm=True),
     Dims(1, 1, 2, 1, 128, 128, 64, R=2),
+    # N=128/P=64 kernel at the ranks whose LDS items do not fill whole thread rounds
+    Dims(2, 1, 4, 2, 64, 128, 32, R=3, has_output_norm=True),
+    Dims(1, 1, 3, 1, 64, 128, 64, R=5, has_z=False),
+    Dims(1, 1, 2, 2, 64, 128, 8, R=6, has_output_norm=True, has_d=False),
+    Dims(1, 1, 2, 1, 64, 128, 32, R=7),
 ], ids=lambda d: f"B{d.B}H{d.H}G{d.G}P{d.P}N{d.N}A{d.A}R{d.R}{'n' if d.has_output_norm else ''}")
 def test_mimo_step_matches_oracle(d):
     st = mimo_decode_states(d, seed=3400 + d.P + d.R)
