@@ -1,4 +1,4 @@
-"""float64 CPU oracle of the Mamba-3 forward path.
+"""float64 CPU oracle of the Mamba-3 forward path and its adjoints.
 
 Test infrastructure: only the tests, the smoke check and the benchmark's CPU
 baseline import this package.  It shares no code with the HIP library.
@@ -20,3 +20,4 @@ from .m3_oracle import (  # noqa: F401
     siso_step,
     softplus,
 )
+from .m3_backward import PREPROCESS_OUTPUTS, preprocess_backward, siso_backward  # noqa: F401

@@ -3,7 +3,9 @@
 Each case plants one mistake in a temporary copy of ``oracle/m3_oracle.py``
 (a dropped term, a wrong sign or index, a swapped order, a transposed
 operand) and runs ``tests/test_oracle.py`` against that copy in a fresh
-process.  The pins must fail for every planted mistake.  Runs on the CPU.
+process; mistakes in the adjoints of ``oracle/m3_backward.py`` run
+``tests/test_oracle_backward.py``.  The pins must fail for every planted
+mistake.  Runs on the CPU.
 """
 
 from __future__ import annotations
@@ -52,6 +54,52 @@ MUTATIONS = {
     "step_keeps_unrotated_key": ("return y, h, theta, K, Xt.copy()",
                                  "return y, h, theta, Bt + bb[None], Xt.copy()"),
 }
+
+# mistakes planted in the adjoints (oracle/m3_backward.py), caught by tests/test_oracle_backward.py
+BACKWARD_MUTATIONS = {
+    "bwd_previous_token_value_dropped": ("dX[:, t - 1] += beta[:, t, :, None] * hk1", "pass"),
+    "bwd_carry_without_decay": ("carry = alpha[:, t, :, None, None] * hbar", "carry = hbar"),
+    "bwd_query_gradient_from_previous_state": (
+        'dQ[:, t] += np.einsum("bhpn,bhp->bhn", h_t, gy)', 'dQ[:, t] += np.einsum("bhpn,bhp->bhn", h_prev, gy)'),
+    "bwd_unrotate_with_plus_theta": ("dKraw = rotate(dK, -theta, A)", "dKraw = rotate(dK, theta, A)"),
+    "bwd_theta_sign": ("dQ[..., A:2 * A] * Qm[..., :A] - dQ[..., :A] * Qm[..., A:2 * A])",
+                       "dQ[..., :A] * Qm[..., A:2 * A] - dQ[..., A:2 * A] * Qm[..., :A])"),
+    "bwd_theta_forward_cumsum": ("tail = np.flip(np.cumsum(np.flip(d_theta, axis=1), axis=1), axis=1)",
+                                 "tail = np.cumsum(d_theta, axis=1)"),
+    "bwd_dt_without_beta_path": ("d_dt = d_gamma * lam + d_beta * (1.0 - lam) * alpha", "d_dt = d_gamma * lam"),
+    "bwd_gate_derivative_without_product_term": ("return s * (1.0 + u * (1.0 - s))", "return s"),
+    "bwd_rms_without_projection": ("return (r * (gy - y * np.mean(gy * y, axis=-1, keepdims=True))).reshape(rows, M)",
+                                   "return (r * gy).reshape(rows, M)"),
+    "bwd_clamp_passes_gradient": ("d_u = np.where(dt_pass, g_dt * sigmoid(u), 0.0)", "d_u = g_dt * sigmoid(u)"),
+    "bwd_a_without_softplus_slope": ("d_a = np.where(a_pass, -dt * g[\"adt\"] * sigmoid(a_raw), 0.0)",
+                                     "d_a = np.where(a_pass, -dt * g[\"adt\"], 0.0)"),
+    "bwd_dt_ignores_adt": ("g_dt = g[\"dt\"] - a_mag * g[\"adt\"]", "g_dt = g[\"dt\"]"),
+}
+
+
+def _run_planted(tmp_path, module, edits, test_file, name):
+    src_path = os.path.join(ORACLE, module)
+    with open(src_path) as f:
+        src = f.read()
+    for old, new in edits if isinstance(edits, list) else [edits]:
+        assert src.count(old) >= 1, f"mutation site of {name!r} not found in the oracle"
+        src = src.replace(old, new, 1)
+    dst = tmp_path / "oracle"
+    shutil.copytree(ORACLE, dst, ignore=shutil.ignore_patterns("__pycache__"))
+    (dst / module).write_text(src)
+    env = dict(os.environ, PYTHONPATH=f"{tmp_path}{os.pathsep}{ROOT}")
+    r = subprocess.run(
+        [sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+         os.path.join(ROOT, "tests", test_file)],
+        env=env, cwd=str(tmp_path), capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"no pin failed with the mistake {name!r} planted:\n{r.stdout[-2000:]}"
+    # The failure must come from an assertion, not from the copy failing to import.
+    assert "failed" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTATIONS))
+def test_backward_pins_catch_planted_mistake(name, tmp_path):
+    _run_planted(tmp_path, "m3_backward.py", BACKWARD_MUTATIONS[name], "test_oracle_backward.py", name)
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))

@@ -216,3 +216,24 @@ def packed_projection(d: Dims, seed: int, dt_range=(1e-3, 0.1)) -> dict:
         "b_bias": (f32(0.02) * rng.standard_normal((H, N), dtype=f32)).astype(f32),
         "d": rng.standard_normal((H,), dtype=f32),
     }
+
+
+def output_gradient(d: Dims, seed: int) -> np.ndarray:
+    """Seeded upstream gradient ~ N(0,1) in the scan-output layout [B,L,H,P]."""
+    rng = np.random.default_rng([seed, 0x4742])
+    return np.ascontiguousarray(rng.standard_normal((d.B, d.L, d.H, d.P), dtype=np.float32))
+
+
+def preprocess_output_gradients(rows: int, inner: int, bc_width: int, heads: int, angles: int,
+                                seed: int, missing=()) -> dict:
+    """Seeded gradients ~ N(0,1) of the eight preprocess outputs (x, z [rows, I];
+    bh, ch [rows, GRN]; dt, adt, trap [rows, H]; angle [rows, A]); names in
+    ``missing`` map to None (no gradient)."""
+    rng = np.random.default_rng([seed, 0x5042])
+    widths = {"x": inner, "z": inner, "bh": bc_width, "ch": bc_width, "dt": heads, "adt": heads,
+              "trap": heads, "angle": angles}
+    out = {}
+    for k, w in widths.items():
+        g = np.ascontiguousarray(rng.standard_normal((rows, w), dtype=np.float32))
+        out[k] = None if k in missing else g
+    return out
