@@ -12,8 +12,9 @@ Prints one JSON line: tokens/s of the step, the scan kernel's roofline
 CPU oracle timed on a bounded sample on the host cores.  After the timed
 region it also measures the other rows of the path at their own workloads
 ("rows"): the decode step at B256 H32 (1 token per step, HBM-bound), the
-rank-4 MIMO decode step at the same geometry, and the MIMO scan at
-B8 L4096 H32 R4 (FP32-matrix-bound).
+rank-4 MIMO decode step at the same geometry, the MIMO scan at
+B8 L4096 H32 R4 (FP32-matrix-bound), the SISO backward at the step's
+geometry and the preprocess backward over its packed projection.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
 """
@@ -76,8 +77,8 @@ def decode_algorithmic_bytes(B, H, G, P, N, A) -> int:
 
 
 def measure_rows(torch, m3, lib, hip, new_event, dev):
-    """Decode-step and MIMO-scan rows, each at its own workload, timed with HIP
-    events on the stream the kernels run on."""
+    """Decode-step, MIMO-scan and backward rows, each at its own workload, timed
+    with HIP events on the stream the kernels run on."""
     from workloads import WORKLOADS, decode_states, mimo_decode_states, ssm_inputs, step_inputs
     ops11 = ("c", "b", "x", "z", "adt", "dt", "trap", "angle", "c_bias", "b_bias", "d")
     rows = {}
@@ -185,6 +186,75 @@ def measure_rows(torch, m3, lib, hip, new_event, dev):
                          "min_flops": flops, "fp32_tflops": flops / (cm * 1e-3) / 1e12,
                          "fp32_frac": flops / (cm * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, "bound": "fp32 matrix",
                          "algorithmic_bytes": byt, "gbs": byt / (cm * 1e-3) / 1e9}
+    del inp, ops, ws, out
+
+    # SISO backward at the forward's geometry: the eleven gradients from dout
+    from workloads import output_gradient, preprocess_output_gradients, packed_projection
+    w = WORKLOADS["siso_b4_l2048"]
+    d = w.dims
+    ins = {k: torch.from_numpy(v).to(dev) for k, v in ssm_inputs(d, seed=w.seed, mimo=False).items()}
+    dout = torch.from_numpy(output_gradient(d, seed=w.seed)).to(dev)
+    cfg = m3.SsmConfig(d.B, d.L, d.H, d.G, d.P, d.N, d.A)
+    grads = {k: torch.empty_like(ins[k]) for k in ops11}
+    ws = torch.empty(m3.siso_bwd_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+
+    def one_b():
+        m3.m3_siso_bwd(dout, *[ins[k] for k in ops11], cfg, grads=grads, workspace=ws)
+    for _ in range(3):
+        one_b()
+    torch.cuda.synchronize()
+    n_calls = 10
+    a.record()
+    for _ in range(n_calls):
+        one_b()
+    b.record()
+    torch.cuda.synchronize()
+    cm = a.elapsed_time(b) / n_calls
+    Bb, Lb, Hb, Pb, Nb, Ab = d.B, d.L, d.H, d.P, d.N, d.A
+    # 12 N P per token-head: the forward state update and read-out, the reverse
+    # adjoint update, and the three adjoint contractions h^T gy, G^T x, G K
+    flops = 12 * Nb * Pb * Bb * Lb * Hb
+    # operands and dout read once, the eleven gradients written once
+    byt = 4 * (2 * (2 * Bb * Lb * d.groups * Nb + 3 * Bb * Lb * Hb * Pb + 3 * Bb * Lb * Hb + Bb * Lb * Ab
+                    + 2 * Hb * Nb + Hb) - Bb * Lb * Hb * Pb)
+    rows["siso_bwd"] = {"workload": "siso_b4_l2048: B4 L2048 H24 P64 N128 A32, dout ~ N(0,1)",
+                        "call_ms": cm, "tokens_per_s": Bb * Lb / (cm * 1e-3), "min_flops": flops,
+                        "fp32_tflops": flops / (cm * 1e-3) / 1e12,
+                        "fp32_frac": flops / (cm * 1e-3) / 1e12 / FP32_PEAK_TFLOPS,
+                        "algorithmic_bytes": byt, "gbs": byt / (cm * 1e-3) / 1e9,
+                        "hbm_frac": byt / (cm * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "workspace_bytes": ws.numel(), "calls_timed": n_calls}
+    del ins, dout, grads, ws
+
+    # preprocess backward over the [8192 x 3432] packed projection, all eight output gradients
+    pk = packed_projection(d, seed=w.seed)
+    I, M = d.H * d.P, d.groups * d.N
+    pcfg = m3.PreprocessConfig(I, d.N, d.H, d.A, d.groups, 1, 1e-5, 1e-3, 0.1, 1e-4)
+    rows_n = d.B * d.L
+    proj = torch.from_numpy(pk["projected"]).to(dev)
+    bias = torch.from_numpy(pk["dt_bias"]).to(dev)
+    pg = {k: torch.from_numpy(v).to(dev)
+          for k, v in preprocess_output_gradients(rows_n, I, M, d.H, d.A, seed=w.seed).items()}
+    pouts = {"projected": torch.empty_like(proj), "dt_bias": torch.empty_like(bias)}
+
+    def one_p():
+        m3.m3_preprocess_bwd(proj, bias, pcfg, pg, outs=pouts)
+    for _ in range(3):
+        one_p()
+    torch.cuda.synchronize()
+    n_calls = 20
+    a.record()
+    for _ in range(n_calls):
+        one_p()
+    b.record()
+    torch.cuda.synchronize()
+    pm = a.elapsed_time(b) / n_calls
+    Wp = pcfg.width
+    pbyt = 4 * (3 * rows_n * Wp + 2 * d.H)   # projected and the gradients read, d_projected written
+    rows["preprocess_bwd"] = {"workload": "[8192 x 3432] packed projection (siso_b4_l2048 geometry)",
+                              "ms": pm, "algorithmic_bytes": pbyt, "gbs": pbyt / (pm * 1e-3) / 1e9,
+                              "hbm_frac": pbyt / (pm * 1e-3) / 1e9 / HBM_PEAK_GBS, "bound": "hbm",
+                              "calls_timed": n_calls}
     return rows
 
 

@@ -1,7 +1,7 @@
 /*
- * m3.h -- C ABI of the MI355X (gfx950) Mamba-3 selective-state forward path.
+ * m3.h -- C ABI of the MI355X (gfx950) Mamba-3 selective-state path.
  *
- * Five operations, named after the public functions of the oarust 0.8.6
+ * Seven operations, named after the public functions of the oarust 0.8.6
  * source page src/rs/ml/matrix/mamba3.rs ("Public API" section) and the
  * ml::matrix API index:
  *
@@ -10,13 +10,16 @@
  *   m3_mimo_fwd     mamba3_mimo         shared-state MIMO scan, forward
  *   m3_siso_step    mamba3_siso_step    one SISO decode token, states in place
  *   m3_mimo_step    mamba3_mimo_step    one MIMO decode token, states in place
+ *   m3_siso_bwd     mamba3_siso_backward        the eleven SISO scan gradients
+ *   m3_preprocess_bwd mamba3_preprocess_backward gradients of projected, dt_bias
  *
  * Conventions shared by every entry point
  * ---------------------------------------
  * Pointers:   every tensor argument is a DEVICE pointer to contiguous,
  *             row-major float32 memory on the current HIP device, in exactly
  *             the layout the comment of that entry point gives.  Only the
- *             angle operand may be NULL, and only when num_rope_angles == 0.
+ *             angle operands may be NULL, and only when num_rope_angles == 0
+ *             (m3_preprocess_bwd also takes NULL for a missing gradient).
  * Ownership:  the caller allocates every input, output, state and workspace
  *             buffer.  The library allocates no device memory on these paths
  *             and keeps no pointer after the call returns.
@@ -225,6 +228,62 @@ int m3_mimo_step(const float* c, const float* b, const float* x, const float* z,
                  const float* norm_weight,
                  float* ssm_state, float* angle_state, float* k_state, float* v_state,
                  m3_ssm_config cfg, float* out, void* stream);
+
+/*
+ * m3_siso_bwd -- mamba3_siso_backward ("Compute all explicit Mamba-3 SISO
+ * adjoints"; SsmBackward for the eleven gradients).  Given the upstream
+ * gradient dout [B,L,H,P] of m3_siso_fwd's output and the same eleven
+ * operands and config as the forward call, writes the gradient of
+ * sum(dout * out) with respect to every operand, each in its operand's
+ * layout:
+ *   d_c, d_b [B,L,G,N] (summed over the heads of each group);
+ *   d_x, d_z [B,L,H,P];  d_adt, d_dt, d_trap [B,L,H];  d_angle [B,L,A]
+ *   (summed over heads);  d_c_bias, d_b_bias [H,N] and d_d [H] (summed over
+ *   batch and sequence).
+ * d_z is all zeros when has_z == 0 and d_d all zeros when has_d == 0.
+ * Outputs are overwritten, not accumulated; they must not alias inputs.
+ * workspace: at least m3_siso_bwd_workspace_bytes(cfg) bytes of device
+ *   memory (chunk-entry states and exit adjoints [B*H, ceil(L/32), P, N]
+ *   twice, per-head query/key adjoints [B,L,H,N] twice, and small
+ *   per-token arrays); the contents need no initialisation.
+ * Rules: those of m3_siso_fwd (M3_ERR_INVALID_ARGUMENT), plus
+ *   M3_ERR_UNSUPPORTED when the per-chunk working set (P, N) or the
+ *   heads-per-group tile exceeds one CU's 160 KiB of LDS (P = 64 with
+ *   N = 128 fits; P = 128 with N = 128 does not).  d_angle may be NULL when
+ *   A == 0.  The reductions run in a fixed order, so repeated calls give
+ *   identical results.
+ */
+size_t m3_siso_bwd_workspace_bytes(m3_ssm_config cfg);
+int m3_siso_bwd(const float* dout, const float* c, const float* b, const float* x,
+                const float* z, const float* adt, const float* dt, const float* trap,
+                const float* angle, const float* c_bias, const float* b_bias, const float* d,
+                m3_ssm_config cfg,
+                float* d_c, float* d_b, float* d_x, float* d_z, float* d_adt, float* d_dt,
+                float* d_trap, float* d_angle, float* d_c_bias, float* d_b_bias, float* d_d,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * m3_preprocess_bwd -- mamba3_preprocess_backward (gradients of projected
+ * and dt_bias; Mamba3PreprocessBackward).  projected [rows, W], dt_bias [H]
+ * and cfg as for m3_preprocess; g_x, g_z [rows, I], g_bh, g_ch
+ * [rows, G*R*N], g_dt, g_adt, g_trap [rows, H], g_angle [rows, A] are the
+ * gradients of the eight preprocess outputs, and any of them may be NULL,
+ * which counts as a zero gradient.  Writes d_projected [rows, W]:
+ *   z, x, trap, angle columns: the output gradient;
+ *   B, C columns, per N-wide row v with y = v / sqrt(mean(v^2) + eps):
+ *     r * g - v * r^3 * mean(g * v),  r = 1 / sqrt(mean(v^2) + eps);
+ *   dt columns: (g_dt - max(softplus(A_raw), a_floor) * g_adt) * sigmoid(u),
+ *     u = dt_raw + dt_bias, where dt_min <= softplus(u) <= dt_max, else 0;
+ *   A columns: -dt * g_adt * sigmoid(A_raw) where softplus(A_raw) >= a_floor,
+ *     else 0;
+ * and d_dt_bias [H] = the column sums of the dt columns, in a fixed order.
+ * Rules: those of m3_preprocess.
+ */
+int m3_preprocess_bwd(const float* projected, const float* dt_bias, uint32_t rows,
+                      m3_preprocess_config cfg,
+                      const float* g_x, const float* g_z, const float* g_bh, const float* g_ch,
+                      const float* g_dt, const float* g_adt, const float* g_trap,
+                      const float* g_angle, float* d_projected, float* d_dt_bias, void* stream);
 
 /*
  * Measurement hook.  After m3_set_profile_events(start, stop) with two

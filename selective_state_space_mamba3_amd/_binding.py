@@ -117,6 +117,12 @@ def lib() -> ctypes.CDLL:
     L.m3_siso_step.argtypes = [_P] * 15 + [_CSsm, _P, _P]
     L.m3_mimo_step.restype = ctypes.c_int
     L.m3_mimo_step.argtypes = [_P] * 19 + [_CSsm, _P, _P]
+    L.m3_siso_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.m3_siso_bwd_workspace_bytes.argtypes = [_CSsm]
+    L.m3_siso_bwd.restype = ctypes.c_int
+    L.m3_siso_bwd.argtypes = [_P] * 12 + [_CSsm] + [_P] * 11 + [_P, ctypes.c_size_t, _P]
+    L.m3_preprocess_bwd.restype = ctypes.c_int
+    L.m3_preprocess_bwd.argtypes = [_P, _P, ctypes.c_uint32, _CPre] + [_P] * 8 + [_P, _P, _P]
     _LIB = L
     return L
 
@@ -317,4 +323,65 @@ def m3_preprocess(projected, dt_bias, cfg: PreprocessConfig, outs: dict | None =
         _expect(k, outs[k], shp, dev)
     _check(L_.m3_preprocess(_ptr(projected), _ptr(dt_bias), rows, c_pre(cfg),
                             *[_ptr(outs[k]) for k in _PRE_OUT], _stream(dev, stream)))
+    return outs
+
+
+def siso_bwd_workspace_bytes(cfg: SsmConfig) -> int:
+    return int(lib().m3_siso_bwd_workspace_bytes(c_ssm(cfg)))
+
+
+def m3_siso_bwd(dout, c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d, cfg: SsmConfig,
+                grads: dict | None = None, workspace=None, stream=None) -> dict:
+    """SISO scan backward on the GPU; returns the eleven gradients by operand name."""
+    L_ = lib()
+    dev = x.device
+    ops = dict(zip(_OPS11, (c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d)))
+    shapes = _scan_shapes(cfg, cfg.groups, (cfg.num_heads, cfg.state_size))
+    for k, shp in shapes.items():
+        _expect(k, ops[k], shp, dev)
+    _expect("dout", dout, shapes["x"], dev)
+    grads = dict(grads or {})
+    for k, shp in shapes.items():
+        if k not in grads:
+            grads[k] = torch.empty(shp, dtype=torch.float32, device=dev)
+        _expect("d_" + k, grads[k], shp, dev)
+    need = siso_bwd_workspace_bytes(cfg)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(L_.m3_siso_bwd(_ptr(dout), *[_ptr(ops[k]) for k in _OPS11], c_ssm(cfg),
+                          *[_ptr(grads[k]) for k in _OPS11], _ptr(workspace), ws_bytes,
+                          _stream(dev, stream)))
+    return grads
+
+
+def m3_preprocess_bwd(projected, dt_bias, cfg: PreprocessConfig, grads: dict, outs: dict | None = None,
+                      stream=None) -> dict:
+    """Preprocess backward; ``grads`` maps output names to gradients (missing or None = zero).
+    Returns {"projected": d_projected [rows, W], "dt_bias": d_dt_bias [H]}."""
+    L_ = lib()
+    dev = projected.device
+    rows = projected.shape[0] if projected.dim() == 2 else -1
+    _expect("projected", projected, (rows, cfg.width), dev)
+    _expect("dt_bias", dt_bias, (cfg.num_heads,), dev)
+    M = cfg.num_groups * cfg.mimo_rank * cfg.state_size
+    shapes = {"x": (rows, cfg.inner_size), "z": (rows, cfg.inner_size), "bh": (rows, M),
+              "ch": (rows, M), "dt": (rows, cfg.num_heads), "adt": (rows, cfg.num_heads),
+              "trap": (rows, cfg.num_heads), "angle": (rows, cfg.num_rope_angles)}
+    for k in grads:
+        if k not in shapes:
+            raise ValueError(f"unknown preprocess output {k!r}")
+    for k, shp in shapes.items():
+        if grads.get(k) is not None:
+            _expect("g_" + k, grads[k], shp, dev)
+    outs = dict(outs or {})
+    if "projected" not in outs:
+        outs["projected"] = torch.empty((rows, cfg.width), dtype=torch.float32, device=dev)
+    if "dt_bias" not in outs:
+        outs["dt_bias"] = torch.empty((cfg.num_heads,), dtype=torch.float32, device=dev)
+    _expect("d_projected", outs["projected"], (rows, cfg.width), dev)
+    _expect("d_dt_bias", outs["dt_bias"], (cfg.num_heads,), dev)
+    _check(L_.m3_preprocess_bwd(_ptr(projected), _ptr(dt_bias), rows, c_pre(cfg),
+                                *[_ptr(grads.get(k)) for k in _PRE_OUT],
+                                _ptr(outs["projected"]), _ptr(outs["dt_bias"]), _stream(dev, stream)))
     return outs

@@ -121,11 +121,12 @@ void m3_set_profile_events(void* start_event, void* stop_event) {
 
 const char* m3_version(void) { return "m3 0.1.0 gfx950"; }
 
-int m3_preprocess(const float* projected, const float* dt_bias, uint32_t rows,
-                  m3_preprocess_config cfg, float* x, float* z, float* bh, float* ch, float* dt,
-                  float* adt, float* trap, float* angle, void* stream) {
-  const char* op = "m3_preprocess";
-  clear_error();
+}  // extern "C"
+
+namespace {
+
+// Preprocess geometry rules shared by the forward and the backward.
+int resolve_pre(const char* op, uint32_t rows, const m3_preprocess_config& cfg, m3::PreGeom* out) {
   if (rows == 0 || cfg.inner_size == 0 || cfg.state_size == 0 || cfg.num_heads == 0 ||
       cfg.num_groups == 0 || cfg.mimo_rank == 0 ||
       2ull * cfg.num_rope_angles > cfg.state_size || !std::isfinite(cfg.epsilon) ||
@@ -143,14 +144,86 @@ int m3_preprocess(const float* projected, const float* dt_bias, uint32_t rows,
   if (GR > kU32 || M > kU32 || W > kU32 || !count_u32({rows, W}) || !count_u32({rows, I}) ||
       !count_u32({rows, M}) || !count_u32({rows, H}) || !count_u32({rows, A}))
     return fail(M3_ERR_INVALID_ARGUMENT, "%s: projected width or an element count exceeds u32", op);
-  int st = check_ptrs(op, {{"projected", projected}, {"dt_bias", dt_bias}, {"x", x}, {"z", z},
-                           {"bh", bh}, {"ch", ch}, {"dt", dt}, {"adt", adt}, {"trap", trap}});
+  *out = m3::PreGeom{rows, cfg.inner_size, cfg.state_size, cfg.num_heads, cfg.num_rope_angles,
+                     cfg.num_groups, cfg.mimo_rank, cfg.epsilon, cfg.dt_min, cfg.dt_max, cfg.a_floor};
+  return M3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int m3_preprocess(const float* projected, const float* dt_bias, uint32_t rows,
+                  m3_preprocess_config cfg, float* x, float* z, float* bh, float* ch, float* dt,
+                  float* adt, float* trap, float* angle, void* stream) {
+  const char* op = "m3_preprocess";
+  clear_error();
+  m3::PreGeom g{};
+  int st = resolve_pre(op, rows, cfg, &g);
   if (st) return st;
-  if (A > 0 && angle == nullptr) return fail(M3_ERR_INVALID_ARGUMENT, "%s: operand angle is NULL", op);
-  m3::PreGeom g{rows, cfg.inner_size, cfg.state_size, cfg.num_heads, cfg.num_rope_angles,
-                cfg.num_groups, cfg.mimo_rank, cfg.epsilon, cfg.dt_min, cfg.dt_max, cfg.a_floor};
+  st = check_ptrs(op, {{"projected", projected}, {"dt_bias", dt_bias}, {"x", x}, {"z", z},
+                       {"bh", bh}, {"ch", ch}, {"dt", dt}, {"adt", adt}, {"trap", trap}});
+  if (st) return st;
+  if (g.A > 0 && angle == nullptr) return fail(M3_ERR_INVALID_ARGUMENT, "%s: operand angle is NULL", op);
   m3::PreOperands o{projected, dt_bias, x, z, bh, ch, dt, adt, trap, angle};
   return hip_status(op, m3::launch_preprocess(g, o, static_cast<hipStream_t>(stream)));
+}
+
+int m3_preprocess_bwd(const float* projected, const float* dt_bias, uint32_t rows,
+                      m3_preprocess_config cfg, const float* g_x, const float* g_z, const float* g_bh,
+                      const float* g_ch, const float* g_dt, const float* g_adt, const float* g_trap,
+                      const float* g_angle, float* d_projected, float* d_dt_bias, void* stream) {
+  const char* op = "m3_preprocess_bwd";
+  clear_error();
+  m3::PreGeom g{};
+  int st = resolve_pre(op, rows, cfg, &g);
+  if (st) return st;
+  st = check_ptrs(op, {{"projected", projected}, {"dt_bias", dt_bias}, {"d_projected", d_projected},
+                       {"d_dt_bias", d_dt_bias}});
+  if (st) return st;
+  m3::PreBwdOperands o{projected, dt_bias, g_x, g_z, g_bh, g_ch, g_dt, g_adt, g_trap,
+                       g.A > 0 ? g_angle : nullptr, d_projected, d_dt_bias};
+  return hip_status(op, m3::launch_preprocess_bwd(g, o, static_cast<hipStream_t>(stream)));
+}
+
+size_t m3_siso_bwd_workspace_bytes(m3_ssm_config cfg) {
+  m3::ScanGeom g{};
+  if (resolve_scan("m3_siso_bwd_workspace_bytes", cfg, false, &g) != M3_OK) return 0;
+  return m3::siso_bwd_workspace_floats(g) * sizeof(float);
+}
+
+int m3_siso_bwd(const float* dout, const float* c, const float* b, const float* x, const float* z,
+                const float* adt, const float* dt, const float* trap, const float* angle,
+                const float* c_bias, const float* b_bias, const float* d, m3_ssm_config cfg,
+                float* d_c, float* d_b, float* d_x, float* d_z, float* d_adt, float* d_dt,
+                float* d_trap, float* d_angle, float* d_c_bias, float* d_b_bias, float* d_d,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  const char* op = "m3_siso_bwd";
+  clear_error();
+  m3::ScanGeom g{};
+  int st = resolve_scan(op, cfg, false, &g);
+  if (st) return st;
+  st = check_ptrs(op, {{"dout", dout}, {"c", c}, {"b", b}, {"x", x}, {"z", z}, {"adt", adt},
+                       {"dt", dt}, {"trap", trap}, {"c_bias", c_bias}, {"b_bias", b_bias}, {"d", d},
+                       {"d_c", d_c}, {"d_b", d_b}, {"d_x", d_x}, {"d_z", d_z}, {"d_adt", d_adt},
+                       {"d_dt", d_dt}, {"d_trap", d_trap}, {"d_c_bias", d_c_bias},
+                       {"d_b_bias", d_b_bias}, {"d_d", d_d}});
+  if (st) return st;
+  if (g.A > 0 && (angle == nullptr || d_angle == nullptr))
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: operand angle or d_angle is NULL", op);
+  if (!m3::siso_bwd_fits(g))
+    return fail(M3_ERR_UNSUPPORTED,
+                "%s: head_dim %u with state_size %u (or %u heads per group) exceeds the LDS of the "
+                "backward kernels",
+                op, g.P, g.N, g.H / g.G);
+  const size_t need = m3::siso_bwd_workspace_floats(g) * sizeof(float);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: workspace of %zu bytes required, %zu given", op, need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  m3::ScanOperands o{c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d,
+                     nullptr, nullptr, nullptr, nullptr, nullptr};
+  m3::BwdOperands go{dout, d_c, d_b, d_x, d_z, d_adt, d_dt, d_trap, d_angle, d_c_bias, d_b_bias, d_d};
+  return hip_status(op, m3::launch_siso_bwd(g, o, go, workspace, static_cast<hipStream_t>(stream)));
 }
 
 size_t m3_siso_fwd_workspace_bytes(m3_ssm_config cfg) {

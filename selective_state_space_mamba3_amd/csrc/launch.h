@@ -33,6 +33,20 @@ struct PreOperands {
   float *x, *z, *bh, *ch, *dt, *adt, *trap, *angle;
 };
 
+// Upstream gradient and the eleven gradient outputs of the SISO backward.
+struct BwdOperands {
+  const float* dout;
+  float *d_c, *d_b, *d_x, *d_z, *d_adt, *d_dt, *d_trap, *d_angle, *d_c_bias, *d_b_bias, *d_d;
+};
+
+// Gradients of the eight preprocess outputs (any may be null: zero) and the
+// two gradient outputs of the preprocess backward.
+struct PreBwdOperands {
+  const float *projected, *dt_bias;
+  const float *g_x, *g_z, *g_bh, *g_ch, *g_dt, *g_adt, *g_trap, *g_angle;
+  float *d_projected, *d_dt_bias;
+};
+
 // Chunked scan plan: chunk length, number of sequence segments.
 struct ScanPlan {
   int chunk;
@@ -63,5 +77,11 @@ hipError_t launch_siso_step(const ScanGeom& g, const ScanOperands& o, const Step
 hipError_t launch_mimo_step(const ScanGeom& g, const ScanOperands& o, const StepStates& s,
                             hipStream_t stream);
 hipError_t launch_preprocess(const PreGeom& g, const PreOperands& o, hipStream_t stream);
+hipError_t launch_preprocess_bwd(const PreGeom& g, const PreBwdOperands& o, hipStream_t stream);
+
+size_t siso_bwd_workspace_floats(const ScanGeom& g);
+bool siso_bwd_fits(const ScanGeom& g);  // LDS of the backward kernels fits one CU
+hipError_t launch_siso_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOperands& go, void* workspace,
+                           hipStream_t stream);
 
 }  // namespace m3

@@ -25,7 +25,8 @@ def _lib():
 def test_library_exports_every_header_function():
     names = m3.header_functions()
     assert set(names) >= {"m3_preprocess", "m3_siso_fwd", "m3_mimo_fwd", "m3_siso_step",
-                          "m3_mimo_step", "m3_last_error", "m3_siso_fwd_workspace_bytes",
+                          "m3_mimo_step", "m3_siso_bwd", "m3_preprocess_bwd",
+                          "m3_siso_bwd_workspace_bytes", "m3_last_error", "m3_siso_fwd_workspace_bytes",
                           "m3_mimo_fwd_workspace_bytes", "m3_version"}
     L = _lib()
     for n in names:
@@ -190,6 +191,57 @@ def test_preprocess_rejects_empty_rows_and_nulls():
         p = [FAKE] * 10
         p[i] = None
         assert L.m3_preprocess(p[0], p[1], 16, bd.c_pre(_pre()), *p[2:], None) == INVALID
+
+
+@pytest.mark.parametrize("bad", SISO_BAD)
+def test_siso_bwd_rejects_broken_geometry(bad):
+    L = _lib()
+    cfg = bd.c_ssm(_ssm(**bad))
+    assert L.m3_siso_bwd(*[FAKE] * 12, cfg, *[FAKE] * 11, FAKE, 1 << 40, None) == INVALID
+    assert "m3_siso_bwd" in m3.last_error()
+    assert L.m3_siso_bwd_workspace_bytes(cfg) == 0
+
+
+def test_siso_bwd_rules():
+    L = _lib()
+    cfg = _ssm()
+    c = bd.c_ssm(cfg)
+    need = L.m3_siso_bwd_workspace_bytes(c)
+    # theta, two [BH, nc, P, N] state buffers, two [B, L, H, N] adjoints, ... (B2 L8 H4 P16 N32 A8)
+    assert need >= 4 * (2 * 2 * 4 * 1 * 16 * 32 + 2 * 2 * 8 * 4 * 32)
+    for i in range(23):  # every operand and gradient except angle / d_angle
+        if i in (8, 19):
+            continue
+        p = [FAKE] * 23
+        p[i] = None
+        assert L.m3_siso_bwd(*p[:12], c, *p[12:], FAKE, need, None) == INVALID, i
+    for i in (8, 19):  # angle, d_angle with A > 0
+        p = [FAKE] * 23
+        p[i] = None
+        assert L.m3_siso_bwd(*p[:12], c, *p[12:], FAKE, need, None) == INVALID
+    assert L.m3_siso_bwd(*[FAKE] * 12, c, *[FAKE] * 11, FAKE, need - 1, None) == INVALID
+    assert "workspace" in m3.last_error()
+    assert L.m3_siso_bwd(*[FAKE] * 12, c, *[FAKE] * 11, None, need, None) == INVALID
+    big = bd.c_ssm(_ssm(head_dim=128, state_size=128, num_rope_angles=8))
+    assert L.m3_siso_bwd(*[FAKE] * 12, big, *[FAKE] * 11, FAKE, 1 << 40, None) == bd.M3_ERR_UNSUPPORTED
+    assert "LDS" in m3.last_error()
+    assert L.m3_siso_bwd_workspace_bytes(big) > 0
+
+
+@pytest.mark.parametrize("bad", PRE_BAD)
+def test_preprocess_bwd_rejects_broken_config(bad):
+    L = _lib()
+    assert L.m3_preprocess_bwd(FAKE, FAKE, 16, bd.c_pre(_pre(**bad)), *[FAKE] * 8, FAKE, FAKE, None) == INVALID
+    assert "m3_preprocess_bwd" in m3.last_error()
+
+
+def test_preprocess_bwd_null_rules():
+    L = _lib()
+    assert L.m3_preprocess_bwd(FAKE, FAKE, 0, bd.c_pre(_pre()), *[FAKE] * 8, FAKE, FAKE, None) == INVALID
+    for i in (0, 1, 10, 11):  # projected, dt_bias, d_projected, d_dt_bias
+        p = [FAKE] * 12
+        p[i] = None
+        assert L.m3_preprocess_bwd(p[0], p[1], 16, bd.c_pre(_pre()), *p[2:], None) == INVALID
 
 
 def test_error_is_thread_local_and_cleared():
