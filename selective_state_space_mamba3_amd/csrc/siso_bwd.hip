@@ -18,18 +18,22 @@
 // V[r][t] = e^(cum_r-cum_t) (t < r).  The scalar adjoints follow from the
 // per-token sums rho_t = gy_t.y_ssm_t, ds_t = x_t.GK_t, e_t = ds_t + (x_t.gy_t)(Q_t.K_t):
 //     d gamma_t = e_t,  d c_t = ds_{t-1}  (c_t = (1-lam_t) dt_t),
-//     d adt_t = Phi_t - gamma_t e_t,  Phi_t = sum_{r>=t} (rho_r - c_{r+1} ds_r - gamma_{r+1} e_{r+1}),
-// the last being the reverse recurrence of <adjoint of h_t, h_t>.
+//     d adt_t = sum_{r>=t} (rho_r - c_{r+1} ds_r - gamma_r e_r),
+// the last from the reverse recurrence of <adjoint of h_t, h_t>, which
+// telescopes into a suffix sum of per-token terms.
 //
-// Launches: (1) cumulative angle per token and head; (2) per chunk, the
-// forward summary sum_s e^(cumx-cum_s) s_s x_s K_s^T and the reverse summary
-// sum_r e^(cum_r) gy_r Q_r^T on FP32 MFMA; (3) element-wise prefix over the
-// chunks, turning them in place into entry states and exit adjoints;
-// (4) per chunk, the products above on FP32 MFMA; (5) per token row, the
-// rotation adjoints (angle derivative, un-rotation onto B/C + bias), the
-// sum over the heads of a group and partial bias sums; (6) per head, the
-// reverse sums over the sequence for adt, dt, trap and the angle; (7) the
-// bias, D and angle reductions, all in a fixed order.
+// Launches: (1) chunk-local cumulative angles and (2) a scan of the tile
+// totals; (3) per chunk, the forward summary sum_s e^(cumx-cum_s) s_s x_s K_s^T
+// and the reverse summary sum_r e^(cum_r) gy_r Q_r^T on FP32 MFMA;
+// (4) element-wise prefix over the chunks, turning them in place into entry
+// states and exit adjoints; (5) per chunk, the products above on FP32 MFMA,
+// the rotation adjoints (angle derivative, un-rotation onto B + b_bias and
+// C + c_bias per head) and chunk-local suffix sums; (6) a scan of the chunk
+// totals; (7) per chunk, d adt, d dt, d trap and the per-head angle adjoint;
+// (8) per token row, the sum over a group's heads and partial bias sums;
+// (9) the bias, D and angle reductions.  Every reduction has a fixed order,
+// so results repeat bit for bit.  Each kernel issues its global loads
+// together, so a workgroup waits on about one memory round trip.
 #include "common.h"
 #include "launch.h"
 
@@ -38,28 +42,34 @@
 namespace m3 {
 namespace {
 
-constexpr int BQ = 32;     // tokens per chunk
-constexpr int MS = BQ + 1; // row stride of the chunk-square matrices in LDS
-constexpr int RB = 16;     // token rows per workgroup in the un-rotation pass
+constexpr int BQ = 32;      // tokens per chunk
+constexpr int MS = BQ + 1;  // row stride of the chunk-square matrices in LDS
+constexpr int RB = 16;      // token rows per workgroup in the group reduction
+constexpr int TT = 64;      // tokens per tile of the cumulative-angle scan
+constexpr int KQ_ITEMS = 8; // (token, column pair) items per thread: 32 * 128 / 512
+constexpr int KQ_ROUND = 4; // of which this many have their loads in flight together
+constexpr int XG_ITEMS = 8; // (token, head_dim) items per thread: 32 * 128 / 512
 
 struct BwdK {
   const float *dout, *c, *b, *x, *z, *adt, *dt, *trap, *angle, *c_bias, *b_bias, *d;
   float *d_c, *d_b, *d_x, *d_z, *d_adt, *d_dt, *d_trap, *d_angle, *d_c_bias, *d_b_bias, *d_d;
-  float* theta;     // [BH][L][A]   cumulative angle
+  float* theta;     // [BH][L][A]     cumulative angle within its 64-token tile
+  float* tpre;      // [BH][nT][A]    sum of the angle increments of the earlier tiles
   float* hs;        // [BH][nc][P][N] forward chunk summaries -> chunk-entry states h'
   float* gs;        // [BH][nc][P][N] reverse chunk summaries -> chunk-exit adjoints G
-  float* decay;     // [BH][nc]     e^(sum of the chunk's adt)
-  float* dtheta;    // [BH][L][A]   d theta -> the per-head angle adjoint
-  float* dq_rot;    // [B][L][H][N] adjoint of the rotated query Q
-  float* dk_rot;    // [B][L][H][N] adjoint of the rotated key K
-  float* rho;       // [BH][L]
-  float* dsv;       // [BH][L]
-  float* ev;        // [BH][L]
-  float* dd_part;   // [BH][nc]     per-chunk sum of x.gy
+  float* decay;     // [BH][nc]       e^(sum of the chunk's adt)
+  float* dtheta;    // [BH][L][A]     chunk-local suffix of d theta -> per-head angle adjoint
+  float* db_head;   // [B][L][H][N]   per-head adjoint of B + b_bias
+  float* dc_head;   // [B][L][H][N]   per-head adjoint of C + c_bias
+  float* dsv;       // [BH][L]        ds_t = x_t . G_t K_t
+  float* ev;        // [BH][L]        e_t = ds_t + (x_t . gy_t)(Q_t . K_t)
+  float* phi_tot;   // [BH][nc]       chunk sums of the d adt terms -> sums over later chunks
+  float* th_tot;    // [BH][nc][A]    chunk sums of d theta -> sums over later chunks
+  float* dd_part;   // [BH][nc]       per-chunk sum of x . gy
   float* bias_part; // [nrb][2][H][N] partial bias sums (0: b_bias, 1: c_bias)
   int B, L, H, G, P, N, A;
   int has_z, has_d;
-  int nc, NT, PT, nrb;
+  int nc, nT, NT, PT, nrb;
 };
 
 __device__ __forceinline__ float dsilu_acc(float u) {
@@ -81,6 +91,90 @@ __device__ __forceinline__ floatx4 mm_tile(const float* a, int am, int ak, const
   return acc;
 }
 
+// The same product when both operands run along k in memory: A[m][k] at
+// a[m * am + k] and B[k][n] at bt[n * bn + k], K a multiple of 16, 16-byte
+// aligned rows.  Lane group q takes k = 16 j + 4 q + e in step (j, e), so
+// each lane reads its operands as 16-byte vectors; A and B agree on the
+// order, which the sum over k does not see.
+__device__ __forceinline__ floatx4 mm_tile_k4(const float* a, int am, const float* bt, int bn, int K,
+                                              floatx4 acc, int lane) {
+  const int r = lane & 15, q = lane >> 4;
+  const float* ap = a + r * am + 4 * q;
+  const float* bq = bt + r * bn + 4 * q;
+#pragma unroll 2
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const floatx4 av = lds_read4(ap + k0), bv = lds_read4(bq + k0);
+    acc = mfma16(av[0], bv[0], acc);
+    acc = mfma16(av[1], bv[1], acc);
+    acc = mfma16(av[2], bv[2], acc);
+    acc = mfma16(av[3], bv[3], acc);
+  }
+  return acc;
+}
+
+// A from LDS along k as in mm_tile_k4; B[k][n] = g[n * ldg + k] from global
+// memory, rows clamped to nrow - 1 and k to kmax - 4 (N % 4 == 0), so reads
+// stay in bounds; A is zero where k runs past the data, and clamped rows give
+// output columns the caller discards.  All B loads are issued first.
+template <int KMAX16>
+__device__ __forceinline__ floatx4 mm_tile_k4_g(const float* a, int am, const float* g, int ldg, int nrow,
+                                                int kmax, int K, floatx4 acc, int lane) {
+  const int r = lane & 15, q = lane >> 4;
+  const float* ap = a + r * am + 4 * q;
+  const float* gp = g + (size_t)min(r, nrow - 1) * ldg;
+  floatx4 bv[KMAX16];
+#pragma unroll
+  for (int j = 0; j < KMAX16; ++j)
+    if (16 * j < K) bv[j] = *reinterpret_cast<const floatx4*>(gp + min(16 * j + 4 * q, kmax - 4));
+#pragma unroll
+  for (int j = 0; j < KMAX16; ++j) {
+    if (16 * j < K) {
+      const floatx4 av = lds_read4(ap + 16 * j);
+      acc = mfma16(av[0], bv[j][0], acc);
+      acc = mfma16(av[1], bv[j][1], acc);
+      acc = mfma16(av[2], bv[j][2], acc);
+      acc = mfma16(av[3], bv[j][3], acc);
+    }
+  }
+  return acc;
+}
+
+// The same product for any N: scalar loads, k = 4 j + q in step j.
+template <int KMAX4>
+__device__ __forceinline__ floatx4 mm_tile_k1_g(const float* a, int am, const float* g, int ldg, int nrow,
+                                                int kmax, int K, floatx4 acc, int lane) {
+  const int r = lane & 15, q = lane >> 4;
+  const float* ap = a + r * am + q;
+  const float* gp = g + (size_t)min(r, nrow - 1) * ldg;
+  float bv[KMAX4];
+#pragma unroll
+  for (int j = 0; j < KMAX4; ++j)
+    if (4 * j < K) bv[j] = gp[min(4 * j + q, kmax - 1)];
+#pragma unroll
+  for (int j = 0; j < KMAX4; ++j)
+    if (4 * j < K) acc = mfma16(ap[4 * j], bv[j], acc);
+  return acc;
+}
+
+// A[m][k] from LDS (a[m * am + k]); B[k][n] = g[k * ldg + n] from global
+// memory, k clamped to krow - 1 and n to ncol - 1 (A is zero past krow; the
+// caller discards output columns past ncol).  K a multiple of 4, at most 4 KMAX4.
+template <int KMAX4>
+__device__ __forceinline__ floatx4 mm_tile_g(const float* a, int am, const float* g, int ldg, int krow,
+                                             int ncol, int K, floatx4 acc, int lane) {
+  const int r = lane & 15, q = lane >> 4;
+  const float* ap = a + r * am + q;
+  const float* gp = g + min(r, ncol - 1);
+  float bv[KMAX4];
+#pragma unroll
+  for (int j = 0; j < KMAX4; ++j)
+    if (4 * j < K) bv[j] = gp[(size_t)min(4 * j + q, krow - 1) * ldg];
+#pragma unroll
+  for (int j = 0; j < KMAX4; ++j)
+    if (4 * j < K) acc = mfma16(ap[4 * j], bv[j], acc);
+  return acc;
+}
+
 // Sum over the 16 lanes of each 16-lane row; the total lands in lane 15 of the row.
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f<0x111>(v);
@@ -90,101 +184,197 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Inclusive suffix sum within each aligned group of W lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float suffix_sum(float v, int lane) {
+#pragma unroll
+  for (int off = 1; off < W; off <<= 1) {
+    const float o = __shfl_down(v, off, W);
+    if ((lane & (W - 1)) + off < W) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float theta_at(const BwdK& p, int bh, int t, int a) {
+  return p.theta[((size_t)bh * p.L + t) * p.A + a] + p.tpre[((size_t)bh * p.nT + t / TT) * p.A + a];
+}
+
 // Rotated, bias-added keys and queries of one chunk into LDS rows of stride
-// ns (columns N .. ns-1 and rows past nv zero).  Column j < A pairs with
-// j + A; A <= j < N - A stands for the plain column j + A.
+// ns (columns N .. 16 NT - 1 and rows past nv zero); with cs / sn non-null
+// also the cosines and sines [BQ][A].  Column j < A pairs with j + A;
+// A <= j < N - A stands for the plain column j + A.  All loads of a thread
+// of a round of KQ_ROUND items are issued before the first is used (clamped
+// in-range indices).
 __device__ void load_kq(const BwdK& p, int b, int h, int g, int t0, int nv, float* Kc, float* Qc, int ns,
-                        int tid, int nthr) {
+                        float* cs_l, float* sn_l, int tid) {
   const int N = p.N, A = p.A, NP = N - A, bh = b * p.H + h;
   const float* bb = p.b_bias + (size_t)h * N;
   const float* cb = p.c_bias + (size_t)h * N;
-  for (int it = tid; it < BQ * NP; it += nthr) {
+  for (int k0 = 0; k0 < KQ_ITEMS && 512 * k0 < BQ * NP; k0 += KQ_ROUND) {
+  float th[KQ_ROUND], b0[KQ_ROUND], b1[KQ_ROUND], c0[KQ_ROUND], c1[KQ_ROUND];
+  float bb0[KQ_ROUND], bb1[KQ_ROUND], cb0[KQ_ROUND], cb1[KQ_ROUND];
+#pragma unroll
+  for (int kk = 0; kk < KQ_ROUND; ++kk) {
+    const int k = kk;
+    const int it = min(tid + 512 * (k0 + kk), BQ * NP - 1);
     const int t = it / NP, j = it - t * NP;
+    const int tc = t0 + min(t, nv - 1);
     const int n0 = j < A ? j : j + A;
-    float k0 = 0.f, k1 = 0.f, q0 = 0.f, q1 = 0.f;
-    if (t < nv) {
-      const size_t row = (((size_t)b * p.L + t0 + t) * p.G + g) * N;
-      if (j < A) {
-        float sn, cs;
-        sincos_acc(p.theta[((size_t)bh * p.L + t0 + t) * A + j], &sn, &cs);
-        const float b0 = p.b[row + j] + bb[j], b1 = p.b[row + j + A] + bb[j + A];
-        const float c0 = p.c[row + j] + cb[j], c1 = p.c[row + j + A] + cb[j + A];
-        k0 = b0 * cs - b1 * sn;
-        k1 = b0 * sn + b1 * cs;
-        q0 = c0 * cs - c1 * sn;
-        q1 = c0 * sn + c1 * cs;
-      } else {
-        k0 = p.b[row + n0] + bb[n0];
-        q0 = p.c[row + n0] + cb[n0];
-      }
-    }
-    Kc[t * ns + n0] = k0;
-    Qc[t * ns + n0] = q0;
+    const int n1 = j < A ? j + A : n0;
+    const size_t row = (((size_t)b * p.L + tc) * p.G + g) * N;
+    th[k] = A > 0 ? theta_at(p, bh, tc, min(j, A - 1)) : 0.f;
+    b0[k] = p.b[row + n0]; b1[k] = p.b[row + n1];
+    c0[k] = p.c[row + n0]; c1[k] = p.c[row + n1];
+    bb0[k] = bb[n0]; bb1[k] = bb[n1];
+    cb0[k] = cb[n0]; cb1[k] = cb[n1];
+  }
+#pragma unroll
+  for (int k = 0; k < KQ_ROUND; ++k) {
+    const int it = tid + 512 * (k0 + k);
+    if (it >= BQ * NP) break;
+    const int t = it / NP, j = it - t * NP;
+    const bool ok = t < nv;
     if (j < A) {
-      Kc[t * ns + j + A] = k1;
-      Qc[t * ns + j + A] = q1;
+      float sn, cs;
+      sincos_acc(th[k], &sn, &cs);
+      const float kb0 = b0[k] + bb0[k], kb1 = b1[k] + bb1[k];
+      const float qc0 = c0[k] + cb0[k], qc1 = c1[k] + cb1[k];
+      Kc[t * ns + j] = ok ? kb0 * cs - kb1 * sn : 0.f;
+      Kc[t * ns + j + A] = ok ? kb0 * sn + kb1 * cs : 0.f;
+      Qc[t * ns + j] = ok ? qc0 * cs - qc1 * sn : 0.f;
+      Qc[t * ns + j + A] = ok ? qc0 * sn + qc1 * cs : 0.f;
+      if (cs_l) {
+        cs_l[t * A + j] = cs;
+        sn_l[t * A + j] = sn;
+      }
+    } else {
+      Kc[t * ns + j + A] = ok ? b0[k] + bb0[k] : 0.f;
+      Qc[t * ns + j + A] = ok ? c0[k] + cb0[k] : 0.f;
     }
   }
-  const int pad = ns - 1 - N;  // zero columns N .. 16 NT - 1
-  for (int it = tid; it < BQ * pad; it += nthr) {
+  }
+  const int pad = p.NT * 16 - N;  // zero columns N .. 16 NT - 1
+  for (int it = tid; it < BQ * pad; it += 512) {
     const int t = it / pad, n = N + (it - t * pad);
     Kc[t * ns + n] = 0.f;
     Qc[t * ns + n] = 0.f;
   }
 }
 
-// (1) theta[bh][t][a] = sum_{s<=t} dt[b,s,h] angle[b,s,a]; one wave per (b, h).
-__global__ __launch_bounds__(64) void bwd_theta_kernel(BwdK p) {
-  const int bh = blockIdx.x, lane = threadIdx.x;
+// x and gy = dout * silu(z) of one chunk into LDS rows of stride ps (zero
+// past nv and P); with wx non-null, row t of x is scaled by wx[t] and row t
+// of gy by wg[t].  Loads first, then the stores.
+__device__ void load_xg(const BwdK& p, int b, int h, int t0, int nv, float* X, float* GY, int ps,
+                        const float* wx, const float* wg, int tid) {
+  const int P = p.P, PP = p.PT * 16;
+  float xv[XG_ITEMS], gv[XG_ITEMS], zv[XG_ITEMS];
+#pragma unroll
+  for (int k = 0; k < XG_ITEMS; ++k) {
+    const int it = min(tid + 512 * k, BQ * PP - 1);
+    const int t = it / PP, pp = it - t * PP;
+    const size_t gi = (((size_t)b * p.L + t0 + min(t, nv - 1)) * p.H + h) * P + min(pp, P - 1);
+    xv[k] = p.x[gi];
+    gv[k] = p.dout[gi];
+    zv[k] = p.has_z ? p.z[gi] : 0.f;
+  }
+#pragma unroll
+  for (int k = 0; k < XG_ITEMS; ++k) {
+    const int it = tid + 512 * k;
+    if (it >= BQ * PP) break;
+    const int t = it / PP, pp = it - t * PP;
+    const bool ok = t < nv && pp < P;
+    float gy = gv[k];
+    if (p.has_z) gy *= siluf_acc(zv[k]);
+    float x = xv[k];
+    if (wx) {
+      x *= wx[t];
+      gy *= wg[t];
+    }
+    X[t * ps + pp] = ok ? x : 0.f;
+    GY[t * ps + pp] = ok ? gy : 0.f;
+  }
+}
+
+// (1) Cumulative angle within each 64-token tile and the tile totals; one wave
+// per (b, h, tile), lane a < A.
+__global__ __launch_bounds__(64) void bwd_theta_local_kernel(BwdK p) {
+  __shared__ float dts[TT];
+  __shared__ float angs[TT * 65];
+  const int bh = blockIdx.x / p.nT, tile = blockIdx.x - bh * p.nT;
   const int b = bh / p.H, h = bh - b * p.H, A = p.A, L = p.L;
+  const int lane = threadIdx.x;
+  const int t0 = tile * TT, nv = min(TT, L - t0);
+  dts[lane] = lane < nv ? p.dt[((size_t)b * L + t0 + lane) * p.H + h] : 0.f;
+  for (int i = lane; i < TT * A; i += 64) {
+    const int t = i / A, a = i - t * A;
+    angs[t * 65 + a] = t < nv ? p.angle[((size_t)b * L + t0 + t) * A + a] : 0.f;
+  }
+  __syncthreads();
   if (lane >= A) return;
   float run = 0.f;
-  const float* dtp = p.dt + (size_t)b * L * p.H + h;
-  const float* ap = p.angle + (size_t)b * L * A + lane;
-  float* out = p.theta + (size_t)bh * L * A + lane;
-#pragma unroll 8
-  for (int t = 0; t < L; ++t) {
-    run = fmaf(dtp[(size_t)t * p.H], ap[(size_t)t * A], run);
+  float* out = p.theta + ((size_t)bh * L + t0) * A + lane;
+  for (int t = 0; t < nv; ++t) {
+    run = fmaf(dts[t], angs[t * 65 + lane], run);
     out[(size_t)t * A] = run;
+  }
+  p.tpre[((size_t)bh * p.nT + tile) * A + lane] = run;
+}
+
+// (2) Exclusive prefix over the tiles of the tile totals, in place; one wave
+// per (b, h, a), lanes over tiles.
+__global__ __launch_bounds__(64) void bwd_theta_scan_kernel(BwdK p) {
+  const int bh = blockIdx.x / p.A, a = blockIdx.x - bh * p.A;
+  const int lane = threadIdx.x;
+  float carry = 0.f;
+  for (int base = 0; base < p.nT; base += 64) {
+    const int tile = base + lane;
+    float* slot = p.tpre + ((size_t)bh * p.nT + tile) * p.A + a;
+    const float v = tile < p.nT ? *slot : 0.f;
+    // inclusive prefix over the 64 lanes
+    float s = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(s, off, 64);
+      if (lane >= off) s += o;
+    }
+    if (tile < p.nT) *slot = carry + s - v;
+    carry += __shfl(s, 63, 64);
   }
 }
 
 // Per-token scalars of a chunk into LDS (wave 0, lanes 0..31 own the tokens):
-// cum (inclusive chunk-local sum of adt), s, gamma.  Tokens past the end
-// get adt = s = gamma = 0, so cum stays flat there.
+// cum (inclusive chunk-local sum of adt), s, gamma, e^cum and e^(cumx - cum).
+// Tokens past the end get adt = s = gamma = 0, so cum stays flat there.
 struct ChunkScalars {
-  float* cum;
-  float* scl;
-  float* gam;
+  float *cum, *scl, *gam, *ec, *ex;
 };
 
 __device__ void chunk_scalars(const BwdK& p, int b, int h, int t0, int nv, const ChunkScalars& cs, int lane) {
-  const int t = t0 + lane;
-  float adt = 0.f, gam = 0.f, s = 0.f;
-  if (lane < nv) {
-    const size_t i = ((size_t)b * p.L + t) * p.H + h;
-    adt = p.adt[i];
-    const float dtv = p.dt[i];
-    gam = sigmoidf_acc(p.trap[i]) * dtv;
-    s = gam;
-    if (t + 1 < p.L) {
-      const size_t i1 = i + p.H;
-      s += (1.f - sigmoidf_acc(p.trap[i1])) * p.dt[i1];
-    }
-  }
+  const int t = t0 + min(lane & 31, nv - 1);
+  const size_t i = ((size_t)b * p.L + t) * p.H + h;
+  const bool has_next = t + 1 < p.L;
+  const size_t i1 = has_next ? i + p.H : i;
+  const float adt_r = p.adt[i], dt_r = p.dt[i], tr_r = p.trap[i], dt1 = p.dt[i1], tr1 = p.trap[i1];
+  const bool ok = lane < nv;
+  const float adt = ok ? adt_r : 0.f;
+  const float gam = ok ? sigmoidf_acc(tr_r) * dt_r : 0.f;
+  const float s = ok ? gam + (has_next ? (1.f - sigmoidf_acc(tr1)) * dt1 : 0.f) : 0.f;
   const float cum = scan32_f(lane < 32 ? adt : 0.f);
+  const float cumx = __shfl(cum, 31, 64);
   if (lane < BQ) {
     cs.cum[lane] = cum;
     cs.scl[lane] = s;
     cs.gam[lane] = gam;
+    cs.ec[lane] = expf(cum);
+    cs.ex[lane] = expf(cumx - cum);
   }
 }
 
-// (2) Per chunk: S = sum_s e^(cumx-cum_s) s_s x_s K_s^T and
+// (3) Per chunk: S = sum_s e^(cumx-cum_s) s_s x_s K_s^T and
 // R = sum_r e^(cum_r) gy_r Q_r^T, both [P][N], and the chunk decay e^cumx.
 __global__ __launch_bounds__(512) void bwd_summary_kernel(BwdK p) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  const int NS = p.NT * 16 + 1, PS = p.PT * 16 + 1, PP = p.PT * 16, NN = p.NT * 16;
+  const int NS = p.NT * 16 + 4, PS = p.PT * 16 + 4;
   float* Kc = lds;
   float* Qc = Kc + BQ * NS;
   float* Xw = Qc + BQ * NS;
@@ -192,29 +382,21 @@ __global__ __launch_bounds__(512) void bwd_summary_kernel(BwdK p) {
   float* cum = Gw + BQ * PS;
   float* scl = cum + BQ;
   float* gam = scl + BQ;
+  float* ec = gam + BQ;
+  float* ex = ec + BQ;
+  float* wx = ex + BQ;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int bh = blockIdx.x / p.nc, c = blockIdx.x - bh * p.nc;
   const int b = bh / p.H, h = bh - b * p.H, g = h / (p.H / p.G);
   const int t0 = c * BQ, nv = min(BQ, p.L - t0);
-  if (wave == 0) chunk_scalars(p, b, h, t0, nv, ChunkScalars{cum, scl, gam}, lane);
-  load_kq(p, b, h, g, t0, nv, Kc, Qc, NS, tid, blockDim.x);
+  if (wave == 0) chunk_scalars(p, b, h, t0, nv, ChunkScalars{cum, scl, gam, ec, ex}, lane);
+  load_kq(p, b, h, g, t0, nv, Kc, Qc, NS, nullptr, nullptr, tid);
   __syncthreads();
-  const float cumx = cum[BQ - 1];
-  for (int it = tid; it < BQ * PP; it += blockDim.x) {
-    const int t = it / PP, pp = it - t * PP;
-    float xw = 0.f, gw = 0.f;
-    if (t < nv && pp < p.P) {
-      const size_t gi = (((size_t)b * p.L + t0 + t) * p.H + h) * p.P + pp;
-      float gy = p.dout[gi];
-      if (p.has_z) gy *= siluf_acc(p.z[gi]);
-      xw = expf(cumx - cum[t]) * scl[t] * p.x[gi];
-      gw = expf(cum[t]) * gy;
-    }
-    Xw[t * PS + pp] = xw;
-    Gw[t * PS + pp] = gw;
-  }
+  if (tid < BQ) wx[tid] = ex[tid] * scl[tid];
   __syncthreads();
-  if (tid == 0) p.decay[blockIdx.x] = expf(cumx);
+  load_xg(p, b, h, t0, nv, Xw, Gw, PS, wx, ec, tid);
+  __syncthreads();
+  if (tid == 0) p.decay[blockIdx.x] = expf(cum[BQ - 1]);
   const int ntile = p.PT * p.NT;
   const size_t base = (size_t)blockIdx.x * p.P * p.N;
   const int r = lane & 15, q = lane >> 4;
@@ -235,11 +417,10 @@ __global__ __launch_bounds__(512) void bwd_summary_kernel(BwdK p) {
       if (pp < p.P && n < p.N) dst[(size_t)pp * p.N + n] = acc[i];
     }
   }
-  (void)NN;
 }
 
-// (3) Element-wise over the chunks of one (b, h): hs[c] <- state before chunk
-// c; gs[c] <- adjoint after chunk c.  In place.
+// (4) Element-wise over the chunks of one (b, h): hs[c] <- state before chunk
+// c; gs[c] <- adjoint after chunk c.  In place; loads run eight chunks ahead.
 __global__ __launch_bounds__(256) void bwd_prefix_kernel(BwdK p, int blocks_per_bh) {
   const int bh = blockIdx.x / blocks_per_bh;
   const int e = (blockIdx.x - bh * blocks_per_bh) * blockDim.x + threadIdx.x;
@@ -248,88 +429,118 @@ __global__ __launch_bounds__(256) void bwd_prefix_kernel(BwdK p, int blocks_per_
   float* hs = p.hs + (size_t)bh * nc * PN + e;
   float* gs = p.gs + (size_t)bh * nc * PN + e;
   const float* dec = p.decay + (size_t)bh * nc;
+  constexpr int U = 8;
   float run = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const float v = hs[(size_t)c * PN];
-    hs[(size_t)c * PN] = run;
-    run = fmaf(dec[c], run, v);
+  for (int c0 = 0; c0 < nc; c0 += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = c0 + u < nc ? hs[(size_t)(c0 + u) * PN] : 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u < nc) {
+        hs[(size_t)(c0 + u) * PN] = run;
+        run = fmaf(dec[c0 + u], run, v[u]);
+      }
+    }
   }
   run = 0.f;
-  for (int c = nc - 1; c >= 0; --c) {
-    const float v = gs[(size_t)c * PN];
-    gs[(size_t)c * PN] = run;
-    run = fmaf(dec[c], run, v);
+  for (int c1 = nc - 1; c1 >= 0; c1 -= U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = c1 - u >= 0 ? gs[(size_t)(c1 - u) * PN] : 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c1 - u >= 0) {
+        gs[(size_t)(c1 - u) * PN] = run;
+        run = fmaf(dec[c1 - u], run, v[u]);
+      }
+    }
   }
 }
 
-// (4) Per chunk: y, GK, dQ, dK on FP32 MFMA; writes d_z, d_x, the rotated
-// query/key adjoints and the per-token sums rho, ds, e and x.gy.
-__global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdK p) {
+struct ChunkLds {
+  int NS, PS;
+  int o_kc, o_qc, o_x, o_gy, o_mqk, o_vv, o_msg, o_cs, o_sn, o_sc, o_part, total;
+};
+
+// x and gy, dead once the products are done, make room for staging one of
+// dQ / dK [BQ][NS]; the masks make room for d theta [BQ][A].
+__host__ __device__ inline ChunkLds chunk_lds(int PT, int NT, int A) {
+  ChunkLds l{};
+  l.NS = NT * 16 + 4;
+  l.PS = PT * 16 + 4;
+  int off = 0;
+  l.o_kc = off; off += BQ * l.NS;
+  l.o_qc = off; off += BQ * l.NS;
+  l.o_x = off;
+  l.o_gy = off + BQ * l.PS;
+  off += 2 * BQ * l.PS > BQ * l.NS ? 2 * BQ * l.PS : BQ * l.NS;
+  l.o_mqk = off; off += BQ * MS;
+  l.o_vv = off; off += BQ * MS;
+  l.o_msg = off; off += BQ * MS;
+  l.o_cs = off; off += BQ * A;
+  l.o_sn = off; off += BQ * A;
+  l.o_sc = off; off += 7 * BQ;
+  l.o_part = off; off += 2 * BQ * PT;
+  l.total = off;
+  return l;
+}
+
+// (5) Per chunk: y, GK, dQ, dK on FP32 MFMA; writes d_z, d_x, the per-head
+// adjoints of B + b_bias and C + c_bias, and the chunk-local suffix sums of
+// the d adt terms (into d_adt) and of d theta, with their chunk totals.
+template <bool VEC4>
+__global__ __launch_bounds__(512, 4) void bwd_chunk_kernel(BwdK p) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  const int NS = p.NT * 16 + 1, PS = p.PT * 16 + 1, PP = p.PT * 16, NN = p.NT * 16;
-  float* Kc = lds;
-  float* Qc = Kc + BQ * NS;
-  float* X = Qc + BQ * NS;
-  float* GY = X + BQ * PS;
-  float* HE = GY + BQ * PS;
-  float* GX = HE + PP * NS;
-  float* MQK = GX + PP * NS;
-  float* VV = MQK + BQ * MS;
-  float* MSG = VV + BQ * MS;
-  float* cum = MSG + BQ * MS;
+  const ChunkLds ll = chunk_lds(p.PT, p.NT, p.A);
+  const int NS = ll.NS, PS = ll.PS, PP = p.PT * 16, NN = p.NT * 16;
+  float* Kc = lds + ll.o_kc;
+  float* Qc = lds + ll.o_qc;
+  float* X = lds + ll.o_x;
+  float* GY = lds + ll.o_gy;
+  float* MQK = lds + ll.o_mqk;
+  float* VV = lds + ll.o_vv;
+  float* MSG = lds + ll.o_msg;
+  float* CS = lds + ll.o_cs;
+  float* SN = lds + ll.o_sn;
+  float* cum = lds + ll.o_sc;
   float* scl = cum + BQ;
   float* gam = scl + BQ;
-  float* qk = gam + BQ;
+  float* ec = gam + BQ;
+  float* ex = ec + BQ;
+  float* qk = ex + BQ;
   float* xg = qk + BQ;
-  float* rho_part = xg + BQ;                // [BQ][PT]
+  float* rho_part = lds + ll.o_part;        // [BQ][PT]
   float* ds_part = rho_part + BQ * p.PT;    // [BQ][PT]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  float* STG = X;                           // after the products: dQ, then dK [BQ][NS]
+  float* DTH = MQK;                         // after the products: d theta [BQ][A]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bh = blockIdx.x / p.nc, c = blockIdx.x - bh * p.nc;
   const int b = bh / p.H, h = bh - b * p.H, g = h / (p.H / p.G);
   const int t0 = c * BQ, nv = min(BQ, p.L - t0);
-  const int P = p.P, N = p.N, H = p.H;
-  const float Dh = p.has_d ? p.d[h] : 0.f;
+  const int P = p.P, N = p.N, H = p.H, A = p.A, NP = N - A;
 
-  if (wave == 0) chunk_scalars(p, b, h, t0, nv, ChunkScalars{cum, scl, gam}, lane);
-  load_kq(p, b, h, g, t0, nv, Kc, Qc, NS, tid, blockDim.x);
-  for (int it = tid; it < BQ * PP; it += blockDim.x) {
-    const int t = it / PP, pp = it - t * PP;
-    float xv = 0.f, gy = 0.f;
-    if (t < nv && pp < P) {
-      const size_t gi = (((size_t)b * p.L + t0 + t) * H + h) * P + pp;
-      xv = p.x[gi];
-      gy = p.dout[gi];
-      if (p.has_z) gy *= siluf_acc(p.z[gi]);
-    }
-    X[t * PS + pp] = xv;
-    GY[t * PS + pp] = gy;
-  }
-  {
-    const size_t base = (size_t)blockIdx.x * P * N;
-    for (int it = tid; it < PP * NN; it += blockDim.x) {
-      const int pp = it / NN, n = it - pp * NN;
-      float he = 0.f, gx = 0.f;
-      if (pp < P && n < N) {
-        he = p.hs[base + (size_t)pp * N + n];
-        gx = p.gs[base + (size_t)pp * N + n];
-      }
-      HE[pp * NS + n] = he;
-      GX[pp * NS + n] = gx;
-    }
-  }
+  // ---- loads: keys/queries, x/gy, scalars (the state and adjoint tiles are
+  // read from global memory by the products that use them)
+  const float* HEg = p.hs + (size_t)blockIdx.x * P * N;  // h'_e [P][N]
+  const float* GXg = p.gs + (size_t)blockIdx.x * P * N;  // G_x [P][N]
+  // VEC4: N % 4 == 0, 16-byte rows: vector loads of the state rows
+  if (wave == 0) chunk_scalars(p, b, h, t0, nv, ChunkScalars{cum, scl, gam, ec, ex}, lane);
+  load_kq(p, b, h, g, t0, nv, Kc, Qc, NS, CS, SN, tid);
+  load_xg(p, b, h, t0, nv, X, GY, PS, nullptr, nullptr, tid);
   __syncthreads();
-  const float cumx = cum[BQ - 1];
+  const float Dh = p.has_d ? p.d[h] : 0.f;
   const int r = lane & 15, q = lane >> 4;
 
-  // chunk-square products, masked: waves 0-3 Q K^T, waves 4-7 gy X^T
-  for (int job = wave; job < 8; job += nw) {
-    const bool sgx = job >= 4;
-    const int mt = (job & 3) >> 1, st = job & 1;
+  // ---- chunk-square products, masked: waves 0-3 Q K^T, waves 4-7 gy x^T
+  {
+    const bool sgx = wave >= 4;
+    const int mt = (wave & 3) >> 1, st = wave & 1;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     if (!sgx)
-      acc = mm_tile(Qc + mt * 16 * NS, NS, 1, Kc + st * 16 * NS, 1, NS, NN, acc, lane);
+      acc = mm_tile_k4(Qc + mt * 16 * NS, NS, Kc + st * 16 * NS, NS, NN, acc, lane);
     else
-      acc = mm_tile(GY + mt * 16 * PS, PS, 1, X + st * 16 * PS, 1, PS, PP, acc, lane);
+      acc = mm_tile_k4(GY + mt * 16 * PS, PS, X + st * 16 * PS, PS, PP, acc, lane);
     const int s = st * 16 + r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -349,72 +560,122 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdK p) {
   }
   __syncthreads();
 
+  // ---- y and GK (per head_dim tile), then dQ and dK (per state tile)
   const int nY = 2 * p.PT, nQ = 2 * p.NT;
-  const int njobs = 2 * nY + 2 * nQ;
-  for (int job = wave; job < njobs; job += nw) {
+  for (int job = wave; job < 2 * nY; job += 8) {
+    const bool isgk = job >= nY;
+    const int jj = isgk ? job - nY : job;
+    const int mt = jj / p.PT, pt = jj - mt * p.PT;
     floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-    if (job < 2 * nY) {
-      const bool isgk = job >= nY;
-      const int jj = isgk ? job - nY : job;
-      const int mt = jj / p.PT, pt = jj - mt * p.PT;
-      if (!isgk) {
-        a1 = mm_tile(Qc + mt * 16 * NS, NS, 1, HE + pt * 16 * NS, 1, NS, NN, a1, lane);
-        a2 = mm_tile(MQK + mt * 16 * MS, MS, 1, X + pt * 16, PS, 1, BQ, a2, lane);
-      } else {
-        a1 = mm_tile(Kc + mt * 16 * NS, NS, 1, GX + pt * 16 * NS, 1, NS, NN, a1, lane);
-        a2 = mm_tile(VV + mt * 16, 1, MS, GY + pt * 16, PS, 1, BQ, a2, lane);
-      }
-      const int pp = pt * 16 + r;
+    const float* Sg = (isgk ? GXg : HEg) + (size_t)pt * 16 * N;
+    const int prow = P - pt * 16;
+    const float* Ra = (isgk ? Kc : Qc) + mt * 16 * NS;
+    if constexpr (VEC4)
+      a1 = mm_tile_k4_g<8>(Ra, NS, Sg, N, prow, N, NN, a1, lane);
+    else
+      a1 = mm_tile_k1_g<32>(Ra, NS, Sg, N, prow, N, NN, a1, lane);
+    if (!isgk)
+      a2 = mm_tile(MQK + mt * 16 * MS, MS, 1, X + pt * 16, PS, 1, BQ, a2, lane);
+    else
+      a2 = mm_tile(VV + mt * 16, 1, MS, GY + pt * 16, PS, 1, BQ, a2, lane);
+    const int pp = pt * 16 + r;
+    float zv[4], gov[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = mt * 16 + 4 * q + i;
-        const bool ok = t < nv && pp < P;
-        const size_t gi = (((size_t)b * p.L + t0 + t) * H + h) * P + pp;
-        const float xv = X[t * PS + pp], gy = GY[t * PS + pp];
-        float part;
-        if (!isgk) {
-          const float y = fmaf(expf(cum[t]), a1[i], a2[i]);
-          part = gy * y;
-          if (ok) {
-            float dz = 0.f;
-            if (p.has_z) {
-              const float zv = p.z[gi];
-              dz = p.dout[gi] * fmaf(Dh, xv, y) * dsilu_acc(zv);
-            }
-            p.d_z[gi] = dz;
-          }
-        } else {
-          const float gk = fmaf(expf(cumx - cum[t]), a1[i], a2[i]);
-          part = xv * gk;
-          if (ok) p.d_x[gi] = fmaf(Dh + gam[t] * qk[t], gy, scl[t] * gk);
-        }
-        part = row16_sum(ok ? part : 0.f);
-        if (r == 15) (isgk ? ds_part : rho_part)[t * p.PT + pt] = part;
+    for (int i = 0; i < 4; ++i) {
+      const int t = mt * 16 + 4 * q + i;
+      const size_t gi = (((size_t)b * p.L + t0 + min(t, nv - 1)) * H + h) * P + min(pp, P - 1);
+      zv[i] = (!isgk && p.has_z) ? p.z[gi] : 0.f;
+      gov[i] = (!isgk && p.has_z) ? p.dout[gi] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = mt * 16 + 4 * q + i;
+      const bool ok = t < nv && pp < P;
+      const size_t gi = (((size_t)b * p.L + t0 + t) * H + h) * P + pp;
+      const float xv = X[t * PS + pp], gy = GY[t * PS + pp];
+      float part;
+      if (!isgk) {
+        const float y = fmaf(ec[t], a1[i], a2[i]);
+        part = gy * y;
+        if (ok) p.d_z[gi] = p.has_z ? gov[i] * fmaf(Dh, xv, y) * dsilu_acc(zv[i]) : 0.f;
+      } else {
+        const float gk = fmaf(ex[t], a1[i], a2[i]);
+        part = xv * gk;
+        if (ok) p.d_x[gi] = fmaf(Dh + gam[t] * qk[t], gy, scl[t] * gk);
       }
-    } else {
-      const bool isdk = job >= 2 * nY + nQ;
-      const int jj = job - 2 * nY - (isdk ? nQ : 0);
+      part = row16_sum(ok ? part : 0.f);
+      if (r == 15) (isgk ? ds_part : rho_part)[t * p.PT + pt] = part;
+    }
+  }
+  floatx4 res[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int job = wave + 8 * k;
+    res[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (job < 2 * nQ) {
+      const bool isdk = job >= nQ;
+      const int jj = isdk ? job - nQ : job;
       const int mt = jj / p.NT, nt = jj - mt * p.NT;
+      floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+      const float* Sg = (isdk ? GXg : HEg) + nt * 16;
       if (!isdk) {
-        a1 = mm_tile(GY + mt * 16 * PS, PS, 1, HE + nt * 16, NS, 1, PP, a1, lane);
+        a1 = mm_tile_g<32>(GY + mt * 16 * PS, PS, Sg, N, P, N - nt * 16, PP, a1, lane);
         a2 = mm_tile(MSG + mt * 16 * MS, MS, 1, Kc + nt * 16, NS, 1, BQ, a2, lane);
       } else {
-        a1 = mm_tile(X + mt * 16 * PS, PS, 1, GX + nt * 16, NS, 1, PP, a1, lane);
+        a1 = mm_tile_g<32>(X + mt * 16 * PS, PS, Sg, N, P, N - nt * 16, PP, a1, lane);
         a2 = mm_tile(MSG + mt * 16, 1, MS, Qc + nt * 16, NS, 1, BQ, a2, lane);
       }
-      const int n = nt * 16 + r;
-      float* dst = isdk ? p.dk_rot : p.dq_rot;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = mt * 16 + 4 * q + i;
-        const float w = isdk ? scl[t] * expf(cumx - cum[t]) : expf(cum[t]);
-        if (t < nv && n < N) dst[(((size_t)b * p.L + t0 + t) * H + h) * N + n] = fmaf(w, a1[i], a2[i]);
+        const float w = isdk ? scl[t] * ex[t] : ec[t];
+        res[k][i] = fmaf(w, a1[i], a2[i]);
+      }
+    }
+  }
+  // ---- rotation adjoints, queries first, then keys: stage the adjoint tiles
+  // in LDS, then d theta and the un-rotated adjoints per head
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();  // x, gy, the masks (pass 0) or the staged dQ (pass 1) are free
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int job = wave + 8 * k;
+      if (job < 2 * nQ && (job >= nQ) == (pass == 1)) {
+        const int jj = pass ? job - nQ : job;
+        const int mt = jj / p.NT, nt = jj - mt * p.NT;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) STG[(mt * 16 + 4 * q + i) * NS + nt * 16 + r] = res[k][i];
+      }
+    }
+    __syncthreads();
+    const float* R = pass ? Kc : Qc;
+    float* dst = pass ? p.db_head : p.dc_head;
+    for (int it = tid; it < BQ * NP; it += 512) {
+      const int t = it / NP, j = it - t * NP;
+      if (t >= nv) {
+        if (j < A && pass == 0) DTH[t * A + j] = 0.f;
+        continue;
+      }
+      const size_t o = (((size_t)b * p.L + t0 + t) * H + h) * N;
+      if (j < A) {
+        const float cs = CS[t * A + j], sn = SN[t * A + j];
+        const float d0 = STG[t * NS + j], d1 = STG[t * NS + j + A];
+        const float v = d1 * R[t * NS + j] - d0 * R[t * NS + j + A];
+        DTH[t * A + j] = pass ? DTH[t * A + j] + v : v;
+        dst[o + j] = d0 * cs + d1 * sn;
+        dst[o + j + A] = d1 * cs - d0 * sn;
+      } else {
+        dst[o + j + A] = STG[t * NS + j + A];
       }
     }
   }
   __syncthreads();
+
+  // ---- chunk-local suffix sums
   if (wave == 0) {
-    float xgv = 0.f;
+    // d adt terms: rho_t - c_{t+1} ds_t - gamma_t e_t, with c_{t+1} = s_t - gamma_t
+    float phi = 0.f, xgv = 0.f;
     if (lane < nv) {
       float rh = 0.f, ds = 0.f;
       for (int pt = 0; pt < p.PT; ++pt) {
@@ -422,207 +683,175 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdK p) {
         ds += ds_part[lane * p.PT + pt];
       }
       xgv = xg[lane];
-      const size_t i = (size_t)bh * p.L + t0 + lane;
-      p.rho[i] = rh;
-      p.dsv[i] = ds;
-      p.ev[i] = fmaf(xgv, qk[lane], ds);
+      const float e = fmaf(xgv, qk[lane], ds);
+      phi = rh - (scl[lane] - gam[lane]) * ds - gam[lane] * e;
+      const size_t ri = (size_t)bh * p.L + t0 + lane;
+      p.dsv[ri] = ds;
+      p.ev[ri] = e;
     }
+    const float loc = suffix_sum<32>(lane < 32 ? phi : 0.f, lane);
+    if (lane < nv) p.d_adt[((size_t)b * p.L + t0 + lane) * H + h] = loc;
+    if (lane == 0) p.phi_tot[blockIdx.x] = loc;
     const float tot = scan32_f(lane < 32 ? xgv : 0.f);
     if (lane == 31) p.dd_part[blockIdx.x] = tot;
+  } else if (tid >= 64 && tid < 64 + A) {
+    const int a = tid - 64;
+    float s = 0.f;
+    float* dst = p.dtheta + ((size_t)bh * p.L + t0) * A + a;
+    for (int t = nv - 1; t >= 0; --t) {
+      s += DTH[t * A + a];
+      dst[(size_t)t * A] = s;
+    }
+    p.th_tot[(size_t)blockIdx.x * A + a] = s;
   }
 }
 
-// (5) Per block of RB token rows (b, t) and group g: angle derivative per
-// head, un-rotation of dK / dQ onto B + b_bias / C + c_bias, the sum over
-// the group's heads into d_b / d_c, and partial bias sums.  Thread (hs, j)
-// owns column pair j of heads hs, hs + nhs, ... for every row of the block.
-__global__ __launch_bounds__(256) void bwd_unrotate_kernel(BwdK p) {
+// (6) Exclusive suffix over the chunks of the chunk totals, in place: one wave
+// per (b, h, column); column 0 is the d adt terms, 1 + a the angle a.
+__global__ __launch_bounds__(64) void bwd_chunk_scan_kernel(BwdK p) {
+  const int ncol = p.A + 1;
+  const int bh = blockIdx.x / ncol, col = blockIdx.x - bh * ncol;
+  const int lane = threadIdx.x, nc = p.nc;
+  float carry = 0.f;
+  for (int top = nc - 1; top >= 0; top -= 64) {
+    const int cidx = top - 63 + lane;  // lanes cover chunks top-63 .. top
+    float* slot = col == 0 ? p.phi_tot + (size_t)bh * nc + cidx
+                           : p.th_tot + ((size_t)bh * nc + cidx) * p.A + (col - 1);
+    const bool ok = cidx >= 0;
+    const float v = ok ? *slot : 0.f;
+    const float s = suffix_sum<64>(v, lane);
+    if (ok) *slot = carry + s - v;
+    carry += __shfl(s, 0, 64);
+  }
+}
+
+// (7) Per chunk: d adt += the later chunks' terms; the angle suffix
+// theta_bar_t[a] = local suffix + later chunks; d dt, d trap and the per-head
+// angle adjoint dt_t theta_bar_t (in place of the suffix).
+__global__ __launch_bounds__(256) void bwd_apply_kernel(BwdK p) {
+  __shared__ float part[8][BQ];
+  const int bh = blockIdx.x / p.nc, c = blockIdx.x - bh * p.nc;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int tid = threadIdx.x, t = tid & 31, k = tid >> 5;
+  const int t0 = c * BQ, nv = min(BQ, p.L - t0), A = p.A, H = p.H;
+  const int tc = t0 + min(t, nv - 1);
+  const size_t si = ((size_t)b * p.L + tc) * H + h;
+  const float dtv = p.dt[si];
+  float acc = 0.f;
+  for (int a = k; a < A; a += 8) {
+    const size_t di = ((size_t)bh * p.L + tc) * A + a;
+    const float tb = p.dtheta[di] + p.th_tot[(size_t)blockIdx.x * A + a];
+    const float an = p.angle[((size_t)b * p.L + tc) * A + a];
+    if (t < nv) p.dtheta[di] = dtv * tb;
+    acc = fmaf(tb, an, acc);
+  }
+  part[k][t] = acc;
+  __syncthreads();
+  if (k == 0 && t < nv) {
+    float rot = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) rot += part[kk][t];
+    const size_t ri = (size_t)bh * p.L + tc;
+    const float lam = sigmoidf_acc(p.trap[si]);
+    const float e = p.ev[ri];
+    const float dc = tc >= 1 ? p.dsv[ri - 1] : 0.f;
+    p.d_adt[si] += p.phi_tot[blockIdx.x];
+    p.d_dt[si] = fmaf(lam, e, fmaf(1.f - lam, dc, rot));
+    p.d_trap[si] = lam * (1.f - lam) * dtv * (e - dc);
+  }
+}
+
+// (8) Per block of RB token rows (b, t) and group g: d_b, d_c = sums of the
+// per-head adjoints over the group's heads, and partial bias sums.  Thread
+// (hs, n) owns column n of heads hs, hs + nhs, ... for every row.
+__global__ __launch_bounds__(256) void bwd_group_kernel(BwdK p) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  const int N = p.N, A = p.A, NP = N - A, H = p.H, G = p.G, HG = H / G;
+  const int N = p.N, H = p.H, G = p.G, HG = H / G;
   const int g = blockIdx.y, blk = blockIdx.x;
   const int tid = threadIdx.x;
-  const int nhs = max(1, (int)blockDim.x / NP);
-  const int hs = tid / NP, j = tid - hs * NP;
-  const bool active = hs < nhs && hs < HG;
-  const int n0 = j < A ? j : j + A;
+  const int nhs = max(1, (int)blockDim.x / N);
+  const int hs = tid / N, n = tid - hs * N;
+  const int nact = min(nhs, HG);
+  const bool active = hs < nact;
   float* bacc = lds;                 // [2][HG][N] bias sums of this block
-  float* gsum = bacc + 2 * HG * N;   // [nhs][4][NP] group partials per head subset
+  float* gsum = bacc + 2 * HG * N;   // [nact][2][N] group partials per head subset
   for (int i = tid; i < 2 * HG * N; i += blockDim.x) bacc[i] = 0.f;
   __syncthreads();
   const int rows = p.B * p.L;
   for (int rr = 0; rr < RB; ++rr) {
     const int row = blk * RB + rr;
     if (row >= rows) break;
-    const int b = row / p.L, t = row - b * p.L;
-    float gb0 = 0.f, gb1 = 0.f, gc0 = 0.f, gc1 = 0.f;
     if (active) {
-      const size_t brow = ((size_t)row * G + g) * N;
+      float gb = 0.f, gc = 0.f;
+      const size_t base = ((size_t)row * H + g * HG) * N + n;
+#pragma unroll 4
       for (int hh = hs; hh < HG; hh += nhs) {
-        const int h = g * HG + hh;
-        const size_t di = ((size_t)row * H + h) * N;
-        const float dk0 = p.dk_rot[di + n0], dq0 = p.dq_rot[di + n0];
-        const float* bb = p.b_bias + (size_t)h * N;
-        const float* cb = p.c_bias + (size_t)h * N;
-        float ub0, ub1 = 0.f, uc0, uc1 = 0.f;
-        if (j < A) {
-          const float dk1 = p.dk_rot[di + j + A], dq1 = p.dq_rot[di + j + A];
-          const size_t ti = (((size_t)b * H + h) * p.L + t) * A + j;
-          float sn, cs;
-          sincos_acc(p.theta[ti], &sn, &cs);
-          const float b0 = p.b[brow + j] + bb[j], b1 = p.b[brow + j + A] + bb[j + A];
-          const float c0 = p.c[brow + j] + cb[j], c1 = p.c[brow + j + A] + cb[j + A];
-          const float K0 = b0 * cs - b1 * sn, K1 = b0 * sn + b1 * cs;
-          const float Q0 = c0 * cs - c1 * sn, Q1 = c0 * sn + c1 * cs;
-          p.dtheta[ti] = dk1 * K0 - dk0 * K1 + dq1 * Q0 - dq0 * Q1;
-          ub0 = dk0 * cs + dk1 * sn;
-          ub1 = dk1 * cs - dk0 * sn;
-          uc0 = dq0 * cs + dq1 * sn;
-          uc1 = dq1 * cs - dq0 * sn;
-        } else {
-          ub0 = dk0;
-          uc0 = dq0;
-        }
-        gb0 += ub0;
-        gb1 += ub1;
-        gc0 += uc0;
-        gc1 += uc1;
-        bacc[hh * N + n0] += ub0;
-        bacc[(HG + hh) * N + n0] += uc0;
-        if (j < A) {
-          bacc[hh * N + j + A] += ub1;
-          bacc[(HG + hh) * N + j + A] += uc1;
-        }
+        const float vb = p.db_head[base + (size_t)hh * N];
+        const float vc = p.dc_head[base + (size_t)hh * N];
+        gb += vb;
+        gc += vc;
+        bacc[hh * N + n] += vb;
+        bacc[(HG + hh) * N + n] += vc;
       }
-      float* gp = gsum + (size_t)hs * 4 * NP;
-      gp[j] = gb0;
-      gp[NP + j] = gb1;
-      gp[2 * NP + j] = gc0;
-      gp[3 * NP + j] = gc1;
+      gsum[(hs * 2) * N + n] = gb;
+      gsum[(hs * 2 + 1) * N + n] = gc;
     }
     __syncthreads();
-    if (tid < NP) {
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-      for (int k = 0; k < min(nhs, HG); ++k) {
-        const float* gp = gsum + (size_t)k * 4 * NP;
-        s0 += gp[tid];
-        s1 += gp[NP + tid];
-        s2 += gp[2 * NP + tid];
-        s3 += gp[3 * NP + tid];
+    if (tid < N) {
+      float sb = 0.f, sc = 0.f;
+      for (int k = 0; k < nact; ++k) {
+        sb += gsum[(k * 2) * N + tid];
+        sc += gsum[(k * 2 + 1) * N + tid];
       }
-      const int m0 = tid < A ? tid : tid + A;
-      const size_t o = ((size_t)row * G + g) * N;
-      p.d_b[o + m0] = s0;
-      p.d_c[o + m0] = s2;
-      if (tid < A) {
-        p.d_b[o + tid + A] = s1;
-        p.d_c[o + tid + A] = s3;
-      }
+      const size_t o = ((size_t)row * G + g) * N + tid;
+      p.d_b[o] = sb;
+      p.d_c[o] = sc;
     }
     __syncthreads();
   }
   for (int i = tid; i < 2 * HG * N; i += blockDim.x) {
     const int which = i / (HG * N), rem = i - which * HG * N;
-    const int hh = rem / N, n = rem - hh * N;
-    p.bias_part[(((size_t)blk * 2 + which) * H + g * HG + hh) * N + n] = bacc[i];
+    const int hh = rem / N, nn = rem - hh * N;
+    p.bias_part[(((size_t)blk * 2 + which) * H + g * HG + hh) * N + nn] = bacc[i];
   }
 }
 
-// Inclusive suffix sum over the 64 lanes of a wave.
-__device__ __forceinline__ float suffix64(float v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float o = __shfl_down(v, off, 64);
-    if (lane + off < 64) v += o;
-  }
-  return v;
-}
-
-// (6) Per (b, h), tokens in reverse tiles of 64: Phi, d adt, d dt, d trap,
-// and the per-head angle adjoint dt_t * sum_{r>=t} d theta_r (in place).
-__global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdK p) {
-  __shared__ float tile[64 * 65];
-  __shared__ float carry[64];
-  __shared__ float ddt_part[4][64];
-  const int bh = blockIdx.x, b = bh / p.H, h = bh - b * p.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int L = p.L, A = p.A, H = p.H;
-  if (tid < 64) carry[tid] = 0.f;
-  float phi_carry = 0.f;
-  __syncthreads();
-  for (int tlo = ((L - 1) / 64) * 64; tlo >= 0; tlo -= 64) {
-    const int t = tlo + lane;
-    const int nt = min(64, L - tlo);
-    // the tile of d theta [64][A] into LDS
-    for (int i = tid; i < 64 * A; i += blockDim.x) {
-      const int tt = i / A, a = i - tt * A;
-      tile[tt * 65 + a] = tt < nt ? p.dtheta[((size_t)bh * L + tlo + tt) * A + a] : 0.f;
-    }
-    __syncthreads();
-    const bool ok = lane < nt;
-    const size_t si = ((size_t)b * L + t) * H + h;
-    const float dtv = ok ? p.dt[si] : 0.f;
-    float part = 0.f;
-    for (int a = wave; a < A; a += 4) {
-      float v = suffix64(tile[lane * 65 + a], lane) + carry[a];
-      if (ok) {
-        p.dtheta[((size_t)bh * L + t) * A + a] = dtv * v;
-        part = fmaf(v, p.angle[((size_t)b * L + t) * A + a], part);
-      }
-      // column a belongs to this wave alone; its LDS read above precedes this write
-      const float tot = __shfl(v, 0, 64);
-      if (lane == 0) carry[a] = tot;
-    }
-    ddt_part[wave][lane] = part;
-    __syncthreads();
-    if (wave == 0) {
-      float psi = 0.f, lam = 0.f, e = 0.f, dc = 0.f, gamv = 0.f;
-      if (ok) {
-        const size_t ri = (size_t)bh * L + t;
-        lam = sigmoidf_acc(p.trap[si]);
-        gamv = lam * dtv;
-        e = p.ev[ri];
-        const float ds = p.dsv[ri];
-        psi = p.rho[ri];
-        if (t + 1 < L) {
-          const size_t s1 = si + H;
-          const float lam1 = sigmoidf_acc(p.trap[s1]), dt1 = p.dt[s1];
-          psi -= (1.f - lam1) * dt1 * ds + lam1 * dt1 * p.ev[ri + 1];
-        }
-        if (t >= 1) dc = p.dsv[ri - 1];
-      }
-      const float phi = suffix64(psi, lane) + phi_carry;
-      phi_carry = __shfl(phi, 0, 64);
-      if (ok) {
-        const float rot = ddt_part[0][lane] + ddt_part[1][lane] + ddt_part[2][lane] + ddt_part[3][lane];
-        p.d_adt[si] = fmaf(-gamv, e, phi);
-        p.d_dt[si] = fmaf(lam, e, fmaf(1.f - lam, dc, rot));
-        p.d_trap[si] = lam * (1.f - lam) * dtv * (e - dc);
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// (7a) d_c_bias, d_b_bias from the block partials; d_d from the chunk partials.
+// (9a) d_b_bias, d_c_bias from the block partials (8 outputs per workgroup,
+// 32 strided partial sums each, then a fixed tree); d_d from the chunk partials.
 __global__ __launch_bounds__(256) void bwd_bias_kernel(BwdK p) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  __shared__ float red[32][9];
   const int HN = p.H * p.N;
+  const int tid = threadIdx.x, o = tid & 7, part = tid >> 3;
+  const int i = blockIdx.x * 8 + o;
+  float s = 0.f;
   if (i < 2 * HN) {
     const int which = i / HN, rem = i - which * HN;
-    float s = 0.f;
-    for (int k = 0; k < p.nrb; ++k) s += p.bias_part[((size_t)k * 2 + which) * HN + rem];
-    (which == 0 ? p.d_b_bias : p.d_c_bias)[rem] = s;
-  } else if (i < 2 * HN + p.H) {
+    for (int k = part; k < p.nrb; k += 32) s += p.bias_part[((size_t)k * 2 + which) * HN + rem];
+  } else if (i < 2 * HN + p.H && p.has_d) {
     const int h = i - 2 * HN;
-    float s = 0.f;
-    if (p.has_d)
-      for (int bb = 0; bb < p.B; ++bb)
-        for (int c = 0; c < p.nc; ++c) s += p.dd_part[((size_t)bb * p.H + h) * p.nc + c];
-    p.d_d[h] = s;
+    const int per = p.B * p.nc;
+    for (int k = part; k < per; k += 32) {
+      const int bb = k / p.nc, cc = k - bb * p.nc;
+      s += p.dd_part[((size_t)bb * p.H + h) * p.nc + cc];
+    }
+  }
+  red[part][o] = s;
+  __syncthreads();
+  for (int w = 16; w > 0; w >>= 1) {
+    if (part < w) red[part][o] += red[part + w][o];
+    __syncthreads();
+  }
+  if (part == 0) {
+    if (i < 2 * HN) {
+      const int which = i / HN, rem = i - which * HN;
+      (which == 0 ? p.d_b_bias : p.d_c_bias)[rem] = red[0][o];
+    } else if (i < 2 * HN + p.H) {
+      p.d_d[i - 2 * HN] = red[0][o];
+    }
   }
 }
 
-// (7b) d_angle[b][t][a] = sum_h (per-head angle adjoint).
+// (9b) d_angle[b][t][a] = sum_h (per-head angle adjoint).
 __global__ __launch_bounds__(256) void bwd_angle_kernel(BwdK p) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t total = (size_t)p.B * p.L * p.A;
@@ -636,14 +865,15 @@ __global__ __launch_bounds__(256) void bwd_angle_kernel(BwdK p) {
 }
 
 struct BwdLayout {
-  size_t theta, hs, gs, decay, dtheta, dq, dk, rho, dsv, ev, ddp, bias, total;
-  int nc, nrb;
+  size_t theta, tpre, hs, gs, decay, dtheta, dbh, dch, dsv, ev, phi, th, ddp, bias, total;
+  int nc, nT, nrb;
 };
 
 BwdLayout bwd_layout(const ScanGeom& g) {
   BwdLayout w{};
   const size_t BH = (size_t)g.B * g.H;
   w.nc = (int)((g.L + BQ - 1) / BQ);
+  w.nT = (int)((g.L + TT - 1) / TT);
   w.nrb = (int)(((size_t)g.B * g.L + RB - 1) / RB);
   size_t off = 0;
   auto take = [&](size_t n) {
@@ -652,29 +882,32 @@ BwdLayout bwd_layout(const ScanGeom& g) {
     return o;
   };
   w.theta = take(BH * g.L * g.A);
+  w.tpre = take(BH * w.nT * g.A);
   w.hs = take(BH * w.nc * g.P * g.N);
   w.gs = take(BH * w.nc * g.P * g.N);
   w.decay = take(BH * w.nc);
   w.dtheta = take(BH * g.L * g.A);
-  w.dq = take((size_t)g.B * g.L * g.H * g.N);
-  w.dk = take((size_t)g.B * g.L * g.H * g.N);
-  w.rho = take(BH * g.L);
+  w.dbh = take((size_t)g.B * g.L * g.H * g.N);
+  w.dch = take((size_t)g.B * g.L * g.H * g.N);
   w.dsv = take(BH * g.L);
   w.ev = take(BH * g.L);
+  w.phi = take(BH * w.nc);
+  w.th = take(BH * w.nc * g.A);
   w.ddp = take(BH * w.nc);
   w.bias = take((size_t)w.nrb * 2 * g.H * g.N);
   w.total = off;
   return w;
 }
 
-size_t chunk_lds_bytes(int PT, int NT) {
-  const int NS = NT * 16 + 1, PS = PT * 16 + 1, PP = PT * 16;
-  return (size_t)(2 * BQ * NS + 2 * BQ * PS + 2 * PP * NS + 3 * BQ * MS + 5 * BQ + 2 * BQ * PT) * sizeof(float);
+size_t summary_lds_bytes(int PT, int NT) {
+  const int NS = NT * 16 + 4, PS = PT * 16 + 4;
+  return (size_t)(2 * BQ * NS + 2 * BQ * PS + 6 * BQ) * sizeof(float);
 }
 
-size_t summary_lds_bytes(int PT, int NT) {
-  const int NS = NT * 16 + 1, PS = PT * 16 + 1;
-  return (size_t)(2 * BQ * NS + 2 * BQ * PS + 3 * BQ) * sizeof(float);
+size_t group_lds_bytes(const ScanGeom& g) {
+  const int HG = (int)(g.H / g.G), N = (int)g.N;
+  const int nact = std::min(std::max(1, 256 / N), HG);
+  return (size_t)(2 * HG * N + nact * 2 * N) * sizeof(float);
 }
 
 void raise_lds(const void* fn, size_t bytes) {
@@ -689,10 +922,10 @@ size_t siso_bwd_workspace_floats(const ScanGeom& g) { return bwd_layout(g).total
 
 bool siso_bwd_fits(const ScanGeom& g) {
   const int PT = (int)((g.P + 15) / 16), NT = (int)((g.N + 15) / 16);
-  const int HG = (int)(g.H / g.G);
-  const int nhs = (int)std::max(1u, 256u / (g.N - g.A));
-  const size_t unrot = (size_t)(2 * HG * g.N + std::min(nhs, HG) * 4 * (g.N - g.A)) * sizeof(float);
-  return chunk_lds_bytes(PT, NT) <= 160 * 1024 && unrot <= 160 * 1024;
+  // per-thread item arrays of the chunk kernel: 32 x (N - A) <= 512 * 8 and 32 x 16 PT <= 512 * 8
+  if (BQ * (int)(g.N - g.A) > 512 * KQ_ITEMS || BQ * PT * 16 > 512 * XG_ITEMS) return false;
+  const size_t chunk = (size_t)chunk_lds(PT, NT, (int)g.A).total * sizeof(float);
+  return chunk <= 160 * 1024 && summary_lds_bytes(PT, NT) <= 160 * 1024 && group_lds_bytes(g) <= 160 * 1024;
 }
 
 hipError_t launch_siso_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOperands& go, void* workspace,
@@ -706,17 +939,19 @@ hipError_t launch_siso_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOp
   k.d_c = go.d_c; k.d_b = go.d_b; k.d_x = go.d_x; k.d_z = go.d_z; k.d_adt = go.d_adt; k.d_dt = go.d_dt;
   k.d_trap = go.d_trap; k.d_angle = go.d_angle; k.d_c_bias = go.d_c_bias; k.d_b_bias = go.d_b_bias;
   k.d_d = go.d_d;
-  k.theta = ws + w.theta; k.hs = ws + w.hs; k.gs = ws + w.gs; k.decay = ws + w.decay;
-  k.dtheta = ws + w.dtheta; k.dq_rot = ws + w.dq; k.dk_rot = ws + w.dk;
-  k.rho = ws + w.rho; k.dsv = ws + w.dsv; k.ev = ws + w.ev; k.dd_part = ws + w.ddp;
-  k.bias_part = ws + w.bias;
+  k.theta = ws + w.theta; k.tpre = ws + w.tpre; k.hs = ws + w.hs; k.gs = ws + w.gs; k.decay = ws + w.decay;
+  k.dtheta = ws + w.dtheta; k.db_head = ws + w.dbh; k.dc_head = ws + w.dch;
+  k.dsv = ws + w.dsv; k.ev = ws + w.ev; k.phi_tot = ws + w.phi; k.th_tot = ws + w.th;
+  k.dd_part = ws + w.ddp; k.bias_part = ws + w.bias;
   k.B = (int)g.B; k.L = (int)g.L; k.H = (int)g.H; k.G = (int)g.G; k.P = (int)g.P; k.N = (int)g.N;
   k.A = (int)g.A; k.has_z = (int)g.has_z; k.has_d = (int)g.has_d;
-  k.nc = w.nc; k.NT = (int)((g.N + 15) / 16); k.PT = (int)((g.P + 15) / 16); k.nrb = w.nrb;
+  k.nc = w.nc; k.nT = w.nT; k.NT = (int)((g.N + 15) / 16); k.PT = (int)((g.P + 15) / 16); k.nrb = w.nrb;
   const unsigned BH = g.B * g.H;
   hipError_t e;
   if (g.A > 0) {
-    hipLaunchKernelGGL(bwd_theta_kernel, dim3(BH), dim3(64), 0, stream, k);
+    hipLaunchKernelGGL(bwd_theta_local_kernel, dim3(BH * w.nT), dim3(64), 0, stream, k);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_theta_scan_kernel, dim3(BH * g.A), dim3(64), 0, stream, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const size_t sl = summary_lds_bytes(k.PT, k.NT);
@@ -726,19 +961,24 @@ hipError_t launch_siso_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOp
   const unsigned pnb = (g.P * g.N + 255) / 256;
   hipLaunchKernelGGL(bwd_prefix_kernel, dim3(pnb * BH), dim3(256), 0, stream, k, (int)pnb);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t cl = chunk_lds_bytes(k.PT, k.NT);
-  raise_lds(reinterpret_cast<const void*>(&bwd_chunk_kernel), cl);
-  hipLaunchKernelGGL(bwd_chunk_kernel, dim3(BH * w.nc), dim3(512), cl, stream, k);
+  const size_t cl = (size_t)chunk_lds(k.PT, k.NT, k.A).total * sizeof(float);
+  if ((g.N & 3u) == 0) {
+    raise_lds(reinterpret_cast<const void*>(&bwd_chunk_kernel<true>), cl);
+    hipLaunchKernelGGL(bwd_chunk_kernel<true>, dim3(BH * w.nc), dim3(512), cl, stream, k);
+  } else {
+    raise_lds(reinterpret_cast<const void*>(&bwd_chunk_kernel<false>), cl);
+    hipLaunchKernelGGL(bwd_chunk_kernel<false>, dim3(BH * w.nc), dim3(512), cl, stream, k);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int NP = (int)(g.N - g.A), HG = (int)(g.H / g.G);
-  const int nhs = std::max(1, 256 / NP);
-  const size_t ul = (size_t)(2 * HG * g.N + std::min(nhs, HG) * 4 * NP) * sizeof(float);
-  raise_lds(reinterpret_cast<const void*>(&bwd_unrotate_kernel), ul);
-  hipLaunchKernelGGL(bwd_unrotate_kernel, dim3(w.nrb, g.G), dim3(256), ul, stream, k);
+  hipLaunchKernelGGL(bwd_chunk_scan_kernel, dim3(BH * (g.A + 1)), dim3(64), 0, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_finalize_kernel, dim3(BH), dim3(256), 0, stream, k);
+  hipLaunchKernelGGL(bwd_apply_kernel, dim3(BH * w.nc), dim3(256), 0, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const unsigned nb = (2u * g.H * g.N + g.H + 255u) / 256u;
+  const size_t gl = group_lds_bytes(g);
+  raise_lds(reinterpret_cast<const void*>(&bwd_group_kernel), gl);
+  hipLaunchKernelGGL(bwd_group_kernel, dim3(w.nrb, g.G), dim3(256), gl, stream, k);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned nb = (2u * g.H * g.N + g.H + 7u) / 8u;
   hipLaunchKernelGGL(bwd_bias_kernel, dim3(nb), dim3(256), 0, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (g.A > 0) {
