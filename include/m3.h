@@ -247,11 +247,11 @@ int m3_mimo_step(const float* c, const float* b, const float* x, const float* z,
  *   twice, per-head query/key adjoints [B,L,H,N] twice, and small
  *   per-token arrays); the contents need no initialisation.
  * Rules: those of m3_siso_fwd (M3_ERR_INVALID_ARGUMENT), plus
- *   M3_ERR_UNSUPPORTED when the per-chunk working set (P, N) or the
- *   heads-per-group tile exceeds one CU's 160 KiB of LDS (P = 64 with
- *   N = 128 fits; P = 128 with N = 128 does not).  d_angle may be NULL when
- *   A == 0.  The reductions run in a fixed order, so repeated calls give
- *   identical results.
+ *   M3_ERR_UNSUPPORTED when the group reduction's tile of 2 * (H/G) * N
+ *   bias sums (plus a few rows) exceeds one CU's 160 KiB of LDS, which takes
+ *   more than about 150 heads per group at N = 128.  d_angle may be NULL
+ *   when A == 0.  The reductions run in a fixed order, so repeated calls
+ *   give identical results.
  */
 size_t m3_siso_bwd_workspace_bytes(m3_ssm_config cfg);
 int m3_siso_bwd(const float* dout, const float* c, const float* b, const float* x,

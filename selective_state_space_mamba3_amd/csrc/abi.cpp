@@ -212,10 +212,8 @@ int m3_siso_bwd(const float* dout, const float* c, const float* b, const float* 
   if (g.A > 0 && (angle == nullptr || d_angle == nullptr))
     return fail(M3_ERR_INVALID_ARGUMENT, "%s: operand angle or d_angle is NULL", op);
   if (!m3::siso_bwd_fits(g))
-    return fail(M3_ERR_UNSUPPORTED,
-                "%s: head_dim %u with state_size %u (or %u heads per group) exceeds the LDS of the "
-                "backward kernels",
-                op, g.P, g.N, g.H / g.G);
+    return fail(M3_ERR_UNSUPPORTED, "%s: %u heads per group with state_size %u exceed the LDS of the "
+                "backward group reduction", op, g.H / g.G, g.N);
   const size_t need = m3::siso_bwd_workspace_floats(g) * sizeof(float);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(M3_ERR_INVALID_ARGUMENT, "%s: workspace of %zu bytes required, %zu given", op, need,

@@ -222,7 +222,7 @@ def test_siso_bwd_rules():
     assert L.m3_siso_bwd(*[FAKE] * 12, c, *[FAKE] * 11, FAKE, need - 1, None) == INVALID
     assert "workspace" in m3.last_error()
     assert L.m3_siso_bwd(*[FAKE] * 12, c, *[FAKE] * 11, None, need, None) == INVALID
-    big = bd.c_ssm(_ssm(head_dim=128, state_size=128, num_rope_angles=8))
+    big = bd.c_ssm(_ssm(num_heads=256, num_groups=1, state_size=128, num_rope_angles=8))  # 256 heads share a group
     assert L.m3_siso_bwd(*[FAKE] * 12, big, *[FAKE] * 11, FAKE, 1 << 40, None) == bd.M3_ERR_UNSUPPORTED
     assert "LDS" in m3.last_error()
     assert L.m3_siso_bwd_workspace_bytes(big) > 0

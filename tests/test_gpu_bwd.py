@@ -30,6 +30,7 @@ def _print_case(tag):
     Dims(2, 50, 2, 1, 5, 6, 3, has_d=False),         # odd sizes
     Dims(1, 96, 2, 1, 64, 128, 32),                  # the N=128 / P=64 geometry
     Dims(1, 40, 2, 1, 32, 64, 0),                    # no rotary angles
+    Dims(1, 70, 2, 1, 128, 128, 64),                 # the largest head_dim, state and angle count
     Dims(1, 31, 2, 2, 16, 32, 16, has_z=False, has_d=False),  # A = N/2, shorter than a chunk
 ], ids=lambda d: f"B{d.B}L{d.L}H{d.H}G{d.G}P{d.P}N{d.N}A{d.A}"
                  f"{'' if d.has_z else 'nz'}{'' if d.has_d else 'nd'}")
