@@ -14,7 +14,8 @@ region it also measures the other rows of the path at their own workloads
 ("rows"): the decode step at B256 H32 (1 token per step, HBM-bound), the
 rank-4 MIMO decode step at the same geometry, the MIMO scan at
 B8 L4096 H32 R4 (FP32-matrix-bound), the SISO backward at the step's
-geometry and the preprocess backward over its packed projection.
+geometry and the preprocess backward over its packed projection, and the
+step's preprocess and scan fused into one call on the packed rows.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
 """
@@ -187,6 +188,36 @@ def measure_rows(torch, m3, lib, hip, new_event, dev):
                          "fp32_frac": flops / (cm * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, "bound": "fp32 matrix",
                          "algorithmic_bytes": byt, "gbs": byt / (cm * 1e-3) / 1e9}
     del inp, ops, ws, out
+
+    # fused preprocess -> scan on the packed rows, the bench step's workload
+    from workloads import packed_projection
+    w = WORKLOADS["siso_b4_l2048"]
+    d = w.dims
+    sets = [packed_projection(d, seed=w.seed + k) for k in range(3)]
+    pcfg = m3.PreprocessConfig(d.H * d.P, d.N, d.H, d.A, d.groups, 1, 1e-5, 1e-3, 0.1, 1e-4)
+    cfg = m3.SsmConfig(d.B, d.L, d.H, d.G, d.P, d.N, d.A)
+    tens = [{k: torch.from_numpy(v).to(dev) for k, v in st.items()} for st in sets]
+    out = torch.empty(d.B, d.L, d.H, d.P, device=dev)
+    ws = torch.empty(m3.siso_fwd_packed_workspace_bytes(pcfg, cfg), dtype=torch.uint8, device=dev)
+
+    def one_f(i):
+        t = tens[i % 3]
+        m3.m3_siso_fwd_packed(t["projected"], t["dt_bias"], t["c_bias"], t["b_bias"], t["d"], pcfg, cfg,
+                              out=out, workspace=ws)
+    for i in range(6):
+        one_f(i)
+    torch.cuda.synchronize()
+    n_calls = 30
+    a.record()
+    for i in range(n_calls):
+        one_f(i)
+    b.record()
+    torch.cuda.synchronize()
+    fm = a.elapsed_time(b) / n_calls
+    rows["fused_step"] = {"workload": "siso_b4_l2048 packed rows [8192 x 3432] -> out, one m3_siso_fwd_packed call",
+                          "ms": fm, "tokens_per_s": d.B * d.L / (fm * 1e-3), "calls_timed": n_calls,
+                          "input_sets": 3}
+    del sets, tens, out, ws
 
     # SISO backward at the forward's geometry: the eleven gradients from dout
     from workloads import output_gradient, preprocess_output_gradients, packed_projection

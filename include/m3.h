@@ -1,12 +1,13 @@
 /*
  * m3.h -- C ABI of the MI355X (gfx950) Mamba-3 selective-state path.
  *
- * Seven operations, named after the public functions of the oarust 0.8.6
+ * Eight operations, named after the public functions of the oarust 0.8.6
  * source page src/rs/ml/matrix/mamba3.rs ("Public API" section) and the
  * ml::matrix API index:
  *
  *   m3_preprocess   mamba3_preprocess   split + transform one packed projection
  *   m3_siso_fwd     mamba3_siso         SISO selective-state scan, forward
+ *   m3_siso_fwd_packed  mamba3_preprocess + mamba3_siso, fused on the packed rows
  *   m3_mimo_fwd     mamba3_mimo         shared-state MIMO scan, forward
  *   m3_siso_step    mamba3_siso_step    one SISO decode token, states in place
  *   m3_mimo_step    mamba3_mimo_step    one MIMO decode token, states in place
@@ -151,6 +152,32 @@ int m3_siso_fwd(const float* c, const float* b, const float* x, const float* z,
                 const float* c_bias, const float* b_bias, const float* d,
                 m3_ssm_config cfg, float* out,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * m3_siso_fwd_packed -- mamba3_preprocess followed by mamba3_siso in one
+ * call that reads the packed projection rows directly.  projected [B*L, W]
+ * (W = 2I + 2GN + 3H + A, columns z | x | B | C | dt | A | trap | angle) and
+ * dt_bias [H] as for m3_preprocess; c_bias, b_bias [H,N] and d [H] as for
+ * m3_siso_fwd; out [B,L,H,P].  out equals m3_siso_fwd applied to the eight
+ * outputs of m3_preprocess of the same rows, but x, z, trap and angle are
+ * read in place from the packed rows instead of being copied out, and only
+ * the normalised B/C rows and dt / adt go through the workspace.  When W,
+ * I and the angle column offset 2I + 2GN + 3H are multiples of 4 (16-byte
+ * rows, as the dense operands have), the same kernel variant runs and the
+ * result is identical bit for bit; otherwise a scalar-load variant may sum
+ * in another order (differences at float32 rounding level).
+ * workspace: at least m3_siso_fwd_packed_workspace_bytes(pcfg, cfg) bytes
+ *   (B*L*(2GN + 2H) floats plus the scan's own workspace); required.
+ * Rules: those of m3_preprocess (rows = B*L) and of m3_siso_fwd, and the two
+ *   configs must agree: inner_size == H*P, state_size == N, num_heads == H,
+ *   num_rope_angles == A, num_groups == G (after G = 0 resolves to H),
+ *   mimo_rank == 1 (M3_ERR_INVALID_ARGUMENT otherwise).
+ */
+size_t m3_siso_fwd_packed_workspace_bytes(m3_preprocess_config pcfg, m3_ssm_config cfg);
+int m3_siso_fwd_packed(const float* projected, const float* dt_bias, const float* c_bias,
+                       const float* b_bias, const float* d, m3_preprocess_config pcfg,
+                       m3_ssm_config cfg, float* out, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /*
  * m3_mimo_fwd -- mamba3_mimo ("Run the shared-state Mamba-3 MIMO selective

@@ -117,6 +117,10 @@ def lib() -> ctypes.CDLL:
     L.m3_siso_step.argtypes = [_P] * 15 + [_CSsm, _P, _P]
     L.m3_mimo_step.restype = ctypes.c_int
     L.m3_mimo_step.argtypes = [_P] * 19 + [_CSsm, _P, _P]
+    L.m3_siso_fwd_packed_workspace_bytes.restype = ctypes.c_size_t
+    L.m3_siso_fwd_packed_workspace_bytes.argtypes = [_CPre, _CSsm]
+    L.m3_siso_fwd_packed.restype = ctypes.c_int
+    L.m3_siso_fwd_packed.argtypes = [_P] * 5 + [_CPre, _CSsm, _P, _P, ctypes.c_size_t, _P]
     L.m3_siso_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.m3_siso_bwd_workspace_bytes.argtypes = [_CSsm]
     L.m3_siso_bwd.restype = ctypes.c_int
@@ -385,3 +389,31 @@ def m3_preprocess_bwd(projected, dt_bias, cfg: PreprocessConfig, grads: dict, ou
                                 *[_ptr(grads.get(k)) for k in _PRE_OUT],
                                 _ptr(outs["projected"]), _ptr(outs["dt_bias"]), _stream(dev, stream)))
     return outs
+
+
+def siso_fwd_packed_workspace_bytes(pcfg: PreprocessConfig, cfg: SsmConfig) -> int:
+    return int(lib().m3_siso_fwd_packed_workspace_bytes(c_pre(pcfg), c_ssm(cfg)))
+
+
+def m3_siso_fwd_packed(projected, dt_bias, c_bias, b_bias, d, pcfg: PreprocessConfig, cfg: SsmConfig,
+                       out=None, workspace=None, stream=None) -> torch.Tensor:
+    """Preprocess + SISO scan on the packed rows [B*L, W]; returns out [B, L, H, P]."""
+    L_ = lib()
+    dev = projected.device
+    B, L, H, P, N = cfg.batch_size, cfg.sequence_length, cfg.num_heads, cfg.head_dim, cfg.state_size
+    _expect("projected", projected, (B * L, pcfg.width), dev)
+    _expect("dt_bias", dt_bias, (H,), dev)
+    _expect("c_bias", c_bias, (H, N), dev)
+    _expect("b_bias", b_bias, (H, N), dev)
+    _expect("d", d, (H,), dev)
+    if out is None:
+        out = torch.empty((B, L, H, P), dtype=torch.float32, device=dev)
+    _expect("out", out, (B, L, H, P), dev)
+    need = siso_fwd_packed_workspace_bytes(pcfg, cfg)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(L_.m3_siso_fwd_packed(_ptr(projected), _ptr(dt_bias), _ptr(c_bias), _ptr(b_bias), _ptr(d),
+                                 c_pre(pcfg), c_ssm(cfg), _ptr(out), _ptr(workspace), ws_bytes,
+                                 _stream(dev, stream)))
+    return out

@@ -224,6 +224,92 @@ int m3_siso_bwd(const float* dout, const float* c, const float* b, const float* 
   return hip_status(op, m3::launch_siso_bwd(g, o, go, workspace, static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Fused preprocess -> scan: the two configs must describe one geometry.
+struct PackedPlan {
+  m3::ScanGeom g;
+  m3::PreGeom pg;
+  m3::ScanPlan plan;
+  size_t o_bh, o_ch, o_dt, o_adt, o_scan, total_bytes;
+  uint32_t W, I, M;
+};
+
+int resolve_packed(const char* op, const m3_preprocess_config& pcfg, const m3_ssm_config& cfg, PackedPlan* pp) {
+  int st = resolve_scan(op, cfg, false, &pp->g);
+  if (st) return st;
+  const m3::ScanGeom& g = pp->g;
+  if (!count_u32({g.B, g.L})) return fail(M3_ERR_INVALID_ARGUMENT, "%s: batch_size * sequence_length exceeds u32", op);
+  st = resolve_pre(op, g.B * g.L, pcfg, &pp->pg);
+  if (st) return st;
+  if ((uint64_t)pcfg.inner_size != (uint64_t)g.H * g.P || pcfg.state_size != g.N || pcfg.num_heads != g.H ||
+      pcfg.num_rope_angles != g.A || pcfg.num_groups != g.G || pcfg.mimo_rank != 1)
+    return fail(M3_ERR_INVALID_ARGUMENT,
+                "%s requires inner_size == num_heads * head_dim and equal state_size, num_heads, "
+                "num_rope_angles and num_groups (resolved) in both configs, and mimo_rank 1",
+                op);
+  pp->I = pcfg.inner_size;
+  pp->M = g.G * g.N;
+  pp->W = 2 * pp->I + 2 * pp->M + 3 * g.H + g.A;
+  pp->plan = m3::plan_siso(g);
+  const size_t rows = (size_t)g.B * g.L;
+  size_t off = 0;
+  auto take = [&](size_t floats) {
+    const size_t o = off;
+    off += (floats + 63) / 64 * 64;  // 256-byte aligned pieces
+    return o;
+  };
+  pp->o_bh = take(rows * pp->M);
+  pp->o_ch = take(rows * pp->M);
+  pp->o_dt = take(rows * g.H);
+  pp->o_adt = take(rows * g.H);
+  pp->o_scan = off;
+  pp->total_bytes = off * sizeof(float) + m3::plan_workspace_bytes(pp->plan);
+  return M3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t m3_siso_fwd_packed_workspace_bytes(m3_preprocess_config pcfg, m3_ssm_config cfg) {
+  PackedPlan pp{};
+  if (resolve_packed("m3_siso_fwd_packed_workspace_bytes", pcfg, cfg, &pp) != M3_OK) return 0;
+  return pp.total_bytes;
+}
+
+int m3_siso_fwd_packed(const float* projected, const float* dt_bias, const float* c_bias,
+                       const float* b_bias, const float* d, m3_preprocess_config pcfg,
+                       m3_ssm_config cfg, float* out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  const char* op = "m3_siso_fwd_packed";
+  clear_error();
+  PackedPlan pp{};
+  int st = resolve_packed(op, pcfg, cfg, &pp);
+  if (st) return st;
+  st = check_ptrs(op, {{"projected", projected}, {"dt_bias", dt_bias}, {"c_bias", c_bias},
+                       {"b_bias", b_bias}, {"d", d}, {"out", out}, {"workspace", workspace}});
+  if (st) return st;
+  if (workspace_bytes < pp.total_bytes)
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: workspace of %zu bytes required, %zu given", op,
+                pp.total_bytes, workspace_bytes);
+  float* ws = static_cast<float*>(workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  m3::PreOperands po{projected, dt_bias, nullptr, nullptr, ws + pp.o_bh, ws + pp.o_ch,
+                     ws + pp.o_dt, ws + pp.o_adt, nullptr, nullptr};
+  st = hip_status(op, m3::launch_preprocess_derived(pp.pg, po, s));
+  if (st) return st;
+  const m3::ScanGeom& g = pp.g;
+  const uint32_t o_tr = 2 * pp.I + 2 * pp.M + 2 * g.H;
+  m3::ScanOperands o{ws + pp.o_ch, ws + pp.o_bh, projected + pp.I, projected, ws + pp.o_adt, ws + pp.o_dt,
+                     projected + o_tr, g.A > 0 ? projected + o_tr + g.H : nullptr, c_bias, b_bias, d,
+                     nullptr, nullptr, nullptr, nullptr, out, pp.W, pp.W, pp.W};
+  void* scan_ws = m3::plan_workspace_bytes(pp.plan) > 0 ? static_cast<void*>(ws + pp.o_scan) : nullptr;
+  return hip_status(op, m3::launch_siso_fwd(g, o, pp.plan, scan_ws, s));
+}
+
 size_t m3_siso_fwd_workspace_bytes(m3_ssm_config cfg) {
   m3::ScanGeom g{};
   if (resolve_scan("m3_siso_fwd_workspace_bytes", cfg, false, &g) != M3_OK) return 0;

@@ -17,6 +17,9 @@ struct ScanOperands {
   const float *c, *b, *x, *z, *adt, *dt, *trap, *angle, *c_bias, *b_bias, *d;
   const float *mimo_x, *mimo_z, *mimo_o, *norm_weight;  // MIMO only
   float* out;
+  // per-token strides of x / z, trap and angle in elements; 0 = dense layout
+  // (H P, H, A).  Packed projection rows give all three the row width.
+  uint32_t xs, ts, as;
 };
 
 struct StepStates {
@@ -77,6 +80,8 @@ hipError_t launch_siso_step(const ScanGeom& g, const ScanOperands& o, const Step
 hipError_t launch_mimo_step(const ScanGeom& g, const ScanOperands& o, const StepStates& s,
                             hipStream_t stream);
 hipError_t launch_preprocess(const PreGeom& g, const PreOperands& o, hipStream_t stream);
+// Only the derived preprocess outputs (bh, ch, dt, adt); the other pointers of o are ignored.
+hipError_t launch_preprocess_derived(const PreGeom& g, const PreOperands& o, hipStream_t stream);
 hipError_t launch_preprocess_bwd(const PreGeom& g, const PreBwdOperands& o, hipStream_t stream);
 
 size_t siso_bwd_workspace_floats(const ScanGeom& g);

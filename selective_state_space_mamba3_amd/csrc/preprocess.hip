@@ -37,7 +37,9 @@ __device__ __forceinline__ void copy_slice(const float* __restrict__ src, float*
   }
 }
 
-__global__ __launch_bounds__(256) void preprocess_kernel(PreKParams p, int vec) {
+// derived != 0: only bh, ch, dt and adt (the fused preprocess -> scan reads
+// x, z, trap and angle straight from the packed rows).
+__global__ __launch_bounds__(256) void preprocess_kernel(PreKParams p, int vec, int derived) {
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
@@ -47,8 +49,10 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreKParams p, int vec) 
   const float* row = p.projected + (size_t)r * p.W;
   const bool v = vec != 0;
 
-  copy_slice(row, p.z + (size_t)r * p.I, p.I, tid, nthreads, v);
-  copy_slice(row + p.I, p.x + (size_t)r * p.I, p.I, tid, nthreads, v);
+  if (!derived) {
+    copy_slice(row, p.z + (size_t)r * p.I, p.I, tid, nthreads, v);
+    copy_slice(row + p.I, p.x + (size_t)r * p.I, p.I, tid, nthreads, v);
+  }
 
   // B and C rows: one wave per N-wide row, lanes over the row.
   const int nrows_bc = 2 * (p.M / p.N);
@@ -71,14 +75,17 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreKParams p, int vec) 
     const float amag = fmaxf(softplusf_acc(sc[p.H + h]), p.a_floor);
     p.dt[(size_t)r * p.H + h] = dtv;
     p.adt[(size_t)r * p.H + h] = -amag * dtv;
-    p.trap[(size_t)r * p.H + h] = sc[2 * p.H + h];
+    if (!derived) p.trap[(size_t)r * p.H + h] = sc[2 * p.H + h];
   }
-  for (int a = tid; a < p.A; a += nthreads) p.angle[(size_t)r * p.A + a] = sc[3 * p.H + a];
+  if (!derived)
+    for (int a = tid; a < p.A; a += nthreads) p.angle[(size_t)r * p.A + a] = sc[3 * p.H + a];
 }
 
 }  // namespace
 
-hipError_t launch_preprocess(const PreGeom& g, const PreOperands& o, hipStream_t stream) {
+namespace {
+
+hipError_t launch_pre(const PreGeom& g, const PreOperands& o, int derived, hipStream_t stream) {
   PreKParams kp{};
   kp.projected = o.projected; kp.dt_bias = o.dt_bias;
   kp.x = o.x; kp.z = o.z; kp.bh = o.bh; kp.ch = o.ch; kp.dt = o.dt; kp.adt = o.adt;
@@ -89,9 +96,19 @@ hipError_t launch_preprocess(const PreGeom& g, const PreOperands& o, hipStream_t
   kp.W = 2 * kp.I + 2 * kp.M + 3 * kp.H + kp.A;
   kp.eps = g.eps; kp.dt_min = g.dt_min; kp.dt_max = g.dt_max; kp.a_floor = g.a_floor;
   auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) % 16u) == 0u; };
-  const int vec = (kp.W % 4 == 0 && kp.I % 4 == 0 && al16(o.projected) && al16(o.x) && al16(o.z)) ? 1 : 0;
-  hipLaunchKernelGGL(preprocess_kernel, dim3(g.rows), dim3(256), 0, stream, kp, vec);
+  const int vec = (!derived && kp.W % 4 == 0 && kp.I % 4 == 0 && al16(o.projected) && al16(o.x) && al16(o.z)) ? 1 : 0;
+  hipLaunchKernelGGL(preprocess_kernel, dim3(g.rows), dim3(256), 0, stream, kp, vec, derived);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_preprocess(const PreGeom& g, const PreOperands& o, hipStream_t stream) {
+  return launch_pre(g, o, 0, stream);
+}
+
+hipError_t launch_preprocess_derived(const PreGeom& g, const PreOperands& o, hipStream_t stream) {
+  return launch_pre(g, o, 1, stream);
 }
 
 }  // namespace m3

@@ -62,6 +62,7 @@ struct ScanKParams {
   int NH, NTH;      // N split into NH parts of NTH 16-wide blocks (one part per wave)
   int RS, rs_log2;  // rank stride of the virtual rows (power of two >= R)
   int Qt;           // tokens per chunk (QV / RS)
+  int xstr, tstr, astr;  // per-token strides of x / z, trap and angle (packed rows share one)
   int seg_len, nseg;
   // LDS layout (float offsets) and row strides
   int o_ql, o_kl, o_xl, o_ml, o_ml2, o_yl, o_yl2, o_cs, o_bias, o_mimo, o_sc, o_run, lds_floats;
@@ -342,7 +343,8 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   // the chunk (or past the last item) load as zero without a branch.
   const int xrow = P / VEC;   // x items per token
   const int brow = N / VEC;   // B / C items per virtual row
-  const int tokx = p.H * P;   // x / z / out elements per token
+  const int tokx = p.H * P;   // out elements per token
+  const int tokxs = p.xstr;   // x / z elements per token (H P, or the packed row width)
   const int tokb = RG * N;    // B / C elements per token
   vec_t xr[KX], br[KB], cr[KB];
   float angr[KA];
@@ -361,15 +363,15 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
 
   auto prefetch = [&](int cs) {
     const int nv = min(Qt, t_end - cs);
-    const rsrc_t xres = make_rsrc(p.x + (((size_t)b * p.L + cs) * p.H + h) * P, (uint32_t)(nv * tokx * 4));
+    const rsrc_t xres = make_rsrc(p.x + ((size_t)b * p.L + cs) * tokxs + (size_t)h * P, (uint32_t)(nv * tokxs * 4));
     const rsrc_t bres = make_rsrc(p.b + ((size_t)b * p.L + cs) * tokb, (uint32_t)(nv * tokb * 4));
     const rsrc_t cres = make_rsrc(p.c + ((size_t)b * p.L + cs) * tokb, (uint32_t)(nv * tokb * 4));
-    const rsrc_t ares = make_rsrc(p.angle + ((size_t)b * p.L + cs) * A, (uint32_t)(nv * A * 4));
+    const rsrc_t ares = make_rsrc(p.angle + ((size_t)b * p.L + cs) * p.astr, (uint32_t)(nv * p.astr * 4));
 #pragma unroll
     for (int k = 0; k < KX; ++k) {
       const int idx = tid + k * nthreads;
       const int t = idx / xrow, pv = idx - t * xrow;
-      xr[k] = bload<VEC>(xres, (uint32_t)(t * tokx + pv * VEC));
+      xr[k] = bload<VEC>(xres, (uint32_t)(t * tokxs + pv * VEC));
     }
     if constexpr (MERGED) {
       const uint32_t row = (uint32_t)(mtok * tokb + (mrc * p.G + g) * N);
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         cr[1] = bload<VEC>(cres, row + mc1);
       }
       if (mpair) {
-        const floatx4 a4 = buf_load4(ares, (uint32_t)(mtok * A + mc0) * 4u);
+        const floatx4 a4 = buf_load4(ares, (uint32_t)(mtok * p.astr + mc0) * 4u);
         angr[0] = a4.x; angr[1] = a4.y; angr[2] = a4.z; angr[3] = a4.w;
       }
       const size_t sbase = ((size_t)b * p.L + cs) * p.H + h;
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       for (int i = 0; i < KA; ++i) {
         const int a = 2 * (i * nwaves + wave) + (lane >> 5);
         const int t = lane & 31;
-        angr[i] = a < A ? buf_load1(ares, (uint32_t)(t * A + a) * 4u) : 0.f;
+        angr[i] = a < A ? buf_load1(ares, (uint32_t)(t * p.astr + a) * 4u) : 0.f;
       }
     }
     if (wave == (MERGED ? sw : 0)) {
@@ -407,11 +409,11 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       const size_t sbase = ((size_t)b * p.L + cs) * p.H + h;
       const uint32_t nl = (uint32_t)min(Qt + 1, p.L - cs);
       const rsrc_t dres = make_rsrc(p.dt + sbase, nl * p.H * 4);
-      const rsrc_t tres = make_rsrc(p.trap + sbase, nl * p.H * 4);
+      const rsrc_t tres = make_rsrc(p.trap + ((size_t)b * p.L + cs) * p.tstr + h, nl * p.tstr * 4);
       const rsrc_t adres = make_rsrc(p.adt + sbase, (uint32_t)(nv * p.H * 4));
       const uint32_t so = (uint32_t)(lane * p.H) * 4u;
       s_dt = buf_load1(dres, so);
-      s_trap = buf_load1(tres, so);
+      s_trap = buf_load1(tres, (uint32_t)(lane * p.tstr) * 4u);
       s_adt = buf_load1(adres, so);
     }
   };
@@ -537,23 +539,24 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
     }
     vec_t zr[KX];
     float zm[KZM][2];
-    const size_t cbase_tok = (((size_t)b * p.L + c0) * p.H + h) * P;  // x / z / out at token c0
+    const size_t cbase_tok = (((size_t)b * p.L + c0) * p.H + h) * P;  // out at token c0
     // z and out: valid tokens of this chunk only (no z reads when has_z is off)
-    const rsrc_t zres = make_rsrc(p.z + cbase_tok, p.has_z ? (uint32_t)(nvalid * tokx * 4) : 0u);
+    const rsrc_t zres = make_rsrc(p.z + ((size_t)b * p.L + c0) * tokxs + (size_t)h * P,
+                                  p.has_z ? (uint32_t)(nvalid * tokxs * 4) : 0u);
     const rsrc_t ores = make_rsrc(p.out + cbase_tok, (uint32_t)(nvalid * tokx * 4));
     if constexpr (FULL && !MIMO) {
 #pragma unroll
       for (int k = 0; k < KX; ++k) {
         const int idx = tid + k * nthreads;
         const int t = idx / xrow, pv = idx - t * xrow;
-        zr[k] = bload<VEC>(zres, (uint32_t)(t * tokx + pv * VEC));
+        zr[k] = bload<VEC>(zres, (uint32_t)(t * tokxs + pv * VEC));
       }
     }
     if constexpr (FULL && MIMO) {
 #pragma unroll
       for (int i = 0; i < KZM; ++i) {
         const int t = wave + i * nwaves;
-        const uint32_t ob = (uint32_t)(t * tokx);
+        const uint32_t ob = (uint32_t)(t * tokxs);
         zm[i][0] = lane < P ? buf_load1(zres, (ob + lane) * 4u) : 0.f;
         zm[i][1] = lane + 64 < P ? buf_load1(zres, (ob + lane + 64) * 4u) : 0.f;
       }
@@ -910,14 +913,17 @@ hipError_t launch_scan(const ScanGeom& g, const ScanOperands& o, const ScanPlan&
   kp.rs_log2 = 0;
   while ((1 << kp.rs_log2) < kp.RS) ++kp.rs_log2;
   kp.Qt = kQV / kp.RS;
+  kp.xstr = o.xs ? (int)o.xs : (int)(g.H * g.P);
+  kp.tstr = o.ts ? (int)o.ts : (int)g.H;
+  kp.astr = o.as ? (int)o.as : (int)g.A;
   kp.seg_len = plan.seg_len;
   kp.nseg = plan.nseg;
   float* ws = static_cast<float*>(workspace);
   kp.ws_state = ws;
   kp.ws_aux = ws ? ws + plan.ws_state_floats : nullptr;
   // 16-byte vector access needs every row width and row start on a 16-byte boundary.
-  const bool vec4 = g.P % 4 == 0 && g.N % 4 == 0 && aligned16(o.x) && aligned16(o.z) && aligned16(o.b) && aligned16(o.c) &&
-                    aligned16(o.out);
+  const bool vec4 = g.P % 4 == 0 && g.N % 4 == 0 && kp.xstr % 4 == 0 && aligned16(o.x) && aligned16(o.z) &&
+                    aligned16(o.b) && aligned16(o.c) && aligned16(o.out);
   // One MFMA wave per (16 head_dim columns, N-part of at most four 16-wide
   // blocks); at least four waves; enough threads that every thread prefetches
   // at most KX x-vectors and KB B/C vectors (8P and 4N threads for both the
@@ -932,7 +938,8 @@ hipError_t launch_scan(const ScanGeom& g, const ScanOperands& o, const ScanPlan&
   const unsigned bhn = g.B * g.H;
   // The N = 128, P = 64 layers (eight waves) get a variant with compile-time
   // strides and rank stride; every other geometry runs the generic variant.
-  if (vec4 && g.N == 128 && g.P == 64 && nwaves == 8 && g.A % 4 == 0) {
+  if (vec4 && g.N == 128 && g.P == 64 && nwaves == 8 && g.A % 4 == 0 && kp.astr % 4 == 0 &&
+      (g.A == 0 || aligned16(o.angle))) {
     if (!mimo) return launch_passes<4, false, 8, 4, 8, 1>(kp, plan, bhn, block, stream);
     switch (kp.RS) {
       case 1: return launch_passes<4, true, 8, 4, 8, 1>(kp, plan, bhn, block, stream);

@@ -25,7 +25,7 @@ def _lib():
 def test_library_exports_every_header_function():
     names = m3.header_functions()
     assert set(names) >= {"m3_preprocess", "m3_siso_fwd", "m3_mimo_fwd", "m3_siso_step",
-                          "m3_mimo_step", "m3_siso_bwd", "m3_preprocess_bwd",
+                          "m3_mimo_step", "m3_siso_bwd", "m3_preprocess_bwd", "m3_siso_fwd_packed",
                           "m3_siso_bwd_workspace_bytes", "m3_last_error", "m3_siso_fwd_workspace_bytes",
                           "m3_mimo_fwd_workspace_bytes", "m3_version"}
     L = _lib()
@@ -242,6 +242,41 @@ def test_preprocess_bwd_null_rules():
         p = [FAKE] * 12
         p[i] = None
         assert L.m3_preprocess_bwd(p[0], p[1], 16, bd.c_pre(_pre()), *p[2:], None) == INVALID
+
+
+def _packed_pre(cfg, **kw):
+    base = dict(inner_size=cfg.num_heads * cfg.head_dim, state_size=cfg.state_size, num_heads=cfg.num_heads,
+                num_rope_angles=cfg.num_rope_angles, num_groups=cfg.num_groups or cfg.num_heads, mimo_rank=1,
+                epsilon=1e-5, dt_min=1e-3, dt_max=0.1, a_floor=1e-4)
+    base.update(kw)
+    return bd.PreprocessConfig(**base)
+
+
+def test_siso_fwd_packed_rules():
+    L = _lib()
+    cfg = _ssm()
+    pc = _packed_pre(cfg)
+    need = L.m3_siso_fwd_packed_workspace_bytes(bd.c_pre(pc), bd.c_ssm(cfg))
+    rows = cfg.batch_size * cfg.sequence_length
+    assert need >= 4 * rows * (2 * cfg.num_groups * cfg.state_size + 2 * cfg.num_heads)
+    call = lambda p, c, s, ws=FAKE, nb=need: L.m3_siso_fwd_packed(*p, bd.c_pre(c), bd.c_ssm(s), FAKE, ws, nb, None)
+    for bad in (dict(inner_size=cfg.num_heads * cfg.head_dim + 4), dict(state_size=16), dict(num_heads=2),
+                dict(num_rope_angles=4), dict(num_groups=1), dict(mimo_rank=2), dict(epsilon=0.0)):
+        assert call([FAKE] * 5, _packed_pre(cfg, **bad), cfg) == INVALID, bad
+        assert "m3_siso_fwd_packed" in m3.last_error()
+        assert L.m3_siso_fwd_packed_workspace_bytes(bd.c_pre(_packed_pre(cfg, **bad)), bd.c_ssm(cfg)) == 0
+    for bad in SISO_BAD:
+        assert call([FAKE] * 5, pc, _ssm(**bad)) == INVALID
+    for i in range(5):
+        p = [FAKE] * 5
+        p[i] = None
+        assert call(p, pc, cfg) == INVALID
+    assert call([FAKE] * 5, pc, cfg, ws=None) == INVALID
+    assert call([FAKE] * 5, pc, cfg, nb=need - 1) == INVALID
+    assert "workspace" in m3.last_error()
+    # num_groups 0 in the scan config resolves to one group per head
+    cfg0 = _ssm(num_groups=0)
+    assert L.m3_siso_fwd_packed_workspace_bytes(bd.c_pre(_packed_pre(cfg0)), bd.c_ssm(cfg0)) > 0
 
 
 def test_error_is_thread_local_and_cleared():
