@@ -118,8 +118,10 @@ __device__ __forceinline__ void set_comp(float& v, int, float x) { v = x; }
 // strides are constants and accesses fold into immediate offsets; RSC fixes
 // the rank stride of the virtual rows (0 = from the parameters).  Fixed-size
 // variants ask for two resident workgroups per CU (NWC / 2 waves per SIMD,
-// at most 128 VGPRs).
-template <int VEC, bool FULL, bool MIMO, int NTC, int PTC, int NWC, int RSC>
+// at most 128 VGPRs).  STR reads x / z, trap and angle with the per-token
+// strides of the parameters (packed projection rows); otherwise they are
+// dense and the strides are H P, H and A.
+template <int VEC, bool FULL, bool MIMO, int NTC, int PTC, int NWC, int RSC, bool STR>
 __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan_chunk_kernel(ScanKParams p) {
   using vec_t = typename VecOf<VEC>::T;
   constexpr int QV = kQV;
@@ -344,7 +346,8 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   const int xrow = P / VEC;   // x items per token
   const int brow = N / VEC;   // B / C items per virtual row
   const int tokx = p.H * P;   // out elements per token
-  const int tokxs = p.xstr;   // x / z elements per token (H P, or the packed row width)
+  const int tokxs = STR ? p.xstr : tokx;  // x / z elements per token
+  const int astr = STR ? p.astr : A;      // angle elements per token
   const int tokb = RG * N;    // B / C elements per token
   vec_t xr[KX], br[KB], cr[KB];
   float angr[KA];
@@ -363,10 +366,12 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
 
   auto prefetch = [&](int cs) {
     const int nv = min(Qt, t_end - cs);
-    const rsrc_t xres = make_rsrc(p.x + ((size_t)b * p.L + cs) * tokxs + (size_t)h * P, (uint32_t)(nv * tokxs * 4));
+    const rsrc_t xres = make_rsrc(STR ? p.x + ((size_t)b * p.L + cs) * tokxs + (size_t)h * P
+                                      : p.x + (((size_t)b * p.L + cs) * p.H + h) * P,
+                                  (uint32_t)(nv * tokxs * 4));
     const rsrc_t bres = make_rsrc(p.b + ((size_t)b * p.L + cs) * tokb, (uint32_t)(nv * tokb * 4));
     const rsrc_t cres = make_rsrc(p.c + ((size_t)b * p.L + cs) * tokb, (uint32_t)(nv * tokb * 4));
-    const rsrc_t ares = make_rsrc(p.angle + ((size_t)b * p.L + cs) * p.astr, (uint32_t)(nv * p.astr * 4));
+    const rsrc_t ares = make_rsrc(p.angle + ((size_t)b * p.L + cs) * astr, (uint32_t)(nv * astr * 4));
 #pragma unroll
     for (int k = 0; k < KX; ++k) {
       const int idx = tid + k * nthreads;
@@ -382,7 +387,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         cr[1] = bload<VEC>(cres, row + mc1);
       }
       if (mpair) {
-        const floatx4 a4 = buf_load4(ares, (uint32_t)(mtok * p.astr + mc0) * 4u);
+        const floatx4 a4 = buf_load4(ares, (uint32_t)(mtok * astr + mc0) * 4u);
         angr[0] = a4.x; angr[1] = a4.y; angr[2] = a4.z; angr[3] = a4.w;
       }
       const size_t sbase = ((size_t)b * p.L + cs) * p.H + h;
@@ -401,7 +406,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       for (int i = 0; i < KA; ++i) {
         const int a = 2 * (i * nwaves + wave) + (lane >> 5);
         const int t = lane & 31;
-        angr[i] = a < A ? buf_load1(ares, (uint32_t)(t * p.astr + a) * 4u) : 0.f;
+        angr[i] = a < A ? buf_load1(ares, (uint32_t)(t * astr + a) * 4u) : 0.f;
       }
     }
     if (wave == (MERGED ? sw : 0)) {
@@ -409,11 +414,12 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       const size_t sbase = ((size_t)b * p.L + cs) * p.H + h;
       const uint32_t nl = (uint32_t)min(Qt + 1, p.L - cs);
       const rsrc_t dres = make_rsrc(p.dt + sbase, nl * p.H * 4);
-      const rsrc_t tres = make_rsrc(p.trap + ((size_t)b * p.L + cs) * p.tstr + h, nl * p.tstr * 4);
+      const rsrc_t tres = STR ? make_rsrc(p.trap + ((size_t)b * p.L + cs) * p.tstr + h, nl * p.tstr * 4)
+                              : make_rsrc(p.trap + sbase, nl * p.H * 4);
       const rsrc_t adres = make_rsrc(p.adt + sbase, (uint32_t)(nv * p.H * 4));
       const uint32_t so = (uint32_t)(lane * p.H) * 4u;
       s_dt = buf_load1(dres, so);
-      s_trap = buf_load1(tres, (uint32_t)(lane * p.tstr) * 4u);
+      s_trap = buf_load1(tres, STR ? (uint32_t)(lane * p.tstr) * 4u : so);
       s_adt = buf_load1(adres, so);
     }
   };
@@ -541,7 +547,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
     float zm[KZM][2];
     const size_t cbase_tok = (((size_t)b * p.L + c0) * p.H + h) * P;  // out at token c0
     // z and out: valid tokens of this chunk only (no z reads when has_z is off)
-    const rsrc_t zres = make_rsrc(p.z + ((size_t)b * p.L + c0) * tokxs + (size_t)h * P,
+    const rsrc_t zres = make_rsrc(STR ? p.z + ((size_t)b * p.L + c0) * tokxs + (size_t)h * P : p.z + cbase_tok,
                                   p.has_z ? (uint32_t)(nvalid * tokxs * 4) : 0u);
     const rsrc_t ores = make_rsrc(p.out + cbase_tok, (uint32_t)(nvalid * tokx * 4));
     if constexpr (FULL && !MIMO) {
@@ -856,7 +862,7 @@ void layout(ScanKParams& kp, bool full, bool mimo) {
   kp.lds_floats = off;
 }
 
-template <int VEC, bool FULL, bool MIMO, int NTC, int PTC, int NWC, int RSC>
+template <int VEC, bool FULL, bool MIMO, int NTC, int PTC, int NWC, int RSC, bool STR>
 hipError_t launch_one(const ScanKParams& kp, unsigned grid, unsigned block, hipStream_t stream) {
   const size_t lds_bytes = (size_t)kp.lds_floats * sizeof(float);
   // Dynamic LDS above 64 KiB needs the opt-in attribute on some runtimes;
@@ -864,22 +870,24 @@ hipError_t launch_one(const ScanKParams& kp, unsigned grid, unsigned block, hipS
   // runtime does not know the attribute.
   static size_t attr_bytes = 64 * 1024;
   if (lds_bytes > attr_bytes) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC, RSC>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC, RSC, STR>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) != hipSuccess)
       (void)hipGetLastError();
     attr_bytes = lds_bytes;
   }
-  hipLaunchKernelGGL((scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC, RSC>), dim3(grid), dim3(block), lds_bytes, stream, kp);
+  hipLaunchKernelGGL((scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC, RSC, STR>), dim3(grid), dim3(block), lds_bytes,
+                     stream, kp);
   return hipGetLastError();
 }
 
-template <int VEC, bool MIMO, int NTC, int PTC, int NWC, int RSC>
+template <int VEC, bool MIMO, int NTC, int PTC, int NWC, int RSC, bool STR = false>
 hipError_t launch_passes(ScanKParams kp, const ScanPlan& plan, unsigned bhn, unsigned block,
                          hipStream_t stream) {
   if (plan.nseg > 1) {
     ScanKParams ka = kp;
     layout(ka, false, MIMO);
-    hipError_t e = launch_one<VEC, false, MIMO, NTC, PTC, NWC, RSC>(ka, bhn * (unsigned)(plan.nseg - 1), block, stream);
+    hipError_t e = launch_one<VEC, false, MIMO, NTC, PTC, NWC, RSC, STR>(ka, bhn * (unsigned)(plan.nseg - 1), block,
+                                                                       stream);
     if (e != hipSuccess) return e;
   }
   layout(kp, true, MIMO);
@@ -888,7 +896,7 @@ hipError_t launch_passes(ScanKParams kp, const ScanPlan& plan, unsigned bhn, uns
     hipError_t e = hipEventRecord(pe.start, stream);
     if (e != hipSuccess) return e;
   }
-  hipError_t e = launch_one<VEC, true, MIMO, NTC, PTC, NWC, RSC>(kp, bhn * (unsigned)plan.nseg, block, stream);
+  hipError_t e = launch_one<VEC, true, MIMO, NTC, PTC, NWC, RSC, STR>(kp, bhn * (unsigned)plan.nseg, block, stream);
   if (e == hipSuccess && pe.stop) e = hipEventRecord(pe.stop, stream);
   return e;
 }
@@ -905,6 +913,8 @@ hipError_t launch_scan(const ScanGeom& g, const ScanOperands& o, const ScanPlan&
   kp.B = g.B; kp.L = g.L; kp.H = g.H; kp.G = g.G; kp.P = g.P; kp.N = g.N; kp.A = g.A; kp.R = g.R;
   kp.has_z = g.has_z; kp.has_d = g.has_d; kp.has_norm = g.has_norm;
   const bool mimo = o.mimo_x != nullptr;
+  const bool strided = o.xs != 0 || o.ts != 0 || o.as != 0;
+  if (strided && mimo) return hipErrorInvalidValue;  // packed rows feed the SISO scan only
   kp.NT = ((int)g.N + 15) / 16;
   kp.PT = ((int)g.P + 15) / 16;
   kp.NH = kp.NT > 4 ? 2 : 1;
@@ -940,7 +950,9 @@ hipError_t launch_scan(const ScanGeom& g, const ScanOperands& o, const ScanPlan&
   // strides and rank stride; every other geometry runs the generic variant.
   if (vec4 && g.N == 128 && g.P == 64 && nwaves == 8 && g.A % 4 == 0 && kp.astr % 4 == 0 &&
       (g.A == 0 || aligned16(o.angle))) {
-    if (!mimo) return launch_passes<4, false, 8, 4, 8, 1>(kp, plan, bhn, block, stream);
+    if (!mimo)
+      return strided ? launch_passes<4, false, 8, 4, 8, 1, true>(kp, plan, bhn, block, stream)
+                     : launch_passes<4, false, 8, 4, 8, 1>(kp, plan, bhn, block, stream);
     switch (kp.RS) {
       case 1: return launch_passes<4, true, 8, 4, 8, 1>(kp, plan, bhn, block, stream);
       case 2: return launch_passes<4, true, 8, 4, 8, 2>(kp, plan, bhn, block, stream);
@@ -948,6 +960,9 @@ hipError_t launch_scan(const ScanGeom& g, const ScanOperands& o, const ScanPlan&
       default: return launch_passes<4, true, 8, 4, 8, 8>(kp, plan, bhn, block, stream);
     }
   }
+  if (strided)  // packed projection rows (SISO only)
+    return vec4 ? launch_passes<4, false, 0, 0, 0, 0, true>(kp, plan, bhn, block, stream)
+                : launch_passes<1, false, 0, 0, 0, 0, true>(kp, plan, bhn, block, stream);
   if (vec4)
     return mimo ? launch_passes<4, true, 0, 0, 0, 0>(kp, plan, bhn, block, stream)
                 : launch_passes<4, false, 0, 0, 0, 0>(kp, plan, bhn, block, stream);
