@@ -556,7 +556,7 @@ def main():
                    "rope_angles": A, "has_z": True, "has_d": True, "input_sets": args.sets},
         "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": kern_gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(),
-                     "kernel": "scan_chunk_kernel<4, true, false, 8, 4, 8, 1> (main scan pass)",
+                     "kernel": "scan_chunk_kernel<4, true, false, 8, 4, 8, 1, false> (main scan pass)",
                      "kernel_ms": kern_avg, "algorithmic_bytes": scan_bytes,
                      "fp32_tflops_min_work": min_flops / (kern_avg * 1e-3) / 1e12,
                      "fp32_frac": min_flops / (kern_avg * 1e-3) / 1e12 / FP32_PEAK_TFLOPS},
