@@ -20,4 +20,4 @@ from .m3_oracle import (  # noqa: F401
     siso_step,
     softplus,
 )
-from .m3_backward import PREPROCESS_OUTPUTS, preprocess_backward, siso_backward  # noqa: F401
+from .m3_backward import PREPROCESS_OUTPUTS, mimo_backward, preprocess_backward, siso_backward  # noqa: F401

@@ -224,3 +224,86 @@ def test_preprocess_backward_every_element_on_a_tiny_case():
         e[idx] = eps
         fd = (_pre_loss(proj + e, bias, gr, cfg) - _pre_loss(proj - e, bias, gr, cfg)) / (2 * eps)
         assert abs(fd - got["projected"][idx]) <= 1e-6 * max(1.0, abs(fd)), (idx, fd, got["projected"][idx])
+
+
+# ---------------------------------------------------------------------------
+# MIMO
+# ---------------------------------------------------------------------------
+
+MOPS = OPS + ("mimo_x", "mimo_z", "mimo_o", "norm_weight")
+
+
+def _mcfg(d: Dims) -> O.SsmConfig:
+    return O.SsmConfig(d.B, d.L, d.H, d.G, d.P, d.N, d.A, d.R, d.has_z, d.has_d, d.has_output_norm)
+
+
+def _mloss(inp: dict, dout, cfg) -> float:
+    return float(np.sum(dout * O.mimo_scan(*[inp[k] for k in MOPS], cfg)))
+
+
+MCASES = [
+    Dims(2, 7, 2, 1, 3, 6, 2, R=2, has_output_norm=True),
+    Dims(1, 9, 4, 2, 4, 4, 1, R=3, has_z=False),
+    Dims(1, 6, 2, 0, 5, 8, 3, R=2, has_d=False, has_output_norm=True),
+    Dims(2, 5, 3, 1, 2, 4, 0, R=1, has_output_norm=True),
+    Dims(1, 8, 2, 2, 3, 4, 2, R=4, has_z=False, has_d=False),
+]
+
+
+@pytest.mark.parametrize("d", MCASES, ids=lambda d: f"B{d.B}L{d.L}H{d.H}G{d.G}P{d.P}N{d.N}A{d.A}R{d.R}"
+                         f"{'n' if d.has_output_norm else ''}{'' if d.has_z else 'nz'}{'' if d.has_d else 'nd'}")
+def test_mimo_backward_matches_directional_finite_differences(d):
+    cfg = _mcfg(d)
+    inp = {k: v.astype(np.float64) for k, v in ssm_inputs(d, seed=800 + d.L, mimo=True).items()}
+    dout = output_gradient(d, seed=810 + d.L).astype(np.float64)
+    grads = O.mimo_backward(dout, *[inp[k] for k in MOPS], cfg, block=3)
+    rng = np.random.default_rng(820 + d.L)
+    for name in MOPS:
+        v = rng.standard_normal(inp[name].shape)
+        plus, minus = dict(inp), dict(inp)
+        plus[name] = inp[name] + 1e-5 * v
+        minus[name] = inp[name] - 1e-5 * v
+        fd = (_mloss(plus, dout, cfg) - _mloss(minus, dout, cfg)) / 2e-5
+        an = float(np.sum(grads[name] * v))
+        assert abs(fd - an) <= 1e-6 * max(abs(fd), abs(an), 1e-3), (name, fd, an)
+    if not d.has_output_norm:
+        assert not np.any(grads["norm_weight"])
+    if not d.has_z:
+        assert not np.any(grads["z"]) and not np.any(grads["mimo_z"])
+
+
+def test_mimo_backward_every_element_on_a_tiny_case():
+    d = Dims(1, 3, 2, 1, 2, 4, 1, R=2, has_output_norm=True)
+    cfg = _mcfg(d)
+    inp = {k: v.astype(np.float64) for k, v in ssm_inputs(d, seed=831, mimo=True).items()}
+    dout = output_gradient(d, seed=832).astype(np.float64)
+    g = O.mimo_backward(dout, *[inp[k] for k in MOPS], cfg)
+    for name in MOPS:
+        assert g[name].shape == inp[name].shape, name
+        for idx in np.ndindex(*g[name].shape):
+            plus, minus = dict(inp), dict(inp)
+            e = np.zeros_like(inp[name])
+            e[idx] = 1e-6   # the norm over P = 2 curves strongly: a smaller step keeps the truncation error down
+            plus[name] = inp[name] + e
+            minus[name] = inp[name] - e
+            fd = (_mloss(plus, dout, cfg) - _mloss(minus, dout, cfg)) / 2e-6
+            assert abs(fd - g[name][idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, g[name][idx])
+
+
+def test_mimo_backward_rank_one_is_siso_backward():
+    d = Dims(2, 11, 4, 2, 3, 6, 2, R=1)
+    inp = ssm_inputs(d, seed=841, mimo=True)
+    H, P = d.H, d.P
+    inp["mimo_x"] = np.ones((H, 1, P), np.float32)
+    inp["mimo_z"] = np.ones((H, 1, P), np.float32)
+    inp["mimo_o"] = np.ones((H, 1, P), np.float32)
+    inp = {k: v.astype(np.float64) for k, v in inp.items()}
+    dout = output_gradient(d, seed=842).astype(np.float64)
+    gm = O.mimo_backward(dout, *[inp[k] for k in MOPS], _mcfg(d))
+    sin = dict(inp)
+    sin["c_bias"], sin["b_bias"] = inp["c_bias"][:, 0], inp["b_bias"][:, 0]
+    gs = O.siso_backward(dout, *[sin[k] for k in OPS], _cfg(d))
+    for k in OPS:
+        np.testing.assert_allclose(gm[k].reshape(gs[k].shape), gs[k], rtol=1e-10, atol=1e-12, err_msg=k)
+    # with unit weights the MIMO weight gradients are the SISO sums they multiply
+    np.testing.assert_allclose(gm["mimo_x"][:, 0], np.sum(gs["x"] * inp["x"], axis=(0, 1)), rtol=1e-10, atol=1e-12)

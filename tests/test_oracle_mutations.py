@@ -74,6 +74,15 @@ BACKWARD_MUTATIONS = {
     "bwd_a_without_softplus_slope": ("d_a = np.where(a_pass, -dt * g[\"adt\"] * sigmoid(a_raw), 0.0)",
                                      "d_a = np.where(a_pass, -dt * g[\"adt\"], 0.0)"),
     "bwd_dt_ignores_adt": ("g_dt = g[\"dt\"] - a_mag * g[\"adt\"]", "g_dt = g[\"dt\"]"),
+    "mimo_bwd_norm_without_projection": ("g3 = rinv * (gn - yn * np.mean(gn * yn, axis=-1, keepdims=True))",
+                                         "g3 = rinv * gn"),
+    "mimo_bwd_gate_without_mimo_z": ("dZ[:, t] += np.sum(du * MZ[None], axis=2)", "dZ[:, t] += np.sum(du, axis=2)"),
+    "mimo_bwd_x_weights_ignored": ("dX = np.sum(dXR * MX[None, None], axis=3)", "dX = np.sum(dXR, axis=3)"),
+    "mimo_bwd_mimo_o_before_norm": ("dMO += np.sum(g * y4, axis=0)", "dMO += np.sum(g * y3, axis=0)"),
+    "mimo_bwd_theta_half": ("dQ[..., A:2 * A] * Qm[..., :A] - dQ[..., :A] * Qm[..., A:2 * A], axis=3)",
+                            "dQ[..., A:2 * A] * Qm[..., :A] - dQ[..., :A] * Qm[..., A:2 * A], axis=3) * 0.5"),
+    "mimo_bwd_bc_rows_transposed": ("bc_rows = np.arange(R)[None, :] * G + grp[:, None]              # [H, R]",
+                                    "bc_rows = grp[:, None] * R + np.arange(R)[None, :]              # [H, R]"),
 }
 
 
