@@ -1,7 +1,7 @@
 /*
  * m3.h -- C ABI of the MI355X (gfx950) Mamba-3 selective-state path.
  *
- * Eight operations, named after the public functions of the oarust 0.8.6
+ * Nine operations, named after the public functions of the oarust 0.8.6
  * source page src/rs/ml/matrix/mamba3.rs ("Public API" section) and the
  * ml::matrix API index:
  *
@@ -12,6 +12,7 @@
  *   m3_siso_step    mamba3_siso_step    one SISO decode token, states in place
  *   m3_mimo_step    mamba3_mimo_step    one MIMO decode token, states in place
  *   m3_siso_bwd     mamba3_siso_backward        the eleven SISO scan gradients
+ *   m3_mimo_bwd     mamba3_mimo_backward        the fifteen MIMO scan gradients
  *   m3_preprocess_bwd mamba3_preprocess_backward gradients of projected, dt_bias
  *
  * Conventions shared by every entry point
@@ -287,6 +288,36 @@ int m3_siso_bwd(const float* dout, const float* c, const float* b, const float* 
                 m3_ssm_config cfg,
                 float* d_c, float* d_b, float* d_x, float* d_z, float* d_adt, float* d_dt,
                 float* d_trap, float* d_angle, float* d_c_bias, float* d_b_bias, float* d_d,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * m3_mimo_bwd -- mamba3_mimo_backward ("deterministic prepare, post,
+ * reverse-core, inverse-rotation, and reduction stages"; Mamba3MimoBackward
+ * for the fifteen gradients).  Given dout [B,L,H,P] and the fifteen
+ * operands and config of the m3_mimo_fwd call, writes the gradient of
+ * sum(dout * out) for every operand in its layout: d_c, d_b [B,L,R*G,N]
+ * (row r*G + g, summed over the group's heads); d_x, d_z [B,L,H,P];
+ * d_adt, d_dt, d_trap [B,L,H]; d_angle [B,L,A]; d_c_bias, d_b_bias [H,R,N];
+ * d_d [H]; d_mimo_x, d_mimo_z, d_mimo_o [H,R,P]; d_norm_weight [H,P]
+ * (all zeros without the norm; d_z and d_mimo_z zero without the gate,
+ * d_d zero without the skip).  Outputs are overwritten.
+ * workspace: at least m3_mimo_bwd_workspace_bytes(cfg) bytes.  Chunks hold
+ *   32 / RS tokens (RS = R rounded up to a power of two), and the entry
+ *   states and exit adjoints [B*H, chunks, P, N] dominate: 8.6 GB at
+ *   B8 L4096 H32 P64 N128 R4.
+ * Rules: those of m3_mimo_fwd, plus M3_ERR_UNSUPPORTED when a kernel's
+ *   working set exceeds one CU's 160 KiB of LDS.  Fixed-order reductions:
+ *   repeated calls give identical results.
+ */
+size_t m3_mimo_bwd_workspace_bytes(m3_ssm_config cfg);
+int m3_mimo_bwd(const float* dout, const float* c, const float* b, const float* x,
+                const float* z, const float* adt, const float* dt, const float* trap,
+                const float* angle, const float* c_bias, const float* b_bias, const float* d,
+                const float* mimo_x, const float* mimo_z, const float* mimo_o,
+                const float* norm_weight, m3_ssm_config cfg,
+                float* d_c, float* d_b, float* d_x, float* d_z, float* d_adt, float* d_dt,
+                float* d_trap, float* d_angle, float* d_c_bias, float* d_b_bias, float* d_d,
+                float* d_mimo_x, float* d_mimo_z, float* d_mimo_o, float* d_norm_weight,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*

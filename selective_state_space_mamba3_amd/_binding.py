@@ -121,6 +121,10 @@ def lib() -> ctypes.CDLL:
     L.m3_siso_fwd_packed_workspace_bytes.argtypes = [_CPre, _CSsm]
     L.m3_siso_fwd_packed.restype = ctypes.c_int
     L.m3_siso_fwd_packed.argtypes = [_P] * 5 + [_CPre, _CSsm, _P, _P, ctypes.c_size_t, _P]
+    L.m3_mimo_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.m3_mimo_bwd_workspace_bytes.argtypes = [_CSsm]
+    L.m3_mimo_bwd.restype = ctypes.c_int
+    L.m3_mimo_bwd.argtypes = [_P] * 16 + [_CSsm] + [_P] * 15 + [_P, ctypes.c_size_t, _P]
     L.m3_siso_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.m3_siso_bwd_workspace_bytes.argtypes = [_CSsm]
     L.m3_siso_bwd.restype = ctypes.c_int
@@ -417,3 +421,40 @@ def m3_siso_fwd_packed(projected, dt_bias, c_bias, b_bias, d, pcfg: PreprocessCo
                                  c_pre(pcfg), c_ssm(cfg), _ptr(out), _ptr(workspace), ws_bytes,
                                  _stream(dev, stream)))
     return out
+
+
+_MIMO4 = ("mimo_x", "mimo_z", "mimo_o", "norm_weight")
+
+
+def mimo_bwd_workspace_bytes(cfg: SsmConfig) -> int:
+    return int(lib().m3_mimo_bwd_workspace_bytes(c_ssm(cfg)))
+
+
+def m3_mimo_bwd(dout, c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d, mimo_x, mimo_z, mimo_o,
+                norm_weight, cfg: SsmConfig, grads: dict | None = None, workspace=None, stream=None) -> dict:
+    """MIMO scan backward on the GPU; returns the fifteen gradients by operand name."""
+    L_ = lib()
+    dev = x.device
+    R = cfg.mimo_rank
+    ops = dict(zip(_OPS11 + _MIMO4, (c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d,
+                                     mimo_x, mimo_z, mimo_o, norm_weight)))
+    shapes = _scan_shapes(cfg, R * cfg.groups, (cfg.num_heads, R, cfg.state_size))
+    for k in ("mimo_x", "mimo_z", "mimo_o"):
+        shapes[k] = (cfg.num_heads, R, cfg.head_dim)
+    shapes["norm_weight"] = (cfg.num_heads, cfg.head_dim)
+    for k, shp in shapes.items():
+        _expect(k, ops[k], shp, dev)
+    _expect("dout", dout, shapes["x"], dev)
+    grads = dict(grads or {})
+    for k, shp in shapes.items():
+        if k not in grads:
+            grads[k] = torch.empty(shp, dtype=torch.float32, device=dev)
+        _expect("d_" + k, grads[k], shp, dev)
+    need = mimo_bwd_workspace_bytes(cfg)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    names = _OPS11 + _MIMO4
+    _check(L_.m3_mimo_bwd(_ptr(dout), *[_ptr(ops[k]) for k in names], c_ssm(cfg),
+                          *[_ptr(grads[k]) for k in names], _ptr(workspace), ws_bytes, _stream(dev, stream)))
+    return grads

@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(REPO, "_build")
 LIB_NAME = "libm3.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["abi.cpp", "scan_fwd.hip", "siso_step.hip", "mimo_step.hip", "preprocess.hip", "siso_bwd.hip",
+SOURCES = ["abi.cpp", "scan_fwd.hip", "siso_step.hip", "mimo_step.hip", "preprocess.hip", "scan_bwd.hip",
            "preprocess_bwd.hip"]
 
 ARCH = "gfx950"

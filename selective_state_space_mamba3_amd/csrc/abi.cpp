@@ -310,6 +310,50 @@ int m3_siso_fwd_packed(const float* projected, const float* dt_bias, const float
   return hip_status(op, m3::launch_siso_fwd(g, o, pp.plan, scan_ws, s));
 }
 
+size_t m3_mimo_bwd_workspace_bytes(m3_ssm_config cfg) {
+  m3::ScanGeom g{};
+  if (resolve_scan("m3_mimo_bwd_workspace_bytes", cfg, true, &g) != M3_OK) return 0;
+  return m3::mimo_bwd_workspace_floats(g) * sizeof(float);
+}
+
+int m3_mimo_bwd(const float* dout, const float* c, const float* b, const float* x, const float* z,
+                const float* adt, const float* dt, const float* trap, const float* angle,
+                const float* c_bias, const float* b_bias, const float* d, const float* mimo_x,
+                const float* mimo_z, const float* mimo_o, const float* norm_weight, m3_ssm_config cfg,
+                float* d_c, float* d_b, float* d_x, float* d_z, float* d_adt, float* d_dt,
+                float* d_trap, float* d_angle, float* d_c_bias, float* d_b_bias, float* d_d,
+                float* d_mimo_x, float* d_mimo_z, float* d_mimo_o, float* d_norm_weight,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  const char* op = "m3_mimo_bwd";
+  clear_error();
+  m3::ScanGeom g{};
+  int st = resolve_scan(op, cfg, true, &g);
+  if (st) return st;
+  st = check_ptrs(op, {{"dout", dout}, {"c", c}, {"b", b}, {"x", x}, {"z", z}, {"adt", adt},
+                       {"dt", dt}, {"trap", trap}, {"c_bias", c_bias}, {"b_bias", b_bias}, {"d", d},
+                       {"mimo_x", mimo_x}, {"mimo_z", mimo_z}, {"mimo_o", mimo_o},
+                       {"norm_weight", norm_weight}, {"d_c", d_c}, {"d_b", d_b}, {"d_x", d_x},
+                       {"d_z", d_z}, {"d_adt", d_adt}, {"d_dt", d_dt}, {"d_trap", d_trap},
+                       {"d_c_bias", d_c_bias}, {"d_b_bias", d_b_bias}, {"d_d", d_d},
+                       {"d_mimo_x", d_mimo_x}, {"d_mimo_z", d_mimo_z}, {"d_mimo_o", d_mimo_o},
+                       {"d_norm_weight", d_norm_weight}});
+  if (st) return st;
+  if (g.A > 0 && (angle == nullptr || d_angle == nullptr))
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: operand angle or d_angle is NULL", op);
+  if (!m3::mimo_bwd_fits(g))
+    return fail(M3_ERR_UNSUPPORTED, "%s: %u heads per group at rank %u with state_size %u exceed the LDS of the "
+                "backward kernels", op, g.H / g.G, g.R, g.N);
+  const size_t need = m3::mimo_bwd_workspace_floats(g) * sizeof(float);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: workspace of %zu bytes required, %zu given", op, need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  m3::ScanOperands o{c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d,
+                     mimo_x, mimo_z, mimo_o, norm_weight, nullptr};
+  m3::BwdOperands go{dout, d_c, d_b, d_x, d_z, d_adt, d_dt, d_trap, d_angle, d_c_bias, d_b_bias, d_d,
+                     d_mimo_x, d_mimo_z, d_mimo_o, d_norm_weight};
+  return hip_status(op, m3::launch_mimo_bwd(g, o, go, workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t m3_siso_fwd_workspace_bytes(m3_ssm_config cfg) {
   m3::ScanGeom g{};
   if (resolve_scan("m3_siso_fwd_workspace_bytes", cfg, false, &g) != M3_OK) return 0;

@@ -40,6 +40,7 @@ struct PreOperands {
 struct BwdOperands {
   const float* dout;
   float *d_c, *d_b, *d_x, *d_z, *d_adt, *d_dt, *d_trap, *d_angle, *d_c_bias, *d_b_bias, *d_d;
+  float *d_mimo_x, *d_mimo_z, *d_mimo_o, *d_norm_weight;  // MIMO only
 };
 
 // Gradients of the eight preprocess outputs (any may be null: zero) and the
@@ -87,6 +88,10 @@ hipError_t launch_preprocess_bwd(const PreGeom& g, const PreBwdOperands& o, hipS
 size_t siso_bwd_workspace_floats(const ScanGeom& g);
 bool siso_bwd_fits(const ScanGeom& g);  // LDS of the backward kernels fits one CU
 hipError_t launch_siso_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOperands& go, void* workspace,
+                           hipStream_t stream);
+size_t mimo_bwd_workspace_floats(const ScanGeom& g);
+bool mimo_bwd_fits(const ScanGeom& g);
+hipError_t launch_mimo_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOperands& go, void* workspace,
                            hipStream_t stream);
 
 }  // namespace m3

@@ -66,9 +66,18 @@ struct BwdK {
   float* phi_tot;   // [BH][nc]       chunk sums of the d adt terms -> sums over later chunks
   float* th_tot;    // [BH][nc][A]    chunk sums of d theta -> sums over later chunks
   float* dd_part;   // [BH][nc]       per-chunk sum of x . gy
-  float* bias_part; // [nrb][2][H][N] partial bias sums (0: b_bias, 1: c_bias)
+  float* bias_part; // [nrb][2][H][R N] partial bias sums (0: b_bias, 1: c_bias)
+  // MIMO: per-rank weights and their gradients; the upstream gradient of each
+  // rank's state read-out gy [BH][nc * BQ][P] (rows v = token * RS + rank);
+  // per-chunk partial sums of the weight gradients
+  const float *mimo_x, *mimo_z, *mimo_o, *norm_weight;
+  float *d_mimo_x, *d_mimo_z, *d_mimo_o, *d_norm_weight;
+  float* gyr;
+  float* rho;       // [BH][L] gy . (state read-out), summed over ranks
+  float *mx_part, *mz_part, *mo_part, *nw_part;  // [BH nc][R P] (nw: [BH nc][P])
   int B, L, H, G, P, N, A;
-  int has_z, has_d;
+  int has_z, has_d, has_norm;
+  int R, RS, rsl, Qt;  // rank, rank stride (power of two), its log2, tokens per chunk
   int nc, nT, NT, PT, nrb;
 };
 
@@ -421,7 +430,8 @@ __global__ __launch_bounds__(512) void bwd_summary_kernel(BwdK p) {
 
 // (4) Element-wise over the chunks of one (b, h): hs[c] <- state before chunk
 // c; gs[c] <- adjoint after chunk c.  In place; loads run eight chunks ahead.
-__global__ __launch_bounds__(256) void bwd_prefix_kernel(BwdK p, int blocks_per_bh) {
+// mode bit 1: forward summaries (hs); bit 2: reverse summaries (gs).
+__global__ __launch_bounds__(256) void bwd_prefix_kernel(BwdK p, int blocks_per_bh, int mode) {
   const int bh = blockIdx.x / blocks_per_bh;
   const int e = (blockIdx.x - bh * blocks_per_bh) * blockDim.x + threadIdx.x;
   const int PN = p.P * p.N, nc = p.nc;
@@ -431,7 +441,7 @@ __global__ __launch_bounds__(256) void bwd_prefix_kernel(BwdK p, int blocks_per_
   const float* dec = p.decay + (size_t)bh * nc;
   constexpr int U = 8;
   float run = 0.f;
-  for (int c0 = 0; c0 < nc; c0 += U) {
+  for (int c0 = 0; (mode & 1) && c0 < nc; c0 += U) {
     float v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = c0 + u < nc ? hs[(size_t)(c0 + u) * PN] : 0.f;
@@ -444,7 +454,7 @@ __global__ __launch_bounds__(256) void bwd_prefix_kernel(BwdK p, int blocks_per_
     }
   }
   run = 0.f;
-  for (int c1 = nc - 1; c1 >= 0; c1 -= U) {
+  for (int c1 = nc - 1; (mode & 2) && c1 >= 0; c1 -= U) {
     float v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = c1 - u >= 0 ? gs[(size_t)(c1 - u) * PN] : 0.f;
@@ -733,7 +743,7 @@ __global__ __launch_bounds__(256) void bwd_apply_kernel(BwdK p) {
   const int bh = blockIdx.x / p.nc, c = blockIdx.x - bh * p.nc;
   const int b = bh / p.H, h = bh - b * p.H;
   const int tid = threadIdx.x, t = tid & 31, k = tid >> 5;
-  const int t0 = c * BQ, nv = min(BQ, p.L - t0), A = p.A, H = p.H;
+  const int t0 = c * p.Qt, nv = min(p.Qt, p.L - t0), A = p.A, H = p.H;
   const int tc = t0 + min(t, nv - 1);
   const size_t si = ((size_t)b * p.L + tc) * H + h;
   const float dtv = p.dt[si];
@@ -762,57 +772,59 @@ __global__ __launch_bounds__(256) void bwd_apply_kernel(BwdK p) {
 }
 
 // (8) Per block of RB token rows (b, t) and group g: d_b, d_c = sums of the
-// per-head adjoints over the group's heads, and partial bias sums.  Thread
-// (hs, n) owns column n of heads hs, hs + nhs, ... for every row.
+// per-head adjoints over the group's heads, and partial bias sums.  A row of
+// per-head adjoints has R N columns (rank r, state n); item (hs, col) owns
+// column col of heads hs, hs + nhs, ... for every row, so each bias sum has
+// one owner.
 __global__ __launch_bounds__(256) void bwd_group_kernel(BwdK p) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  const int N = p.N, H = p.H, G = p.G, HG = H / G;
+  const int N = p.N, H = p.H, G = p.G, HG = H / G, R = p.R, RN = R * N;
   const int g = blockIdx.y, blk = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int nhs = max(1, (int)blockDim.x / N);
-  const int hs = tid / N, n = tid - hs * N;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int nhs = max(1, nthr / RN);
   const int nact = min(nhs, HG);
-  const bool active = hs < nact;
-  float* bacc = lds;                 // [2][HG][N] bias sums of this block
-  float* gsum = bacc + 2 * HG * N;   // [nact][2][N] group partials per head subset
-  for (int i = tid; i < 2 * HG * N; i += blockDim.x) bacc[i] = 0.f;
+  float* bacc = lds;                  // [2][HG][RN] bias sums of this block
+  float* gsum = bacc + 2 * HG * RN;   // [nact][2][RN] group partials per head subset
+  for (int i = tid; i < 2 * HG * RN; i += nthr) bacc[i] = 0.f;
   __syncthreads();
   const int rows = p.B * p.L;
   for (int rr = 0; rr < RB; ++rr) {
     const int row = blk * RB + rr;
     if (row >= rows) break;
-    if (active) {
+    for (int it = tid; it < nact * RN; it += nthr) {
+      const int hs = it / RN, col = it - hs * RN;
       float gb = 0.f, gc = 0.f;
-      const size_t base = ((size_t)row * H + g * HG) * N + n;
+      const size_t base = ((size_t)row * H + g * HG) * RN + col;
 #pragma unroll 4
       for (int hh = hs; hh < HG; hh += nhs) {
-        const float vb = p.db_head[base + (size_t)hh * N];
-        const float vc = p.dc_head[base + (size_t)hh * N];
+        const float vb = p.db_head[base + (size_t)hh * RN];
+        const float vc = p.dc_head[base + (size_t)hh * RN];
         gb += vb;
         gc += vc;
-        bacc[hh * N + n] += vb;
-        bacc[(HG + hh) * N + n] += vc;
+        bacc[hh * RN + col] += vb;
+        bacc[(HG + hh) * RN + col] += vc;
       }
-      gsum[(hs * 2) * N + n] = gb;
-      gsum[(hs * 2 + 1) * N + n] = gc;
+      gsum[(hs * 2) * RN + col] = gb;
+      gsum[(hs * 2 + 1) * RN + col] = gc;
     }
     __syncthreads();
-    if (tid < N) {
+    for (int col = tid; col < RN; col += nthr) {
       float sb = 0.f, sc = 0.f;
       for (int k = 0; k < nact; ++k) {
-        sb += gsum[(k * 2) * N + tid];
-        sc += gsum[(k * 2 + 1) * N + tid];
+        sb += gsum[(k * 2) * RN + col];
+        sc += gsum[(k * 2 + 1) * RN + col];
       }
-      const size_t o = ((size_t)row * G + g) * N + tid;
+      const int r = col / N, n = col - r * N;
+      const size_t o = ((size_t)row * R * G + r * G + g) * N + n;  // B / C row r G + g
       p.d_b[o] = sb;
       p.d_c[o] = sc;
     }
     __syncthreads();
   }
-  for (int i = tid; i < 2 * HG * N; i += blockDim.x) {
-    const int which = i / (HG * N), rem = i - which * HG * N;
-    const int hh = rem / N, nn = rem - hh * N;
-    p.bias_part[(((size_t)blk * 2 + which) * H + g * HG + hh) * N + nn] = bacc[i];
+  for (int i = tid; i < 2 * HG * RN; i += nthr) {
+    const int which = i / (HG * RN), rem = i - which * HG * RN;
+    const int hh = rem / RN, col = rem - hh * RN;
+    p.bias_part[(((size_t)blk * 2 + which) * H + g * HG + hh) * RN + col] = bacc[i];
   }
 }
 
@@ -820,7 +832,7 @@ __global__ __launch_bounds__(256) void bwd_group_kernel(BwdK p) {
 // 32 strided partial sums each, then a fixed tree); d_d from the chunk partials.
 __global__ __launch_bounds__(256) void bwd_bias_kernel(BwdK p) {
   __shared__ float red[32][9];
-  const int HN = p.H * p.N;
+  const int HN = p.H * p.R * p.N;
   const int tid = threadIdx.x, o = tid & 7, part = tid >> 3;
   const int i = blockIdx.x * 8 + o;
   float s = 0.f;
@@ -864,6 +876,649 @@ __global__ __launch_bounds__(256) void bwd_angle_kernel(BwdK p) {
   p.d_angle[i] = s;
 }
 
+// ---------------------------------------------------------------------------
+// MIMO backward.  A chunk holds BQ = 32 virtual rows v = t RS + r (token t,
+// rank r; rows of padding ranks r >= R stay zero), Qt = BQ / RS tokens, as
+// in the forward scan.  The state is shared by the ranks, so every formula
+// above holds with x K^T replaced by the rank sum: the masks take the tokens
+// of the two rows (all rank pairs of one token get lam dt), d gamma and the
+// same-token terms sum over rank pairs, and d x sums mimo_x * dX_r over ranks.
+// ---------------------------------------------------------------------------
+
+// Keys / queries of the chunk's virtual rows into LDS (stride ns, zero rows
+// and columns past the data); with cs_l the cosines / sines [BQ][A].
+__device__ void load_kq_m(const BwdK& p, int b, int h, int g, int t0, int nv, float* Kc, float* Qc, int ns,
+                          float* cs_l, float* sn_l, int tid, int nthr) {
+  const int N = p.N, A = p.A, NP = N - A, bh = b * p.H + h, RG = p.R * p.G;
+  for (int it = tid; it < BQ * NP; it += nthr) {
+    const int v = it / NP, j = it - v * NP;
+    const int t = v >> p.rsl, r = v & (p.RS - 1);
+    const bool ok = t < nv && r < p.R;
+    const int n0 = j < A ? j : j + A;
+    float k0 = 0.f, k1 = 0.f, q0 = 0.f, q1 = 0.f, cs = 1.f, sn = 0.f;
+    if (ok) {
+      const size_t row = (((size_t)b * p.L + t0 + t) * RG + r * p.G + g) * N;
+      const float* bb = p.b_bias + ((size_t)h * p.R + r) * N;
+      const float* cb = p.c_bias + ((size_t)h * p.R + r) * N;
+      if (j < A) {
+        sincos_acc(theta_at(p, bh, t0 + t, j), &sn, &cs);
+        const float b0 = p.b[row + j] + bb[j], b1 = p.b[row + j + A] + bb[j + A];
+        const float c0 = p.c[row + j] + cb[j], c1 = p.c[row + j + A] + cb[j + A];
+        k0 = b0 * cs - b1 * sn;
+        k1 = b0 * sn + b1 * cs;
+        q0 = c0 * cs - c1 * sn;
+        q1 = c0 * sn + c1 * cs;
+      } else {
+        k0 = p.b[row + n0] + bb[n0];
+        q0 = p.c[row + n0] + cb[n0];
+      }
+    }
+    Kc[v * ns + n0] = k0;
+    Qc[v * ns + n0] = q0;
+    if (j < A) {
+      Kc[v * ns + j + A] = k1;
+      Qc[v * ns + j + A] = q1;
+      if (cs_l) {
+        cs_l[v * A + j] = cs;
+        sn_l[v * A + j] = sn;
+      }
+    }
+  }
+  const int pad = p.NT * 16 - N;
+  for (int it = tid; it < BQ * pad; it += nthr) {
+    const int v = it / pad, n = N + (it - v * pad);
+    Kc[v * ns + n] = 0.f;
+    Qc[v * ns + n] = 0.f;
+  }
+}
+
+// X_v = x_t * mimo_x[h, r] of the chunk's virtual rows into LDS (stride ps),
+// times wx[t] when wx is given; with xt also the raw x rows [Qt][ps].
+__device__ void load_x_m(const BwdK& p, int b, int h, int t0, int nv, float* X, int ps, const float* wx,
+                         float* xt, int tid, int nthr) {
+  const int P = p.P, PP = p.PT * 16;
+  for (int it = tid; it < BQ * PP; it += nthr) {
+    const int v = it / PP, pp = it - v * PP;
+    const int t = v >> p.rsl, r = v & (p.RS - 1);
+    float xv = 0.f;
+    if (t < nv && r < p.R && pp < P) {
+      const float xr = p.x[(((size_t)b * p.L + t0 + t) * p.H + h) * P + pp];
+      xv = xr * p.mimo_x[((size_t)h * p.R + r) * P + pp];
+      if (xt && r == 0) xt[t * ps + pp] = xr;
+      if (wx) xv *= wx[t];
+    } else if (xt && r == 0 && t < p.Qt) {
+      xt[t * ps + pp] = 0.f;
+    }
+    X[v * ps + pp] = xv;
+  }
+}
+
+// Mask weights between virtual rows: M[v][w] and V[v][w] as for tokens, by
+// the tokens of the rows.
+__device__ __forceinline__ void row_masks(int tv, int tw, const float* cum, const float* scl, const float* gam,
+                                          float* m, float* dec) {
+  *dec = tw < tv ? expf(cum[tv] - cum[tw]) : 0.f;
+  *m = tw < tv ? *dec * scl[tw] : (tw == tv ? gam[tv] : 0.f);
+}
+
+// (M2) Per chunk: forward summary S = sum_v e^(cumx-cum_t) s_t X_v K_v^T and the decay.
+__global__ __launch_bounds__(512) void mimo_summary_kernel(BwdK p) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const int NS = p.NT * 16 + 4, PS = p.PT * 16 + 4;
+  float* Kc = lds;
+  float* Qc = Kc + BQ * NS;  // loaded with the keys; unused here
+  float* Xw = Qc + BQ * NS;
+  float* cum = Xw + BQ * PS;
+  float* scl = cum + BQ;
+  float* gam = scl + BQ;
+  float* ec = gam + BQ;
+  float* ex = ec + BQ;
+  float* wx = ex + BQ;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int bh = blockIdx.x / p.nc, c = blockIdx.x - bh * p.nc;
+  const int b = bh / p.H, h = bh - b * p.H, g = h / (p.H / p.G);
+  const int t0 = c * p.Qt, nv = min(p.Qt, p.L - t0);
+  if (wave == 0) chunk_scalars(p, b, h, t0, nv, ChunkScalars{cum, scl, gam, ec, ex}, lane);
+  load_kq_m(p, b, h, g, t0, nv, Kc, Qc, NS, nullptr, nullptr, tid, blockDim.x);
+  __syncthreads();
+  if (tid < BQ) wx[tid] = ex[tid] * scl[tid];
+  __syncthreads();
+  load_x_m(p, b, h, t0, nv, Xw, PS, wx, nullptr, tid, blockDim.x);
+  __syncthreads();
+  if (tid == 0) p.decay[blockIdx.x] = expf(cum[BQ - 1]);
+  const int ntile = p.PT * p.NT;
+  const size_t base = (size_t)blockIdx.x * p.P * p.N;
+  const int r = lane & 15, q = lane >> 4;
+  for (int job = wave; job < ntile; job += nw) {
+    const int pt = job / p.NT, nt = job - pt * p.NT;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mm_tile(Xw + pt * 16, 1, PS, Kc + nt * 16, NS, 1, BQ, acc, lane);
+    const int n = nt * 16 + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pp = pt * 16 + 4 * q + i;
+      if (pp < p.P && n < p.N) p.hs[base + (size_t)pp * p.N + n] = acc[i];
+    }
+  }
+}
+
+constexpr float kMimoNormEpsBwd = 1.0e-5f;  // the MIMO output-norm epsilon of the MIMO push constants
+
+// Sum over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ float wave_sum(float v) { return read_lane_f(scan64_f(v), 63); }
+
+// (M4) Per chunk: the per-rank read-outs y_v = e^cum_t Q_v h'_e^T + (M o Q K^T) X,
+// then the MIMO epilogue's adjoint per token (mimo_o, output norm, gate, D):
+// gy_v (stored), d_z, rho_t and per-chunk partial sums of the weight
+// gradients; last the reverse summary sum_v e^cum_t gy_v Q_v^T.
+__global__ __launch_bounds__(512) void mimo_post_kernel(BwdK p) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const int NS = p.NT * 16 + 4, PS = p.PT * 16 + 4, PP = p.PT * 16, NN = p.NT * 16;
+  float* Kc = lds;
+  float* Qc = Kc + BQ * NS;
+  float* X = Qc + BQ * NS;
+  float* Y = X + BQ * PS;
+  float* GY = Y + BQ * PS;
+  float* MQK = GY + BQ * PS;
+  float* red = MQK + BQ * MS;        // [8][RS P] cross-wave partials
+  float* cum = red + 8 * p.RS * PP;
+  float* scl = cum + BQ;
+  float* gam = scl + BQ;
+  float* ec = gam + BQ;
+  float* ex = ec + BQ;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int bh = blockIdx.x / p.nc, c = blockIdx.x - bh * p.nc;
+  const int b = bh / p.H, h = bh - b * p.H, g = h / (p.H / p.G);
+  const int t0 = c * p.Qt, nv = min(p.Qt, p.L - t0);
+  const int P = p.P, N = p.N, H = p.H, R = p.R, rsl = p.rsl;
+  const float* HEg = p.hs + (size_t)blockIdx.x * P * N;
+  if (wave == 0) chunk_scalars(p, b, h, t0, nv, ChunkScalars{cum, scl, gam, ec, ex}, lane);
+  load_kq_m(p, b, h, g, t0, nv, Kc, Qc, NS, nullptr, nullptr, tid, blockDim.x);
+  load_x_m(p, b, h, t0, nv, X, PS, nullptr, nullptr, tid, blockDim.x);
+  __syncthreads();
+  const int r = lane & 15, q = lane >> 4;
+  if (wave < 4) {  // masked Q K^T
+    const int mt = wave >> 1, st = wave & 1;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mm_tile_k4(Qc + mt * 16 * NS, NS, Kc + st * 16 * NS, NS, NN, acc, lane);
+    const int w = st * 16 + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = mt * 16 + 4 * q + i;
+      float m, dec;
+      row_masks(v >> rsl, w >> rsl, cum, scl, gam, &m, &dec);
+      MQK[v * MS + w] = m * acc[i];
+    }
+  }
+  __syncthreads();
+  for (int job = wave; job < 2 * p.PT; job += nw) {  // y tiles
+    const int mt = job / p.PT, pt = job - mt * p.PT;
+    floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+    a1 = mm_tile_k1_g<32>(Qc + mt * 16 * NS, NS, HEg + (size_t)pt * 16 * N, N, P - pt * 16, N, NN, a1, lane);
+    a2 = mm_tile(MQK + mt * 16 * MS, MS, 1, X + pt * 16, PS, 1, BQ, a2, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = mt * 16 + 4 * q + i;
+      Y[v * PS + pt * 16 + r] = fmaf(ec[v >> rsl], a1[i], a2[i]);
+    }
+  }
+  __syncthreads();
+
+  // epilogue adjoint: wave w owns tokens w, w + 8, ...; lanes over head_dim (two per lane)
+  const float Dh = p.has_d ? p.d[h] : 0.f;
+  float mo_acc[8][2], mz_acc[8][2], nw_acc[2] = {0.f, 0.f}, dd_acc = 0.f;
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) mo_acc[rr][0] = mo_acc[rr][1] = mz_acc[rr][0] = mz_acc[rr][1] = 0.f;
+  for (int t = wave; t < p.Qt; t += nw) {
+    const bool tok = t < nv;
+    const size_t ti = (((size_t)b * p.L + t0 + min(t, nv - 1)) * H + h) * P;
+    float go[2], zv[2], dz[2] = {0.f, 0.f}, rho = 0.f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int pp = lane + 64 * k;
+      go[k] = (tok && pp < P) ? p.dout[ti + pp] : 0.f;
+      zv[k] = (tok && pp < P && p.has_z) ? p.z[ti + pp] : 0.f;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      if (rr >= p.RS) break;
+      const int v = (t << rsl) + rr;
+      const bool ok = tok && rr < R;
+      float y2[2], y3[2], sil[2], u[2], y1v[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int pp = lane + 64 * k;
+        const bool in = ok && pp < P;
+        y1v[k] = in ? Y[v * PS + pp] : 0.f;
+        y2[k] = fmaf(Dh, in ? X[v * PS + pp] : 0.f, y1v[k]);
+        const float mz = in && p.has_z ? p.mimo_z[((size_t)h * R + rr) * P + pp] : 0.f;
+        u[k] = zv[k] * mz;
+        sil[k] = p.has_z ? siluf_acc(u[k]) : 1.f;
+        y3[k] = y2[k] * sil[k];
+      }
+      float rinv = 1.f, yn[2] = {y3[0], y3[1]}, nwv[2] = {1.f, 1.f};
+      if (p.has_norm) {
+        const float ss = wave_sum(y3[0] * y3[0] + y3[1] * y3[1]);
+        rinv = 1.f / sqrtf(ss / (float)P + kMimoNormEpsBwd);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int pp = lane + 64 * k;
+          yn[k] = y3[k] * rinv;
+          nwv[k] = (ok && pp < P) ? p.norm_weight[(size_t)h * P + pp] : 0.f;
+        }
+      }
+      float g4[2], g3[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int pp = lane + 64 * k;
+        const float mo = (ok && pp < P) ? p.mimo_o[((size_t)h * R + rr) * P + pp] : 0.f;
+        const float y4 = p.has_norm ? yn[k] * nwv[k] : y3[k];
+        mo_acc[rr][k] = fmaf(go[k], y4, mo_acc[rr][k]);
+        g4[k] = go[k] * mo;
+      }
+      if (p.has_norm) {
+        float gn[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          nw_acc[k] = fmaf(g4[k], yn[k], nw_acc[k]);
+          gn[k] = g4[k] * nwv[k];
+        }
+        const float mg = wave_sum(gn[0] * yn[0] + gn[1] * yn[1]) / (float)P;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) g3[k] = rinv * (gn[k] - yn[k] * mg);
+      } else {
+        g3[0] = g4[0];
+        g3[1] = g4[1];
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int pp = lane + 64 * k;
+        float g2 = g3[k];
+        if (p.has_z) {
+          const float du = g3[k] * y2[k] * dsilu_acc(u[k]);
+          const float mz = (ok && pp < P) ? p.mimo_z[((size_t)h * R + rr) * P + pp] : 0.f;
+          mz_acc[rr][k] = fmaf(du, zv[k], mz_acc[rr][k]);
+          dz[k] = fmaf(du, mz, dz[k]);
+          g2 = g3[k] * sil[k];
+        }
+        if (!(ok && pp < P)) g2 = 0.f;
+        rho = fmaf(g2, y1v[k], rho);
+        dd_acc = fmaf(g2, (ok && pp < P) ? X[v * PS + pp] : 0.f, dd_acc);
+        if (pp < PP) GY[v * PS + pp] = g2;
+        if (pp < P) p.gyr[((size_t)blockIdx.x * BQ + v) * P + pp] = g2;
+      }
+    }
+    if (tok) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int pp = lane + 64 * k;
+        if (pp < P) p.d_z[ti + pp] = dz[k];
+      }
+      const float rs = wave_sum(rho);
+      if (lane == 0) p.rho[(size_t)bh * p.L + t0 + t] = rs;
+    }
+  }
+  // per-chunk partial sums of the weight gradients: waves in order
+  const int RP = p.RS * PP;
+  const size_t cp = (size_t)blockIdx.x;
+  for (int which = 0; which < 3; ++which) {
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      if (rr >= p.RS) break;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int pp = lane + 64 * k;
+        if (pp < PP) {
+          const float v = which == 0 ? mo_acc[rr][k] : which == 1 ? mz_acc[rr][k] : (rr == 0 ? nw_acc[k] : 0.f);
+          red[wave * RP + rr * PP + pp] = v;
+        }
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < (which == 2 ? P : R * P); i += blockDim.x) {
+      const int rr = i / P, pp = i - rr * P;
+      float s = 0.f;
+      for (int w = 0; w < nw; ++w) s += red[w * RP + rr * PP + pp];
+      if (which == 0) p.mo_part[cp * R * P + i] = s;
+      else if (which == 1) p.mz_part[cp * R * P + i] = s;
+      else p.nw_part[cp * P + i] = s;
+    }
+  }
+  {
+    const float dsum = wave_sum(dd_acc);
+    __syncthreads();
+    if (lane == 0) red[wave] = dsum;
+    __syncthreads();
+    if (tid == 0) {
+      float s = 0.f;
+      for (int w = 0; w < nw; ++w) s += red[w];
+      p.dd_part[cp] = s;
+    }
+  }
+  // reverse summary: [p][n] = sum_v e^cum_t gy_v[p] Q_v[n]
+  __syncthreads();
+  for (int it = tid; it < BQ * PP; it += blockDim.x) {
+    const int v = it / PP, pp = it - v * PP;
+    Y[v * PS + pp] = ec[v >> rsl] * GY[v * PS + pp];
+  }
+  __syncthreads();
+  const size_t base = (size_t)blockIdx.x * P * N;
+  for (int job = wave; job < p.PT * p.NT; job += nw) {
+    const int pt = job / p.NT, nt = job - pt * p.NT;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mm_tile(Y + pt * 16, 1, PS, Qc + nt * 16, NS, 1, BQ, acc, lane);
+    const int n = nt * 16 + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pp = pt * 16 + 4 * q + i;
+      if (pp < P && n < N) p.gs[base + (size_t)pp * N + n] = acc[i];
+    }
+  }
+}
+
+struct MimoChunkLds {
+  int NS, PS;
+  int o_kc, o_qc, o_x, o_gy, o_dx, o_xt, o_vv, o_msg, o_sqd, o_sgd, o_cs, o_sn, o_sc, o_part, total;
+};
+
+__host__ __device__ inline MimoChunkLds mimo_chunk_lds(int PT, int NT, int A, int RS, int Qt) {
+  MimoChunkLds l{};
+  l.NS = NT * 16 + 4;
+  l.PS = PT * 16 + 4;
+  int off = 0;
+  l.o_kc = off; off += BQ * l.NS;
+  l.o_qc = off; off += BQ * l.NS;
+  l.o_x = off;
+  l.o_gy = off + BQ * l.PS;
+  off += 2 * BQ * l.PS > BQ * l.NS ? 2 * BQ * l.PS : BQ * l.NS;  // x, gy; then the dQ / dK staging
+  l.o_dx = off; off += BQ * l.PS;                                // dX_v
+  l.o_xt = off; off += Qt * l.PS;                                // raw x per token
+  l.o_vv = off; off += BQ * MS;
+  l.o_msg = off; off += BQ * MS;                                 // then d theta [Qt][A]
+  l.o_sqd = off; off += BQ * RS;                                 // same-token Q_v . K_w
+  l.o_sgd = off; off += BQ * RS;                                 // same-token gy_v . X_w
+  l.o_cs = off; off += BQ * A;
+  l.o_sn = off; off += BQ * A;
+  l.o_sc = off; off += 5 * BQ;
+  l.o_part = off; off += BQ * PT;                                // ds partials
+  l.total = off;
+  return l;
+}
+
+// (M6) Per chunk: G K, dQ, dK of the virtual rows on FP32 MFMA with gy from
+// the post kernel; d x (rank sum of mimo_x dX_r), partial mimo_x sums, the
+// per-head rank-row adjoints of B + b_bias and C + c_bias, and the local
+// suffix sums of the d adt terms and of d theta.
+template <bool VEC4>
+__global__ __launch_bounds__(512, 4) void mimo_chunk_kernel(BwdK p) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const MimoChunkLds ll = mimo_chunk_lds(p.PT, p.NT, p.A, p.RS, p.Qt);
+  const int NS = ll.NS, PS = ll.PS, PP = p.PT * 16, NN = p.NT * 16;
+  float* Kc = lds + ll.o_kc;
+  float* Qc = lds + ll.o_qc;
+  float* X = lds + ll.o_x;
+  float* GY = lds + ll.o_gy;
+  float* DX = lds + ll.o_dx;
+  float* XT = lds + ll.o_xt;
+  float* VV = lds + ll.o_vv;
+  float* MSG = lds + ll.o_msg;
+  float* SQD = lds + ll.o_sqd;
+  float* SGD = lds + ll.o_sgd;
+  float* CS = lds + ll.o_cs;
+  float* SN = lds + ll.o_sn;
+  float* cum = lds + ll.o_sc;
+  float* scl = cum + BQ;
+  float* gam = scl + BQ;
+  float* ec = gam + BQ;
+  float* ex = ec + BQ;
+  float* ds_part = lds + ll.o_part;  // [BQ][PT]
+  float* STG = X;                    // after the products: dQ, then dK [BQ][NS]
+  float* DTH = MSG;                  // after the products: d theta [Qt][A]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bh = blockIdx.x / p.nc, c = blockIdx.x - bh * p.nc;
+  const int b = bh / p.H, h = bh - b * p.H, g = h / (p.H / p.G);
+  const int t0 = c * p.Qt, nv = min(p.Qt, p.L - t0);
+  const int P = p.P, N = p.N, H = p.H, A = p.A, NP = N - A, R = p.R, RS = p.RS, rsl = p.rsl;
+  const float* HEg = p.hs + (size_t)blockIdx.x * P * N;
+  const float* GXg = p.gs + (size_t)blockIdx.x * P * N;
+
+  if (wave == 0) chunk_scalars(p, b, h, t0, nv, ChunkScalars{cum, scl, gam, ec, ex}, lane);
+  load_kq_m(p, b, h, g, t0, nv, Kc, Qc, NS, CS, SN, tid, 512);
+  load_x_m(p, b, h, t0, nv, X, PS, nullptr, XT, tid, 512);
+  for (int it = tid; it < BQ * PP; it += 512) {
+    const int v = it / PP, pp = it - v * PP;
+    GY[v * PS + pp] = pp < P ? p.gyr[((size_t)blockIdx.x * BQ + v) * P + pp] : 0.f;
+  }
+  __syncthreads();
+  const float Dh = p.has_d ? p.d[h] : 0.f;
+  const int r = lane & 15, q = lane >> 4;
+
+  // masked Q K^T (waves 0-3) and gy X^T (waves 4-7), and their same-token blocks
+  {
+    const bool sgx = wave >= 4;
+    const int mt = (wave & 3) >> 1, st = wave & 1;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (!sgx)
+      acc = mm_tile_k4(Qc + mt * 16 * NS, NS, Kc + st * 16 * NS, NS, NN, acc, lane);
+    else
+      acc = mm_tile_k4(GY + mt * 16 * PS, PS, X + st * 16 * PS, PS, PP, acc, lane);
+    const int w = st * 16 + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = mt * 16 + 4 * q + i;
+      const int tv = v >> rsl, tw = w >> rsl;
+      float m, dec;
+      row_masks(tv, tw, cum, scl, gam, &m, &dec);
+      if (!sgx) {
+        VV[v * MS + w] = dec * acc[i];
+        if (tv == tw) SQD[v * RS + (w & (RS - 1))] = acc[i];
+      } else {
+        MSG[v * MS + w] = m * acc[i];
+        if (tv == tw) SGD[v * RS + (w & (RS - 1))] = acc[i];
+      }
+    }
+  }
+  __syncthreads();
+
+  // G K tiles: dX_v = D gy_v + s_t G K_v + lam_t dt_t sum_{w in t} (Q_w . K_v) gy_w
+  const int nY = 2 * p.PT, nQ = 2 * p.NT;
+  for (int job = wave; job < nY; job += 8) {
+    const int mt = job / p.PT, pt = job - mt * p.PT;
+    floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+    const float* Sg = GXg + (size_t)pt * 16 * N;
+    if constexpr (VEC4)
+      a1 = mm_tile_k4_g<8>(Kc + mt * 16 * NS, NS, Sg, N, P - pt * 16, N, NN, a1, lane);
+    else
+      a1 = mm_tile_k1_g<32>(Kc + mt * 16 * NS, NS, Sg, N, P - pt * 16, N, NN, a1, lane);
+    a2 = mm_tile(VV + mt * 16, 1, MS, GY + pt * 16, PS, 1, BQ, a2, lane);
+    const int pp = pt * 16 + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = mt * 16 + 4 * q + i;
+      const int tv = v >> rsl, rv = v & (RS - 1);
+      const float gk = fmaf(ex[tv], a1[i], a2[i]);
+      float same = 0.f;
+      for (int rw = 0; rw < RS; ++rw) {
+        const int w = (tv << rsl) + rw;
+        same = fmaf(SQD[w * RS + rv], GY[w * PS + pp], same);
+      }
+      DX[v * PS + pp] = fmaf(Dh, GY[v * PS + pp], fmaf(scl[tv], gk, gam[tv] * same));
+      const bool ok = tv < nv && rv < R && pp < P;
+      const float part = row16_sum(ok ? X[v * PS + pp] * gk : 0.f);
+      if (r == 15) ds_part[v * p.PT + pt] = part;
+    }
+  }
+  floatx4 res[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int job = wave + 8 * k;
+    res[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (job < 2 * nQ) {
+      const bool isdk = job >= nQ;
+      const int jj = isdk ? job - nQ : job;
+      const int mt = jj / p.NT, nt = jj - mt * p.NT;
+      floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+      const float* Sg = (isdk ? GXg : HEg) + nt * 16;
+      if (!isdk) {
+        a1 = mm_tile_g<32>(GY + mt * 16 * PS, PS, Sg, N, P, N - nt * 16, PP, a1, lane);
+        a2 = mm_tile(MSG + mt * 16 * MS, MS, 1, Kc + nt * 16, NS, 1, BQ, a2, lane);
+      } else {
+        a1 = mm_tile_g<32>(X + mt * 16 * PS, PS, Sg, N, P, N - nt * 16, PP, a1, lane);
+        a2 = mm_tile(MSG + mt * 16, 1, MS, Qc + nt * 16, NS, 1, BQ, a2, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tv = (mt * 16 + 4 * q + i) >> rsl;
+        const float wgt = isdk ? scl[tv] * ex[tv] : ec[tv];
+        res[k][i] = fmaf(wgt, a1[i], a2[i]);
+      }
+    }
+  }
+  __syncthreads();  // DX complete; x, gy, the masks free after this point
+
+  // d x = sum_r mimo_x[h, r] dX_r, and per-chunk partial sums of dX_r * x for d mimo_x
+  for (int it = tid; it < p.Qt * P; it += 512) {
+    const int t = it / P, pp = it - t * P;
+    if (t < nv) {
+      float s = 0.f;
+      for (int rr = 0; rr < R; ++rr) s = fmaf(p.mimo_x[((size_t)h * R + rr) * P + pp], DX[((t << rsl) + rr) * PS + pp], s);
+      p.d_x[(((size_t)b * p.L + t0 + t) * H + h) * P + pp] = s;
+    }
+  }
+  for (int it = tid; it < R * P; it += 512) {
+    const int rr = it / P, pp = it - rr * P;
+    float s = 0.f;
+    for (int t = 0; t < nv; ++t) s = fmaf(DX[((t << rsl) + rr) * PS + pp], XT[t * PS + pp], s);
+    p.mx_part[(size_t)blockIdx.x * R * P + it] = s;
+  }
+
+  // the per-token sums before the masks' region is reused for d theta
+  float e_tok = 0.f, ds_tok = 0.f;
+  if (wave == 0 && lane < nv) {
+    for (int rr = 0; rr < R; ++rr) {
+      const int v = (lane << rsl) + rr;
+      for (int pt = 0; pt < p.PT; ++pt) ds_tok += ds_part[v * p.PT + pt];
+      for (int rw = 0; rw < R; ++rw) {
+        const int w = (lane << rsl) + rw;
+        e_tok = fmaf(SGD[w * RS + rr], SQD[w * RS + rr], e_tok);
+      }
+    }
+    e_tok += ds_tok;
+  }
+
+  // rotation adjoints: queries, then keys, staged through LDS
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int job = wave + 8 * k;
+      if (job < 2 * nQ && (job >= nQ) == (pass == 1)) {
+        const int jj = pass ? job - nQ : job;
+        const int mt = jj / p.NT, nt = jj - mt * p.NT;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) STG[(mt * 16 + 4 * q + i) * NS + nt * 16 + r] = res[k][i];
+      }
+    }
+    __syncthreads();
+    const float* Rw = pass ? Kc : Qc;
+    float* dst = pass ? p.db_head : p.dc_head;
+    for (int it = tid; it < p.Qt * NP; it += 512) {
+      const int t = it / NP, j = it - t * NP;
+      if (t >= nv) {
+        if (j < A && pass == 0) DTH[t * A + j] = 0.f;
+        continue;
+      }
+      float dth = 0.f;
+      for (int rr = 0; rr < R; ++rr) {
+        const int v = (t << rsl) + rr;
+        const size_t o = ((((size_t)b * p.L + t0 + t) * H + h) * R + rr) * N;
+        if (j < A) {
+          const float cs = CS[v * A + j], sn = SN[v * A + j];
+          const float d0 = STG[v * NS + j], d1 = STG[v * NS + j + A];
+          dth += d1 * Rw[v * NS + j] - d0 * Rw[v * NS + j + A];
+          dst[o + j] = d0 * cs + d1 * sn;
+          dst[o + j + A] = d1 * cs - d0 * sn;
+        } else {
+          dst[o + j + A] = STG[v * NS + j + A];
+        }
+      }
+      if (j < A) DTH[t * A + j] = pass ? DTH[t * A + j] + dth : dth;
+    }
+  }
+  __syncthreads();
+
+  // chunk-local suffix sums over the tokens
+  if (wave == 0) {
+    float phi = 0.f;
+    if (lane < nv) {
+      const size_t ri = (size_t)bh * p.L + t0 + lane;
+      phi = p.rho[ri] - (scl[lane] - gam[lane]) * ds_tok - gam[lane] * e_tok;
+      p.dsv[ri] = ds_tok;
+      p.ev[ri] = e_tok;
+    }
+    const float loc = suffix_sum<32>(lane < 32 ? phi : 0.f, lane);
+    if (lane < nv) p.d_adt[((size_t)b * p.L + t0 + lane) * H + h] = loc;
+    if (lane == 0) p.phi_tot[blockIdx.x] = loc;
+  } else if (tid >= 64 && tid < 64 + A) {
+    const int a = tid - 64;
+    float s = 0.f;
+    float* dstp = p.dtheta + ((size_t)bh * p.L + t0) * A + a;
+    for (int t = nv - 1; t >= 0; --t) {
+      s += DTH[t * A + a];
+      dstp[(size_t)t * A] = s;
+    }
+    p.th_tot[(size_t)blockIdx.x * A + a] = s;
+  }
+}
+
+// (M10) mimo_x / mimo_z / mimo_o / norm_weight gradients: sums of the chunk
+// partials over batch and chunks in a fixed order (32 strided partial sums
+// per output, then a tree).
+__global__ __launch_bounds__(256) void mimo_weights_kernel(BwdK p) {
+  __shared__ float red[32][9];
+  const int RP = p.R * p.P, HRP = p.H * RP;
+  const int tid = threadIdx.x, o = tid & 7, part = tid >> 3;
+  const int i = blockIdx.x * 8 + o;  // [mx | mz | mo] x [H][R][P], then nw [H][P]
+  const int per = p.B * p.nc;
+  float s = 0.f;
+  int which = -1, h = 0, rem = 0;
+  if (i < 3 * HRP) {
+    which = i / HRP;
+    const int k = i - which * HRP;
+    h = k / RP;
+    rem = k - h * RP;
+    const float* src = which == 0 ? p.mx_part : which == 1 ? p.mz_part : p.mo_part;
+    for (int k2 = part; k2 < per; k2 += 32) {
+      const int bb = k2 / p.nc, cc = k2 - bb * p.nc;
+      s += src[(((size_t)bb * p.H + h) * p.nc + cc) * RP + rem];
+    }
+  } else if (i < 3 * HRP + p.H * p.P) {
+    which = 3;
+    const int k = i - 3 * HRP;
+    h = k / p.P;
+    rem = k - h * p.P;
+    for (int k2 = part; k2 < per; k2 += 32) {
+      const int bb = k2 / p.nc, cc = k2 - bb * p.nc;
+      s += p.nw_part[(((size_t)bb * p.H + h) * p.nc + cc) * p.P + rem];
+    }
+  }
+  red[part][o] = s;
+  __syncthreads();
+  for (int w = 16; w > 0; w >>= 1) {
+    if (part < w) red[part][o] += red[part + w][o];
+    __syncthreads();
+  }
+  if (part == 0 && which >= 0) {
+    const float v = red[0][o];
+    if (which == 0) p.d_mimo_x[(size_t)h * RP + rem] = v;
+    else if (which == 1) p.d_mimo_z[(size_t)h * RP + rem] = p.has_z ? v : 0.f;
+    else if (which == 2) p.d_mimo_o[(size_t)h * RP + rem] = v;
+    else p.d_norm_weight[(size_t)h * p.P + rem] = p.has_norm ? v : 0.f;
+  }
+}
+
 struct BwdLayout {
   size_t theta, tpre, hs, gs, decay, dtheta, dbh, dch, dsv, ev, phi, th, ddp, bias, total;
   int nc, nT, nrb;
@@ -905,9 +1560,9 @@ size_t summary_lds_bytes(int PT, int NT) {
 }
 
 size_t group_lds_bytes(const ScanGeom& g) {
-  const int HG = (int)(g.H / g.G), N = (int)g.N;
-  const int nact = std::min(std::max(1, 256 / N), HG);
-  return (size_t)(2 * HG * N + nact * 2 * N) * sizeof(float);
+  const int HG = (int)(g.H / g.G), RN = (int)(g.R * g.N);
+  const int nact = std::min(std::max(1, 256 / RN), HG);
+  return (size_t)(2 * HG * RN + nact * 2 * RN) * sizeof(float);
 }
 
 void raise_lds(const void* fn, size_t bytes) {
@@ -945,6 +1600,7 @@ hipError_t launch_siso_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOp
   k.dd_part = ws + w.ddp; k.bias_part = ws + w.bias;
   k.B = (int)g.B; k.L = (int)g.L; k.H = (int)g.H; k.G = (int)g.G; k.P = (int)g.P; k.N = (int)g.N;
   k.A = (int)g.A; k.has_z = (int)g.has_z; k.has_d = (int)g.has_d;
+  k.R = 1; k.RS = 1; k.rsl = 0; k.Qt = BQ;
   k.nc = w.nc; k.nT = w.nT; k.NT = (int)((g.N + 15) / 16); k.PT = (int)((g.P + 15) / 16); k.nrb = w.nrb;
   const unsigned BH = g.B * g.H;
   hipError_t e;
@@ -959,7 +1615,7 @@ hipError_t launch_siso_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOp
   hipLaunchKernelGGL(bwd_summary_kernel, dim3(BH * w.nc), dim3(512), sl, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned pnb = (g.P * g.N + 255) / 256;
-  hipLaunchKernelGGL(bwd_prefix_kernel, dim3(pnb * BH), dim3(256), 0, stream, k, (int)pnb);
+  hipLaunchKernelGGL(bwd_prefix_kernel, dim3(pnb * BH), dim3(256), 0, stream, k, (int)pnb, 3);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t cl = (size_t)chunk_lds(k.PT, k.NT, k.A).total * sizeof(float);
   if ((g.N & 3u) == 0) {
@@ -980,6 +1636,157 @@ hipError_t launch_siso_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOp
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned nb = (2u * g.H * g.N + g.H + 7u) / 8u;
   hipLaunchKernelGGL(bwd_bias_kernel, dim3(nb), dim3(256), 0, stream, k);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (g.A > 0) {
+    const size_t tot = (size_t)g.B * g.L * g.A;
+    hipLaunchKernelGGL(bwd_angle_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream, k);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace m3
+
+namespace m3 {
+namespace {
+
+struct MimoLayout {
+  size_t theta, tpre, hs, gs, decay, dtheta, dbh, dch, gyr, rho, dsv, ev, phi, th, ddp, mx, mz, mo, nw, bias, total;
+  int RS, rsl, Qt, nc, nT, nrb;
+};
+
+MimoLayout mimo_layout(const ScanGeom& g) {
+  MimoLayout w{};
+  w.RS = 1;
+  while (w.RS < (int)g.R) w.RS <<= 1;
+  w.rsl = 0;
+  while ((1 << w.rsl) < w.RS) ++w.rsl;
+  w.Qt = BQ / w.RS;
+  const size_t BH = (size_t)g.B * g.H;
+  w.nc = (int)((g.L + w.Qt - 1) / w.Qt);
+  w.nT = (int)((g.L + TT - 1) / TT);
+  w.nrb = (int)(((size_t)g.B * g.L + RB - 1) / RB);
+  const size_t nch = BH * w.nc;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off += (n + 63) / 64 * 64;
+    return o;
+  };
+  w.theta = take(BH * g.L * g.A);
+  w.tpre = take(BH * w.nT * g.A);
+  w.hs = take(nch * g.P * g.N);
+  w.gs = take(nch * g.P * g.N);
+  w.decay = take(nch);
+  w.dtheta = take(BH * g.L * g.A);
+  w.dbh = take((size_t)g.B * g.L * g.H * g.R * g.N);
+  w.dch = take((size_t)g.B * g.L * g.H * g.R * g.N);
+  w.gyr = take(nch * BQ * g.P);
+  w.rho = take(BH * g.L);
+  w.dsv = take(BH * g.L);
+  w.ev = take(BH * g.L);
+  w.phi = take(nch);
+  w.th = take(nch * g.A);
+  w.ddp = take(nch);
+  w.mx = take(nch * g.R * g.P);
+  w.mz = take(nch * g.R * g.P);
+  w.mo = take(nch * g.R * g.P);
+  w.nw = take(nch * g.P);
+  w.bias = take((size_t)w.nrb * 2 * g.H * g.R * g.N);
+  w.total = off;
+  return w;
+}
+
+size_t mimo_summary_lds(int PT, int NT) {
+  const int NS = NT * 16 + 4, PS = PT * 16 + 4;
+  return (size_t)(2 * BQ * NS + BQ * PS + 6 * BQ) * sizeof(float);
+}
+
+size_t mimo_post_lds(int PT, int NT, int RS) {
+  const int NS = NT * 16 + 4, PS = PT * 16 + 4;
+  return (size_t)(2 * BQ * NS + 3 * BQ * PS + BQ * MS + 8 * RS * PT * 16 + 5 * BQ) * sizeof(float);
+}
+
+}  // namespace
+
+size_t mimo_bwd_workspace_floats(const ScanGeom& g) { return mimo_layout(g).total; }
+
+bool mimo_bwd_fits(const ScanGeom& g) {
+  const MimoLayout w = mimo_layout(g);
+  const int PT = (int)((g.P + 15) / 16), NT = (int)((g.N + 15) / 16);
+  const size_t lim = 160 * 1024;
+  const size_t chunk = (size_t)mimo_chunk_lds(PT, NT, (int)g.A, w.RS, w.Qt).total * sizeof(float);
+  return w.RS <= 8 && chunk <= lim && mimo_post_lds(PT, NT, w.RS) <= lim && mimo_summary_lds(PT, NT) <= lim &&
+         group_lds_bytes(g) <= lim;
+}
+
+hipError_t launch_mimo_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOperands& go, void* workspace,
+                           hipStream_t stream) {
+  const MimoLayout w = mimo_layout(g);
+  float* ws = static_cast<float*>(workspace);
+  BwdK k{};
+  k.dout = go.dout;
+  k.c = o.c; k.b = o.b; k.x = o.x; k.z = o.z; k.adt = o.adt; k.dt = o.dt; k.trap = o.trap;
+  k.angle = o.angle; k.c_bias = o.c_bias; k.b_bias = o.b_bias; k.d = o.d;
+  k.mimo_x = o.mimo_x; k.mimo_z = o.mimo_z; k.mimo_o = o.mimo_o; k.norm_weight = o.norm_weight;
+  k.d_c = go.d_c; k.d_b = go.d_b; k.d_x = go.d_x; k.d_z = go.d_z; k.d_adt = go.d_adt; k.d_dt = go.d_dt;
+  k.d_trap = go.d_trap; k.d_angle = go.d_angle; k.d_c_bias = go.d_c_bias; k.d_b_bias = go.d_b_bias;
+  k.d_d = go.d_d;
+  k.d_mimo_x = go.d_mimo_x; k.d_mimo_z = go.d_mimo_z; k.d_mimo_o = go.d_mimo_o;
+  k.d_norm_weight = go.d_norm_weight;
+  k.theta = ws + w.theta; k.tpre = ws + w.tpre; k.hs = ws + w.hs; k.gs = ws + w.gs; k.decay = ws + w.decay;
+  k.dtheta = ws + w.dtheta; k.db_head = ws + w.dbh; k.dc_head = ws + w.dch; k.gyr = ws + w.gyr;
+  k.rho = ws + w.rho; k.dsv = ws + w.dsv; k.ev = ws + w.ev; k.phi_tot = ws + w.phi; k.th_tot = ws + w.th;
+  k.dd_part = ws + w.ddp; k.mx_part = ws + w.mx; k.mz_part = ws + w.mz; k.mo_part = ws + w.mo;
+  k.nw_part = ws + w.nw; k.bias_part = ws + w.bias;
+  k.B = (int)g.B; k.L = (int)g.L; k.H = (int)g.H; k.G = (int)g.G; k.P = (int)g.P; k.N = (int)g.N;
+  k.A = (int)g.A; k.has_z = (int)g.has_z; k.has_d = (int)g.has_d; k.has_norm = (int)g.has_norm;
+  k.R = (int)g.R; k.RS = w.RS; k.rsl = w.rsl; k.Qt = w.Qt;
+  k.nc = w.nc; k.nT = w.nT; k.NT = (int)((g.N + 15) / 16); k.PT = (int)((g.P + 15) / 16); k.nrb = w.nrb;
+  const unsigned BH = g.B * g.H;
+  const unsigned nch = BH * (unsigned)w.nc;
+  hipError_t e;
+  if (g.A > 0) {
+    hipLaunchKernelGGL(bwd_theta_local_kernel, dim3(BH * w.nT), dim3(64), 0, stream, k);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_theta_scan_kernel, dim3(BH * g.A), dim3(64), 0, stream, k);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const size_t sl = mimo_summary_lds(k.PT, k.NT);
+  raise_lds(reinterpret_cast<const void*>(&mimo_summary_kernel), sl);
+  hipLaunchKernelGGL(mimo_summary_kernel, dim3(nch), dim3(512), sl, stream, k);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned pnb = (g.P * g.N + 255) / 256;
+  hipLaunchKernelGGL(bwd_prefix_kernel, dim3(pnb * BH), dim3(256), 0, stream, k, (int)pnb, 1);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t pl = mimo_post_lds(k.PT, k.NT, w.RS);
+  raise_lds(reinterpret_cast<const void*>(&mimo_post_kernel), pl);
+  hipLaunchKernelGGL(mimo_post_kernel, dim3(nch), dim3(512), pl, stream, k);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_prefix_kernel, dim3(pnb * BH), dim3(256), 0, stream, k, (int)pnb, 2);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t cl = (size_t)mimo_chunk_lds(k.PT, k.NT, k.A, w.RS, w.Qt).total * sizeof(float);
+  if ((g.N & 3u) == 0) {
+    raise_lds(reinterpret_cast<const void*>(&mimo_chunk_kernel<true>), cl);
+    hipLaunchKernelGGL(mimo_chunk_kernel<true>, dim3(nch), dim3(512), cl, stream, k);
+  } else {
+    raise_lds(reinterpret_cast<const void*>(&mimo_chunk_kernel<false>), cl);
+    hipLaunchKernelGGL(mimo_chunk_kernel<false>, dim3(nch), dim3(512), cl, stream, k);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_chunk_scan_kernel, dim3(BH * (g.A + 1)), dim3(64), 0, stream, k);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_apply_kernel, dim3(nch), dim3(256), 0, stream, k);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t gl = group_lds_bytes(g);
+  raise_lds(reinterpret_cast<const void*>(&bwd_group_kernel), gl);
+  hipLaunchKernelGGL(bwd_group_kernel, dim3(w.nrb, g.G), dim3(256), gl, stream, k);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned nb = (2u * g.H * g.R * g.N + g.H + 7u) / 8u;
+  hipLaunchKernelGGL(bwd_bias_kernel, dim3(nb), dim3(256), 0, stream, k);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned nwb = (3u * g.H * g.R * g.P + g.H * g.P + 7u) / 8u;
+  hipLaunchKernelGGL(mimo_weights_kernel, dim3(nwb), dim3(256), 0, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (g.A > 0) {
     const size_t tot = (size_t)g.B * g.L * g.A;

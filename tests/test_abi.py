@@ -26,6 +26,7 @@ def test_library_exports_every_header_function():
     names = m3.header_functions()
     assert set(names) >= {"m3_preprocess", "m3_siso_fwd", "m3_mimo_fwd", "m3_siso_step",
                           "m3_mimo_step", "m3_siso_bwd", "m3_preprocess_bwd", "m3_siso_fwd_packed",
+                          "m3_mimo_bwd", "m3_mimo_bwd_workspace_bytes",
                           "m3_siso_bwd_workspace_bytes", "m3_last_error", "m3_siso_fwd_workspace_bytes",
                           "m3_mimo_fwd_workspace_bytes", "m3_version"}
     L = _lib()
@@ -226,6 +227,32 @@ def test_siso_bwd_rules():
     assert L.m3_siso_bwd(*[FAKE] * 12, big, *[FAKE] * 11, FAKE, 1 << 40, None) == bd.M3_ERR_UNSUPPORTED
     assert "LDS" in m3.last_error()
     assert L.m3_siso_bwd_workspace_bytes(big) > 0
+
+
+def test_mimo_bwd_rules():
+    L = _lib()
+    cfg = bd.c_ssm(_ssm(mimo_rank=3, has_output_norm=True))
+    need = L.m3_mimo_bwd_workspace_bytes(cfg)
+    assert need > 0
+    call = lambda p, c, ws=FAKE, nb=need: L.m3_mimo_bwd(*p[:16], c, *p[16:], ws, nb, None)
+    for i in range(31):  # every operand and gradient except angle (8) and d_angle (23)
+        if i in (8, 23):
+            continue
+        p = [FAKE] * 31
+        p[i] = None
+        assert call(p, cfg) == INVALID, i
+    for i in (8, 23):
+        p = [FAKE] * 31
+        p[i] = None
+        assert call(p, cfg) == INVALID
+    assert call([FAKE] * 31, cfg, nb=need - 1) == INVALID
+    assert "workspace" in m3.last_error()
+    assert call([FAKE] * 31, cfg, ws=None) == INVALID
+    for bad in (dict(mimo_rank=0), dict(mimo_rank=9), dict(head_dim=129), dict(num_groups=3)):
+        assert call([FAKE] * 31, bd.c_ssm(_ssm(**bad))) == INVALID, bad
+        assert L.m3_mimo_bwd_workspace_bytes(bd.c_ssm(_ssm(**bad))) == 0
+    big = bd.c_ssm(_ssm(num_heads=256, num_groups=1, state_size=128, mimo_rank=4))
+    assert call([FAKE] * 31, big, nb=1 << 40) == bd.M3_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("bad", PRE_BAD)
