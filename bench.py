@@ -14,8 +14,9 @@ region it also measures the other rows of the path at their own workloads
 ("rows"): the decode step at B256 H32 (1 token per step, HBM-bound), the
 rank-4 MIMO decode step at the same geometry, the MIMO scan at
 B8 L4096 H32 R4 (FP32-matrix-bound), the SISO backward at the step's
-geometry and the preprocess backward over its packed projection, and the
-step's preprocess and scan fused into one call on the packed rows.
+geometry, the MIMO backward at the MIMO scan's geometry, the preprocess
+backward over the step's packed projection, and the step's preprocess and
+scan fused into one call on the packed rows.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
 """
@@ -257,7 +258,41 @@ def measure_rows(torch, m3, lib, hip, new_event, dev):
                         "workspace_bytes": ws.numel(), "calls_timed": n_calls}
     del ins, dout, grads, ws
 
+    # MIMO backward at the MIMO scan's geometry
+    w = WORKLOADS["mimo_b8_l4096_r4"]
+    d = w.dims
+    ins = {k: torch.from_numpy(v).to(dev) for k, v in ssm_inputs(d, seed=w.seed, dt_range=w.dt_range).items()}
+    dout = torch.from_numpy(output_gradient(d, seed=w.seed)).to(dev)
+    cfg = m3.SsmConfig(d.B, d.L, d.H, d.G, d.P, d.N, d.A, d.R, True, True, True)
+    names15 = ops11 + ("mimo_x", "mimo_z", "mimo_o", "norm_weight")
+    grads = {k: torch.empty_like(ins[k]) for k in names15}
+    ws = torch.empty(m3.mimo_bwd_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+
+    def one_mb():
+        m3.m3_mimo_bwd(dout, *[ins[k] for k in names15], cfg, grads=grads, workspace=ws)
+    for _ in range(2):
+        one_mb()
+    torch.cuda.synchronize()
+    n_calls = 5
+    a.record()
+    for _ in range(n_calls):
+        one_mb()
+    b.record()
+    torch.cuda.synchronize()
+    mbm = a.elapsed_time(b) / n_calls
+    Bm, Lm, Hm, Pm, Nm, Rm = d.B, d.L, d.H, d.P, d.N, d.R
+    # 12 R N P per token-head: as the SISO backward, with the rank sums
+    mflops = 12 * Rm * Nm * Pm * Bm * Lm * Hm
+    rows["mimo_bwd"] = {"workload": "mimo_b8_l4096_r4: B8 L4096 H32 P64 N128 A32 R4, output norm, dout ~ N(0,1)",
+                        "call_ms": mbm, "tokens_per_s": Bm * Lm / (mbm * 1e-3), "min_flops": mflops,
+                        "fp32_tflops": mflops / (mbm * 1e-3) / 1e12,
+                        "fp32_frac": mflops / (mbm * 1e-3) / 1e12 / FP32_PEAK_TFLOPS,
+                        "workspace_bytes": ws.numel(), "calls_timed": n_calls}
+    del ins, dout, grads, ws
+
     # preprocess backward over the [8192 x 3432] packed projection, all eight output gradients
+    w = WORKLOADS["siso_b4_l2048"]
+    d = w.dims
     pk = packed_projection(d, seed=w.seed)
     I, M = d.H * d.P, d.groups * d.N
     pcfg = m3.PreprocessConfig(I, d.N, d.H, d.A, d.groups, 1, 1e-5, 1e-3, 0.1, 1e-4)

@@ -1010,8 +1010,11 @@ __device__ __forceinline__ float wave_sum(float v) { return read_lane_f(scan64_f
 // (M4) Per chunk: the per-rank read-outs y_v = e^cum_t Q_v h'_e^T + (M o Q K^T) X,
 // then the MIMO epilogue's adjoint per token (mimo_o, output norm, gate, D):
 // gy_v (stored), d_z, rho_t and per-chunk partial sums of the weight
-// gradients; last the reverse summary sum_v e^cum_t gy_v Q_v^T.
-__global__ __launch_bounds__(512) void mimo_post_kernel(BwdK p) {
+// gradients; last the reverse summary sum_v e^cum_t gy_v Q_v^T.  The
+// per-rank weights and the chunk's dout / z rows are staged in LDS with the
+// other operands, so the epilogue loop waits on no memory.
+template <bool VEC4, int RSC>
+__global__ __launch_bounds__(512, 4) void mimo_post_kernel(BwdK p) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int NS = p.NT * 16 + 4, PS = p.PT * 16 + 4, PP = p.PT * 16, NN = p.NT * 16;
   float* Kc = lds;
@@ -1021,7 +1024,12 @@ __global__ __launch_bounds__(512) void mimo_post_kernel(BwdK p) {
   float* GY = Y + BQ * PS;
   float* MQK = GY + BQ * PS;
   float* red = MQK + BQ * MS;        // [8][RS P] cross-wave partials
-  float* cum = red + 8 * p.RS * PP;
+  float* WZ = red + 8 * p.RS * PP;   // mimo_z [R][P]
+  float* WO = WZ + p.R * p.P;        // mimo_o [R][P]
+  float* WN = WO + p.R * p.P;        // norm_weight [P]
+  float* GO = WN + p.P;              // dout of the chunk's tokens [Qt][P]
+  float* ZT = GO + p.Qt * p.P;       // z of the chunk's tokens [Qt][P]
+  float* cum = ZT + p.Qt * p.P;
   float* scl = cum + BQ;
   float* gam = scl + BQ;
   float* ec = gam + BQ;
@@ -1035,6 +1043,17 @@ __global__ __launch_bounds__(512) void mimo_post_kernel(BwdK p) {
   if (wave == 0) chunk_scalars(p, b, h, t0, nv, ChunkScalars{cum, scl, gam, ec, ex}, lane);
   load_kq_m(p, b, h, g, t0, nv, Kc, Qc, NS, nullptr, nullptr, tid, blockDim.x);
   load_x_m(p, b, h, t0, nv, X, PS, nullptr, nullptr, tid, blockDim.x);
+  for (int i = tid; i < R * P; i += blockDim.x) {
+    WZ[i] = p.has_z ? p.mimo_z[(size_t)h * R * P + i] : 0.f;
+    WO[i] = p.mimo_o[(size_t)h * R * P + i];
+  }
+  for (int i = tid; i < P; i += blockDim.x) WN[i] = p.has_norm ? p.norm_weight[(size_t)h * P + i] : 0.f;
+  for (int i = tid; i < p.Qt * P; i += blockDim.x) {
+    const int t = i / P, pp = i - t * P;
+    const size_t gi = (((size_t)b * p.L + t0 + min(t, nv - 1)) * H + h) * P + pp;
+    GO[i] = t < nv ? p.dout[gi] : 0.f;
+    ZT[i] = (t < nv && p.has_z) ? p.z[gi] : 0.f;
+  }
   __syncthreads();
   const int r = lane & 15, q = lane >> 4;
   if (wave < 4) {  // masked Q K^T
@@ -1054,7 +1073,10 @@ __global__ __launch_bounds__(512) void mimo_post_kernel(BwdK p) {
   for (int job = wave; job < 2 * p.PT; job += nw) {  // y tiles
     const int mt = job / p.PT, pt = job - mt * p.PT;
     floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-    a1 = mm_tile_k1_g<32>(Qc + mt * 16 * NS, NS, HEg + (size_t)pt * 16 * N, N, P - pt * 16, N, NN, a1, lane);
+    if constexpr (VEC4)
+      a1 = mm_tile_k4_g<8>(Qc + mt * 16 * NS, NS, HEg + (size_t)pt * 16 * N, N, P - pt * 16, N, NN, a1, lane);
+    else
+      a1 = mm_tile_k1_g<32>(Qc + mt * 16 * NS, NS, HEg + (size_t)pt * 16 * N, N, P - pt * 16, N, NN, a1, lane);
     a2 = mm_tile(MQK + mt * 16 * MS, MS, 1, X + pt * 16, PS, 1, BQ, a2, lane);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1066,9 +1088,9 @@ __global__ __launch_bounds__(512) void mimo_post_kernel(BwdK p) {
 
   // epilogue adjoint: wave w owns tokens w, w + 8, ...; lanes over head_dim (two per lane)
   const float Dh = p.has_d ? p.d[h] : 0.f;
-  float mo_acc[8][2], mz_acc[8][2], nw_acc[2] = {0.f, 0.f}, dd_acc = 0.f;
+  float mo_acc[RSC][2], mz_acc[RSC][2], nw_acc[2] = {0.f, 0.f}, dd_acc = 0.f;
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) mo_acc[rr][0] = mo_acc[rr][1] = mz_acc[rr][0] = mz_acc[rr][1] = 0.f;
+  for (int rr = 0; rr < RSC; ++rr) mo_acc[rr][0] = mo_acc[rr][1] = mz_acc[rr][0] = mz_acc[rr][1] = 0.f;
   for (int t = wave; t < p.Qt; t += nw) {
     const bool tok = t < nv;
     const size_t ti = (((size_t)b * p.L + t0 + min(t, nv - 1)) * H + h) * P;
@@ -1076,12 +1098,11 @@ __global__ __launch_bounds__(512) void mimo_post_kernel(BwdK p) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int pp = lane + 64 * k;
-      go[k] = (tok && pp < P) ? p.dout[ti + pp] : 0.f;
-      zv[k] = (tok && pp < P && p.has_z) ? p.z[ti + pp] : 0.f;
+      go[k] = pp < P ? GO[t * P + pp] : 0.f;
+      zv[k] = pp < P ? ZT[t * P + pp] : 0.f;
     }
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      if (rr >= p.RS) break;
+    for (int rr = 0; rr < RSC; ++rr) {
       const int v = (t << rsl) + rr;
       const bool ok = tok && rr < R;
       float y2[2], y3[2], sil[2], u[2], y1v[2];
@@ -1091,7 +1112,7 @@ __global__ __launch_bounds__(512) void mimo_post_kernel(BwdK p) {
         const bool in = ok && pp < P;
         y1v[k] = in ? Y[v * PS + pp] : 0.f;
         y2[k] = fmaf(Dh, in ? X[v * PS + pp] : 0.f, y1v[k]);
-        const float mz = in && p.has_z ? p.mimo_z[((size_t)h * R + rr) * P + pp] : 0.f;
+        const float mz = in ? WZ[rr * P + pp] : 0.f;
         u[k] = zv[k] * mz;
         sil[k] = p.has_z ? siluf_acc(u[k]) : 1.f;
         y3[k] = y2[k] * sil[k];
@@ -1104,14 +1125,14 @@ __global__ __launch_bounds__(512) void mimo_post_kernel(BwdK p) {
         for (int k = 0; k < 2; ++k) {
           const int pp = lane + 64 * k;
           yn[k] = y3[k] * rinv;
-          nwv[k] = (ok && pp < P) ? p.norm_weight[(size_t)h * P + pp] : 0.f;
+          nwv[k] = (ok && pp < P) ? WN[pp] : 0.f;
         }
       }
       float g4[2], g3[2];
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int pp = lane + 64 * k;
-        const float mo = (ok && pp < P) ? p.mimo_o[((size_t)h * R + rr) * P + pp] : 0.f;
+        const float mo = (ok && pp < P) ? WO[rr * P + pp] : 0.f;
         const float y4 = p.has_norm ? yn[k] * nwv[k] : y3[k];
         mo_acc[rr][k] = fmaf(go[k], y4, mo_acc[rr][k]);
         g4[k] = go[k] * mo;
@@ -1136,7 +1157,7 @@ __global__ __launch_bounds__(512) void mimo_post_kernel(BwdK p) {
         float g2 = g3[k];
         if (p.has_z) {
           const float du = g3[k] * y2[k] * dsilu_acc(u[k]);
-          const float mz = (ok && pp < P) ? p.mimo_z[((size_t)h * R + rr) * P + pp] : 0.f;
+          const float mz = (ok && pp < P) ? WZ[rr * P + pp] : 0.f;
           mz_acc[rr][k] = fmaf(du, zv[k], mz_acc[rr][k]);
           dz[k] = fmaf(du, mz, dz[k]);
           g2 = g3[k] * sil[k];
@@ -1164,8 +1185,7 @@ __global__ __launch_bounds__(512) void mimo_post_kernel(BwdK p) {
   for (int which = 0; which < 3; ++which) {
     __syncthreads();
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      if (rr >= p.RS) break;
+    for (int rr = 0; rr < RSC; ++rr) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int pp = lane + 64 * k;
@@ -1702,9 +1722,27 @@ size_t mimo_summary_lds(int PT, int NT) {
   return (size_t)(2 * BQ * NS + BQ * PS + 6 * BQ) * sizeof(float);
 }
 
-size_t mimo_post_lds(int PT, int NT, int RS) {
+template <bool VEC4, int RSC>
+hipError_t launch_post_rs(const BwdK& k, unsigned nch, size_t pl, hipStream_t stream) {
+  raise_lds(reinterpret_cast<const void*>(&mimo_post_kernel<VEC4, RSC>), pl);
+  hipLaunchKernelGGL((mimo_post_kernel<VEC4, RSC>), dim3(nch), dim3(512), pl, stream, k);
+  return hipGetLastError();
+}
+
+template <bool VEC4>
+hipError_t launch_post(const BwdK& k, int RS, unsigned nch, size_t pl, hipStream_t stream) {
+  switch (RS) {
+    case 1: return launch_post_rs<VEC4, 1>(k, nch, pl, stream);
+    case 2: return launch_post_rs<VEC4, 2>(k, nch, pl, stream);
+    case 4: return launch_post_rs<VEC4, 4>(k, nch, pl, stream);
+    default: return launch_post_rs<VEC4, 8>(k, nch, pl, stream);
+  }
+}
+
+size_t mimo_post_lds(int PT, int NT, int RS, int R, int P, int Qt) {
   const int NS = NT * 16 + 4, PS = PT * 16 + 4;
-  return (size_t)(2 * BQ * NS + 3 * BQ * PS + BQ * MS + 8 * RS * PT * 16 + 5 * BQ) * sizeof(float);
+  return (size_t)(2 * BQ * NS + 3 * BQ * PS + BQ * MS + 8 * RS * PT * 16 + 2 * R * P + P + 2 * Qt * P + 5 * BQ) *
+         sizeof(float);
 }
 
 }  // namespace
@@ -1716,7 +1754,7 @@ bool mimo_bwd_fits(const ScanGeom& g) {
   const int PT = (int)((g.P + 15) / 16), NT = (int)((g.N + 15) / 16);
   const size_t lim = 160 * 1024;
   const size_t chunk = (size_t)mimo_chunk_lds(PT, NT, (int)g.A, w.RS, w.Qt).total * sizeof(float);
-  return w.RS <= 8 && chunk <= lim && mimo_post_lds(PT, NT, w.RS) <= lim && mimo_summary_lds(PT, NT) <= lim &&
+  return w.RS <= 8 && chunk <= lim && mimo_post_lds(PT, NT, w.RS, (int)g.R, (int)g.P, w.Qt) <= lim && mimo_summary_lds(PT, NT) <= lim &&
          group_lds_bytes(g) <= lim;
 }
 
@@ -1759,9 +1797,11 @@ hipError_t launch_mimo_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOp
   const unsigned pnb = (g.P * g.N + 255) / 256;
   hipLaunchKernelGGL(bwd_prefix_kernel, dim3(pnb * BH), dim3(256), 0, stream, k, (int)pnb, 1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t pl = mimo_post_lds(k.PT, k.NT, w.RS);
-  raise_lds(reinterpret_cast<const void*>(&mimo_post_kernel), pl);
-  hipLaunchKernelGGL(mimo_post_kernel, dim3(nch), dim3(512), pl, stream, k);
+  const size_t pl = mimo_post_lds(k.PT, k.NT, w.RS, k.R, k.P, w.Qt);
+  if ((g.N & 3u) == 0)
+    e = launch_post<true>(k, w.RS, nch, pl, stream);
+  else
+    e = launch_post<false>(k, w.RS, nch, pl, stream);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_prefix_kernel, dim3(pnb * BH), dim3(256), 0, stream, k, (int)pnb, 2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
