@@ -304,6 +304,121 @@ __device__ void load_xg(const BwdK& p, int b, int h, int t0, int nv, float* X, f
   }
 }
 
+// Chunk geometry: state size N, head_dim P, angle count A and their 16-wide
+// tile counts.  The specialised kernels fix them at compile time (NC > 0), so
+// index division and loop bounds fold to constants.
+struct Geom {
+  int N, P, A, NT, PT;
+};
+
+template <int NC, int PC, int AC>
+__device__ __forceinline__ Geom geom_of(const BwdK& p) {
+  if constexpr (NC > 0)
+    return Geom{NC, PC, AC, (NC + 15) / 16, (PC + 15) / 16};
+  else
+    return Geom{p.N, p.P, p.A, p.NT, p.PT};
+}
+
+__device__ __forceinline__ floatx4 ldg4(const float* q) { return *reinterpret_cast<const floatx4*>(q); }
+__device__ __forceinline__ void sts4(float* q, floatx4 v) { *reinterpret_cast<floatx4*>(q) = v; }
+
+__device__ __forceinline__ float dsilu_fast(float u) {
+  const float s = sigmoid_fast(u);
+  return s * (1.f + u * (1.f - s));
+}
+
+// load_kq with 16-byte accesses, for N and A multiples of 4, N a multiple of
+// 16 (no pad columns), 16-byte aligned operand rows and LDS rows.  An item is
+// four columns of one token: the first BQ A / 4 threads take the rotated
+// pairs (columns j .. j + 3 with their partners j + A ..), then all threads
+// share the plain columns 2 A .. N - 1; branches are wave-uniform when
+// BQ A / 4 is a multiple of 64.  Row offsets within the chunk are 32-bit.
+__device__ __forceinline__ void load_kq4(const BwdK& p, const Geom gm, int b, int h, int g, int t0, int nv,
+                                         float* Kc, float* Qc, int ns, float* cs_l, float* sn_l, int tid) {
+  const int N = gm.N, A = gm.A, A4 = A / 4, NP4 = (N - 2 * A) / 4;
+  const int bh = b * p.H + h, GN = p.G * N;
+  const size_t row0 = ((size_t)b * p.L + t0) * GN + (size_t)g * N;
+  const float* brow = p.b + row0;  // token t0 + t, column n at brow[t * GN + n]
+  const float* crow = p.c + row0;
+  const float* bb = p.b_bias + (size_t)h * N;
+  const float* cb = p.c_bias + (size_t)h * N;
+  if (A > 0) {
+    const float* th = p.theta + ((size_t)bh * p.L + t0) * A;
+    const float* tp = p.tpre + ((size_t)bh * p.nT + t0 / TT) * A;  // a chunk lies inside one tile
+    for (int it = tid; it < BQ * A4; it += 512) {
+      const int t = it / A4, j = 4 * (it - t * A4);
+      const int tc = min(t, nv - 1), ro = tc * GN;
+      const floatx4 th4 = ldg4(th + tc * A + j), tp4 = ldg4(tp + j);
+      const floatx4 b0 = ldg4(brow + ro + j), b1 = ldg4(brow + ro + j + A);
+      const floatx4 c0 = ldg4(crow + ro + j), c1 = ldg4(crow + ro + j + A);
+      const floatx4 bb0 = ldg4(bb + j), bb1 = ldg4(bb + j + A), cb0 = ldg4(cb + j), cb1 = ldg4(cb + j + A);
+      const bool ok = t < nv;
+      floatx4 k0, k1, q0, q1, cs4, sn4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float sn, cs;
+        sincos_acc(th4[e] + tp4[e], &sn, &cs);
+        const float kb0 = b0[e] + bb0[e], kb1 = b1[e] + bb1[e];
+        const float qc0 = c0[e] + cb0[e], qc1 = c1[e] + cb1[e];
+        k0[e] = ok ? kb0 * cs - kb1 * sn : 0.f;
+        k1[e] = ok ? kb0 * sn + kb1 * cs : 0.f;
+        q0[e] = ok ? qc0 * cs - qc1 * sn : 0.f;
+        q1[e] = ok ? qc0 * sn + qc1 * cs : 0.f;
+        cs4[e] = cs;
+        sn4[e] = sn;
+      }
+      sts4(Kc + t * ns + j, k0);
+      sts4(Kc + t * ns + j + A, k1);
+      sts4(Qc + t * ns + j, q0);
+      sts4(Qc + t * ns + j + A, q1);
+      if (cs_l) {
+        sts4(cs_l + t * A + j, cs4);
+        sts4(sn_l + t * A + j, sn4);
+      }
+    }
+  }
+  for (int it = tid; it < BQ * NP4; it += 512) {
+    const int t = it / NP4, n = 2 * A + 4 * (it - t * NP4);
+    const int tc = min(t, nv - 1), ro = tc * GN;
+    const floatx4 b4 = ldg4(brow + ro + n), c4 = ldg4(crow + ro + n);
+    const floatx4 bb4 = ldg4(bb + n), cb4 = ldg4(cb + n);
+    const bool ok = t < nv;
+    floatx4 kv, qv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kv[e] = ok ? b4[e] + bb4[e] : 0.f;
+      qv[e] = ok ? c4[e] + cb4[e] : 0.f;
+    }
+    sts4(Kc + t * ns + n, kv);
+    sts4(Qc + t * ns + n, qv);
+  }
+}
+
+// load_xg with 16-byte accesses, for P a multiple of 16 (no pad columns) and
+// 16-byte aligned rows: item (token, four head_dim columns).
+__device__ __forceinline__ void load_xg4(const BwdK& p, const Geom gm, int b, int h, int t0, int nv, float* X,
+                                         float* GY, int ps, const float* wx, const float* wg, int tid) {
+  const int P = gm.P, P4 = P / 4, HP = p.H * P;
+  const size_t row0 = (((size_t)b * p.L + t0) * p.H + h) * P;  // token t0 + t at row0 + t * HP
+  for (int it = tid; it < BQ * P4; it += 512) {
+    const int t = it / P4, pp = 4 * (it - t * P4);
+    const int o = min(t, nv - 1) * HP + pp;
+    const floatx4 x4 = ldg4(p.x + row0 + o), g4 = ldg4(p.dout + row0 + o);
+    const floatx4 z4 = p.has_z ? ldg4(p.z + row0 + o) : floatx4{0.f, 0.f, 0.f, 0.f};
+    const bool ok = t < nv;
+    const float sx = wx ? wx[t] : 1.f, sg = wg ? wg[t] : 1.f;
+    floatx4 xv, gv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float gy = p.has_z ? g4[e] * silu_fast(z4[e]) : g4[e];
+      xv[e] = ok ? x4[e] * sx : 0.f;
+      gv[e] = ok ? gy * sg : 0.f;
+    }
+    sts4(X + t * ps + pp, xv);
+    sts4(GY + t * ps + pp, gv);
+  }
+}
+
 // (1) Cumulative angle within each 64-token tile and the tile totals; one wave
 // per (b, h, tile), lane a < A.
 __global__ __launch_bounds__(64) void bwd_theta_local_kernel(BwdK p) {
@@ -381,9 +496,12 @@ __device__ void chunk_scalars(const BwdK& p, int b, int h, int t0, int nv, const
 
 // (3) Per chunk: S = sum_s e^(cumx-cum_s) s_s x_s K_s^T and
 // R = sum_r e^(cum_r) gy_r Q_r^T, both [P][N], and the chunk decay e^cumx.
+// NC > 0: geometry fixed at (NC, PC, AC) with the 16-byte loaders.
+template <int NC, int PC, int AC>
 __global__ __launch_bounds__(512) void bwd_summary_kernel(BwdK p) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  const int NS = p.NT * 16 + 4, PS = p.PT * 16 + 4;
+  const Geom gm = geom_of<NC, PC, AC>(p);
+  const int NS = gm.NT * 16 + 4, PS = gm.PT * 16 + 4, P = gm.P, N = gm.N;
   float* Kc = lds;
   float* Qc = Kc + BQ * NS;
   float* Xw = Qc + BQ * NS;
@@ -399,20 +517,26 @@ __global__ __launch_bounds__(512) void bwd_summary_kernel(BwdK p) {
   const int b = bh / p.H, h = bh - b * p.H, g = h / (p.H / p.G);
   const int t0 = c * BQ, nv = min(BQ, p.L - t0);
   if (wave == 0) chunk_scalars(p, b, h, t0, nv, ChunkScalars{cum, scl, gam, ec, ex}, lane);
-  load_kq(p, b, h, g, t0, nv, Kc, Qc, NS, nullptr, nullptr, tid);
+  if constexpr (NC > 0)
+    load_kq4(p, gm, b, h, g, t0, nv, Kc, Qc, NS, nullptr, nullptr, tid);
+  else
+    load_kq(p, b, h, g, t0, nv, Kc, Qc, NS, nullptr, nullptr, tid);
   __syncthreads();
   if (tid < BQ) wx[tid] = ex[tid] * scl[tid];
   __syncthreads();
-  load_xg(p, b, h, t0, nv, Xw, Gw, PS, wx, ec, tid);
+  if constexpr (NC > 0)
+    load_xg4(p, gm, b, h, t0, nv, Xw, Gw, PS, wx, ec, tid);
+  else
+    load_xg(p, b, h, t0, nv, Xw, Gw, PS, wx, ec, tid);
   __syncthreads();
   if (tid == 0) p.decay[blockIdx.x] = expf(cum[BQ - 1]);
-  const int ntile = p.PT * p.NT;
-  const size_t base = (size_t)blockIdx.x * p.P * p.N;
+  const int ntile = gm.PT * gm.NT;
+  const size_t base = (size_t)blockIdx.x * P * N;
   const int r = lane & 15, q = lane >> 4;
   for (int job = wave; job < 2 * ntile; job += nw) {
     const bool rev = job >= ntile;
     const int jt = rev ? job - ntile : job;
-    const int pt = jt / p.NT, nt = jt - pt * p.NT;
+    const int pt = jt / gm.NT, nt = jt - pt * gm.NT;
     // [p][n] = sum_t W[t][p] V[t][n]: A[m=p][k=t] = W[t][p], B[k=t][n] = V[t][n]
     const float* W = rev ? Gw : Xw;
     const float* V = rev ? Qc : Kc;
@@ -423,46 +547,43 @@ __global__ __launch_bounds__(512) void bwd_summary_kernel(BwdK p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pp = pt * 16 + 4 * q + i;
-      if (pp < p.P && n < p.N) dst[(size_t)pp * p.N + n] = acc[i];
+      if (pp < P && n < N) dst[pp * N + n] = acc[i];
     }
   }
 }
 
 // (4) Element-wise over the chunks of one (b, h): hs[c] <- state before chunk
-// c; gs[c] <- adjoint after chunk c.  In place; loads run eight chunks ahead.
-// mode bit 1: forward summaries (hs); bit 2: reverse summaries (gs).
+// c; gs[c] <- adjoint after chunk c.  In place; loads run U chunks ahead.
+// mode 1: forward summaries (hs); 2: reverse summaries (gs); 3: both, one
+// direction per blockIdx.y.  A thread owns V consecutive elements (V = 4:
+// 16-byte accesses, P N a multiple of 4 and 16-byte aligned summaries).
+template <int V>
 __global__ __launch_bounds__(256) void bwd_prefix_kernel(BwdK p, int blocks_per_bh, int mode) {
+  typedef float vec __attribute__((ext_vector_type(V)));
   const int bh = blockIdx.x / blocks_per_bh;
-  const int e = (blockIdx.x - bh * blocks_per_bh) * blockDim.x + threadIdx.x;
+  const int e = ((blockIdx.x - bh * blocks_per_bh) * blockDim.x + threadIdx.x) * V;
   const int PN = p.P * p.N, nc = p.nc;
   if (e >= PN) return;
-  float* hs = p.hs + (size_t)bh * nc * PN + e;
-  float* gs = p.gs + (size_t)bh * nc * PN + e;
+  const bool rev = mode == 2 || (mode == 3 && blockIdx.y == 1);
+  float* base = (rev ? p.gs : p.hs) + (size_t)bh * nc * PN + e;
   const float* dec = p.decay + (size_t)bh * nc;
   constexpr int U = 8;
-  float run = 0.f;
-  for (int c0 = 0; (mode & 1) && c0 < nc; c0 += U) {
-    float v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = c0 + u < nc ? hs[(size_t)(c0 + u) * PN] : 0.f;
+  vec run = (vec)0.f;
+  for (int i0 = 0; i0 < nc; i0 += U) {
+    vec v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (c0 + u < nc) {
-        hs[(size_t)(c0 + u) * PN] = run;
-        run = fmaf(dec[c0 + u], run, v[u]);
-      }
+      const int c = rev ? nc - 1 - (i0 + u) : i0 + u;
+      v[u] = i0 + u < nc ? *reinterpret_cast<const vec*>(base + (size_t)c * PN) : (vec)0.f;
     }
-  }
-  run = 0.f;
-  for (int c1 = nc - 1; (mode & 2) && c1 >= 0; c1 -= U) {
-    float v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = c1 - u >= 0 ? gs[(size_t)(c1 - u) * PN] : 0.f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (c1 - u >= 0) {
-        gs[(size_t)(c1 - u) * PN] = run;
-        run = fmaf(dec[c1 - u], run, v[u]);
+      if (i0 + u < nc) {
+        const int c = rev ? nc - 1 - (i0 + u) : i0 + u;
+        *reinterpret_cast<vec*>(base + (size_t)c * PN) = run;
+        const float dc = dec[c];
+#pragma unroll
+        for (int l = 0; l < V; ++l) run[l] = fmaf(dc, run[l], v[u][l]);
       }
     }
   }
@@ -499,11 +620,18 @@ __host__ __device__ inline ChunkLds chunk_lds(int PT, int NT, int A) {
 // (5) Per chunk: y, GK, dQ, dK on FP32 MFMA; writes d_z, d_x, the per-head
 // adjoints of B + b_bias and C + c_bias, and the chunk-local suffix sums of
 // the d adt terms (into d_adt) and of d theta, with their chunk totals.
-template <bool VEC4>
+// NC > 0: geometry fixed at (NC, PC, AC) = (16 x 8 waves, multiple of 16,
+// multiple of 4 with BQ AC / 4 a multiple of 64), 16-byte loaders and stores,
+// and each wave reuses its state columns for both token halves of dQ and dK.
+template <bool VEC4, int NC, int PC, int AC>
 __global__ __launch_bounds__(512, 4) void bwd_chunk_kernel(BwdK p) {
+  constexpr bool FIX = NC > 0;
+  static_assert(!FIX || (NC == 128 && PC % 16 == 0 && AC % 4 == 0 && (BQ * AC / 4) % 64 == 0),
+                "fixed geometry: N = 128 (one state tile per wave), P a multiple of 16");
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  const ChunkLds ll = chunk_lds(p.PT, p.NT, p.A);
-  const int NS = ll.NS, PS = ll.PS, PP = p.PT * 16, NN = p.NT * 16;
+  const Geom gm = geom_of<NC, PC, AC>(p);
+  const ChunkLds ll = chunk_lds(gm.PT, gm.NT, gm.A);
+  const int NS = ll.NS, PS = ll.PS, PP = gm.PT * 16, NN = gm.NT * 16;
   float* Kc = lds + ll.o_kc;
   float* Qc = lds + ll.o_qc;
   float* X = lds + ll.o_x;
@@ -521,14 +649,16 @@ __global__ __launch_bounds__(512, 4) void bwd_chunk_kernel(BwdK p) {
   float* qk = ex + BQ;
   float* xg = qk + BQ;
   float* rho_part = lds + ll.o_part;        // [BQ][PT]
-  float* ds_part = rho_part + BQ * p.PT;    // [BQ][PT]
+  float* ds_part = rho_part + BQ * gm.PT;   // [BQ][PT]
   float* STG = X;                           // after the products: dQ, then dK [BQ][NS]
   float* DTH = MQK;                         // after the products: d theta [BQ][A]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bh = blockIdx.x / p.nc, c = blockIdx.x - bh * p.nc;
   const int b = bh / p.H, h = bh - b * p.H, g = h / (p.H / p.G);
   const int t0 = c * BQ, nv = min(BQ, p.L - t0);
-  const int P = p.P, N = p.N, H = p.H, A = p.A, NP = N - A;
+  const int P = gm.P, N = gm.N, H = p.H, A = gm.A, NP = N - A;
+  const int HP = H * P;
+  const size_t xrow0 = (((size_t)b * p.L + t0) * H + h) * P;  // token t0 + t, column pp at xrow0 + t HP + pp
 
   // ---- loads: keys/queries, x/gy, scalars (the state and adjoint tiles are
   // read from global memory by the products that use them)
@@ -536,8 +666,13 @@ __global__ __launch_bounds__(512, 4) void bwd_chunk_kernel(BwdK p) {
   const float* GXg = p.gs + (size_t)blockIdx.x * P * N;  // G_x [P][N]
   // VEC4: N % 4 == 0, 16-byte rows: vector loads of the state rows
   if (wave == 0) chunk_scalars(p, b, h, t0, nv, ChunkScalars{cum, scl, gam, ec, ex}, lane);
-  load_kq(p, b, h, g, t0, nv, Kc, Qc, NS, CS, SN, tid);
-  load_xg(p, b, h, t0, nv, X, GY, PS, nullptr, nullptr, tid);
+  if constexpr (FIX) {
+    load_kq4(p, gm, b, h, g, t0, nv, Kc, Qc, NS, CS, SN, tid);
+    load_xg4(p, gm, b, h, t0, nv, X, GY, PS, nullptr, nullptr, tid);
+  } else {
+    load_kq(p, b, h, g, t0, nv, Kc, Qc, NS, CS, SN, tid);
+    load_xg(p, b, h, t0, nv, X, GY, PS, nullptr, nullptr, tid);
+  }
   __syncthreads();
   const float Dh = p.has_d ? p.d[h] : 0.f;
   const int r = lane & 15, q = lane >> 4;
@@ -556,7 +691,7 @@ __global__ __launch_bounds__(512, 4) void bwd_chunk_kernel(BwdK p) {
     for (int i = 0; i < 4; ++i) {
       const int t = mt * 16 + 4 * q + i;
       const float v = acc[i];
-      const float dec = s < t ? expf(cum[t] - cum[s]) : 0.f;
+      const float dec = s < t ? (FIX ? exp_fast(cum[t] - cum[s]) : expf(cum[t] - cum[s])) : 0.f;
       const float m = s < t ? dec * scl[s] : (s == t ? gam[t] : 0.f);
       if (!sgx) {
         MQK[t * MS + s] = m * v;
@@ -571,11 +706,11 @@ __global__ __launch_bounds__(512, 4) void bwd_chunk_kernel(BwdK p) {
   __syncthreads();
 
   // ---- y and GK (per head_dim tile), then dQ and dK (per state tile)
-  const int nY = 2 * p.PT, nQ = 2 * p.NT;
+  const int nY = 2 * gm.PT, nQ = 2 * gm.NT;
   for (int job = wave; job < 2 * nY; job += 8) {
     const bool isgk = job >= nY;
     const int jj = isgk ? job - nY : job;
-    const int mt = jj / p.PT, pt = jj - mt * p.PT;
+    const int mt = jj / gm.PT, pt = jj - mt * gm.PT;
     floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
     const float* Sg = (isgk ? GXg : HEg) + (size_t)pt * 16 * N;
     const int prow = P - pt * 16;
@@ -593,48 +728,53 @@ __global__ __launch_bounds__(512, 4) void bwd_chunk_kernel(BwdK p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = mt * 16 + 4 * q + i;
-      const size_t gi = (((size_t)b * p.L + t0 + min(t, nv - 1)) * H + h) * P + min(pp, P - 1);
-      zv[i] = (!isgk && p.has_z) ? p.z[gi] : 0.f;
-      gov[i] = (!isgk && p.has_z) ? p.dout[gi] : 0.f;
+      const int o = min(t, nv - 1) * HP + min(pp, P - 1);
+      zv[i] = (!isgk && p.has_z) ? p.z[xrow0 + o] : 0.f;
+      gov[i] = (!isgk && p.has_z) ? p.dout[xrow0 + o] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = mt * 16 + 4 * q + i;
       const bool ok = t < nv && pp < P;
-      const size_t gi = (((size_t)b * p.L + t0 + t) * H + h) * P + pp;
+      const size_t gi = xrow0 + t * HP + pp;
       const float xv = X[t * PS + pp], gy = GY[t * PS + pp];
       float part;
       if (!isgk) {
         const float y = fmaf(ec[t], a1[i], a2[i]);
         part = gy * y;
-        if (ok) p.d_z[gi] = p.has_z ? gov[i] * fmaf(Dh, xv, y) * dsilu_acc(zv[i]) : 0.f;
+        if (ok) p.d_z[gi] = p.has_z ? gov[i] * fmaf(Dh, xv, y) * (FIX ? dsilu_fast(zv[i]) : dsilu_acc(zv[i])) : 0.f;
       } else {
         const float gk = fmaf(ex[t], a1[i], a2[i]);
         part = xv * gk;
         if (ok) p.d_x[gi] = fmaf(Dh + gam[t] * qk[t], gy, scl[t] * gk);
       }
       part = row16_sum(ok ? part : 0.f);
-      if (r == 15) (isgk ? ds_part : rho_part)[t * p.PT + pt] = part;
+      if (r == 15) (isgk ? ds_part : rho_part)[t * gm.PT + pt] = part;
     }
   }
   floatx4 res[4];
+  if constexpr (FIX) {
+    // job k of wave w: state columns 16 w .. 16 w + 15, token half k & 1,
+    // dQ (k < 2) or dK; the state columns are loaded once for both halves.
+    const int nt = wave;
+    float sh[PC / 4], sg[PC / 4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int job = wave + 8 * k;
-    res[k] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (job < 2 * nQ) {
-      const bool isdk = job >= nQ;
-      const int jj = isdk ? job - nQ : job;
-      const int mt = jj / p.NT, nt = jj - mt * p.NT;
+    for (int j = 0; j < PC / 4; ++j) {
+      sh[j] = HEg[(4 * j + q) * N + nt * 16 + r];
+      sg[j] = GXg[(4 * j + q) * N + nt * 16 + r];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool isdk = k >= 2;
+      const int mt = k & 1;
       floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-      const float* Sg = (isdk ? GXg : HEg) + nt * 16;
-      if (!isdk) {
-        a1 = mm_tile_g<32>(GY + mt * 16 * PS, PS, Sg, N, P, N - nt * 16, PP, a1, lane);
+      const float* Ar = (isdk ? X : GY) + (mt * 16 + r) * PS + q;  // A[m=t][k=p]
+#pragma unroll
+      for (int j = 0; j < PC / 4; ++j) a1 = mfma16(Ar[4 * j], isdk ? sg[j] : sh[j], a1);
+      if (!isdk)
         a2 = mm_tile(MSG + mt * 16 * MS, MS, 1, Kc + nt * 16, NS, 1, BQ, a2, lane);
-      } else {
-        a1 = mm_tile_g<32>(X + mt * 16 * PS, PS, Sg, N, P, N - nt * 16, PP, a1, lane);
+      else
         a2 = mm_tile(MSG + mt * 16, 1, MS, Qc + nt * 16, NS, 1, BQ, a2, lane);
-      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = mt * 16 + 4 * q + i;
@@ -642,9 +782,37 @@ __global__ __launch_bounds__(512, 4) void bwd_chunk_kernel(BwdK p) {
         res[k][i] = fmaf(w, a1[i], a2[i]);
       }
     }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int job = wave + 8 * k;
+      res[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (job < 2 * nQ) {
+        const bool isdk = job >= nQ;
+        const int jj = isdk ? job - nQ : job;
+        const int mt = jj / gm.NT, nt = jj - mt * gm.NT;
+        floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+        const float* Sg = (isdk ? GXg : HEg) + nt * 16;
+        if (!isdk) {
+          a1 = mm_tile_g<32>(GY + mt * 16 * PS, PS, Sg, N, P, N - nt * 16, PP, a1, lane);
+          a2 = mm_tile(MSG + mt * 16 * MS, MS, 1, Kc + nt * 16, NS, 1, BQ, a2, lane);
+        } else {
+          a1 = mm_tile_g<32>(X + mt * 16 * PS, PS, Sg, N, P, N - nt * 16, PP, a1, lane);
+          a2 = mm_tile(MSG + mt * 16, 1, MS, Qc + nt * 16, NS, 1, BQ, a2, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = mt * 16 + 4 * q + i;
+          const float w = isdk ? scl[t] * ex[t] : ec[t];
+          res[k][i] = fmaf(w, a1[i], a2[i]);
+        }
+      }
+    }
   }
   // ---- rotation adjoints, queries first, then keys: stage the adjoint tiles
   // in LDS, then d theta and the un-rotated adjoints per head
+  const size_t hrow0 = (((size_t)b * p.L + t0) * H + h) * N;  // token t0 + t at hrow0 + t H N
+  const int HN = H * N;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     __syncthreads();  // x, gy, the masks (pass 0) or the staged dQ (pass 1) are free
@@ -653,30 +821,60 @@ __global__ __launch_bounds__(512, 4) void bwd_chunk_kernel(BwdK p) {
       const int job = wave + 8 * k;
       if (job < 2 * nQ && (job >= nQ) == (pass == 1)) {
         const int jj = pass ? job - nQ : job;
-        const int mt = jj / p.NT, nt = jj - mt * p.NT;
+        const int mt = jj / gm.NT, nt = jj - mt * gm.NT;
 #pragma unroll
         for (int i = 0; i < 4; ++i) STG[(mt * 16 + 4 * q + i) * NS + nt * 16 + r] = res[k][i];
       }
     }
     __syncthreads();
     const float* R = pass ? Kc : Qc;
-    float* dst = pass ? p.db_head : p.dc_head;
-    for (int it = tid; it < BQ * NP; it += 512) {
-      const int t = it / NP, j = it - t * NP;
-      if (t >= nv) {
-        if (j < A && pass == 0) DTH[t * A + j] = 0.f;
-        continue;
+    float* dst = (pass ? p.db_head : p.dc_head) + hrow0;
+    if constexpr (FIX) {
+      constexpr int A4 = AC / 4, NP4 = (NC - 2 * AC) / 4;
+      for (int it = tid; it < BQ * A4; it += 512) {
+        const int t = it / A4, j = 4 * (it - t * A4);
+        if (t >= nv) {
+          if (pass == 0) sts4(DTH + t * A + j, floatx4{0.f, 0.f, 0.f, 0.f});
+          continue;
+        }
+        const floatx4 cs = lds_read4(CS + t * A + j), sn = lds_read4(SN + t * A + j);
+        const floatx4 d0 = lds_read4(STG + t * NS + j), d1 = lds_read4(STG + t * NS + j + A);
+        const floatx4 r0 = lds_read4(R + t * NS + j), r1 = lds_read4(R + t * NS + j + A);
+        floatx4 th = pass ? lds_read4(DTH + t * A + j) : floatx4{0.f, 0.f, 0.f, 0.f};
+        floatx4 u0, u1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = d1[e] * r0[e] - d0[e] * r1[e];
+          th[e] = pass ? th[e] + v : v;
+          u0[e] = d0[e] * cs[e] + d1[e] * sn[e];
+          u1[e] = d1[e] * cs[e] - d0[e] * sn[e];
+        }
+        sts4(DTH + t * A + j, th);
+        sts4(dst + t * HN + j, u0);
+        sts4(dst + t * HN + j + A, u1);
       }
-      const size_t o = (((size_t)b * p.L + t0 + t) * H + h) * N;
-      if (j < A) {
-        const float cs = CS[t * A + j], sn = SN[t * A + j];
-        const float d0 = STG[t * NS + j], d1 = STG[t * NS + j + A];
-        const float v = d1 * R[t * NS + j] - d0 * R[t * NS + j + A];
-        DTH[t * A + j] = pass ? DTH[t * A + j] + v : v;
-        dst[o + j] = d0 * cs + d1 * sn;
-        dst[o + j + A] = d1 * cs - d0 * sn;
-      } else {
-        dst[o + j + A] = STG[t * NS + j + A];
+      for (int it = tid; it < BQ * NP4; it += 512) {
+        const int t = it / NP4, n = 2 * AC + 4 * (it - t * NP4);
+        if (t < nv) sts4(dst + t * HN + n, lds_read4(STG + t * NS + n));
+      }
+    } else {
+      for (int it = tid; it < BQ * NP; it += 512) {
+        const int t = it / NP, j = it - t * NP;
+        if (t >= nv) {
+          if (j < A && pass == 0) DTH[t * A + j] = 0.f;
+          continue;
+        }
+        const int o = t * HN;
+        if (j < A) {
+          const float cs = CS[t * A + j], sn = SN[t * A + j];
+          const float d0 = STG[t * NS + j], d1 = STG[t * NS + j + A];
+          const float v = d1 * R[t * NS + j] - d0 * R[t * NS + j + A];
+          DTH[t * A + j] = pass ? DTH[t * A + j] + v : v;
+          dst[o + j] = d0 * cs + d1 * sn;
+          dst[o + j + A] = d1 * cs - d0 * sn;
+        } else {
+          dst[o + j + A] = STG[t * NS + j + A];
+        }
       }
     }
   }
@@ -688,9 +886,9 @@ __global__ __launch_bounds__(512, 4) void bwd_chunk_kernel(BwdK p) {
     float phi = 0.f, xgv = 0.f;
     if (lane < nv) {
       float rh = 0.f, ds = 0.f;
-      for (int pt = 0; pt < p.PT; ++pt) {
-        rh += rho_part[lane * p.PT + pt];
-        ds += ds_part[lane * p.PT + pt];
+      for (int pt = 0; pt < gm.PT; ++pt) {
+        rh += rho_part[lane * gm.PT + pt];
+        ds += ds_part[lane * gm.PT + pt];
       }
       xgv = xg[lane];
       const float e = fmaf(xgv, qk[lane], ds);
@@ -710,7 +908,7 @@ __global__ __launch_bounds__(512, 4) void bwd_chunk_kernel(BwdK p) {
     float* dst = p.dtheta + ((size_t)bh * p.L + t0) * A + a;
     for (int t = nv - 1; t >= 0; --t) {
       s += DTH[t * A + a];
-      dst[(size_t)t * A] = s;
+      dst[t * A] = s;
     }
     p.th_tot[(size_t)blockIdx.x * A + a] = s;
   }
@@ -1585,6 +1783,21 @@ size_t group_lds_bytes(const ScanGeom& g) {
   return (size_t)(2 * HG * RN + nact * 2 * RN) * sizeof(float);
 }
 
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0u; }
+
+// The chunk prefix (4) over the summaries of mode (1: hs, 2: gs, 3: both).
+hipError_t launch_prefix(const ScanGeom& g, const BwdK& k, int mode, const void* workspace, hipStream_t stream) {
+  const unsigned BH = g.B * g.H, PN = g.P * g.N, ndir = mode == 3 ? 2u : 1u;
+  if (PN % 4u == 0 && aligned16(workspace)) {
+    const unsigned nb = (PN / 4u + 255u) / 256u;
+    hipLaunchKernelGGL(bwd_prefix_kernel<4>, dim3(nb * BH, ndir), dim3(256), 0, stream, k, (int)nb, mode);
+  } else {
+    const unsigned nb = (PN + 255u) / 256u;
+    hipLaunchKernelGGL(bwd_prefix_kernel<1>, dim3(nb * BH, ndir), dim3(256), 0, stream, k, (int)nb, mode);
+  }
+  return hipGetLastError();
+}
+
 void raise_lds(const void* fn, size_t bytes) {
   if (bytes > 64 * 1024 &&
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess)
@@ -1630,20 +1843,31 @@ hipError_t launch_siso_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOp
     hipLaunchKernelGGL(bwd_theta_scan_kernel, dim3(BH * g.A), dim3(64), 0, stream, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // the N = 128 / P = 64 / A = 32 geometry with 16-byte aligned operands
+  // takes the kernels specialised for it
+  const bool fixed = g.N == 128 && g.P == 64 && g.A == 32 && aligned16(workspace) && aligned16(o.b) &&
+                     aligned16(o.c) && aligned16(o.x) && aligned16(go.dout) && aligned16(o.b_bias) &&
+                     aligned16(o.c_bias) && (!g.has_z || aligned16(o.z));
   const size_t sl = summary_lds_bytes(k.PT, k.NT);
-  raise_lds(reinterpret_cast<const void*>(&bwd_summary_kernel), sl);
-  hipLaunchKernelGGL(bwd_summary_kernel, dim3(BH * w.nc), dim3(512), sl, stream, k);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const unsigned pnb = (g.P * g.N + 255) / 256;
-  hipLaunchKernelGGL(bwd_prefix_kernel, dim3(pnb * BH), dim3(256), 0, stream, k, (int)pnb, 3);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t cl = (size_t)chunk_lds(k.PT, k.NT, k.A).total * sizeof(float);
-  if ((g.N & 3u) == 0) {
-    raise_lds(reinterpret_cast<const void*>(&bwd_chunk_kernel<true>), cl);
-    hipLaunchKernelGGL(bwd_chunk_kernel<true>, dim3(BH * w.nc), dim3(512), cl, stream, k);
+  if (fixed) {
+    raise_lds(reinterpret_cast<const void*>(&bwd_summary_kernel<128, 64, 32>), sl);
+    hipLaunchKernelGGL((bwd_summary_kernel<128, 64, 32>), dim3(BH * w.nc), dim3(512), sl, stream, k);
   } else {
-    raise_lds(reinterpret_cast<const void*>(&bwd_chunk_kernel<false>), cl);
-    hipLaunchKernelGGL(bwd_chunk_kernel<false>, dim3(BH * w.nc), dim3(512), cl, stream, k);
+    raise_lds(reinterpret_cast<const void*>(&bwd_summary_kernel<0, 0, -1>), sl);
+    hipLaunchKernelGGL((bwd_summary_kernel<0, 0, -1>), dim3(BH * w.nc), dim3(512), sl, stream, k);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_prefix(g, k, 3, workspace, stream)) != hipSuccess) return e;
+  const size_t cl = (size_t)chunk_lds(k.PT, k.NT, k.A).total * sizeof(float);
+  if (fixed) {
+    raise_lds(reinterpret_cast<const void*>(&bwd_chunk_kernel<true, 128, 64, 32>), cl);
+    hipLaunchKernelGGL((bwd_chunk_kernel<true, 128, 64, 32>), dim3(BH * w.nc), dim3(512), cl, stream, k);
+  } else if ((g.N & 3u) == 0 && aligned16(workspace)) {
+    raise_lds(reinterpret_cast<const void*>(&bwd_chunk_kernel<true, 0, 0, -1>), cl);
+    hipLaunchKernelGGL((bwd_chunk_kernel<true, 0, 0, -1>), dim3(BH * w.nc), dim3(512), cl, stream, k);
+  } else {
+    raise_lds(reinterpret_cast<const void*>(&bwd_chunk_kernel<false, 0, 0, -1>), cl);
+    hipLaunchKernelGGL((bwd_chunk_kernel<false, 0, 0, -1>), dim3(BH * w.nc), dim3(512), cl, stream, k);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_chunk_scan_kernel, dim3(BH * (g.A + 1)), dim3(64), 0, stream, k);
@@ -1794,19 +2018,17 @@ hipError_t launch_mimo_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOp
   raise_lds(reinterpret_cast<const void*>(&mimo_summary_kernel), sl);
   hipLaunchKernelGGL(mimo_summary_kernel, dim3(nch), dim3(512), sl, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const unsigned pnb = (g.P * g.N + 255) / 256;
-  hipLaunchKernelGGL(bwd_prefix_kernel, dim3(pnb * BH), dim3(256), 0, stream, k, (int)pnb, 1);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_prefix(g, k, 1, workspace, stream)) != hipSuccess) return e;
   const size_t pl = mimo_post_lds(k.PT, k.NT, w.RS, k.R, k.P, w.Qt);
-  if ((g.N & 3u) == 0)
+  const bool vec4 = (g.N & 3u) == 0 && aligned16(workspace);  // 16-byte state rows
+  if (vec4)
     e = launch_post<true>(k, w.RS, nch, pl, stream);
   else
     e = launch_post<false>(k, w.RS, nch, pl, stream);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_prefix_kernel, dim3(pnb * BH), dim3(256), 0, stream, k, (int)pnb, 2);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_prefix(g, k, 2, workspace, stream)) != hipSuccess) return e;
   const size_t cl = (size_t)mimo_chunk_lds(k.PT, k.NT, k.A, w.RS, w.Qt).total * sizeof(float);
-  if ((g.N & 3u) == 0) {
+  if (vec4) {
     raise_lds(reinterpret_cast<const void*>(&mimo_chunk_kernel<true>), cl);
     hipLaunchKernelGGL(mimo_chunk_kernel<true>, dim3(nch), dim3(512), cl, stream, k);
   } else {

@@ -28,7 +28,9 @@ def _print_case(tag):
     Dims(2, 75, 4, 2, 16, 32, 8),                    # ragged last chunk, groups
     Dims(1, 33, 3, 0, 24, 40, 20, has_z=False),      # one head per group, N not a multiple of 16
     Dims(2, 50, 2, 1, 5, 6, 3, has_d=False),         # odd sizes
-    Dims(1, 96, 2, 1, 64, 128, 32),                  # the N=128 / P=64 geometry
+    Dims(1, 96, 2, 1, 64, 128, 32),                  # the N=128 / P=64 / A=32 geometry (its own kernels)
+    Dims(1, 77, 4, 2, 64, 128, 32),                  # the same kernels, ragged last chunk, groups
+    Dims(2, 45, 2, 1, 64, 128, 32, has_z=False, has_d=False),  # the same kernels without z and D
     Dims(1, 40, 2, 1, 32, 64, 0),                    # no rotary angles
     Dims(1, 70, 2, 1, 128, 128, 64),                 # the largest head_dim, state and angle count
     Dims(1, 31, 2, 2, 16, 32, 16, has_z=False, has_d=False),  # A = N/2, shorter than a chunk
@@ -59,6 +61,33 @@ def test_siso_bwd_is_deterministic():
     b = _gpu_bwd(inp, dout, d)
     for k in OPS11:
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def _offset_view(a: np.ndarray) -> torch.Tensor:
+    """A device copy of ``a`` that starts 4 bytes into its allocation, so its
+    rows are not 16-byte aligned."""
+    buf = torch.empty(a.size + 1, dtype=torch.float32, device="cuda")
+    v = buf[1:].view(a.shape)
+    v.copy_(torch.from_numpy(a))
+    return v
+
+
+def test_siso_bwd_unaligned_operands():
+    """B and x 4 bytes off 16-byte alignment: the N=128 / P=64 / A=32 geometry
+    then runs on the general kernels, with the same results to the parity bound."""
+    d = Dims(1, 70, 2, 1, 64, 128, 32)
+    _print_case(f"siso_bwd unaligned {d}")
+    inp = ssm_inputs(d, seed=5301, mimo=False)
+    dout = output_gradient(d, seed=5302)
+    dev_inp = to_dev(inp)
+    dev_inp["b"] = _offset_view(inp["b"])
+    dev_inp["x"] = _offset_view(inp["x"])
+    got = _gpu_bwd(dev_inp, torch.from_numpy(dout).cuda(), d)
+    aligned = _gpu_bwd(to_dev(inp), torch.from_numpy(dout).cuda(), d)
+    ref = O.siso_backward(dout, *[inp[k] for k in OPS11], cfg_oracle(d))
+    for k in OPS11:
+        assert_parity(got[k], ref[k], f"d_{k} (unaligned)")
+        assert_parity(aligned[k], ref[k], f"d_{k} (aligned)")
 
 
 def test_siso_bwd_full_b4_l2048_sampled():
