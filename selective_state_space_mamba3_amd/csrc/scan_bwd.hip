@@ -1151,6 +1151,97 @@ __device__ void load_x_m(const BwdK& p, int b, int h, int t0, int nv, float* X, 
   }
 }
 
+// load_kq_m with 16-byte accesses (conditions of load_kq4): item (virtual
+// row v = t RS + r, four columns); rows of padding ranks or past the end are zero.
+__device__ __forceinline__ void load_kq4_m(const BwdK& p, const Geom gm, int b, int h, int g, int t0, int nv,
+                                           float* Kc, float* Qc, int ns, float* cs_l, float* sn_l, int tid) {
+  const int N = gm.N, A = gm.A, A4 = A / 4, NP4 = (N - 2 * A) / 4;
+  const int bh = b * p.H + h, R = p.R, G = p.G, RGN = R * G * N, rsl = p.rsl, rmask = p.RS - 1;
+  const size_t row0 = ((size_t)b * p.L + t0) * RGN + (size_t)g * N;  // (t, r) at row0 + t R G N + r G N
+  const float* bbh = p.b_bias + (size_t)h * R * N;                    // rank r at + r N
+  const float* cbh = p.c_bias + (size_t)h * R * N;
+  if (A > 0) {
+    const float* th = p.theta + ((size_t)bh * p.L + t0) * A;
+    const float* tp = p.tpre + ((size_t)bh * p.nT + t0 / TT) * A;  // a chunk lies inside one tile
+    for (int it = tid; it < BQ * A4; it += 512) {
+      const int v = it / A4, j = 4 * (it - v * A4);
+      const int t = v >> rsl, r = v & rmask;
+      const bool ok = t < nv && r < R;
+      const int tc = min(t, nv - 1), rc = min(r, R - 1);
+      const int ro = tc * RGN + rc * G * N, bo = rc * N;
+      const floatx4 th4 = ldg4(th + tc * A + j), tp4 = ldg4(tp + j);
+      const floatx4 b0 = ldg4(p.b + row0 + ro + j), b1 = ldg4(p.b + row0 + ro + j + A);
+      const floatx4 c0 = ldg4(p.c + row0 + ro + j), c1 = ldg4(p.c + row0 + ro + j + A);
+      const floatx4 bb0 = ldg4(bbh + bo + j), bb1 = ldg4(bbh + bo + j + A);
+      const floatx4 cb0 = ldg4(cbh + bo + j), cb1 = ldg4(cbh + bo + j + A);
+      floatx4 k0, k1, q0, q1, cs4, sn4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float sn, cs;
+        sincos_acc(th4[e] + tp4[e], &sn, &cs);
+        const float kb0 = b0[e] + bb0[e], kb1 = b1[e] + bb1[e];
+        const float qc0 = c0[e] + cb0[e], qc1 = c1[e] + cb1[e];
+        k0[e] = ok ? kb0 * cs - kb1 * sn : 0.f;
+        k1[e] = ok ? kb0 * sn + kb1 * cs : 0.f;
+        q0[e] = ok ? qc0 * cs - qc1 * sn : 0.f;
+        q1[e] = ok ? qc0 * sn + qc1 * cs : 0.f;
+        cs4[e] = cs;
+        sn4[e] = sn;
+      }
+      sts4(Kc + v * ns + j, k0);
+      sts4(Kc + v * ns + j + A, k1);
+      sts4(Qc + v * ns + j, q0);
+      sts4(Qc + v * ns + j + A, q1);
+      if (cs_l) {
+        sts4(cs_l + v * A + j, cs4);
+        sts4(sn_l + v * A + j, sn4);
+      }
+    }
+  }
+  for (int it = tid; it < BQ * NP4; it += 512) {
+    const int v = it / NP4, n = 2 * A + 4 * (it - v * NP4);
+    const int t = v >> rsl, r = v & rmask;
+    const bool ok = t < nv && r < R;
+    const int tc = min(t, nv - 1), rc = min(r, R - 1);
+    const int ro = tc * RGN + rc * G * N, bo = rc * N;
+    const floatx4 b4 = ldg4(p.b + row0 + ro + n), c4 = ldg4(p.c + row0 + ro + n);
+    const floatx4 bb4 = ldg4(bbh + bo + n), cb4 = ldg4(cbh + bo + n);
+    floatx4 kv, qv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kv[e] = ok ? b4[e] + bb4[e] : 0.f;
+      qv[e] = ok ? c4[e] + cb4[e] : 0.f;
+    }
+    sts4(Kc + v * ns + n, kv);
+    sts4(Qc + v * ns + n, qv);
+  }
+}
+
+// load_x_m with 16-byte accesses (P a multiple of 16, 16-byte aligned rows):
+// X_v = x_t mimo_x[h, r] (times wx[t]); with xt the raw x rows [Qt][ps].
+__device__ __forceinline__ void load_x4_m(const BwdK& p, const Geom gm, int b, int h, int t0, int nv, float* X,
+                                          int ps, const float* wx, float* xt, int tid) {
+  const int P = gm.P, P4 = P / 4, HP = p.H * P, R = p.R, rsl = p.rsl, rmask = p.RS - 1;
+  const size_t row0 = (((size_t)b * p.L + t0) * p.H + h) * P;
+  const float* mx = p.mimo_x + (size_t)h * R * P;
+  for (int it = tid; it < BQ * P4; it += 512) {
+    const int v = it / P4, pp = 4 * (it - v * P4);
+    const int t = v >> rsl, r = v & rmask;
+    const bool ok = t < nv && r < R;
+    const floatx4 x4 = ldg4(p.x + row0 + min(t, nv - 1) * HP + pp);
+    const floatx4 w4 = ldg4(mx + min(r, R - 1) * P + pp);
+    const float sx = wx ? wx[t] : 1.f;
+    floatx4 xv, xr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xv[e] = ok ? x4[e] * w4[e] * sx : 0.f;
+      xr[e] = t < nv ? x4[e] : 0.f;
+    }
+    sts4(X + v * ps + pp, xv);
+    if (xt && r == 0) sts4(xt + t * ps + pp, xr);
+  }
+}
+
 // Mask weights between virtual rows: M[v][w] and V[v][w] as for tokens, by
 // the tokens of the rows.
 __device__ __forceinline__ void row_masks(int tv, int tw, const float* cum, const float* scl, const float* gam,
@@ -1160,9 +1251,12 @@ __device__ __forceinline__ void row_masks(int tv, int tw, const float* cum, cons
 }
 
 // (M2) Per chunk: forward summary S = sum_v e^(cumx-cum_t) s_t X_v K_v^T and the decay.
+// NC > 0: geometry fixed at (NC, PC, AC) with the 16-byte loaders.
+template <int NC, int PC, int AC>
 __global__ __launch_bounds__(512) void mimo_summary_kernel(BwdK p) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  const int NS = p.NT * 16 + 4, PS = p.PT * 16 + 4;
+  const Geom gm = geom_of<NC, PC, AC>(p);
+  const int NS = gm.NT * 16 + 4, PS = gm.PT * 16 + 4, P = gm.P, N = gm.N;
   float* Kc = lds;
   float* Qc = Kc + BQ * NS;  // loaded with the keys; unused here
   float* Xw = Qc + BQ * NS;
@@ -1177,25 +1271,31 @@ __global__ __launch_bounds__(512) void mimo_summary_kernel(BwdK p) {
   const int b = bh / p.H, h = bh - b * p.H, g = h / (p.H / p.G);
   const int t0 = c * p.Qt, nv = min(p.Qt, p.L - t0);
   if (wave == 0) chunk_scalars(p, b, h, t0, nv, ChunkScalars{cum, scl, gam, ec, ex}, lane);
-  load_kq_m(p, b, h, g, t0, nv, Kc, Qc, NS, nullptr, nullptr, tid, blockDim.x);
+  if constexpr (NC > 0)
+    load_kq4_m(p, gm, b, h, g, t0, nv, Kc, Qc, NS, nullptr, nullptr, tid);
+  else
+    load_kq_m(p, b, h, g, t0, nv, Kc, Qc, NS, nullptr, nullptr, tid, blockDim.x);
   __syncthreads();
   if (tid < BQ) wx[tid] = ex[tid] * scl[tid];
   __syncthreads();
-  load_x_m(p, b, h, t0, nv, Xw, PS, wx, nullptr, tid, blockDim.x);
+  if constexpr (NC > 0)
+    load_x4_m(p, gm, b, h, t0, nv, Xw, PS, wx, nullptr, tid);
+  else
+    load_x_m(p, b, h, t0, nv, Xw, PS, wx, nullptr, tid, blockDim.x);
   __syncthreads();
   if (tid == 0) p.decay[blockIdx.x] = expf(cum[BQ - 1]);
-  const int ntile = p.PT * p.NT;
-  const size_t base = (size_t)blockIdx.x * p.P * p.N;
+  const int ntile = gm.PT * gm.NT;
+  float* dst = p.hs + (size_t)blockIdx.x * P * N;
   const int r = lane & 15, q = lane >> 4;
   for (int job = wave; job < ntile; job += nw) {
-    const int pt = job / p.NT, nt = job - pt * p.NT;
+    const int pt = job / gm.NT, nt = job - pt * gm.NT;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = mm_tile(Xw + pt * 16, 1, PS, Kc + nt * 16, NS, 1, BQ, acc, lane);
     const int n = nt * 16 + r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pp = pt * 16 + 4 * q + i;
-      if (pp < p.P && n < p.N) p.hs[base + (size_t)pp * p.N + n] = acc[i];
+      if (pp < P && n < N) dst[pp * N + n] = acc[i];
     }
   }
 }
@@ -1211,10 +1311,12 @@ __device__ __forceinline__ float wave_sum(float v) { return read_lane_f(scan64_f
 // gradients; last the reverse summary sum_v e^cum_t gy_v Q_v^T.  The
 // per-rank weights and the chunk's dout / z rows are staged in LDS with the
 // other operands, so the epilogue loop waits on no memory.
-template <bool VEC4, int RSC>
+template <bool VEC4, int RSC, int NC, int PC, int AC>
 __global__ __launch_bounds__(512, 4) void mimo_post_kernel(BwdK p) {
+  constexpr bool FIX = NC > 0;
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  const int NS = p.NT * 16 + 4, PS = p.PT * 16 + 4, PP = p.PT * 16, NN = p.NT * 16;
+  const Geom gm = geom_of<NC, PC, AC>(p);
+  const int NS = gm.NT * 16 + 4, PS = gm.PT * 16 + 4, PP = gm.PT * 16, NN = gm.NT * 16;
   float* Kc = lds;
   float* Qc = Kc + BQ * NS;
   float* X = Qc + BQ * NS;
@@ -1223,11 +1325,11 @@ __global__ __launch_bounds__(512, 4) void mimo_post_kernel(BwdK p) {
   float* MQK = GY + BQ * PS;
   float* red = MQK + BQ * MS;        // [8][RS P] cross-wave partials
   float* WZ = red + 8 * p.RS * PP;   // mimo_z [R][P]
-  float* WO = WZ + p.R * p.P;        // mimo_o [R][P]
-  float* WN = WO + p.R * p.P;        // norm_weight [P]
-  float* GO = WN + p.P;              // dout of the chunk's tokens [Qt][P]
-  float* ZT = GO + p.Qt * p.P;       // z of the chunk's tokens [Qt][P]
-  float* cum = ZT + p.Qt * p.P;
+  float* WO = WZ + p.R * gm.P;       // mimo_o [R][P]
+  float* WN = WO + p.R * gm.P;       // norm_weight [P]
+  float* GO = WN + gm.P;             // dout of the chunk's tokens [Qt][P]
+  float* ZT = GO + p.Qt * gm.P;      // z of the chunk's tokens [Qt][P]
+  float* cum = ZT + p.Qt * gm.P;
   float* scl = cum + BQ;
   float* gam = scl + BQ;
   float* ec = gam + BQ;
@@ -1236,11 +1338,16 @@ __global__ __launch_bounds__(512, 4) void mimo_post_kernel(BwdK p) {
   const int bh = blockIdx.x / p.nc, c = blockIdx.x - bh * p.nc;
   const int b = bh / p.H, h = bh - b * p.H, g = h / (p.H / p.G);
   const int t0 = c * p.Qt, nv = min(p.Qt, p.L - t0);
-  const int P = p.P, N = p.N, H = p.H, R = p.R, rsl = p.rsl;
+  const int P = gm.P, N = gm.N, H = p.H, R = p.R, rsl = p.rsl;
   const float* HEg = p.hs + (size_t)blockIdx.x * P * N;
   if (wave == 0) chunk_scalars(p, b, h, t0, nv, ChunkScalars{cum, scl, gam, ec, ex}, lane);
-  load_kq_m(p, b, h, g, t0, nv, Kc, Qc, NS, nullptr, nullptr, tid, blockDim.x);
-  load_x_m(p, b, h, t0, nv, X, PS, nullptr, nullptr, tid, blockDim.x);
+  if constexpr (FIX) {
+    load_kq4_m(p, gm, b, h, g, t0, nv, Kc, Qc, NS, nullptr, nullptr, tid);
+    load_x4_m(p, gm, b, h, t0, nv, X, PS, nullptr, nullptr, tid);
+  } else {
+    load_kq_m(p, b, h, g, t0, nv, Kc, Qc, NS, nullptr, nullptr, tid, blockDim.x);
+    load_x_m(p, b, h, t0, nv, X, PS, nullptr, nullptr, tid, blockDim.x);
+  }
   for (int i = tid; i < R * P; i += blockDim.x) {
     WZ[i] = p.has_z ? p.mimo_z[(size_t)h * R * P + i] : 0.f;
     WO[i] = p.mimo_o[(size_t)h * R * P + i];
@@ -1262,14 +1369,20 @@ __global__ __launch_bounds__(512, 4) void mimo_post_kernel(BwdK p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int v = mt * 16 + 4 * q + i;
+      const int tv = v >> rsl, tw = w >> rsl;
       float m, dec;
-      row_masks(v >> rsl, w >> rsl, cum, scl, gam, &m, &dec);
+      if constexpr (FIX) {
+        dec = tw < tv ? exp_fast(cum[tv] - cum[tw]) : 0.f;
+        m = tw < tv ? dec * scl[tw] : (tw == tv ? gam[tv] : 0.f);
+      } else {
+        row_masks(tv, tw, cum, scl, gam, &m, &dec);
+      }
       MQK[v * MS + w] = m * acc[i];
     }
   }
   __syncthreads();
-  for (int job = wave; job < 2 * p.PT; job += nw) {  // y tiles
-    const int mt = job / p.PT, pt = job - mt * p.PT;
+  for (int job = wave; job < 2 * gm.PT; job += nw) {  // y tiles
+    const int mt = job / gm.PT, pt = job - mt * gm.PT;
     floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
     if constexpr (VEC4)
       a1 = mm_tile_k4_g<8>(Qc + mt * 16 * NS, NS, HEg + (size_t)pt * 16 * N, N, P - pt * 16, N, NN, a1, lane);
@@ -1312,7 +1425,7 @@ __global__ __launch_bounds__(512, 4) void mimo_post_kernel(BwdK p) {
         y2[k] = fmaf(Dh, in ? X[v * PS + pp] : 0.f, y1v[k]);
         const float mz = in ? WZ[rr * P + pp] : 0.f;
         u[k] = zv[k] * mz;
-        sil[k] = p.has_z ? siluf_acc(u[k]) : 1.f;
+        sil[k] = p.has_z ? (FIX ? sigmoid_fast(u[k]) * u[k] : siluf_acc(u[k])) : 1.f;
         y3[k] = y2[k] * sil[k];
       }
       float rinv = 1.f, yn[2] = {y3[0], y3[1]}, nwv[2] = {1.f, 1.f};
@@ -1354,7 +1467,7 @@ __global__ __launch_bounds__(512, 4) void mimo_post_kernel(BwdK p) {
         const int pp = lane + 64 * k;
         float g2 = g3[k];
         if (p.has_z) {
-          const float du = g3[k] * y2[k] * dsilu_acc(u[k]);
+          const float du = g3[k] * y2[k] * (FIX ? dsilu_fast(u[k]) : dsilu_acc(u[k]));
           const float mz = (ok && pp < P) ? WZ[rr * P + pp] : 0.f;
           mz_acc[rr][k] = fmaf(du, zv[k], mz_acc[rr][k]);
           dz[k] = fmaf(du, mz, dz[k]);
@@ -1422,8 +1535,8 @@ __global__ __launch_bounds__(512, 4) void mimo_post_kernel(BwdK p) {
   }
   __syncthreads();
   const size_t base = (size_t)blockIdx.x * P * N;
-  for (int job = wave; job < p.PT * p.NT; job += nw) {
-    const int pt = job / p.NT, nt = job - pt * p.NT;
+  for (int job = wave; job < gm.PT * gm.NT; job += nw) {
+    const int pt = job / gm.NT, nt = job - pt * gm.NT;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = mm_tile(Y + pt * 16, 1, PS, Qc + nt * 16, NS, 1, BQ, acc, lane);
     const int n = nt * 16 + r;
@@ -1467,12 +1580,17 @@ __host__ __device__ inline MimoChunkLds mimo_chunk_lds(int PT, int NT, int A, in
 // (M6) Per chunk: G K, dQ, dK of the virtual rows on FP32 MFMA with gy from
 // the post kernel; d x (rank sum of mimo_x dX_r), partial mimo_x sums, the
 // per-head rank-row adjoints of B + b_bias and C + c_bias, and the local
-// suffix sums of the d adt terms and of d theta.
-template <bool VEC4>
+// suffix sums of the d adt terms and of d theta.  NC > 0: geometry fixed at
+// (NC, PC, AC) as for bwd_chunk_kernel.
+template <bool VEC4, int NC, int PC, int AC>
 __global__ __launch_bounds__(512, 4) void mimo_chunk_kernel(BwdK p) {
+  constexpr bool FIX = NC > 0;
+  static_assert(!FIX || (NC == 128 && PC % 16 == 0 && AC % 4 == 0 && (BQ * AC / 4) % 64 == 0),
+                "fixed geometry: N = 128 (one state tile per wave), P a multiple of 16");
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  const MimoChunkLds ll = mimo_chunk_lds(p.PT, p.NT, p.A, p.RS, p.Qt);
-  const int NS = ll.NS, PS = ll.PS, PP = p.PT * 16, NN = p.NT * 16;
+  const Geom gm = geom_of<NC, PC, AC>(p);
+  const MimoChunkLds ll = mimo_chunk_lds(gm.PT, gm.NT, gm.A, p.RS, p.Qt);
+  const int NS = ll.NS, PS = ll.PS, PP = gm.PT * 16, NN = gm.NT * 16;
   float* Kc = lds + ll.o_kc;
   float* Qc = lds + ll.o_qc;
   float* X = lds + ll.o_x;
@@ -1497,16 +1615,27 @@ __global__ __launch_bounds__(512, 4) void mimo_chunk_kernel(BwdK p) {
   const int bh = blockIdx.x / p.nc, c = blockIdx.x - bh * p.nc;
   const int b = bh / p.H, h = bh - b * p.H, g = h / (p.H / p.G);
   const int t0 = c * p.Qt, nv = min(p.Qt, p.L - t0);
-  const int P = p.P, N = p.N, H = p.H, A = p.A, NP = N - A, R = p.R, RS = p.RS, rsl = p.rsl;
+  const int P = gm.P, N = gm.N, H = p.H, A = gm.A, NP = N - A, R = p.R, RS = p.RS, rsl = p.rsl;
   const float* HEg = p.hs + (size_t)blockIdx.x * P * N;
   const float* GXg = p.gs + (size_t)blockIdx.x * P * N;
+  const float* gyc = p.gyr + (size_t)blockIdx.x * BQ * P;  // row v at gyc + v P
 
   if (wave == 0) chunk_scalars(p, b, h, t0, nv, ChunkScalars{cum, scl, gam, ec, ex}, lane);
-  load_kq_m(p, b, h, g, t0, nv, Kc, Qc, NS, CS, SN, tid, 512);
-  load_x_m(p, b, h, t0, nv, X, PS, nullptr, XT, tid, 512);
-  for (int it = tid; it < BQ * PP; it += 512) {
-    const int v = it / PP, pp = it - v * PP;
-    GY[v * PS + pp] = pp < P ? p.gyr[((size_t)blockIdx.x * BQ + v) * P + pp] : 0.f;
+  if constexpr (FIX) {
+    load_kq4_m(p, gm, b, h, g, t0, nv, Kc, Qc, NS, CS, SN, tid);
+    load_x4_m(p, gm, b, h, t0, nv, X, PS, nullptr, XT, tid);
+    constexpr int P4 = PC / 4;
+    for (int it = tid; it < BQ * P4; it += 512) {
+      const int v = it / P4, pp = 4 * (it - v * P4);
+      sts4(GY + v * PS + pp, ldg4(gyc + v * P + pp));
+    }
+  } else {
+    load_kq_m(p, b, h, g, t0, nv, Kc, Qc, NS, CS, SN, tid, 512);
+    load_x_m(p, b, h, t0, nv, X, PS, nullptr, XT, tid, 512);
+    for (int it = tid; it < BQ * PP; it += 512) {
+      const int v = it / PP, pp = it - v * PP;
+      GY[v * PS + pp] = pp < P ? gyc[v * P + pp] : 0.f;
+    }
   }
   __syncthreads();
   const float Dh = p.has_d ? p.d[h] : 0.f;
@@ -1527,7 +1656,12 @@ __global__ __launch_bounds__(512, 4) void mimo_chunk_kernel(BwdK p) {
       const int v = mt * 16 + 4 * q + i;
       const int tv = v >> rsl, tw = w >> rsl;
       float m, dec;
-      row_masks(tv, tw, cum, scl, gam, &m, &dec);
+      if constexpr (FIX) {
+        dec = tw < tv ? exp_fast(cum[tv] - cum[tw]) : 0.f;
+        m = tw < tv ? dec * scl[tw] : (tw == tv ? gam[tv] : 0.f);
+      } else {
+        row_masks(tv, tw, cum, scl, gam, &m, &dec);
+      }
       if (!sgx) {
         VV[v * MS + w] = dec * acc[i];
         if (tv == tw) SQD[v * RS + (w & (RS - 1))] = acc[i];
@@ -1540,9 +1674,9 @@ __global__ __launch_bounds__(512, 4) void mimo_chunk_kernel(BwdK p) {
   __syncthreads();
 
   // G K tiles: dX_v = D gy_v + s_t G K_v + lam_t dt_t sum_{w in t} (Q_w . K_v) gy_w
-  const int nY = 2 * p.PT, nQ = 2 * p.NT;
+  const int nY = 2 * gm.PT, nQ = 2 * gm.NT;
   for (int job = wave; job < nY; job += 8) {
-    const int mt = job / p.PT, pt = job - mt * p.PT;
+    const int mt = job / gm.PT, pt = job - mt * gm.PT;
     floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
     const float* Sg = GXg + (size_t)pt * 16 * N;
     if constexpr (VEC4)
@@ -1564,27 +1698,31 @@ __global__ __launch_bounds__(512, 4) void mimo_chunk_kernel(BwdK p) {
       DX[v * PS + pp] = fmaf(Dh, GY[v * PS + pp], fmaf(scl[tv], gk, gam[tv] * same));
       const bool ok = tv < nv && rv < R && pp < P;
       const float part = row16_sum(ok ? X[v * PS + pp] * gk : 0.f);
-      if (r == 15) ds_part[v * p.PT + pt] = part;
+      if (r == 15) ds_part[v * gm.PT + pt] = part;
     }
   }
   floatx4 res[4];
+  if constexpr (FIX) {
+    // as in bwd_chunk_kernel: wave w owns state columns 16 w .. 16 w + 15
+    const int nt = wave;
+    float sh[PC / 4], sg[PC / 4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int job = wave + 8 * k;
-    res[k] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (job < 2 * nQ) {
-      const bool isdk = job >= nQ;
-      const int jj = isdk ? job - nQ : job;
-      const int mt = jj / p.NT, nt = jj - mt * p.NT;
+    for (int j = 0; j < PC / 4; ++j) {
+      sh[j] = HEg[(4 * j + q) * N + nt * 16 + r];
+      sg[j] = GXg[(4 * j + q) * N + nt * 16 + r];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool isdk = k >= 2;
+      const int mt = k & 1;
       floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-      const float* Sg = (isdk ? GXg : HEg) + nt * 16;
-      if (!isdk) {
-        a1 = mm_tile_g<32>(GY + mt * 16 * PS, PS, Sg, N, P, N - nt * 16, PP, a1, lane);
+      const float* Ar = (isdk ? X : GY) + (mt * 16 + r) * PS + q;
+#pragma unroll
+      for (int j = 0; j < PC / 4; ++j) a1 = mfma16(Ar[4 * j], isdk ? sg[j] : sh[j], a1);
+      if (!isdk)
         a2 = mm_tile(MSG + mt * 16 * MS, MS, 1, Kc + nt * 16, NS, 1, BQ, a2, lane);
-      } else {
-        a1 = mm_tile_g<32>(X + mt * 16 * PS, PS, Sg, N, P, N - nt * 16, PP, a1, lane);
+      else
         a2 = mm_tile(MSG + mt * 16, 1, MS, Qc + nt * 16, NS, 1, BQ, a2, lane);
-      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tv = (mt * 16 + 4 * q + i) >> rsl;
@@ -1592,16 +1730,44 @@ __global__ __launch_bounds__(512, 4) void mimo_chunk_kernel(BwdK p) {
         res[k][i] = fmaf(wgt, a1[i], a2[i]);
       }
     }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int job = wave + 8 * k;
+      res[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (job < 2 * nQ) {
+        const bool isdk = job >= nQ;
+        const int jj = isdk ? job - nQ : job;
+        const int mt = jj / gm.NT, nt = jj - mt * gm.NT;
+        floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+        const float* Sg = (isdk ? GXg : HEg) + nt * 16;
+        if (!isdk) {
+          a1 = mm_tile_g<32>(GY + mt * 16 * PS, PS, Sg, N, P, N - nt * 16, PP, a1, lane);
+          a2 = mm_tile(MSG + mt * 16 * MS, MS, 1, Kc + nt * 16, NS, 1, BQ, a2, lane);
+        } else {
+          a1 = mm_tile_g<32>(X + mt * 16 * PS, PS, Sg, N, P, N - nt * 16, PP, a1, lane);
+          a2 = mm_tile(MSG + mt * 16, 1, MS, Qc + nt * 16, NS, 1, BQ, a2, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tv = (mt * 16 + 4 * q + i) >> rsl;
+          const float wgt = isdk ? scl[tv] * ex[tv] : ec[tv];
+          res[k][i] = fmaf(wgt, a1[i], a2[i]);
+        }
+      }
+    }
   }
   __syncthreads();  // DX complete; x, gy, the masks free after this point
 
   // d x = sum_r mimo_x[h, r] dX_r, and per-chunk partial sums of dX_r * x for d mimo_x
+  const size_t xrow0 = (((size_t)b * p.L + t0) * H + h) * P;  // token t at xrow0 + t H P
+  const float* mxh = p.mimo_x + (size_t)h * R * P;
   for (int it = tid; it < p.Qt * P; it += 512) {
     const int t = it / P, pp = it - t * P;
     if (t < nv) {
       float s = 0.f;
-      for (int rr = 0; rr < R; ++rr) s = fmaf(p.mimo_x[((size_t)h * R + rr) * P + pp], DX[((t << rsl) + rr) * PS + pp], s);
-      p.d_x[(((size_t)b * p.L + t0 + t) * H + h) * P + pp] = s;
+      for (int rr = 0; rr < R; ++rr) s = fmaf(mxh[rr * P + pp], DX[((t << rsl) + rr) * PS + pp], s);
+      p.d_x[xrow0 + t * H * P + pp] = s;
     }
   }
   for (int it = tid; it < R * P; it += 512) {
@@ -1616,7 +1782,7 @@ __global__ __launch_bounds__(512, 4) void mimo_chunk_kernel(BwdK p) {
   if (wave == 0 && lane < nv) {
     for (int rr = 0; rr < R; ++rr) {
       const int v = (lane << rsl) + rr;
-      for (int pt = 0; pt < p.PT; ++pt) ds_tok += ds_part[v * p.PT + pt];
+      for (int pt = 0; pt < gm.PT; ++pt) ds_tok += ds_part[v * gm.PT + pt];
       for (int rw = 0; rw < R; ++rw) {
         const int w = (lane << rsl) + rw;
         e_tok = fmaf(SGD[w * RS + rr], SQD[w * RS + rr], e_tok);
@@ -1626,6 +1792,8 @@ __global__ __launch_bounds__(512, 4) void mimo_chunk_kernel(BwdK p) {
   }
 
   // rotation adjoints: queries, then keys, staged through LDS
+  const size_t hrow0 = (((size_t)b * p.L + t0) * H + h) * R * N;  // (t, r) at hrow0 + (t H R + r) N
+  const int HRN = H * R * N;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     __syncthreads();
@@ -1634,35 +1802,74 @@ __global__ __launch_bounds__(512, 4) void mimo_chunk_kernel(BwdK p) {
       const int job = wave + 8 * k;
       if (job < 2 * nQ && (job >= nQ) == (pass == 1)) {
         const int jj = pass ? job - nQ : job;
-        const int mt = jj / p.NT, nt = jj - mt * p.NT;
+        const int mt = jj / gm.NT, nt = jj - mt * gm.NT;
 #pragma unroll
         for (int i = 0; i < 4; ++i) STG[(mt * 16 + 4 * q + i) * NS + nt * 16 + r] = res[k][i];
       }
     }
     __syncthreads();
     const float* Rw = pass ? Kc : Qc;
-    float* dst = pass ? p.db_head : p.dc_head;
-    for (int it = tid; it < p.Qt * NP; it += 512) {
-      const int t = it / NP, j = it - t * NP;
-      if (t >= nv) {
-        if (j < A && pass == 0) DTH[t * A + j] = 0.f;
-        continue;
-      }
-      float dth = 0.f;
-      for (int rr = 0; rr < R; ++rr) {
-        const int v = (t << rsl) + rr;
-        const size_t o = ((((size_t)b * p.L + t0 + t) * H + h) * R + rr) * N;
-        if (j < A) {
-          const float cs = CS[v * A + j], sn = SN[v * A + j];
-          const float d0 = STG[v * NS + j], d1 = STG[v * NS + j + A];
-          dth += d1 * Rw[v * NS + j] - d0 * Rw[v * NS + j + A];
-          dst[o + j] = d0 * cs + d1 * sn;
-          dst[o + j + A] = d1 * cs - d0 * sn;
-        } else {
-          dst[o + j + A] = STG[v * NS + j + A];
+    float* dst = (pass ? p.db_head : p.dc_head) + hrow0;
+    if constexpr (FIX) {
+      constexpr int A4 = AC / 4, NP4 = (NC - 2 * AC) / 4;
+      // rotated columns: item (token, four angles), ranks summed into d theta
+      for (int it = tid; it < p.Qt * A4; it += 512) {
+        const int t = it / A4, j = 4 * (it - t * A4);
+        if (t >= nv) {
+          if (pass == 0) sts4(DTH + t * A + j, floatx4{0.f, 0.f, 0.f, 0.f});
+          continue;
         }
+        floatx4 dth = pass ? lds_read4(DTH + t * A + j) : floatx4{0.f, 0.f, 0.f, 0.f};
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int rr = 0; rr < R; ++rr) {
+          const int v = (t << rsl) + rr;
+          const floatx4 cs = lds_read4(CS + v * A + j), sn = lds_read4(SN + v * A + j);
+          const floatx4 d0 = lds_read4(STG + v * NS + j), d1 = lds_read4(STG + v * NS + j + A);
+          const floatx4 r0 = lds_read4(Rw + v * NS + j), r1 = lds_read4(Rw + v * NS + j + A);
+          floatx4 u0, u1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[e] += d1[e] * r0[e] - d0[e] * r1[e];
+            u0[e] = d0[e] * cs[e] + d1[e] * sn[e];
+            u1[e] = d1[e] * cs[e] - d0[e] * sn[e];
+          }
+          const int o = (t * H * R + rr) * N;
+          sts4(dst + o + j, u0);
+          sts4(dst + o + j + A, u1);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dth[e] = pass ? dth[e] + acc[e] : acc[e];
+        sts4(DTH + t * A + j, dth);
       }
-      if (j < A) DTH[t * A + j] = pass ? DTH[t * A + j] + dth : dth;
+      // plain columns: item (virtual row, four columns)
+      for (int it = tid; it < BQ * NP4; it += 512) {
+        const int v = it / NP4, n = 2 * AC + 4 * (it - v * NP4);
+        const int t = v >> rsl, rr = v & (RS - 1);
+        if (t < nv && rr < R) sts4(dst + (t * H * R + rr) * N + n, lds_read4(STG + v * NS + n));
+      }
+    } else {
+      for (int it = tid; it < p.Qt * NP; it += 512) {
+        const int t = it / NP, j = it - t * NP;
+        if (t >= nv) {
+          if (j < A && pass == 0) DTH[t * A + j] = 0.f;
+          continue;
+        }
+        float dth = 0.f;
+        for (int rr = 0; rr < R; ++rr) {
+          const int v = (t << rsl) + rr;
+          const int o = (t * H * R + rr) * N;
+          if (j < A) {
+            const float cs = CS[v * A + j], sn = SN[v * A + j];
+            const float d0 = STG[v * NS + j], d1 = STG[v * NS + j + A];
+            dth += d1 * Rw[v * NS + j] - d0 * Rw[v * NS + j + A];
+            dst[o + j] = d0 * cs + d1 * sn;
+            dst[o + j + A] = d1 * cs - d0 * sn;
+          } else {
+            dst[o + j + A] = STG[v * NS + j + A];
+          }
+        }
+        if (j < A) DTH[t * A + j] = pass ? DTH[t * A + j] + dth : dth;
+      }
     }
   }
   __syncthreads();
@@ -1685,7 +1892,7 @@ __global__ __launch_bounds__(512, 4) void mimo_chunk_kernel(BwdK p) {
     float* dstp = p.dtheta + ((size_t)bh * p.L + t0) * A + a;
     for (int t = nv - 1; t >= 0; --t) {
       s += DTH[t * A + a];
-      dstp[(size_t)t * A] = s;
+      dstp[t * A] = s;
     }
     p.th_tot[(size_t)blockIdx.x * A + a] = s;
   }
@@ -1946,20 +2153,20 @@ size_t mimo_summary_lds(int PT, int NT) {
   return (size_t)(2 * BQ * NS + BQ * PS + 6 * BQ) * sizeof(float);
 }
 
-template <bool VEC4, int RSC>
+template <bool VEC4, int RSC, int NC, int PC, int AC>
 hipError_t launch_post_rs(const BwdK& k, unsigned nch, size_t pl, hipStream_t stream) {
-  raise_lds(reinterpret_cast<const void*>(&mimo_post_kernel<VEC4, RSC>), pl);
-  hipLaunchKernelGGL((mimo_post_kernel<VEC4, RSC>), dim3(nch), dim3(512), pl, stream, k);
+  raise_lds(reinterpret_cast<const void*>(&mimo_post_kernel<VEC4, RSC, NC, PC, AC>), pl);
+  hipLaunchKernelGGL((mimo_post_kernel<VEC4, RSC, NC, PC, AC>), dim3(nch), dim3(512), pl, stream, k);
   return hipGetLastError();
 }
 
-template <bool VEC4>
+template <bool VEC4, int NC, int PC, int AC>
 hipError_t launch_post(const BwdK& k, int RS, unsigned nch, size_t pl, hipStream_t stream) {
   switch (RS) {
-    case 1: return launch_post_rs<VEC4, 1>(k, nch, pl, stream);
-    case 2: return launch_post_rs<VEC4, 2>(k, nch, pl, stream);
-    case 4: return launch_post_rs<VEC4, 4>(k, nch, pl, stream);
-    default: return launch_post_rs<VEC4, 8>(k, nch, pl, stream);
+    case 1: return launch_post_rs<VEC4, 1, NC, PC, AC>(k, nch, pl, stream);
+    case 2: return launch_post_rs<VEC4, 2, NC, PC, AC>(k, nch, pl, stream);
+    case 4: return launch_post_rs<VEC4, 4, NC, PC, AC>(k, nch, pl, stream);
+    default: return launch_post_rs<VEC4, 8, NC, PC, AC>(k, nch, pl, stream);
   }
 }
 
@@ -2014,26 +2221,43 @@ hipError_t launch_mimo_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOp
     hipLaunchKernelGGL(bwd_theta_scan_kernel, dim3(BH * g.A), dim3(64), 0, stream, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // the N = 128 / P = 64 / A = 32 geometry with 16-byte aligned operands
+  // takes the kernels specialised for it
+  const MimoChunkLds cll = mimo_chunk_lds(k.PT, k.NT, k.A, w.RS, w.Qt);
+  const bool fixed = g.N == 128 && g.P == 64 && g.A == 32 && aligned16(workspace) && aligned16(o.b) &&
+                     aligned16(o.c) && aligned16(o.x) && aligned16(go.dout) && aligned16(o.b_bias) &&
+                     aligned16(o.c_bias) && aligned16(o.mimo_x) && (!g.has_z || aligned16(o.z)) &&
+                     cll.o_xt % 4 == 0 && cll.o_msg % 4 == 0 && cll.o_cs % 4 == 0 && cll.o_sn % 4 == 0;
   const size_t sl = mimo_summary_lds(k.PT, k.NT);
-  raise_lds(reinterpret_cast<const void*>(&mimo_summary_kernel), sl);
-  hipLaunchKernelGGL(mimo_summary_kernel, dim3(nch), dim3(512), sl, stream, k);
+  if (fixed) {
+    raise_lds(reinterpret_cast<const void*>(&mimo_summary_kernel<128, 64, 32>), sl);
+    hipLaunchKernelGGL((mimo_summary_kernel<128, 64, 32>), dim3(nch), dim3(512), sl, stream, k);
+  } else {
+    raise_lds(reinterpret_cast<const void*>(&mimo_summary_kernel<0, 0, -1>), sl);
+    hipLaunchKernelGGL((mimo_summary_kernel<0, 0, -1>), dim3(nch), dim3(512), sl, stream, k);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_prefix(g, k, 1, workspace, stream)) != hipSuccess) return e;
   const size_t pl = mimo_post_lds(k.PT, k.NT, w.RS, k.R, k.P, w.Qt);
   const bool vec4 = (g.N & 3u) == 0 && aligned16(workspace);  // 16-byte state rows
-  if (vec4)
-    e = launch_post<true>(k, w.RS, nch, pl, stream);
+  if (fixed)
+    e = launch_post<true, 128, 64, 32>(k, w.RS, nch, pl, stream);
+  else if (vec4)
+    e = launch_post<true, 0, 0, -1>(k, w.RS, nch, pl, stream);
   else
-    e = launch_post<false>(k, w.RS, nch, pl, stream);
+    e = launch_post<false, 0, 0, -1>(k, w.RS, nch, pl, stream);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_prefix(g, k, 2, workspace, stream)) != hipSuccess) return e;
-  const size_t cl = (size_t)mimo_chunk_lds(k.PT, k.NT, k.A, w.RS, w.Qt).total * sizeof(float);
-  if (vec4) {
-    raise_lds(reinterpret_cast<const void*>(&mimo_chunk_kernel<true>), cl);
-    hipLaunchKernelGGL(mimo_chunk_kernel<true>, dim3(nch), dim3(512), cl, stream, k);
+  const size_t cl = (size_t)cll.total * sizeof(float);
+  if (fixed) {
+    raise_lds(reinterpret_cast<const void*>(&mimo_chunk_kernel<true, 128, 64, 32>), cl);
+    hipLaunchKernelGGL((mimo_chunk_kernel<true, 128, 64, 32>), dim3(nch), dim3(512), cl, stream, k);
+  } else if (vec4) {
+    raise_lds(reinterpret_cast<const void*>(&mimo_chunk_kernel<true, 0, 0, -1>), cl);
+    hipLaunchKernelGGL((mimo_chunk_kernel<true, 0, 0, -1>), dim3(nch), dim3(512), cl, stream, k);
   } else {
-    raise_lds(reinterpret_cast<const void*>(&mimo_chunk_kernel<false>), cl);
-    hipLaunchKernelGGL(mimo_chunk_kernel<false>, dim3(nch), dim3(512), cl, stream, k);
+    raise_lds(reinterpret_cast<const void*>(&mimo_chunk_kernel<false, 0, 0, -1>), cl);
+    hipLaunchKernelGGL((mimo_chunk_kernel<false, 0, 0, -1>), dim3(nch), dim3(512), cl, stream, k);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_chunk_scan_kernel, dim3(BH * (g.A + 1)), dim3(64), 0, stream, k);

@@ -24,7 +24,11 @@ def _gpu_bwd(inp_dev, dout_dev, d):
 @pytest.mark.parametrize("d", [
     Dims(1, 40, 2, 1, 16, 32, 8, R=2, has_output_norm=True),
     Dims(2, 37, 4, 2, 16, 32, 8, R=3, has_z=False),                 # a padding rank, groups
-    Dims(1, 70, 2, 1, 64, 128, 32, R=4, has_output_norm=True),      # the N=128 / P=64 geometry
+    Dims(1, 70, 2, 1, 64, 128, 32, R=4, has_output_norm=True),      # the N=128 / P=64 / A=32 kernels
+    Dims(1, 45, 2, 1, 64, 128, 32, R=3, has_output_norm=True),      # the same, a padding rank, ragged
+    Dims(2, 37, 4, 2, 64, 128, 32, R=2, has_z=False),               # the same, groups, no z
+    Dims(1, 20, 2, 1, 64, 128, 32, R=8, has_d=False),               # the same, eight ranks
+    Dims(1, 33, 2, 1, 64, 128, 32, R=1, has_output_norm=True),      # the same, one rank
     Dims(1, 50, 2, 1, 32, 64, 16, R=1, has_output_norm=True),
     Dims(1, 21, 2, 2, 16, 16, 4, R=8, has_d=False),
     Dims(2, 30, 2, 1, 5, 6, 3, R=2, has_output_norm=True),          # odd sizes
@@ -57,6 +61,25 @@ def test_mimo_bwd_is_deterministic():
     b = _gpu_bwd(inp, dout, d)
     for k in OPS15:
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_mimo_bwd_unaligned_operands():
+    """B, x and mimo_x 4 bytes off 16-byte alignment: the N=128 / P=64 / A=32
+    geometry then runs on the general kernels, with the same results to the
+    parity bound."""
+    d = Dims(1, 30, 2, 1, 64, 128, 32, R=4, has_output_norm=True)
+    print(f"[case] mimo_bwd unaligned {d}", flush=True)
+    inp = ssm_inputs(d, seed=9301, mimo=True)
+    dout = output_gradient(d, seed=9302)
+    dev_inp = to_dev(inp)
+    for k in ("b", "x", "mimo_x"):
+        buf = torch.empty(inp[k].size + 1, dtype=torch.float32, device="cuda")
+        dev_inp[k] = buf[1:].view(inp[k].shape)
+        dev_inp[k].copy_(torch.from_numpy(inp[k]))
+    got = _gpu_bwd(dev_inp, torch.from_numpy(dout).cuda(), d)
+    ref = O.mimo_backward(dout, *[inp[k] for k in OPS15], cfg_oracle(d))
+    for k in OPS15:
+        assert_parity(got[k], ref[k], f"d_{k} (unaligned)")
 
 
 def test_mimo_bwd_full_b8_l4096_r4_sampled():
