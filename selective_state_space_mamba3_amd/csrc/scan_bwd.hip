@@ -1026,6 +1026,63 @@ __global__ __launch_bounds__(256) void bwd_group_kernel(BwdK p) {
   }
 }
 
+// (8) with 16-byte accesses (N % 4 == 0, 16-byte aligned d_b, d_c and per-head
+// adjoints): item (head subset hs, four columns) sums heads hs, hs + nhs, ...
+// of the group for each of the block's RB rows in registers, writes the
+// per-head bias partial of those rows, and the head subsets meet in LDS in a
+// fixed order for d_b / d_c.
+__global__ __launch_bounds__(256) void bwd_group4_kernel(BwdK p) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // [nhs][RB][C4] float4
+  const int N = p.N, H = p.H, G = p.G, HG = H / G, R = p.R, RN = R * N, C4 = RN / 4;
+  const int g = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
+  const int nhs = min(max(1, 256 / C4), HG);
+  const int rows = p.B * p.L, row0 = blk * RB;
+  for (int which = 0; which < 2; ++which) {
+    const float* src = which ? p.dc_head : p.db_head;
+    float* out = which ? p.d_c : p.d_b;
+    for (int it = tid; it < nhs * C4; it += 256) {
+      const int hs = it / C4, c4 = it - hs * C4;
+      floatx4 gacc[RB];
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) gacc[rr] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int hh = hs; hh < HG; hh += nhs) {
+        const float* col = src + ((size_t)row0 * H + g * HG + hh) * RN + 4 * c4;  // row row0 + rr at + rr H RN
+        floatx4 v[RB];
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr)
+          v[rr] = row0 + rr < rows ? ldg4(col + (size_t)rr * H * RN) : floatx4{0.f, 0.f, 0.f, 0.f};
+        floatx4 bs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) {
+          bs += v[rr];
+          gacc[rr] += v[rr];
+        }
+        sts4(p.bias_part + (((size_t)blk * 2 + which) * H + g * HG + hh) * RN + 4 * c4, bs);
+      }
+      if (nhs == 1) {
+        const int cc = 4 * c4, r = cc / N, n = cc - r * N;
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr)
+          if (row0 + rr < rows) sts4(out + ((size_t)(row0 + rr) * R * G + r * G + g) * N + n, gacc[rr]);
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) sts4(lds + ((hs * RB + rr) * C4 + c4) * 4, gacc[rr]);
+      }
+    }
+    if (nhs > 1) {
+      __syncthreads();
+      for (int it = tid; it < RB * C4; it += 256) {
+        const int rr = it / C4, c4 = it - rr * C4;
+        floatx4 s = lds_read4(lds + (rr * C4 + c4) * 4);
+        for (int k = 1; k < nhs; ++k) s += lds_read4(lds + ((k * RB + rr) * C4 + c4) * 4);
+        const int cc = 4 * c4, r = cc / N, n = cc - r * N;
+        if (row0 + rr < rows) sts4(out + ((size_t)(row0 + rr) * R * G + r * G + g) * N + n, s);
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // (9a) d_b_bias, d_c_bias from the block partials (8 outputs per workgroup,
 // 32 strided partial sums each, then a fixed tree); d_d from the chunk partials.
 __global__ __launch_bounds__(256) void bwd_bias_kernel(BwdK p) {
@@ -1992,6 +2049,29 @@ size_t group_lds_bytes(const ScanGeom& g) {
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0u; }
 
+void raise_lds(const void* fn, size_t bytes) {
+  if (bytes > 64 * 1024 &&
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess)
+    (void)hipGetLastError();
+}
+
+// The group reduction (8): 16-byte version when the layout allows it.
+hipError_t launch_group(const ScanGeom& g, const BwdK& k, const BwdOperands& go, const void* workspace,
+                        hipStream_t stream) {
+  const unsigned C4 = (unsigned)(g.R * g.N / 4), HG = (unsigned)(g.H / g.G);
+  if (g.N % 4u == 0 && aligned16(workspace) && aligned16(go.d_b) && aligned16(go.d_c)) {
+    const unsigned nhs = std::min(std::max(1u, 256u / C4), HG);
+    const size_t bytes = nhs > 1 ? (size_t)nhs * RB * C4 * 16 : 0;
+    raise_lds(reinterpret_cast<const void*>(&bwd_group4_kernel), bytes);
+    hipLaunchKernelGGL(bwd_group4_kernel, dim3(k.nrb, g.G), dim3(256), bytes, stream, k);
+  } else {
+    const size_t gl = group_lds_bytes(g);
+    raise_lds(reinterpret_cast<const void*>(&bwd_group_kernel), gl);
+    hipLaunchKernelGGL(bwd_group_kernel, dim3(k.nrb, g.G), dim3(256), gl, stream, k);
+  }
+  return hipGetLastError();
+}
+
 // The chunk prefix (4) over the summaries of mode (1: hs, 2: gs, 3: both).
 hipError_t launch_prefix(const ScanGeom& g, const BwdK& k, int mode, const void* workspace, hipStream_t stream) {
   const unsigned BH = g.B * g.H, PN = g.P * g.N, ndir = mode == 3 ? 2u : 1u;
@@ -2005,11 +2085,6 @@ hipError_t launch_prefix(const ScanGeom& g, const BwdK& k, int mode, const void*
   return hipGetLastError();
 }
 
-void raise_lds(const void* fn, size_t bytes) {
-  if (bytes > 64 * 1024 &&
-      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess)
-    (void)hipGetLastError();
-}
 
 }  // namespace
 
@@ -2081,10 +2156,7 @@ hipError_t launch_siso_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOp
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_apply_kernel, dim3(BH * w.nc), dim3(256), 0, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t gl = group_lds_bytes(g);
-  raise_lds(reinterpret_cast<const void*>(&bwd_group_kernel), gl);
-  hipLaunchKernelGGL(bwd_group_kernel, dim3(w.nrb, g.G), dim3(256), gl, stream, k);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_group(g, k, go, workspace, stream)) != hipSuccess) return e;
   const unsigned nb = (2u * g.H * g.N + g.H + 7u) / 8u;
   hipLaunchKernelGGL(bwd_bias_kernel, dim3(nb), dim3(256), 0, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -2264,10 +2336,7 @@ hipError_t launch_mimo_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOp
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_apply_kernel, dim3(nch), dim3(256), 0, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t gl = group_lds_bytes(g);
-  raise_lds(reinterpret_cast<const void*>(&bwd_group_kernel), gl);
-  hipLaunchKernelGGL(bwd_group_kernel, dim3(w.nrb, g.G), dim3(256), gl, stream, k);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_group(g, k, go, workspace, stream)) != hipSuccess) return e;
   const unsigned nb = (2u * g.H * g.R * g.N + g.H + 7u) / 8u;
   hipLaunchKernelGGL(bwd_bias_kernel, dim3(nb), dim3(256), 0, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
