@@ -707,49 +707,105 @@ __global__ __launch_bounds__(512, 4) void bwd_chunk_kernel(BwdK p) {
 
   // ---- y and GK (per head_dim tile), then dQ and dK (per state tile)
   const int nY = 2 * gm.PT, nQ = 2 * gm.NT;
-  for (int job = wave; job < 2 * nY; job += 8) {
-    const bool isgk = job >= nY;
-    const int jj = isgk ? job - nY : job;
-    const int mt = jj / gm.PT, pt = jj - mt * gm.PT;
-    floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-    const float* Sg = (isgk ? GXg : HEg) + (size_t)pt * 16 * N;
-    const int prow = P - pt * 16;
-    const float* Ra = (isgk ? Kc : Qc) + mt * 16 * NS;
-    if constexpr (VEC4)
-      a1 = mm_tile_k4_g<8>(Ra, NS, Sg, N, prow, N, NN, a1, lane);
-    else
-      a1 = mm_tile_k1_g<32>(Ra, NS, Sg, N, prow, N, NN, a1, lane);
-    if (!isgk)
-      a2 = mm_tile(MQK + mt * 16 * MS, MS, 1, X + pt * 16, PS, 1, BQ, a2, lane);
-    else
-      a2 = mm_tile(VV + mt * 16, 1, MS, GY + pt * 16, PS, 1, BQ, a2, lane);
-    const int pp = pt * 16 + r;
-    float zv[4], gov[4];
+  if constexpr (FIX) {
+    // wave w: y (w < 4) or G K (w >= 4) for head_dim tile pt = w & 3 and both
+    // token halves, so each state tile is read from global memory once
+    const bool isgk = wave >= 4;
+    const int pt = wave & 3;
+    const float* Sg = (isgk ? GXg : HEg) + (pt * 16 + r) * N + 4 * q;  // B[k][n] = S[pt 16 + n][k]
+    floatx4 sv[NC / 16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = mt * 16 + 4 * q + i;
-      const int o = min(t, nv - 1) * HP + min(pp, P - 1);
-      zv[i] = (!isgk && p.has_z) ? p.z[xrow0 + o] : 0.f;
-      gov[i] = (!isgk && p.has_z) ? p.dout[xrow0 + o] : 0.f;
-    }
+    for (int j = 0; j < NC / 16; ++j) sv[j] = ldg4(Sg + 16 * j);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = mt * 16 + 4 * q + i;
-      const bool ok = t < nv && pp < P;
-      const size_t gi = xrow0 + t * HP + pp;
-      const float xv = X[t * PS + pp], gy = GY[t * PS + pp];
-      float part;
-      if (!isgk) {
-        const float y = fmaf(ec[t], a1[i], a2[i]);
-        part = gy * y;
-        if (ok) p.d_z[gi] = p.has_z ? gov[i] * fmaf(Dh, xv, y) * (FIX ? dsilu_fast(zv[i]) : dsilu_acc(zv[i])) : 0.f;
-      } else {
-        const float gk = fmaf(ex[t], a1[i], a2[i]);
-        part = xv * gk;
-        if (ok) p.d_x[gi] = fmaf(Dh + gam[t] * qk[t], gy, scl[t] * gk);
+    for (int mt = 0; mt < 2; ++mt) {
+      floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+      const float* ap = (isgk ? Kc : Qc) + (mt * 16 + r) * NS + 4 * q;
+#pragma unroll
+      for (int j = 0; j < NC / 16; ++j) {
+        const floatx4 av = lds_read4(ap + 16 * j);
+        a1 = mfma16(av[0], sv[j][0], a1);
+        a1 = mfma16(av[1], sv[j][1], a1);
+        a1 = mfma16(av[2], sv[j][2], a1);
+        a1 = mfma16(av[3], sv[j][3], a1);
       }
-      part = row16_sum(ok ? part : 0.f);
-      if (r == 15) (isgk ? ds_part : rho_part)[t * gm.PT + pt] = part;
+      if (!isgk)
+        a2 = mm_tile(MQK + mt * 16 * MS, MS, 1, X + pt * 16, PS, 1, BQ, a2, lane);
+      else
+        a2 = mm_tile(VV + mt * 16, 1, MS, GY + pt * 16, PS, 1, BQ, a2, lane);
+      const int pp = pt * 16 + r;
+      float zv[4], gov[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = mt * 16 + 4 * q + i;
+        const int o = min(t, nv - 1) * HP + min(pp, P - 1);
+        zv[i] = (!isgk && p.has_z) ? p.z[xrow0 + o] : 0.f;
+        gov[i] = (!isgk && p.has_z) ? p.dout[xrow0 + o] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = mt * 16 + 4 * q + i;
+        const bool ok = t < nv && pp < P;
+        const size_t gi = xrow0 + t * HP + pp;
+        const float xv = X[t * PS + pp], gy = GY[t * PS + pp];
+        float part;
+        if (!isgk) {
+          const float y = fmaf(ec[t], a1[i], a2[i]);
+          part = gy * y;
+          if (ok) p.d_z[gi] = p.has_z ? gov[i] * fmaf(Dh, xv, y) * (FIX ? dsilu_fast(zv[i]) : dsilu_acc(zv[i])) : 0.f;
+        } else {
+          const float gk = fmaf(ex[t], a1[i], a2[i]);
+          part = xv * gk;
+          if (ok) p.d_x[gi] = fmaf(Dh + gam[t] * qk[t], gy, scl[t] * gk);
+        }
+        part = row16_sum(ok ? part : 0.f);
+        if (r == 15) (isgk ? ds_part : rho_part)[t * gm.PT + pt] = part;
+      }
+    }
+  } else {
+    for (int job = wave; job < 2 * nY; job += 8) {
+      const bool isgk = job >= nY;
+      const int jj = isgk ? job - nY : job;
+      const int mt = jj / gm.PT, pt = jj - mt * gm.PT;
+      floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+      const float* Sg = (isgk ? GXg : HEg) + (size_t)pt * 16 * N;
+      const int prow = P - pt * 16;
+      const float* Ra = (isgk ? Kc : Qc) + mt * 16 * NS;
+      if constexpr (VEC4)
+        a1 = mm_tile_k4_g<8>(Ra, NS, Sg, N, prow, N, NN, a1, lane);
+      else
+        a1 = mm_tile_k1_g<32>(Ra, NS, Sg, N, prow, N, NN, a1, lane);
+      if (!isgk)
+        a2 = mm_tile(MQK + mt * 16 * MS, MS, 1, X + pt * 16, PS, 1, BQ, a2, lane);
+      else
+        a2 = mm_tile(VV + mt * 16, 1, MS, GY + pt * 16, PS, 1, BQ, a2, lane);
+      const int pp = pt * 16 + r;
+      float zv[4], gov[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = mt * 16 + 4 * q + i;
+        const int o = min(t, nv - 1) * HP + min(pp, P - 1);
+        zv[i] = (!isgk && p.has_z) ? p.z[xrow0 + o] : 0.f;
+        gov[i] = (!isgk && p.has_z) ? p.dout[xrow0 + o] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = mt * 16 + 4 * q + i;
+        const bool ok = t < nv && pp < P;
+        const size_t gi = xrow0 + t * HP + pp;
+        const float xv = X[t * PS + pp], gy = GY[t * PS + pp];
+        float part;
+        if (!isgk) {
+          const float y = fmaf(ec[t], a1[i], a2[i]);
+          part = gy * y;
+          if (ok) p.d_z[gi] = p.has_z ? gov[i] * fmaf(Dh, xv, y) * (FIX ? dsilu_fast(zv[i]) : dsilu_acc(zv[i])) : 0.f;
+        } else {
+          const float gk = fmaf(ex[t], a1[i], a2[i]);
+          part = xv * gk;
+          if (ok) p.d_x[gi] = fmaf(Dh + gam[t] * qk[t], gy, scl[t] * gk);
+        }
+        part = row16_sum(ok ? part : 0.f);
+        if (r == 15) (isgk ? ds_part : rho_part)[t * gm.PT + pt] = part;
+      }
     }
   }
   floatx4 res[4];
@@ -1438,18 +1494,60 @@ __global__ __launch_bounds__(512, 4) void mimo_post_kernel(BwdK p) {
     }
   }
   __syncthreads();
-  for (int job = wave; job < 2 * gm.PT; job += nw) {  // y tiles
-    const int mt = job / gm.PT, pt = job - mt * gm.PT;
-    floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (VEC4)
-      a1 = mm_tile_k4_g<8>(Qc + mt * 16 * NS, NS, HEg + (size_t)pt * 16 * N, N, P - pt * 16, N, NN, a1, lane);
-    else
-      a1 = mm_tile_k1_g<32>(Qc + mt * 16 * NS, NS, HEg + (size_t)pt * 16 * N, N, P - pt * 16, N, NN, a1, lane);
+  if constexpr (FIX) {
+    // y tiles: waves w and w + 4 share head_dim tile w (PT == 4), each over
+    // one half of the state columns and both row halves, so each state tile
+    // is read from global memory once; they swap partial products through
+    // the key rows (dead after the masked Q K^T) and wave w + 4 h finishes
+    // row half h, summing the state halves in order.
+    static_assert(PC == 64, "four head_dim tiles, two waves each");
+    const int pt = wave & 3, kh = wave >> 2;
+    const float* Sg = HEg + (pt * 16 + r) * N + (NC / 2) * kh + 4 * q;
+    floatx4 sv[NC / 32];
+#pragma unroll
+    for (int j = 0; j < NC / 32; ++j) sv[j] = ldg4(Sg + 16 * j);
+    floatx4 part[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      floatx4 a1 = {0.f, 0.f, 0.f, 0.f};
+      const float* ap = Qc + (mt * 16 + r) * NS + (NC / 2) * kh + 4 * q;
+#pragma unroll
+      for (int j = 0; j < NC / 32; ++j) {
+        const floatx4 av = lds_read4(ap + 16 * j);
+        a1 = mfma16(av[0], sv[j][0], a1);
+        a1 = mfma16(av[1], sv[j][1], a1);
+        a1 = mfma16(av[2], sv[j][2], a1);
+        a1 = mfma16(av[3], sv[j][3], a1);
+      }
+      part[mt] = a1;
+    }
+    float* xch = Kc;  // [8 waves][64 lanes] float4
+    sts4(xch + (wave * 64 + lane) * 4, kh ? part[0] : part[1]);
+    __syncthreads();
+    const floatx4 other = lds_read4(xch + ((wave ^ 4) * 64 + lane) * 4);
+    const int mt = kh;
+    const floatx4 a1 = kh ? other + part[1] : part[0] + other;
+    floatx4 a2 = {0.f, 0.f, 0.f, 0.f};
     a2 = mm_tile(MQK + mt * 16 * MS, MS, 1, X + pt * 16, PS, 1, BQ, a2, lane);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int v = mt * 16 + 4 * q + i;
       Y[v * PS + pt * 16 + r] = fmaf(ec[v >> rsl], a1[i], a2[i]);
+    }
+  } else {
+    for (int job = wave; job < 2 * gm.PT; job += nw) {  // y tiles
+      const int mt = job / gm.PT, pt = job - mt * gm.PT;
+      floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (VEC4)
+        a1 = mm_tile_k4_g<8>(Qc + mt * 16 * NS, NS, HEg + (size_t)pt * 16 * N, N, P - pt * 16, N, NN, a1, lane);
+      else
+        a1 = mm_tile_k1_g<32>(Qc + mt * 16 * NS, NS, HEg + (size_t)pt * 16 * N, N, P - pt * 16, N, NN, a1, lane);
+      a2 = mm_tile(MQK + mt * 16 * MS, MS, 1, X + pt * 16, PS, 1, BQ, a2, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = mt * 16 + 4 * q + i;
+        Y[v * PS + pt * 16 + r] = fmaf(ec[v >> rsl], a1[i], a2[i]);
+      }
     }
   }
   __syncthreads();
