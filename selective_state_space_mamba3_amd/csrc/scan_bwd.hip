@@ -444,6 +444,36 @@ __global__ __launch_bounds__(64) void bwd_theta_local_kernel(BwdK p) {
   p.tpre[((size_t)bh * p.nT + tile) * A + lane] = run;
 }
 
+// (1) for A <= 32: one wave per (b, h, tile), half-wave e over tokens
+// 32 e .. 32 e + 31 of the tile and lane a < 32 over the angles; the angles
+// are read straight from global memory (a 128-byte row per token), dt
+// travels between lanes, and the second half adds the first half's total.
+__global__ __launch_bounds__(64) void bwd_theta_local32_kernel(BwdK p) {
+  const int bh = blockIdx.x / p.nT, tile = blockIdx.x - bh * p.nT;
+  const int b = bh / p.H, h = bh - b * p.H, A = p.A, L = p.L;
+  const int lane = threadIdx.x, a = lane & 31, e = lane >> 5;
+  const int t0 = tile * TT, nv = min(TT, L - t0);
+  const float dtv = lane < nv ? p.dt[((size_t)b * L + t0 + lane) * p.H + h] : 0.f;  // lane = token
+  const bool col = a < A;
+  const float* ang = p.angle + ((size_t)b * L + t0 + 32 * e) * A + min(a, A - 1);
+  float th[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) th[i] = (col && 32 * e + i < nv) ? ang[i * A] : 0.f;
+  float run = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    run = fmaf(__shfl(dtv, 32 * e + i, 64), th[i], run);
+    th[i] = run;
+  }
+  const float first = __shfl(run, a, 64);  // the first half's total for angle a
+  const float add = e ? first : 0.f;
+  float* out = p.theta + ((size_t)bh * L + t0 + 32 * e) * A + a;
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if (col && 32 * e + i < nv) out[i * A] = th[i] + add;
+  if (e == 1 && col) p.tpre[((size_t)bh * p.nT + tile) * A + a] = run + add;
+}
+
 // (2) Exclusive prefix over the tiles of the tile totals, in place; one wave
 // per (b, h, a), lanes over tiles.
 __global__ __launch_bounds__(64) void bwd_theta_scan_kernel(BwdK p) {
@@ -989,37 +1019,51 @@ __global__ __launch_bounds__(64) void bwd_chunk_scan_kernel(BwdK p) {
   }
 }
 
-// (7) Per chunk: d adt += the later chunks' terms; the angle suffix
-// theta_bar_t[a] = local suffix + later chunks; d dt, d trap and the per-head
-// angle adjoint dt_t theta_bar_t (in place of the suffix).
+// (7) Per 32-token tile of one (b, h): d adt += the later chunks' terms; the
+// angle suffix theta_bar_t[a] = local suffix + later chunks; d dt, d trap and
+// the per-head angle adjoint dt_t theta_bar_t (in place of the suffix).  A
+// tile spans 32 / Qt chunks; each token reads the totals of its own chunk.
 __global__ __launch_bounds__(256) void bwd_apply_kernel(BwdK p) {
-  __shared__ float part[8][BQ];
-  const int bh = blockIdx.x / p.nc, c = blockIdx.x - bh * p.nc;
+  __shared__ float part[8][32];
+  const int ntile = (p.L + 31) / 32;
+  const int bh = blockIdx.x / ntile, tile = blockIdx.x - bh * ntile;
   const int b = bh / p.H, h = bh - b * p.H;
   const int tid = threadIdx.x, t = tid & 31, k = tid >> 5;
-  const int t0 = c * p.Qt, nv = min(p.Qt, p.L - t0), A = p.A, H = p.H;
-  const int tc = t0 + min(t, nv - 1);
+  const int A = p.A, H = p.H;
+  const int tt = tile * 32 + t;
+  const bool ok = tt < p.L;
+  const int tc = min(tt, p.L - 1);
+  const size_t ci = (size_t)bh * p.nc + tc / p.Qt;  // the token's chunk
   const size_t si = ((size_t)b * p.L + tc) * H + h;
   const float dtv = p.dt[si];
+  // the token scalars are loaded with the angle terms, before the barrier
+  const size_t ri = (size_t)bh * p.L + tc;
+  float trv = 0.f, e = 0.f, dc = 0.f, dadt = 0.f, ptot = 0.f;
+  if (k == 0) {
+    trv = p.trap[si];
+    e = p.ev[ri];
+    dc = tc >= 1 ? p.dsv[ri - 1] : 0.f;
+    dadt = p.d_adt[si];
+    ptot = p.phi_tot[ci];
+  }
+  float* dth = p.dtheta + ((size_t)bh * p.L + tc) * A;
+  const float* tht = p.th_tot + ci * A;
+  const float* ang = p.angle + ((size_t)b * p.L + tc) * A;
   float acc = 0.f;
+#pragma unroll 4
   for (int a = k; a < A; a += 8) {
-    const size_t di = ((size_t)bh * p.L + tc) * A + a;
-    const float tb = p.dtheta[di] + p.th_tot[(size_t)blockIdx.x * A + a];
-    const float an = p.angle[((size_t)b * p.L + tc) * A + a];
-    if (t < nv) p.dtheta[di] = dtv * tb;
-    acc = fmaf(tb, an, acc);
+    const float tb = dth[a] + tht[a];
+    if (ok) dth[a] = dtv * tb;
+    acc = fmaf(tb, ang[a], acc);
   }
   part[k][t] = acc;
   __syncthreads();
-  if (k == 0 && t < nv) {
+  if (k == 0 && ok) {
     float rot = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) rot += part[kk][t];
-    const size_t ri = (size_t)bh * p.L + tc;
-    const float lam = sigmoidf_acc(p.trap[si]);
-    const float e = p.ev[ri];
-    const float dc = tc >= 1 ? p.dsv[ri - 1] : 0.f;
-    p.d_adt[si] += p.phi_tot[blockIdx.x];
+    const float lam = sigmoidf_acc(trv);
+    p.d_adt[si] = dadt + ptot;
     p.d_dt[si] = fmaf(lam, e, fmaf(1.f - lam, dc, rot));
     p.d_trap[si] = lam * (1.f - lam) * dtv * (e - dc);
   }
@@ -1139,38 +1183,46 @@ __global__ __launch_bounds__(256) void bwd_group4_kernel(BwdK p) {
   }
 }
 
-// (9a) d_b_bias, d_c_bias from the block partials (8 outputs per workgroup,
-// 32 strided partial sums each, then a fixed tree); d_d from the chunk partials.
-__global__ __launch_bounds__(256) void bwd_bias_kernel(BwdK p) {
-  __shared__ float red[32][9];
-  const int HN = p.H * p.R * p.N;
-  const int tid = threadIdx.x, o = tid & 7, part = tid >> 3;
-  const int i = blockIdx.x * 8 + o;
+// (9a) d_b_bias and d_c_bias: column sums of the group kernel's block
+// partials [nrb][2][H][R N]; a workgroup of 16 waves takes 64 consecutive
+// columns (lane = column), wave w the partial rows w, w + 16, ... in order,
+// and the 16 wave sums are added in order.  The workgroups after the bias
+// columns sum d_d over the chunks' partials the same way (lane = head).
+__global__ __launch_bounds__(1024) void bwd_bias_kernel(BwdK p) {
+  __shared__ float red[16][64];
+  const int HN = p.H * p.R * p.N, ncol = 2 * HN, nbb = (ncol + 63) / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float s = 0.f;
-  if (i < 2 * HN) {
-    const int which = i / HN, rem = i - which * HN;
-    for (int k = part; k < p.nrb; k += 32) s += p.bias_part[((size_t)k * 2 + which) * HN + rem];
-  } else if (i < 2 * HN + p.H && p.has_d) {
-    const int h = i - 2 * HN;
-    const int per = p.B * p.nc;
-    for (int k = part; k < per; k += 32) {
-      const int bb = k / p.nc, cc = k - bb * p.nc;
-      s += p.dd_part[((size_t)bb * p.H + h) * p.nc + cc];
+  int out = -1;
+  if ((int)blockIdx.x < nbb) {
+    const int col = blockIdx.x * 64 + lane;
+    if (col < ncol) {
+      out = col;
+      const float* src = p.bias_part + col;  // partial row k at + k 2 H R N
+#pragma unroll 4
+      for (int k = w; k < p.nrb; k += 16) s += src[(size_t)k * ncol];
+    }
+  } else {
+    const int hh = ((int)blockIdx.x - nbb) * 64 + lane;
+    if (hh < p.H) {
+      out = ncol + hh;
+      const int per = p.B * p.nc;
+      if (p.has_d) {
+        for (int k = w; k < per; k += 16) {
+          const int bb = k / p.nc, cc = k - bb * p.nc;
+          s += p.dd_part[((size_t)bb * p.H + hh) * p.nc + cc];
+        }
+      }
     }
   }
-  red[part][o] = s;
+  red[w][lane] = s;
   __syncthreads();
-  for (int w = 16; w > 0; w >>= 1) {
-    if (part < w) red[part][o] += red[part + w][o];
-    __syncthreads();
-  }
-  if (part == 0) {
-    if (i < 2 * HN) {
-      const int which = i / HN, rem = i - which * HN;
-      (which == 0 ? p.d_b_bias : p.d_c_bias)[rem] = red[0][o];
-    } else if (i < 2 * HN + p.H) {
-      p.d_d[i - 2 * HN] = red[0][o];
-    }
+  if (w == 0 && out >= 0) {
+    float t = red[0][lane];
+    for (int k = 1; k < 16; ++k) t += red[k][lane];
+    if (out < HN) p.d_b_bias[out] = t;
+    else if (out < ncol) p.d_c_bias[out - HN] = t;
+    else p.d_d[out - ncol] = t;
   }
 }
 
@@ -2054,48 +2106,46 @@ __global__ __launch_bounds__(512, 4) void mimo_chunk_kernel(BwdK p) {
 }
 
 // (M10) mimo_x / mimo_z / mimo_o / norm_weight gradients: sums of the chunk
-// partials over batch and chunks in a fixed order (32 strided partial sums
-// per output, then a tree).
-__global__ __launch_bounds__(256) void mimo_weights_kernel(BwdK p) {
-  __shared__ float red[32][9];
-  const int RP = p.R * p.P, HRP = p.H * RP;
-  const int tid = threadIdx.x, o = tid & 7, part = tid >> 3;
-  const int i = blockIdx.x * 8 + o;  // [mx | mz | mo] x [H][R][P], then nw [H][P]
-  const int per = p.B * p.nc;
-  float s = 0.f;
-  int which = -1, h = 0, rem = 0;
-  if (i < 3 * HRP) {
-    which = i / HRP;
-    const int k = i - which * HRP;
-    h = k / RP;
-    rem = k - h * RP;
-    const float* src = which == 0 ? p.mx_part : which == 1 ? p.mz_part : p.mo_part;
-    for (int k2 = part; k2 < per; k2 += 32) {
-      const int bb = k2 / p.nc, cc = k2 - bb * p.nc;
-      s += src[(((size_t)bb * p.H + h) * p.nc + cc) * RP + rem];
-    }
-  } else if (i < 3 * HRP + p.H * p.P) {
+// partials over batch and chunks.  A workgroup of 16 waves takes 64
+// consecutive columns of one head's [R P] (or [P]) block (lane = column),
+// wave w the (batch, chunk) pairs w, w + 16, ... in order, and the 16 wave
+// sums are added in order.
+__global__ __launch_bounds__(1024) void mimo_weights_kernel(BwdK p) {
+  __shared__ float red[16][64];
+  const int RP = p.R * p.P, cb_rp = (RP + 63) / 64, cb_p = (p.P + 63) / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // workgroups: [which 0..2][h][cb_rp], then [h][cb_p] for the norm weight
+  int blk = blockIdx.x, which, width;
+  if (blk < 3 * p.H * cb_rp) {
+    which = blk / (p.H * cb_rp);
+    blk -= which * p.H * cb_rp;
+    width = RP;
+  } else {
     which = 3;
-    const int k = i - 3 * HRP;
-    h = k / p.P;
-    rem = k - h * p.P;
-    for (int k2 = part; k2 < per; k2 += 32) {
-      const int bb = k2 / p.nc, cc = k2 - bb * p.nc;
-      s += p.nw_part[(((size_t)bb * p.H + h) * p.nc + cc) * p.P + rem];
+    blk -= 3 * p.H * cb_rp;
+    width = p.P;
+  }
+  const int cbn = which == 3 ? cb_p : cb_rp;
+  const int h = blk / cbn;
+  const int col = (blk - h * cbn) * 64 + lane;
+  const float* src = which == 0 ? p.mx_part : which == 1 ? p.mz_part : which == 2 ? p.mo_part : p.nw_part;
+  float s = 0.f;
+  if (col < width) {
+    const int per = p.B * p.nc;
+    for (int k = w; k < per; k += 16) {
+      const int bb = k / p.nc, cc = k - bb * p.nc;
+      s += src[(((size_t)bb * p.H + h) * p.nc + cc) * width + col];
     }
   }
-  red[part][o] = s;
+  red[w][lane] = s;
   __syncthreads();
-  for (int w = 16; w > 0; w >>= 1) {
-    if (part < w) red[part][o] += red[part + w][o];
-    __syncthreads();
-  }
-  if (part == 0 && which >= 0) {
-    const float v = red[0][o];
-    if (which == 0) p.d_mimo_x[(size_t)h * RP + rem] = v;
-    else if (which == 1) p.d_mimo_z[(size_t)h * RP + rem] = p.has_z ? v : 0.f;
-    else if (which == 2) p.d_mimo_o[(size_t)h * RP + rem] = v;
-    else p.d_norm_weight[(size_t)h * p.P + rem] = p.has_norm ? v : 0.f;
+  if (w == 0 && col < width) {
+    float t = red[0][lane];
+    for (int k = 1; k < 16; ++k) t += red[k][lane];
+    if (which == 0) p.d_mimo_x[(size_t)h * RP + col] = t;
+    else if (which == 1) p.d_mimo_z[(size_t)h * RP + col] = p.has_z ? t : 0.f;
+    else if (which == 2) p.d_mimo_o[(size_t)h * RP + col] = t;
+    else p.d_norm_weight[(size_t)h * p.P + col] = p.has_norm ? t : 0.f;
   }
 }
 
@@ -2218,7 +2268,10 @@ hipError_t launch_siso_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOp
   const unsigned BH = g.B * g.H;
   hipError_t e;
   if (g.A > 0) {
-    hipLaunchKernelGGL(bwd_theta_local_kernel, dim3(BH * w.nT), dim3(64), 0, stream, k);
+    if (g.A <= 32)
+      hipLaunchKernelGGL(bwd_theta_local32_kernel, dim3(BH * w.nT), dim3(64), 0, stream, k);
+    else
+      hipLaunchKernelGGL(bwd_theta_local_kernel, dim3(BH * w.nT), dim3(64), 0, stream, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_theta_scan_kernel, dim3(BH * g.A), dim3(64), 0, stream, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -2252,11 +2305,11 @@ hipError_t launch_siso_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOp
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_chunk_scan_kernel, dim3(BH * (g.A + 1)), dim3(64), 0, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_apply_kernel, dim3(BH * w.nc), dim3(256), 0, stream, k);
+  hipLaunchKernelGGL(bwd_apply_kernel, dim3(BH * ((g.L + 31) / 32)), dim3(256), 0, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_group(g, k, go, workspace, stream)) != hipSuccess) return e;
-  const unsigned nb = (2u * g.H * g.N + g.H + 7u) / 8u;
-  hipLaunchKernelGGL(bwd_bias_kernel, dim3(nb), dim3(256), 0, stream, k);
+  const unsigned nb = (2u * g.H * g.N + 63u) / 64u + (g.H + 63u) / 64u;
+  hipLaunchKernelGGL(bwd_bias_kernel, dim3(nb), dim3(1024), 0, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (g.A > 0) {
     const size_t tot = (size_t)g.B * g.L * g.A;
@@ -2386,7 +2439,10 @@ hipError_t launch_mimo_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOp
   const unsigned nch = BH * (unsigned)w.nc;
   hipError_t e;
   if (g.A > 0) {
-    hipLaunchKernelGGL(bwd_theta_local_kernel, dim3(BH * w.nT), dim3(64), 0, stream, k);
+    if (g.A <= 32)
+      hipLaunchKernelGGL(bwd_theta_local32_kernel, dim3(BH * w.nT), dim3(64), 0, stream, k);
+    else
+      hipLaunchKernelGGL(bwd_theta_local_kernel, dim3(BH * w.nT), dim3(64), 0, stream, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_theta_scan_kernel, dim3(BH * g.A), dim3(64), 0, stream, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -2432,14 +2488,14 @@ hipError_t launch_mimo_bwd(const ScanGeom& g, const ScanOperands& o, const BwdOp
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_chunk_scan_kernel, dim3(BH * (g.A + 1)), dim3(64), 0, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_apply_kernel, dim3(nch), dim3(256), 0, stream, k);
+  hipLaunchKernelGGL(bwd_apply_kernel, dim3(BH * ((g.L + 31) / 32)), dim3(256), 0, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_group(g, k, go, workspace, stream)) != hipSuccess) return e;
-  const unsigned nb = (2u * g.H * g.R * g.N + g.H + 7u) / 8u;
-  hipLaunchKernelGGL(bwd_bias_kernel, dim3(nb), dim3(256), 0, stream, k);
+  const unsigned nb = (2u * g.H * g.R * g.N + 63u) / 64u + (g.H + 63u) / 64u;
+  hipLaunchKernelGGL(bwd_bias_kernel, dim3(nb), dim3(1024), 0, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const unsigned nwb = (3u * g.H * g.R * g.P + g.H * g.P + 7u) / 8u;
-  hipLaunchKernelGGL(mimo_weights_kernel, dim3(nwb), dim3(256), 0, stream, k);
+  const unsigned nwb = 3u * g.H * ((g.R * g.P + 63u) / 64u) + g.H * ((g.P + 63u) / 64u);
+  hipLaunchKernelGGL(mimo_weights_kernel, dim3(nwb), dim3(1024), 0, stream, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (g.A > 0) {
     const size_t tot = (size_t)g.B * g.L * g.A;
