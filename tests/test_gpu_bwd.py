@@ -23,6 +23,18 @@ def _print_case(tag):
     print(f"[case] {tag}", flush=True)
 
 
+def _angle_zero(got, ref, d):
+    """One token: Q_0 . K_0 does not change under the shared rotation, so the
+    angle gradient is exactly zero and both sides hold only the rounding
+    residue of the rotation terms that cancel.  The check bounds that residue
+    by the parity tolerance times the scale of the key adjoint d_b."""
+    if not (d.L == 1 and d.A > 0):
+        return False
+    assert np.abs(ref["angle"]).max() <= 1e-12 * np.abs(ref["b"]).max()
+    assert np.abs(got["angle"]).max() <= 1e-4 * np.abs(ref["b"]).max()
+    return True
+
+
 @pytest.mark.parametrize("d", [
     Dims(1, 64, 2, 1, 16, 16, 8),                    # two whole chunks
     Dims(2, 75, 4, 2, 16, 32, 8),                    # ragged last chunk, groups
@@ -31,6 +43,8 @@ def _print_case(tag):
     Dims(1, 96, 2, 1, 64, 128, 32),                  # the N=128 / P=64 / A=32 geometry (its own kernels)
     Dims(1, 77, 4, 2, 64, 128, 32),                  # the same kernels, ragged last chunk, groups
     Dims(2, 45, 2, 1, 64, 128, 32, has_z=False, has_d=False),  # the same kernels without z and D
+    Dims(1, 1, 2, 1, 64, 128, 32),                   # the same kernels, a single token
+    Dims(3, 20, 2, 2, 64, 128, 32),                  # the same kernels, one partial chunk, one head per group
     Dims(1, 40, 2, 1, 32, 64, 0),                    # no rotary angles
     Dims(1, 70, 2, 1, 128, 128, 64),                 # the largest head_dim, state and angle count
     Dims(1, 31, 2, 2, 16, 32, 16, has_z=False, has_d=False),  # A = N/2, shorter than a chunk
@@ -43,7 +57,7 @@ def test_siso_bwd_matches_oracle(d):
     got = _gpu_bwd(to_dev(inp), torch.from_numpy(dout).cuda(), d)
     ref = O.siso_backward(dout, *[inp[k] for k in OPS11], cfg_oracle(d))
     for k in OPS11:
-        if k == "angle" and d.A == 0:
+        if k == "angle" and (d.A == 0 or _angle_zero(got, ref, d)):
             continue
         assert_parity(got[k], ref[k], f"d_{k}")
     if not d.has_z:

@@ -21,6 +21,18 @@ def _gpu_bwd(inp_dev, dout_dev, d):
     return {k: v.cpu().numpy() for k, v in g.items()}
 
 
+def _angle_zero(got, ref, d):
+    """One token: Q_0 . K_0 does not change under the shared rotation, so the
+    angle gradient is exactly zero and both sides hold only the rounding
+    residue of the rotation terms that cancel.  The check bounds that residue
+    by the parity tolerance times the scale of the key adjoint d_b."""
+    if not (d.L == 1 and d.A > 0):
+        return False
+    assert np.abs(ref["angle"]).max() <= 1e-12 * np.abs(ref["b"]).max()
+    assert np.abs(got["angle"]).max() <= 1e-4 * np.abs(ref["b"]).max()
+    return True
+
+
 @pytest.mark.parametrize("d", [
     Dims(1, 40, 2, 1, 16, 32, 8, R=2, has_output_norm=True),
     Dims(2, 37, 4, 2, 16, 32, 8, R=3, has_z=False),                 # a padding rank, groups
@@ -29,6 +41,8 @@ def _gpu_bwd(inp_dev, dout_dev, d):
     Dims(2, 37, 4, 2, 64, 128, 32, R=2, has_z=False),               # the same, groups, no z
     Dims(1, 20, 2, 1, 64, 128, 32, R=8, has_d=False),               # the same, eight ranks
     Dims(1, 33, 2, 1, 64, 128, 32, R=1, has_output_norm=True),      # the same, one rank
+    Dims(2, 1, 2, 2, 64, 128, 32, R=4, has_output_norm=True),       # the same, a single token, one head per group
+    Dims(1, 6, 2, 1, 64, 128, 32, R=8),                             # the same, one partial chunk of eight ranks
     Dims(1, 50, 2, 1, 32, 64, 16, R=1, has_output_norm=True),
     Dims(1, 21, 2, 2, 16, 16, 4, R=8, has_d=False),
     Dims(2, 30, 2, 1, 5, 6, 3, R=2, has_output_norm=True),          # odd sizes
@@ -42,7 +56,7 @@ def test_mimo_bwd_matches_oracle(d):
     got = _gpu_bwd(to_dev(inp), torch.from_numpy(dout).cuda(), d)
     ref = O.mimo_backward(dout, *[inp[k] for k in OPS15], cfg_oracle(d))
     for k in OPS15:
-        if (k == "angle" and d.A == 0) or (k == "norm_weight" and not d.has_output_norm):
+        if (k == "angle" and (d.A == 0 or _angle_zero(got, ref, d))) or (k == "norm_weight" and not d.has_output_norm):
             continue
         if (k in ("z", "mimo_z") and not d.has_z) or (k == "d" and not d.has_d):
             assert not np.any(got[k]), k
