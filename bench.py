@@ -39,7 +39,8 @@ HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, GB/s
 FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 (vector and matrix)
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_b4_l2048_traffic.json")
-MAIN_KERNEL = "scan_chunk_kernel<4, true, false"  # main scan pass of the N=128/P=64 SISO variant
+MAIN_KERNEL = "scan_chunk_kernel<4, true, false, 8, 4, 8, 1, true>"  # main pass on the packed rows (the step)
+DENSE_KERNEL = "scan_chunk_kernel<4, true, false, 8, 4, 8, 1, false>"  # main pass on dense operands
 COPY_KERNEL = "neg_kernel"  # torch.neg over a float32 buffer: reads and writes n*4 bytes once
 
 
@@ -57,7 +58,8 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first: the GPU reaches its steady clocks after some tens of ms of work")
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated through the timed loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=24, help="heads in the oracle's timed sample")
@@ -190,35 +192,6 @@ def measure_rows(torch, m3, lib, hip, new_event, dev):
                          "algorithmic_bytes": byt, "gbs": byt / (cm * 1e-3) / 1e9}
     del inp, ops, ws, out
 
-    # fused preprocess -> scan on the packed rows, the bench step's workload
-    from workloads import packed_projection
-    w = WORKLOADS["siso_b4_l2048"]
-    d = w.dims
-    sets = [packed_projection(d, seed=w.seed + k) for k in range(3)]
-    pcfg = m3.PreprocessConfig(d.H * d.P, d.N, d.H, d.A, d.groups, 1, 1e-5, 1e-3, 0.1, 1e-4)
-    cfg = m3.SsmConfig(d.B, d.L, d.H, d.G, d.P, d.N, d.A)
-    tens = [{k: torch.from_numpy(v).to(dev) for k, v in st.items()} for st in sets]
-    out = torch.empty(d.B, d.L, d.H, d.P, device=dev)
-    ws = torch.empty(m3.siso_fwd_packed_workspace_bytes(pcfg, cfg), dtype=torch.uint8, device=dev)
-
-    def one_f(i):
-        t = tens[i % 3]
-        m3.m3_siso_fwd_packed(t["projected"], t["dt_bias"], t["c_bias"], t["b_bias"], t["d"], pcfg, cfg,
-                              out=out, workspace=ws)
-    for i in range(6):
-        one_f(i)
-    torch.cuda.synchronize()
-    n_calls = 30
-    a.record()
-    for i in range(n_calls):
-        one_f(i)
-    b.record()
-    torch.cuda.synchronize()
-    fm = a.elapsed_time(b) / n_calls
-    rows["fused_step"] = {"workload": "siso_b4_l2048 packed rows [8192 x 3432] -> out, one m3_siso_fwd_packed call",
-                          "ms": fm, "tokens_per_s": d.B * d.L / (fm * 1e-3), "calls_timed": n_calls,
-                          "input_sets": 3}
-    del sets, tens, out, ws
 
     # SISO backward at the forward's geometry: the eleven gradients from dout
     from workloads import output_gradient, preprocess_output_gradients, packed_projection
@@ -351,7 +324,7 @@ def summarize(stats_dir, fetch_dir, write_dir, calib_mib):
     fetch_scale = known / (f_copy * 1024.0)
     write_scale = known / (w_copy * 1024.0)
     out = {
-        "kernel": MAIN_KERNEL + ", ...> (main scan pass)",
+        "kernel": MAIN_KERNEL + " (main scan pass on the packed rows)",
         "workload": "siso_b4_l2048 (B4 L2048 H24 G1 P64 N128 A32), bench.py default run",
         "kernel_source_sha256": kernel_source_hash(),
         "fetch_kib_per_dispatch": f_main, "write_kib_per_dispatch": w_main,
@@ -376,7 +349,7 @@ def recorded_traffic():
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if rec.get("kernel_source_sha256") != kernel_source_hash() or not rec.get("kernel", "").startswith(MAIN_KERNEL):
         return None
     return rec.get("traffic_bytes")
 
@@ -433,6 +406,7 @@ def main():
                 "trap": torch.empty(rows, H, device=dev), "angle": torch.empty(rows, A, device=dev)}
         ds["pre"] = outs
         ds["out"] = torch.empty(B, L, H, P, device=dev)
+        ds["out2"] = torch.empty(B, L, H, P, device=dev)
         sets.append(ds)
     ws = torch.empty(max(1, m3.siso_fwd_workspace_bytes(scfg)), dtype=torch.uint8, device=dev)
 
@@ -442,13 +416,21 @@ def main():
                 o["z"].view(B, L, H, P), o["adt"].view(B, L, H), o["dt"].view(B, L, H),
                 o["trap"].view(B, L, H), o["angle"].view(B, L, A), s["c_bias"], s["b_bias"], s["d"])
 
-    def step(s, ev=None):
+    fws = torch.empty(max(1, m3.siso_fwd_packed_workspace_bytes(pcfg, scfg)), dtype=torch.uint8, device=dev)
+
+    def step(s):
+        """The bench step: preprocess fused into the scan, one call on the packed rows."""
+        m3.m3_siso_fwd_packed(s["projected"], s["dt_bias"], s["c_bias"], s["b_bias"], s["d"], pcfg, scfg,
+                              out=s["out"], workspace=fws)
+
+    def two_call(s, ev=None):
+        """The same pass as two calls: m3_preprocess, then m3_siso_fwd on its outputs."""
         if ev is not None:
             ev[0].record()
         m3.m3_preprocess(s["projected"], s["dt_bias"], pcfg, outs=s["pre"])
         if ev is not None:
             ev[1].record()
-        m3.m3_siso_fwd(*scan_operands(s), scfg, out=s["out"], workspace=ws)
+        m3.m3_siso_fwd(*scan_operands(s), scfg, out=s["out2"], workspace=ws)
         if ev is not None:
             ev[2].record()
 
@@ -458,7 +440,9 @@ def main():
         import oracle as O
         s0 = sets[0]
         step(s0)
+        two_call(s0)
         torch.cuda.synchronize()
+        same = bool(torch.equal(s0["out"], s0["out2"]))
         hs = host_sets[0]
         ocfg = O.PreprocessConfig(I, N, H, A, G, 1, 1e-5, 1e-3, 0.1, 1e-4)
         pre = O.preprocess(hs["projected"], hs["dt_bias"], ocfg)
@@ -471,7 +455,8 @@ def main():
         got = s0["out"].cpu().numpy()[:, :, heads]
         e = O.parity_error(got, ref)
         parity = {"e": e["e"], "tol": 1e-4, "sample": f"all batch rows of heads {heads}, full sequence",
-                  "pass": bool(e["e"] <= 1e-4 and e["nonfinite"] == 0)}
+                  "pass": bool(e["e"] <= 1e-4 and e["nonfinite"] == 0 and same),
+                  "two_call_bit_identical": same}
         if not parity["pass"]:
             print(json.dumps({"parity_failed": parity}), file=sys.stderr)
             return 4
@@ -479,6 +464,7 @@ def main():
     # ---- warmup ------------------------------------------------------------
     for i in range(args.warmup):
         step(sets[i % len(sets)])
+        two_call(sets[i % len(sets)])
     torch.cuda.synchronize()
 
     # ---- timed region ------------------------------------------------------
@@ -496,7 +482,6 @@ def main():
 
     K = args.steps
     kern_ev = [(new_event(), new_event()) for _ in range(K)]
-    step_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -504,10 +489,24 @@ def main():
     t_begin.record()
     for i in range(K):
         lib.m3_set_profile_events(kern_ev[i][0], kern_ev[i][1])
-        step(sets[i % len(sets)], step_ev[i])
+        step(sets[i % len(sets)])
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    lib.m3_set_profile_events(None, None)
+
+    # the two-call form of the same pass, after the timed region: its own
+    # breakdown and the dense main pass's time
+    dense_ev = [(new_event(), new_event()) for _ in range(K)]
+    step_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t2_begin = torch.cuda.Event(enable_timing=True)
+    t2_end = torch.cuda.Event(enable_timing=True)
+    t2_begin.record()
+    for i in range(K):
+        lib.m3_set_profile_events(dense_ev[i][0], dense_ev[i][1])
+        two_call(sets[i % len(sets)], step_ev[i])
+    t2_end.record()
+    torch.cuda.synchronize()
     lib.m3_set_profile_events(None, None)
 
     if args.calib_copy_mib > 0:
@@ -521,22 +520,27 @@ def main():
 
     rows_out = None
     if not args.no_rows:
-        del sets, ws
+        del sets, ws, fws
         torch.cuda.empty_cache()
         rows_out = measure_rows(torch, m3, lib, hip, new_event, dev)
 
     ms_total = t_begin.elapsed_time(t_end)
     ms_step = ms_total / K
     f = ctypes.c_float()
-    kern_ms = []
-    for a, b in kern_ev:
-        hip.hipEventElapsedTime(ctypes.byref(f), a, b)
-        kern_ms.append(f.value)
-        hip.hipEventDestroy(a)
-        hip.hipEventDestroy(b)
+
+    def event_ms(pairs):
+        out = []
+        for a, b in pairs:
+            hip.hipEventElapsedTime(ctypes.byref(f), a, b)
+            out.append(f.value)
+            hip.hipEventDestroy(a)
+            hip.hipEventDestroy(b)
+        return float(np.mean(out))
+    kern_avg = event_ms(kern_ev)
+    dense_avg = event_ms(dense_ev)
     pre_ms = [ev[0].elapsed_time(ev[1]) for ev in step_ev]
     scan_ms = [ev[1].elapsed_time(ev[2]) for ev in step_ev]
-    kern_avg = float(np.mean(kern_ms))
+    two_ms = t2_begin.elapsed_time(t2_end) / K
     tokens = B * L
     scan_bytes = scan_algorithmic_bytes(B, L, H, G, P, N, A)
     pre_bytes = preprocess_algorithmic_bytes(rows, W, I, M, H, A)
@@ -586,15 +590,21 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "siso_b4_l2048: m3_preprocess [8192 x 3432] -> m3_siso_fwd",
+        "config": {"workload": "siso_b4_l2048: m3_siso_fwd_packed on the [8192 x 3432] packed projection "
+                               "(preprocess fused into the scan)",
                    "batch": B, "seq_len": L, "heads": H, "groups": G, "head_dim": P, "state": N,
                    "rope_angles": A, "has_z": True, "has_d": True, "input_sets": args.sets},
         "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": kern_gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(),
-                     "kernel": "scan_chunk_kernel<4, true, false, 8, 4, 8, 1, false> (main scan pass)",
+                     "kernel": MAIN_KERNEL + " (main scan pass on the packed rows)",
                      "kernel_ms": kern_avg, "algorithmic_bytes": scan_bytes,
                      "fp32_tflops_min_work": min_flops / (kern_avg * 1e-3) / 1e12,
                      "fp32_frac": min_flops / (kern_avg * 1e-3) / 1e12 / FP32_PEAK_TFLOPS},
+        "two_call_step": {"ms": two_ms, "tokens_per_s": tokens / (two_ms * 1e-3),
+                          "calls": "m3_preprocess then m3_siso_fwd", "main_kernel": DENSE_KERNEL,
+                          "main_kernel_ms": dense_avg, "main_kernel_gbs": scan_bytes / (dense_avg * 1e-3) / 1e9,
+                          "main_kernel_hbm_frac": scan_bytes / (dense_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "steps_timed": K},
         "scan": {"call_ms": scan_call_ms, "tokens_per_s": tokens / (scan_call_ms * 1e-3),
                  "gbs": scan_bytes / (scan_call_ms * 1e-3) / 1e9,
                  "hbm_frac": scan_bytes / (scan_call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
