@@ -81,6 +81,68 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreKParams p, int vec, 
     for (int a = tid; a < p.A; a += nthreads) p.angle[(size_t)r * p.A + a] = sc[3 * p.H + a];
 }
 
+// The derived outputs only (bh, ch, dt, adt) for the fused preprocess ->
+// scan: one wave per packed row, four rows per workgroup, so the whole grid
+// is resident at once.  Each wave loads a B row and the matching C row
+// together, then reduces both; lanes h < H take the dt / A columns.
+__global__ __launch_bounds__(256) void preprocess_derived_kernel(PreKParams p) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= p.rows) return;
+  const float* row = p.projected + (size_t)r * p.W;
+  const int nb = p.M / p.N;  // B rows (and C rows) per packed row
+  for (int k = 0; k < nb; ++k) {
+    const float* sb = row + 2 * p.I + k * p.N;
+    const float* scc = sb + p.M;
+    float vb[2], vc[2], sbs = 0.f, scs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = lane + 64 * e;
+      vb[e] = i < p.N ? sb[i] : 0.f;
+      vc[e] = i < p.N ? scc[i] : 0.f;
+    }
+    // each lane sums its elements in index order, as preprocess_kernel does,
+    // so both kernels give the same bits
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      sbs = fmaf(vb[e], vb[e], sbs);
+      scs = fmaf(vc[e], vc[e], scs);
+    }
+    for (int i = lane + 128; i < p.N; i += 64) {  // N > 128: the rest of the sums
+      sbs = fmaf(sb[i], sb[i], sbs);
+      scs = fmaf(scc[i], scc[i], scs);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      sbs += __shfl_xor(sbs, off, 64);
+      scs += __shfl_xor(scs, off, 64);
+    }
+    const float ib = 1.f / sqrtf(sbs / (float)p.N + p.eps);
+    const float ic = 1.f / sqrtf(scs / (float)p.N + p.eps);
+    float* db = p.bh + (size_t)r * p.M + (size_t)k * p.N;
+    float* dc = p.ch + (size_t)r * p.M + (size_t)k * p.N;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = lane + 64 * e;
+      if (i < p.N) {
+        db[i] = vb[e] * ib;
+        dc[i] = vc[e] * ic;
+      }
+    }
+    for (int i = lane + 128; i < p.N; i += 64) {
+      db[i] = sb[i] * ib;
+      dc[i] = scc[i] * ic;
+    }
+  }
+  const float* sc = row + 2 * p.I + 2 * p.M;
+  for (int h = lane; h < p.H; h += 64) {
+    const float dtv = fminf(fmaxf(softplusf_acc(sc[h] + p.dt_bias[h]), p.dt_min), p.dt_max);
+    const float amag = fmaxf(softplusf_acc(sc[p.H + h]), p.a_floor);
+    p.dt[(size_t)r * p.H + h] = dtv;
+    p.adt[(size_t)r * p.H + h] = -amag * dtv;
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -97,7 +159,10 @@ hipError_t launch_pre(const PreGeom& g, const PreOperands& o, int derived, hipSt
   kp.eps = g.eps; kp.dt_min = g.dt_min; kp.dt_max = g.dt_max; kp.a_floor = g.a_floor;
   auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) % 16u) == 0u; };
   const int vec = (!derived && kp.W % 4 == 0 && kp.I % 4 == 0 && al16(o.projected) && al16(o.x) && al16(o.z)) ? 1 : 0;
-  hipLaunchKernelGGL(preprocess_kernel, dim3(g.rows), dim3(256), 0, stream, kp, vec, derived);
+  if (derived)
+    hipLaunchKernelGGL(preprocess_derived_kernel, dim3((g.rows + 3) / 4), dim3(256), 0, stream, kp);
+  else
+    hipLaunchKernelGGL(preprocess_kernel, dim3(g.rows), dim3(256), 0, stream, kp, vec, derived);
   return hipGetLastError();
 }
 
