@@ -279,7 +279,10 @@ int m3_mimo_step(const float* c, const float* b, const float* x, const float* z,
  *   bias sums (plus a few rows) exceeds one CU's 160 KiB of LDS, which takes
  *   more than about 150 heads per group at N = 128.  d_angle may be NULL
  *   when A == 0.  The reductions run in a fixed order, so repeated calls
- *   give identical results.
+ *   with the same pointers give identical results.  At N = 128, P = 64,
+ *   A = 32, kernels compiled for that geometry run when b, c, x, z, dout,
+ *   both biases and the workspace are 16-byte aligned; with a misaligned
+ *   one the general kernels run, whose results may differ in the last bits.
  */
 size_t m3_siso_bwd_workspace_bytes(m3_ssm_config cfg);
 int m3_siso_bwd(const float* dout, const float* c, const float* b, const float* x,
@@ -307,7 +310,10 @@ int m3_siso_bwd(const float* dout, const float* c, const float* b, const float* 
  *   B8 L4096 H32 P64 N128 R4.
  * Rules: those of m3_mimo_fwd, plus M3_ERR_UNSUPPORTED when a kernel's
  *   working set exceeds one CU's 160 KiB of LDS.  Fixed-order reductions:
- *   repeated calls give identical results.
+ *   repeated calls with the same pointers give identical results.  As for
+ *   m3_siso_bwd, N = 128 / P = 64 / A = 32 with 16-byte aligned operands
+ *   (mimo_x included) and workspace takes kernels compiled for that
+ *   geometry, which may differ from the general ones in the last bits.
  */
 size_t m3_mimo_bwd_workspace_bytes(m3_ssm_config cfg);
 int m3_mimo_bwd(const float* dout, const float* c, const float* b, const float* x,
