@@ -17,6 +17,48 @@ __device__ __forceinline__ floatx4 mfma16(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Three-term bf16 split of fp32 products on v_mfma_f32_16x16x32_bf16.  An
+// fp32 value x is written as hi + lo with hi = bf16(x) and lo = bf16(x - hi)
+// (both round-to-nearest-even); a product a b is then taken as
+// a_hi b_hi + a_hi b_lo + a_lo b_hi, which drops only a_lo b_lo and the
+// rounding of the two lo parts: relative error about 2^-16 per product, with
+// fp32 accumulation.  Lane l supplies A[l % 16][k] and B[k][l % 16] for eight
+// k-slots (the same slot -> k map for both operands, so any assignment of the
+// contraction index to slots is valid); the result layout matches mfma16.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef unsigned int uintx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mfma_bf16(uintx4 a, uintx4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+// a b with both operands split: three bf16 MFMAs into one accumulator.
+__device__ __forceinline__ floatx4 mfma_bf16x3(uintx4 ah, uintx4 al, uintx4 bh, uintx4 bl, floatx4 c) {
+  c = mfma_bf16(ah, bh, c);
+  c = mfma_bf16(ah, bl, c);
+  return mfma_bf16(al, bh, c);
+}
+// Split two fp32 values; the first goes to the low 16 bits of each word.
+__device__ __forceinline__ void split2_bf16(float x0, float x1, unsigned& hi, unsigned& lo) {
+  hi = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){x0, x1}, bf16x2));
+  const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){x0 - h0, x1 - h1}, bf16x2));
+}
+// Eight fp32 values into packed bf16x8 hi / lo operands.
+__device__ __forceinline__ void split8_bf16(const float* v, uintx4& hi, uintx4& lo) {
+  unsigned h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) split2_bf16(v[2 * i], v[2 * i + 1], h[i], l[i]);
+  hi = uintx4{h[0], h[1], h[2], h[3]};
+  lo = uintx4{l[0], l[1], l[2], l[3]};
+}
+// Exchange a word with the neighbouring lane (lanes 2i and 2i + 1; DPP quad_perm 1,0,3,2).
+__device__ __forceinline__ unsigned swap_pair_u(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false);
+}
+
 // exp(x) through the hardware exp2 (v_exp_f32): relative error about
 // |x| * 2^-23 from the log2(e) scaling, used where the result multiplies
 // terms that are themselves negligible once |x| is large.
@@ -147,7 +189,6 @@ __device__ __forceinline__ floatx4 buf_load4(rsrc_t r, uint32_t byte_off) {
 __device__ __forceinline__ float buf_load1(rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
 }
-typedef unsigned int uintx4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t byte_off, floatx4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uintx4, v), r, byte_off, 0, 0);
 }

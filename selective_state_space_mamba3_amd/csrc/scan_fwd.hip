@@ -42,6 +42,8 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
+
 namespace m3 {
 namespace {
 
@@ -49,6 +51,10 @@ constexpr int kAux = 68;        // per segment summary: angle increment [<=64], 
 constexpr int kAuxDecay = 64;
 constexpr float kNormEps = 1.0e-5f;  // MIMO output-norm epsilon of the MIMO push constants
 constexpr int kQV = 32;         // virtual rows per chunk
+// Summary-pass key buffer, transposed for the bf16 state update: per state
+// coordinate n one row of 40 bf16 (32 virtual rows + 8 of padding, 20 words),
+// so that the 16 rows read by one lane group start 20 banks apart.
+constexpr int kKTw = 20;
 
 struct ScanKParams {
   const float *c, *b, *x, *z, *adt, *dt, *trap, *angle, *c_bias, *b_bias, *d;
@@ -176,6 +182,14 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   // S is split over six waves (three tile pairs x two N-halves).
   constexpr bool MERGED = FIXED && NTC * 16 == 16 * NWC && RSC > 0;
   const int sw = nwaves - 1;  // wave that computes the per-token scalars
+  // The SISO summary pass of the merged layout runs its state update on bf16
+  // MFMA with the three-term split (v_mfma_f32_16x16x32_bf16, k = the chunk's 32
+  // virtual rows); its keys go to LDS split and transposed, [n][slot].  Lane
+  // group q of an MFMA operand holds virtual rows 4q..4q+3 and 16+4q..16+4q+3
+  // in its eight k-slots, so row v sits in slot position
+  //     pos(v) = 8 ((v >> 2) & 3) + 4 (v >> 4) + (v & 3)
+  // of its key row, and the x rows a lane reads are 4 apart (16 banks apart).
+  constexpr bool BF3 = !FULL && MERGED && !MIMO;
 
   float* Ql = lds + p.o_ql;   // [QV][ks] C (+bias), pairs rotated in place   (main pass)
   float* Kl = lds + p.o_kl;   // [QV][ks] B (+bias), pairs rotated in place
@@ -199,6 +213,8 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   float* sc_w = sc_scl + QV;
   float* sc_dt = sc_w + QV;
   float* run = lds + p.o_run;  // [0,64) running theta, [64] chunk decay
+  unsigned* KTh = reinterpret_cast<unsigned*>(Kl);  // [N][kKTw] bf16 pairs of K, hi parts  (BF3)
+  unsigned* KTl = KTh + N * kKTw;                     // lo parts
 
   for (int i = tid; i < p.lds_floats; i += nthreads) lds[i] = 0.f;
   __syncthreads();
@@ -518,8 +534,35 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         q0 = k0;
         q1 = k0;
       }
-      vstore<VEC>(Kl + mt * ks + mc0, k0);
-      vstore<VEC>(Kl + mt * ks + mc1, k1);
+      if constexpr (BF3) {
+        // Lanes 2i, 2i + 1 (virtual rows mt, mt + 1) trade halves so that each
+        // writes one word (row mt, row mt + 1) for four columns: the even lane
+        // for its columns mc0.., the odd lane for its columns mc1..
+        unsigned hh[4], ll[4];
+        split2_bf16(k0[0], k0[1], hh[0], ll[0]);
+        split2_bf16(k0[2], k0[3], hh[1], ll[1]);
+        split2_bf16(k1[0], k1[1], hh[2], ll[2]);
+        split2_bf16(k1[2], k1[3], hh[3], ll[3]);
+        const bool odd = (mt & 1) != 0;
+        const int col = odd ? mc1 : mc0;
+        const int wd = (8 * ((mt >> 2) & 3) + 4 * (mt >> 4) + (mt & 2)) >> 1;  // pos(mt & ~1) / 2
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          const unsigned* v4 = part ? ll : hh;
+          unsigned* dst = (part ? KTl : KTh) + col * kKTw + wd;
+          const unsigned r0 = swap_pair_u(odd ? v4[0] : v4[2]);
+          const unsigned r1 = swap_pair_u(odd ? v4[1] : v4[3]);
+          const unsigned a0 = odd ? r0 : v4[0], a1 = odd ? r1 : v4[1];      // row mt & ~1
+          const unsigned b0 = odd ? v4[2] : r0, b1 = odd ? v4[3] : r1;      // row mt | 1
+          dst[0 * kKTw] = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
+          dst[1 * kKTw] = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
+          dst[2 * kKTw] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
+          dst[3 * kKTw] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
+        }
+      } else {
+        vstore<VEC>(Kl + mt * ks + mc0, k0);
+        vstore<VEC>(Kl + mt * ks + mc1, k1);
+      }
       if (FULL) {
         vstore<VEC>(Ql + mt * ks + mc0, q0);
         vstore<VEC>(Ql + mt * ks + mc1, q1);
@@ -697,7 +740,25 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       const float dec = run[64];
 #pragma unroll
       for (int j = 0; j < JMAX; ++j) Hacc[j] *= dec;
-      for (int sb = 0; sb < TB; ++sb) {
+      if constexpr (BF3) {
+        // B operand: w x of column p0 + l16 at virtual rows 4 lq + i, 16 + 4 lq + i
+        float wx[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int v = 16 * (i >> 2) + 4 * lq + (i & 3);
+          wx[i] = Xl[v * xs + p0 + l16] * sc_w[v >> rsl];
+        }
+        uintx4 bh, bl;
+        split8_bf16(wx, bh, bl);
+#pragma unroll
+        for (int j = 0; j < JMAX; ++j) {
+          const int n = (nb0 + j) * 16 + l16;
+          const uintx4 ah = *reinterpret_cast<const uintx4*>(KTh + n * kKTw + 4 * lq);
+          const uintx4 al = *reinterpret_cast<const uintx4*>(KTl + n * kKTw + 4 * lq);
+          Hacc[j] = mfma_bf16x3(ah, al, bh, bl, Hacc[j]);
+        }
+      }
+      for (int sb = 0; sb < (BF3 ? 0 : TB); ++sb) {
         const int v0 = sb * 16 + 4 * lq;
         const float* xc = Xl + v0 * xs + p0 + l16;
         const float xw0 = xc[0] * sc_w[(v0 + 0) >> rsl];
@@ -845,7 +906,7 @@ void layout(ScanKParams& kp, bool full, bool mimo) {
   kp.ys = kp.PT * 16 + 4;
   int off = 0;
   kp.o_ql = off; off += full ? QV * kp.ks : 0;
-  kp.o_kl = off; off += QV * kp.ks;
+  kp.o_kl = off; off += full ? QV * kp.ks : std::max(QV * kp.ks, 2 * kp.NT * 16 * kKTw);
   kp.o_xl = off; off += QV * kp.xs;
   kp.o_ml = off; off += full ? QV * kp.ms : 0;
   kp.o_ml2 = off; off += (full && kp.NH > 1) ? QV * kp.ms : 0;
