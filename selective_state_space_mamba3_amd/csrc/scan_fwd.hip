@@ -27,12 +27,19 @@
 //     segment.  The N-parts' partial outputs meet in LDS.  The block has
 //     enough waves that each thread prefetches at most two 16-byte B and C
 //     vectors, so a wave fits in 128 VGPRs and four waves share each SIMD.
-//   * Intra-chunk S = Q K^T, the decay/trapezoid mask, M X, the carried-state
-//     read Q h'^T and the state update K^T (w X) all run on
-//     v_mfma_f32_16x16x4_f32.
+//   * Intra-chunk S = Q K^T, the decay/trapezoid mask, M X and the
+//     carried-state read Q h'^T run on v_mfma_f32_16x16x4_f32.  The state
+//     update K^T (w X) does too, except in the SISO N = 128 / P = 64 variant,
+//     where it runs on v_mfma_f32_16x16x32_bf16 with each fp32 operand split
+//     into a bf16 head and remainder (three products, fp32 accumulation,
+//     about 2^-16 relative error per product): the fp32 matrix pipe issues
+//     through the vector ALU on gfx950, and the update is a third of the
+//     chunk's matrix work.
 //   * The next chunk's x, B, C, angle and scalars are loaded into registers
 //     while the current chunk's MFMA work runs; z is loaded at the start of
-//     the chunk that uses it.  The cumulative angle is a 32-lane scan.
+//     the chunk that uses it.  (The bf16-update variant issues the next x
+//     and this chunk's z after S, where its registers allow.)  The
+//     cumulative angle is a 32-lane scan.
 //   * Sequence segments: a first pass computes each segment's end state
 //     from a zero entry (plus its decay product and angle increment) into
 //     the workspace; the main pass folds the earlier segments' summaries
@@ -51,10 +58,11 @@ constexpr int kAux = 68;        // per segment summary: angle increment [<=64], 
 constexpr int kAuxDecay = 64;
 constexpr float kNormEps = 1.0e-5f;  // MIMO output-norm epsilon of the MIMO push constants
 constexpr int kQV = 32;         // virtual rows per chunk
-// Summary-pass key buffer, transposed for the bf16 state update: per state
-// coordinate n one row of 40 bf16 (32 virtual rows + 8 of padding, 20 words),
-// so that the 16 rows read by one lane group start 20 banks apart.
-constexpr int kKTw = 20;
+// Key buffer of the bf16 state update, transposed: per state coordinate n one
+// row of 32 bf16 (16 words), its four 16-byte blocks stored in the order
+// q ^ ((n >> 2) & 3), so that the 16 rows read by one lane group hit 16
+// different bank groups.
+constexpr int kKTw = 16;
 
 struct ScanKParams {
   const float *c, *b, *x, *z, *adt, *dt, *trap, *angle, *c_bias, *b_bias, *d;
@@ -71,9 +79,19 @@ struct ScanKParams {
   int xstr, tstr, astr;  // per-token strides of x / z, trap and angle (packed rows share one)
   int seg_len, nseg;
   // LDS layout (float offsets) and row strides
-  int o_ql, o_kl, o_xl, o_ml, o_ml2, o_yl, o_yl2, o_cs, o_bias, o_mimo, o_sc, o_run, lds_floats;
+  int o_ql, o_kl, o_kt, o_xl, o_ml, o_ml2, o_yl, o_yl2, o_cs, o_bias, o_mimo, o_sc, o_run, lds_floats;
   int ks, xs, ms, ys;
 };
+
+// Compile-time variants: the fixed-size one (block counts and wave count known)
+// and, within it, the merged key/query layout (one 8-column group of the B / C
+// rows per half-wave).
+__host__ __device__ constexpr bool fixed_variant(int NTC, int PTC, int NWC) {
+  return NTC > 0 && PTC > 0 && NWC > 0 && NTC % (NTC > 4 ? 2 : 1) == 0 && PTC * (NTC > 4 ? 2 : 1) == NWC;
+}
+__host__ __device__ constexpr bool merged_variant(int NTC, int PTC, int NWC, int RSC) {
+  return fixed_variant(NTC, PTC, NWC) && NTC * 16 == 16 * NWC && RSC > 0;
+}
 
 template <int VEC>
 struct VecOf;
@@ -169,8 +187,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   // In the fixed-size variant every wave is an MFMA wave with NTH state
   // blocks, known at compile time, so the block loops carry no branches and
   // the scheduler can overlap LDS reads with MFMAs across them.
-  constexpr bool FIXED = NTC > 0 && PTC > 0 && NWC > 0 && NTC % (NTC > 4 ? 2 : 1) == 0 &&
-                         PTC * (NTC > 4 ? 2 : 1) == NWC;
+  constexpr bool FIXED = fixed_variant(NTC, PTC, NWC);
   const bool mma_wave = FIXED || wave < PT * NH;
   const int pt = wave % PT;             // head_dim block of this MFMA wave
   const int nb0 = (wave / PT) * NTH;    // first state block of this MFMA wave
@@ -180,16 +197,18 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   // B / C rows (N / 8 == 2 * waves), either a rotated pair group
   // (a0..a0+3, a0+A..a0+A+3) or a plain group, and rotates it in registers;
   // S is split over six waves (three tile pairs x two N-halves).
-  constexpr bool MERGED = FIXED && NTC * 16 == 16 * NWC && RSC > 0;
+  constexpr bool MERGED = merged_variant(NTC, PTC, NWC, RSC);
   const int sw = nwaves - 1;  // wave that computes the per-token scalars
-  // The SISO summary pass of the merged layout runs its state update on bf16
-  // MFMA with the three-term split (v_mfma_f32_16x16x32_bf16, k = the chunk's 32
-  // virtual rows); its keys go to LDS split and transposed, [n][slot].  Lane
+  // SISO in the merged layout runs its state update on bf16 MFMA with the
+  // three-term split (v_mfma_f32_16x16x32_bf16, k = the chunk's 32 virtual
+  // rows); its keys go to LDS split and transposed, [n][slot].  In the main
+  // pass they sit beside the fp32 keys that S = Q K^T reads, and the raw y
+  // buffers overlay those fp32 keys, which are dead once S is formed.  Lane
   // group q of an MFMA operand holds virtual rows 4q..4q+3 and 16+4q..16+4q+3
   // in its eight k-slots, so row v sits in slot position
   //     pos(v) = 8 ((v >> 2) & 3) + 4 (v >> 4) + (v & 3)
   // of its key row, and the x rows a lane reads are 4 apart (16 banks apart).
-  constexpr bool BF3 = !FULL && MERGED && !MIMO;
+  constexpr bool BF3 = MERGED && !MIMO;
 
   float* Ql = lds + p.o_ql;   // [QV][ks] C (+bias), pairs rotated in place   (main pass)
   float* Kl = lds + p.o_kl;   // [QV][ks] B (+bias), pairs rotated in place
@@ -213,7 +232,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   float* sc_w = sc_scl + QV;
   float* sc_dt = sc_w + QV;
   float* run = lds + p.o_run;  // [0,64) running theta, [64] chunk decay
-  unsigned* KTh = reinterpret_cast<unsigned*>(Kl);  // [N][kKTw] bf16 pairs of K, hi parts  (BF3)
+  unsigned* KTh = reinterpret_cast<unsigned*>(lds + p.o_kt);  // [N][kKTw] bf16 pairs of K, hi parts (BF3)
   unsigned* KTl = KTh + N * kKTw;                     // lo parts
 
   for (int i = tid; i < p.lds_floats; i += nthreads) lds[i] = 0.f;
@@ -380,20 +399,29 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   const int mc1 = mpair ? mc0 + A : mc0 + 4;
   float mdt = 0.f;
 
-  auto prefetch = [&](int cs) {
+  // x rows of the chunk at token cs
+  auto prefetch_x = [&](int cs) {
     const int nv = min(Qt, t_end - cs);
     const rsrc_t xres = make_rsrc(STR ? p.x + ((size_t)b * p.L + cs) * tokxs + (size_t)h * P
                                       : p.x + (((size_t)b * p.L + cs) * p.H + h) * P,
                                   (uint32_t)(nv * tokxs * 4));
-    const rsrc_t bres = make_rsrc(p.b + ((size_t)b * p.L + cs) * tokb, (uint32_t)(nv * tokb * 4));
-    const rsrc_t cres = make_rsrc(p.c + ((size_t)b * p.L + cs) * tokb, (uint32_t)(nv * tokb * 4));
-    const rsrc_t ares = make_rsrc(p.angle + ((size_t)b * p.L + cs) * astr, (uint32_t)(nv * astr * 4));
 #pragma unroll
     for (int k = 0; k < KX; ++k) {
       const int idx = tid + k * nthreads;
       const int t = idx / xrow, pv = idx - t * xrow;
       xr[k] = bload<VEC>(xres, (uint32_t)(t * tokxs + pv * VEC));
     }
+  };
+  // The main pass with the bf16 update is short of registers across S, so it
+  // issues the next chunk's x loads after S (they land during the read-out,
+  // the update and the epilogue); the other variants load x with the rest.
+  constexpr bool LATE_X = FULL && BF3;
+  auto prefetch = [&](int cs) {
+    const int nv = min(Qt, t_end - cs);
+    const rsrc_t bres = make_rsrc(p.b + ((size_t)b * p.L + cs) * tokb, (uint32_t)(nv * tokb * 4));
+    const rsrc_t cres = make_rsrc(p.c + ((size_t)b * p.L + cs) * tokb, (uint32_t)(nv * tokb * 4));
+    const rsrc_t ares = make_rsrc(p.angle + ((size_t)b * p.L + cs) * astr, (uint32_t)(nv * astr * 4));
+    if constexpr (!LATE_X) prefetch_x(cs);
     if constexpr (MERGED) {
       const uint32_t row = (uint32_t)(mtok * tokb + (mrc * p.G + g) * N);
       br[0] = bload<VEC>(bres, row + mc0);
@@ -441,6 +469,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   };
 
   prefetch(t_begin);
+  if constexpr (LATE_X) prefetch_x(t_begin);
   __syncthreads();
 
   for (int c0 = t_begin; c0 < t_end; c0 += Qt) {
@@ -534,21 +563,33 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         q0 = k0;
         q1 = k0;
       }
+      if (FULL || !BF3) {
+        vstore<VEC>(Kl + mt * ks + mc0, k0);
+        vstore<VEC>(Kl + mt * ks + mc1, k1);
+      }
       if constexpr (BF3) {
         // Lanes 2i, 2i + 1 (virtual rows mt, mt + 1) trade halves so that each
         // writes one word (row mt, row mt + 1) for four columns: the even lane
-        // for its columns mc0.., the odd lane for its columns mc1..
-        unsigned hh[4], ll[4];
-        split2_bf16(k0[0], k0[1], hh[0], ll[0]);
-        split2_bf16(k0[2], k0[3], hh[1], ll[1]);
-        split2_bf16(k1[0], k1[1], hh[2], ll[2]);
-        split2_bf16(k1[2], k1[3], hh[3], ll[3]);
+        // for its columns mc0.., the odd lane for its columns mc1..  The head
+        // parts go first, then the remainders (fewer live registers).
         const bool odd = (mt & 1) != 0;
         const int col = odd ? mc1 : mc0;
-        const int wd = (8 * ((mt >> 2) & 3) + 4 * (mt >> 4) + (mt & 2)) >> 1;  // pos(mt & ~1) / 2
+        // word pos(mt & ~1) / 2 of the row: block (mt >> 2) & 3, swizzled by
+        // the row (the same for the four rows col..col + 3), word 2 (mt >> 4) + ((mt >> 1) & 1)
+        const int wd = 4 * (((mt >> 2) & 3) ^ ((col >> 2) & 3)) + 2 * (mt >> 4) + ((mt >> 1) & 1);
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
-          const unsigned* v4 = part ? ll : hh;
+          unsigned v4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x0 = i < 2 ? k0[2 * i] : k1[2 * i - 4], x1 = i < 2 ? k0[2 * i + 1] : k1[2 * i - 3];
+            unsigned hi = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){x0, x1}, bf16x2));
+            if (part) {
+              const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
+              hi = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){x0 - h0, x1 - h1}, bf16x2));
+            }
+            v4[i] = hi;
+          }
           unsigned* dst = (part ? KTl : KTh) + col * kKTw + wd;
           const unsigned r0 = swap_pair_u(odd ? v4[0] : v4[2]);
           const unsigned r1 = swap_pair_u(odd ? v4[1] : v4[3]);
@@ -559,9 +600,6 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
           dst[2 * kKTw] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
           dst[3 * kKTw] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
         }
-      } else {
-        vstore<VEC>(Kl + mt * ks + mc0, k0);
-        vstore<VEC>(Kl + mt * ks + mc1, k1);
       }
       if (FULL) {
         vstore<VEC>(Ql + mt * ks + mc0, q0);
@@ -593,14 +631,17 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
     const rsrc_t zres = make_rsrc(STR ? p.z + ((size_t)b * p.L + c0) * tokxs + (size_t)h * P : p.z + cbase_tok,
                                   p.has_z ? (uint32_t)(nvalid * tokxs * 4) : 0u);
     const rsrc_t ores = make_rsrc(p.out + cbase_tok, (uint32_t)(nvalid * tokx * 4));
-    if constexpr (FULL && !MIMO) {
+    auto load_z = [&]() {
 #pragma unroll
       for (int k = 0; k < KX; ++k) {
         const int idx = tid + k * nthreads;
         const int t = idx / xrow, pv = idx - t * xrow;
         zr[k] = bload<VEC>(zres, (uint32_t)(t * tokxs + pv * VEC));
       }
-    }
+    };
+    // With the bf16 update the z loads wait until S is formed (the registers
+    // are short across S); they land during the read-out and update.
+    if constexpr (FULL && !MIMO && !BF3) load_z();
     if constexpr (FULL && MIMO) {
 #pragma unroll
       for (int i = 0; i < KZM; ++i) {
@@ -687,15 +728,16 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       lds_barrier();
     }
 
+    if constexpr (FULL && !MIMO && BF3) load_z();
+    if constexpr (LATE_X) {
+      if (c0 + Qt < t_end) prefetch_x(c0 + Qt);
+    }
     if (mma_wave) {
       if constexpr (FULL) {
         // ---- P5a: Y = M X + diag(exp(cum)) Q h'^T over this wave's state
-        //      blocks; N-part 0 adds the intra-chunk M X.  One accumulator per
-        //      16-row block keeps independent MFMA chains in flight.
-        floatx4 acc[TB];
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) acc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (nb0 == 0) {
+        //      blocks; N-part 0 adds the intra-chunk M X.
+        // M X: Ml (+ Ml2) rows times the chunk's x.
+        auto add_mx = [&](floatx4* acc) {
 #pragma unroll
           for (int tb = 0; tb < TB; ++tb) {
             for (int sb = 0; sb <= tb; ++sb) {
@@ -708,33 +750,61 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
               acc[tb] = mfma16(a4.w, xc[3 * xs], acc[tb]);
             }
           }
-        }
-        // Q h'^T in its own accumulators; exp(cum) scales its rows afterwards
-        floatx4 aci[TB];
+        };
+        // Q h'^T, this wave's state blocks
+        auto add_qh = [&](floatx4* aci) {
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) aci[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+          for (int j = 0; j < JMAX; ++j) {
+            if (FIXED || j < ntw) {
+              const int nb = nb0 + j;
 #pragma unroll
-        for (int j = 0; j < JMAX; ++j) {
-          if (FIXED || j < ntw) {
-            const int nb = nb0 + j;
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-              const floatx4 a4 = lds_read4(Ql + (tb * 16 + l16) * ks + nb * 16 + 4 * lq);
-              aci[tb] = mfma16(a4.x, Hacc[j].x, aci[tb]);
-              aci[tb] = mfma16(a4.y, Hacc[j].y, aci[tb]);
-              aci[tb] = mfma16(a4.z, Hacc[j].z, aci[tb]);
-              aci[tb] = mfma16(a4.w, Hacc[j].w, aci[tb]);
+              for (int tb = 0; tb < TB; ++tb) {
+                const floatx4 a4 = lds_read4(Ql + (tb * 16 + l16) * ks + nb * 16 + 4 * lq);
+                aci[tb] = mfma16(a4.x, Hacc[j].x, aci[tb]);
+                aci[tb] = mfma16(a4.y, Hacc[j].y, aci[tb]);
+                aci[tb] = mfma16(a4.z, Hacc[j].z, aci[tb]);
+                aci[tb] = mfma16(a4.w, Hacc[j].w, aci[tb]);
+              }
             }
           }
-        }
+        };
         float* Yd = nb0 == 0 ? Yl : Yl2;
+        if constexpr (BF3) {
+          // one accumulator set (this kernel is short of registers): Q h'^T,
+          // its rows scaled by exp(cum), then M X accumulated on top
+          floatx4 acc[TB];
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
+          for (int tb = 0; tb < TB; ++tb) acc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+          add_qh(acc);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int v = tb * 16 + 4 * lq + r;
-            Yd[v * ys + p0 + l16] = fmaf(sc_ecum[v >> rsl], aci[tb][r], acc[tb][r]);
+          for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[tb][r] *= sc_ecum[(tb * 16 + 4 * lq + r) >> rsl];
+          if (nb0 == 0) add_mx(acc);
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Yd[(tb * 16 + 4 * lq + r) * ys + p0 + l16] = acc[tb][r];
+        } else {
+          // One accumulator per 16-row block keeps independent MFMA chains in
+          // flight; Q h'^T in its own accumulators, exp(cum) scales its rows
+          // afterwards.
+          floatx4 acc[TB], aci[TB];
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb) {
+            acc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            aci[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
           }
+          if (nb0 == 0) add_mx(acc);
+          add_qh(aci);
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int v = tb * 16 + 4 * lq + r;
+              Yd[v * ys + p0 + l16] = fmaf(sc_ecum[v >> rsl], aci[tb][r], acc[tb][r]);
+            }
+        }
       }
       // ---- P5b: state update h' = decay h' + K^T (w X) ------------------------
       const float dec = run[64];
@@ -753,8 +823,9 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
 #pragma unroll
         for (int j = 0; j < JMAX; ++j) {
           const int n = (nb0 + j) * 16 + l16;
-          const uintx4 ah = *reinterpret_cast<const uintx4*>(KTh + n * kKTw + 4 * lq);
-          const uintx4 al = *reinterpret_cast<const uintx4*>(KTl + n * kKTw + 4 * lq);
+          const int blk = 4 * (lq ^ ((n >> 2) & 3));
+          const uintx4 ah = *reinterpret_cast<const uintx4*>(KTh + n * kKTw + blk);
+          const uintx4 al = *reinterpret_cast<const uintx4*>(KTl + n * kKTw + blk);
           Hacc[j] = mfma_bf16x3(ah, al, bh, bl, Hacc[j]);
         }
       }
@@ -898,20 +969,33 @@ ScanPlan make_plan(const ScanGeom& g) {
 
 // LDS layout of one pass; the summary pass needs no Q, M or Y buffers.  Rows
 // are padded by four floats so that rows 4 apart start 16 banks apart.
-void layout(ScanKParams& kp, bool full, bool mimo) {
+//
+// With the bf16 state update (bf3) the keys are also kept split and
+// transposed (o_kt); the summary pass keeps no fp32 keys, and in the main
+// pass the two raw y buffers overlay the fp32 keys, whose last reader is
+// S = Q K^T (a barrier separates it from the y writes); the key buffer is
+// enlarged where the two do not fit in it.
+void layout(ScanKParams& kp, bool full, bool mimo, bool bf3) {
   const int QV = kQV;
   kp.ks = kp.NT * 16 + 4;
   kp.xs = kp.PT * 16 + 4;
   kp.ms = QV + 4;
   kp.ys = kp.PT * 16 + 4;
+  const bool y_over_k = full && bf3 && kp.NH > 1;
   int off = 0;
   kp.o_ql = off; off += full ? QV * kp.ks : 0;
-  kp.o_kl = off; off += full ? QV * kp.ks : std::max(QV * kp.ks, 2 * kp.NT * 16 * kKTw);
+  kp.o_kl = off; off += (full || !bf3) ? (y_over_k ? std::max(QV * kp.ks, 2 * QV * kp.ys) : QV * kp.ks) : 0;
+  kp.o_kt = off; off += bf3 ? 2 * kp.NT * 16 * kKTw : 0;
   kp.o_xl = off; off += QV * kp.xs;
   kp.o_ml = off; off += full ? QV * kp.ms : 0;
   kp.o_ml2 = off; off += (full && kp.NH > 1) ? QV * kp.ms : 0;
-  kp.o_yl = off; off += full ? QV * kp.ys : 0;
-  kp.o_yl2 = off; off += (full && kp.NH > 1) ? QV * kp.ys : 0;
+  if (y_over_k) {
+    kp.o_yl = kp.o_kl;
+    kp.o_yl2 = kp.o_kl + QV * kp.ys;
+  } else {
+    kp.o_yl = off; off += full ? QV * kp.ys : 0;
+    kp.o_yl2 = off; off += (full && kp.NH > 1) ? QV * kp.ys : 0;
+  }
   // the entry-state fold overlays [PT*16][NT*16+4] floats on the chunk buffers
   if (full && off < kp.PT * 16 * (kp.NT * 16 + 4)) off = kp.PT * 16 * (kp.NT * 16 + 4);
   kp.o_cs = off; off += 2 * 64;
@@ -944,14 +1028,15 @@ hipError_t launch_one(const ScanKParams& kp, unsigned grid, unsigned block, hipS
 template <int VEC, bool MIMO, int NTC, int PTC, int NWC, int RSC, bool STR = false>
 hipError_t launch_passes(ScanKParams kp, const ScanPlan& plan, unsigned bhn, unsigned block,
                          hipStream_t stream) {
+  constexpr bool kBf3 = merged_variant(NTC, PTC, NWC, RSC) && !MIMO;  // as in the kernel
   if (plan.nseg > 1) {
     ScanKParams ka = kp;
-    layout(ka, false, MIMO);
+    layout(ka, false, MIMO, kBf3);
     hipError_t e = launch_one<VEC, false, MIMO, NTC, PTC, NWC, RSC, STR>(ka, bhn * (unsigned)(plan.nseg - 1), block,
                                                                        stream);
     if (e != hipSuccess) return e;
   }
-  layout(kp, true, MIMO);
+  layout(kp, true, MIMO, kBf3);
   const ProfileEvents& pe = profile_events();
   if (pe.start) {
     hipError_t e = hipEventRecord(pe.start, stream);
