@@ -48,6 +48,21 @@ def test_siso_trap_extremes(sign):
     assert_parity(got, oracle_siso(inp, d), f"X6_trap_{sign * 40}")
 
 
+@pytest.mark.parametrize("nseg", [1, 3])
+def test_siso_wide_dynamic_range(nseg, monkeypatch):
+    """x spread over eight decades per token and fast decay (dt up to 0.2):
+    the head-geometry kernels split their state-update operands into bf16
+    heads and remainders, whose error is relative to each product, so the
+    bar holds at any mix of scales."""
+    monkeypatch.setenv("M3_SCAN_NSEG", str(nseg))
+    d = Dims(2, 300, 3, 1, 64, 128, 32)
+    inp = ssm_inputs(d, seed=2030, dt_range=(1e-3, 0.2))
+    rng = np.random.default_rng(2031)
+    inp["x"] = (inp["x"] * 10.0 ** rng.uniform(-4.0, 4.0, size=(d.B, d.L, 1, 1))).astype(np.float32)
+    got = gpu_siso(to_dev(inp), d).cpu().numpy()
+    assert_parity(got, oracle_siso(inp, d), f"wide_range_segments_{nseg}")
+
+
 @pytest.mark.parametrize("nseg", [1, 2, 3, 7])
 def test_siso_forced_segments(nseg, monkeypatch):
     # the same answer whatever the number of sequence segments
