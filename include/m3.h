@@ -38,15 +38,13 @@
  * Precision:  float32 storage and arithmetic.  sin / cos are accurate to a
  *             few ulp; the state decay uses an accurate exp; the
  *             intra-chunk decay mask, exp(cum) and the SiLU gate use the
- *             hardware exp2 (relative error about |x| 2^-23).  One
- *             exception: the SISO scan at head_dim 64 / state 128 with
- *             16-byte aligned operands (m3_siso_fwd, m3_siso_fwd_packed)
- *             forms its chunk state updates K^T (w x) from bf16 products of
- *             three-term splits (each fp32 operand as a bf16 head plus a bf16
- *             remainder; head*head + head*rest + rest*head, accumulated in
- *             fp32), a relative error of about 2^-16 per product; measured
- *             against a float64 reference at B4 L2048 H24 this gives
- *             max |g - o| / max(|o|, rms(o)) of about 5e-5.
+ *             hardware exp2 (relative error about |x| 2^-23).  At
+ *             head_dim 64 / state 128 with 16-byte aligned operands the
+ *             chunk state updates K^T (w x) (SISO: m3_siso_fwd,
+ *             m3_siso_fwd_packed; MIMO: its segment summaries) take bf16
+ *             matrix products of six-term splits (each fp32 operand as three
+ *             bf16 pieces, six products accumulated in fp32): about 2^-23
+ *             relative error per product, the fp32 level.
  */
 #ifndef M3_H
 #define M3_H
@@ -173,9 +171,8 @@ int m3_siso_fwd(const float* c, const float* b, const float* x, const float* z,
  * the normalised B/C rows and dt / adt go through the workspace.  When W,
  * I and the angle column offset 2I + 2GN + 3H are multiples of 4 (16-byte
  * rows, as the dense operands have), the same kernel variant runs and the
- * result is identical bit for bit; otherwise a scalar-load variant runs,
- * with float32 state updates (differences at the level of the split-bf16
- * updates described under Precision).
+ * result is identical bit for bit; otherwise a scalar-load variant runs
+ * and may sum in another order (differences at float32 rounding level).
  * workspace: at least m3_siso_fwd_packed_workspace_bytes(pcfg, cfg) bytes
  *   (B*L*(2GN + 2H) floats plus the scan's own workspace); required.
  * Rules: those of m3_preprocess (rows = B*L) and of m3_siso_fwd, and the two

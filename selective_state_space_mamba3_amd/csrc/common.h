@@ -17,14 +17,10 @@ __device__ __forceinline__ floatx4 mfma16(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Three-term bf16 split of fp32 products on v_mfma_f32_16x16x32_bf16.  An
-// fp32 value x is written as hi + lo with hi = bf16(x) and lo = bf16(x - hi)
-// (both round-to-nearest-even); a product a b is then taken as
-// a_hi b_hi + a_hi b_lo + a_lo b_hi, which drops only a_lo b_lo and the
-// rounding of the two lo parts: relative error about 2^-16 per product, with
-// fp32 accumulation.  Lane l supplies A[l % 16][k] and B[k][l % 16] for eight
-// k-slots (the same slot -> k map for both operands, so any assignment of the
-// contraction index to slots is valid); the result layout matches mfma16.
+// Split fp32 products on v_mfma_f32_16x16x32_bf16.  Lane l supplies
+// A[l % 16][k] and B[k][l % 16] for eight k-slots (the same slot -> k map
+// for both operands, so any assignment of the contraction index to slots is
+// valid); the result layout matches mfma16.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
@@ -34,25 +30,36 @@ __device__ __forceinline__ floatx4 mfma_bf16(uintx4 a, uintx4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                  0, 0);
 }
-// a b with both operands split: three bf16 MFMAs into one accumulator.
-__device__ __forceinline__ floatx4 mfma_bf16x3(uintx4 ah, uintx4 al, uintx4 bh, uintx4 bl, floatx4 c) {
-  c = mfma_bf16(ah, bh, c);
-  c = mfma_bf16(ah, bl, c);
-  return mfma_bf16(al, bh, c);
+// Six-term form: each fp32 operand as head + middle + tail bf16 pieces, each
+// the round-to-nearest bf16 of what the earlier ones leave (x = h + m + t + e,
+// |e| <= 2^-24 |x|), and the products h h, h m, m h, h t, t h, m m
+// accumulated in fp32, smallest first; the dropped m t, t m and t t are
+// below 2^-24, so a product is exact to about 2^-23, fp32 level.
+__device__ __forceinline__ floatx4 mfma_bf16x6(uintx4 ah, uintx4 am, uintx4 at, uintx4 bh, uintx4 bm, uintx4 bt,
+                                                floatx4 c) {
+  c = mfma_bf16(am, bm, c);
+  c = mfma_bf16(ah, bt, c);
+  c = mfma_bf16(at, bh, c);
+  c = mfma_bf16(ah, bm, c);
+  c = mfma_bf16(am, bh, c);
+  return mfma_bf16(ah, bh, c);
 }
-// Split two fp32 values; the first goes to the low 16 bits of each word.
-__device__ __forceinline__ void split2_bf16(float x0, float x1, unsigned& hi, unsigned& lo) {
-  hi = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){x0, x1}, bf16x2));
-  const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
-  lo = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){x0 - h0, x1 - h1}, bf16x2));
+// Split two fp32 values into three bf16 pieces each (first value in the low
+// 16 bits of each word).
+__device__ __forceinline__ void split2_bf16x3(float x0, float x1, unsigned& h, unsigned& m, unsigned& t) {
+  h = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){x0, x1}, bf16x2));
+  const float r0 = x0 - __uint_as_float(h << 16), r1 = x1 - __uint_as_float(h & 0xffff0000u);
+  m = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){r0, r1}, bf16x2));
+  const float s0 = r0 - __uint_as_float(m << 16), s1 = r1 - __uint_as_float(m & 0xffff0000u);
+  t = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){s0, s1}, bf16x2));
 }
-// Eight fp32 values into packed bf16x8 hi / lo operands.
-__device__ __forceinline__ void split8_bf16(const float* v, uintx4& hi, uintx4& lo) {
-  unsigned h[4], l[4];
+__device__ __forceinline__ void split8_bf16x3(const float* v, uintx4& h, uintx4& m, uintx4& t) {
+  unsigned a[4], b[4], c[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) split2_bf16(v[2 * i], v[2 * i + 1], h[i], l[i]);
-  hi = uintx4{h[0], h[1], h[2], h[3]};
-  lo = uintx4{l[0], l[1], l[2], l[3]};
+  for (int i = 0; i < 4; ++i) split2_bf16x3(v[2 * i], v[2 * i + 1], a[i], b[i], c[i]);
+  h = uintx4{a[0], a[1], a[2], a[3]};
+  m = uintx4{b[0], b[1], b[2], b[3]};
+  t = uintx4{c[0], c[1], c[2], c[3]};
 }
 // Exchange a word with the neighbouring lane (lanes 2i and 2i + 1; DPP quad_perm 1,0,3,2).
 __device__ __forceinline__ unsigned swap_pair_u(unsigned v) {

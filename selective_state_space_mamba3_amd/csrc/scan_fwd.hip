@@ -29,12 +29,13 @@
 //     vectors, so a wave fits in 128 VGPRs and four waves share each SIMD.
 //   * Intra-chunk S = Q K^T, the decay/trapezoid mask, M X and the
 //     carried-state read Q h'^T run on v_mfma_f32_16x16x4_f32.  The state
-//     update K^T (w X) does too, except in the SISO N = 128 / P = 64 variant,
-//     where it runs on v_mfma_f32_16x16x32_bf16 with each fp32 operand split
-//     into a bf16 head and remainder (three products, fp32 accumulation,
-//     about 2^-16 relative error per product): the fp32 matrix pipe issues
-//     through the vector ALU on gfx950, and the update is a third of the
-//     chunk's matrix work.
+//     update K^T (w X) does too, except in the N = 128 / P = 64 variant
+//     (SISO both passes, MIMO the summary pass), where it runs on
+//     v_mfma_f32_16x16x32_bf16 with each fp32 operand split into three bf16
+//     pieces and six products accumulated in fp32 (about 2^-23 relative
+//     error per product, fp32 level): the fp32 matrix pipe issues through
+//     the vector ALU on gfx950, bf16 products do not, and the update is a
+//     third of the chunk's matrix work.
 //   * The next chunk's x, B, C, angle and scalars are loaded into registers
 //     while the current chunk's MFMA work runs; z is loaded at the start of
 //     the chunk that uses it.  (The bf16-update variant issues the next x
@@ -199,16 +200,18 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   // S is split over six waves (three tile pairs x two N-halves).
   constexpr bool MERGED = merged_variant(NTC, PTC, NWC, RSC);
   const int sw = nwaves - 1;  // wave that computes the per-token scalars
-  // SISO in the merged layout runs its state update on bf16 MFMA with the
-  // three-term split (v_mfma_f32_16x16x32_bf16, k = the chunk's 32 virtual
-  // rows); its keys go to LDS split and transposed, [n][slot].  In the main
-  // pass they sit beside the fp32 keys that S = Q K^T reads, and the raw y
-  // buffers overlay those fp32 keys, which are dead once S is formed.  Lane
+  // The merged layout runs its state update on bf16 MFMA with the six-term
+  // split (v_mfma_f32_16x16x32_bf16, k = the chunk's 32 virtual rows; fp32
+  // accuracy) in the summary pass, and for SISO in the main pass too (the
+  // MIMO main pass has no LDS left for it).  Its keys go to LDS split into
+  // three bf16 planes and transposed, [n][slot].  In the main pass they sit
+  // beside the fp32 keys that S = Q K^T reads, and the raw y buffers overlay
+  // those fp32 keys, which are dead once S is formed.  Lane
   // group q of an MFMA operand holds virtual rows 4q..4q+3 and 16+4q..16+4q+3
   // in its eight k-slots, so row v sits in slot position
   //     pos(v) = 8 ((v >> 2) & 3) + 4 (v >> 4) + (v & 3)
   // of its key row, and the x rows a lane reads are 4 apart (16 banks apart).
-  constexpr bool BF3 = MERGED && !MIMO;
+  constexpr bool SPLIT = MERGED && (!MIMO || !FULL);
 
   float* Ql = lds + p.o_ql;   // [QV][ks] C (+bias), pairs rotated in place   (main pass)
   float* Kl = lds + p.o_kl;   // [QV][ks] B (+bias), pairs rotated in place
@@ -232,8 +235,9 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   float* sc_w = sc_scl + QV;
   float* sc_dt = sc_w + QV;
   float* run = lds + p.o_run;  // [0,64) running theta, [64] chunk decay
-  unsigned* KTh = reinterpret_cast<unsigned*>(lds + p.o_kt);  // [N][kKTw] bf16 pairs of K, hi parts (BF3)
-  unsigned* KTl = KTh + N * kKTw;                     // lo parts
+  unsigned* KTh = reinterpret_cast<unsigned*>(lds + p.o_kt);  // [N][kKTw] bf16 pairs of K, head parts (SPLIT)
+  unsigned* KTm = KTh + N * kKTw;                     // middle parts
+  unsigned* KTl = KTm + N * kKTw;                     // tail parts
 
   for (int i = tid; i < p.lds_floats; i += nthreads) lds[i] = 0.f;
   __syncthreads();
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   // The main pass with the bf16 update is short of registers across S, so it
   // issues the next chunk's x loads after S (they land during the read-out,
   // the update and the epilogue); the other variants load x with the rest.
-  constexpr bool LATE_X = FULL && BF3;
+  constexpr bool LATE_X = FULL && SPLIT;
   auto prefetch = [&](int cs) {
     const int nv = min(Qt, t_end - cs);
     const rsrc_t bres = make_rsrc(p.b + ((size_t)b * p.L + cs) * tokb, (uint32_t)(nv * tokb * 4));
@@ -563,34 +567,33 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         q0 = k0;
         q1 = k0;
       }
-      if (FULL || !BF3) {
+      if (FULL || !SPLIT) {
         vstore<VEC>(Kl + mt * ks + mc0, k0);
         vstore<VEC>(Kl + mt * ks + mc1, k1);
       }
-      if constexpr (BF3) {
+      if constexpr (SPLIT) {
         // Lanes 2i, 2i + 1 (virtual rows mt, mt + 1) trade halves so that each
         // writes one word (row mt, row mt + 1) for four columns: the even lane
         // for its columns mc0.., the odd lane for its columns mc1..  The head
-        // parts go first, then the remainders (fewer live registers).
+        // plane goes first, then the middle and tail planes of the remainders.
         const bool odd = (mt & 1) != 0;
         const int col = odd ? mc1 : mc0;
         // word pos(mt & ~1) / 2 of the row: block (mt >> 2) & 3, swizzled by
         // the row (the same for the four rows col..col + 3), word 2 (mt >> 4) + ((mt >> 1) & 1)
         const int wd = 4 * (((mt >> 2) & 3) ^ ((col >> 2) & 3)) + 2 * (mt >> 4) + ((mt >> 1) & 1);
+        float res[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};  // running remainders
 #pragma unroll
-        for (int part = 0; part < 2; ++part) {
+        for (int part = 0; part < 3; ++part) {
           unsigned v4[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float x0 = i < 2 ? k0[2 * i] : k1[2 * i - 4], x1 = i < 2 ? k0[2 * i + 1] : k1[2 * i - 3];
-            unsigned hi = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){x0, x1}, bf16x2));
-            if (part) {
-              const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
-              hi = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){x0 - h0, x1 - h1}, bf16x2));
+            v4[i] = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){res[2 * i], res[2 * i + 1]}, bf16x2));
+            if (part < 2) {
+              res[2 * i] -= __uint_as_float(v4[i] << 16);
+              res[2 * i + 1] -= __uint_as_float(v4[i] & 0xffff0000u);
             }
-            v4[i] = hi;
           }
-          unsigned* dst = (part ? KTl : KTh) + col * kKTw + wd;
+          unsigned* dst = KTh + part * N * kKTw + col * kKTw + wd;
           const unsigned r0 = swap_pair_u(odd ? v4[0] : v4[2]);
           const unsigned r1 = swap_pair_u(odd ? v4[1] : v4[3]);
           const unsigned a0 = odd ? r0 : v4[0], a1 = odd ? r1 : v4[1];      // row mt & ~1
@@ -641,7 +644,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
     };
     // With the bf16 update the z loads wait until S is formed (the registers
     // are short across S); they land during the read-out and update.
-    if constexpr (FULL && !MIMO && !BF3) load_z();
+    if constexpr (FULL && !MIMO && !SPLIT) load_z();
     if constexpr (FULL && MIMO) {
 #pragma unroll
       for (int i = 0; i < KZM; ++i) {
@@ -728,7 +731,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       lds_barrier();
     }
 
-    if constexpr (FULL && !MIMO && BF3) load_z();
+    if constexpr (FULL && !MIMO && SPLIT) load_z();
     if constexpr (LATE_X) {
       if (c0 + Qt < t_end) prefetch_x(c0 + Qt);
     }
@@ -769,7 +772,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
           }
         };
         float* Yd = nb0 == 0 ? Yl : Yl2;
-        if constexpr (BF3) {
+        if constexpr (SPLIT) {
           // one accumulator set (this kernel is short of registers): Q h'^T,
           // its rows scaled by exp(cum), then M X accumulated on top
           floatx4 acc[TB];
@@ -810,7 +813,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       const float dec = run[64];
 #pragma unroll
       for (int j = 0; j < JMAX; ++j) Hacc[j] *= dec;
-      if constexpr (BF3) {
+      if constexpr (SPLIT) {
         // B operand: w x of column p0 + l16 at virtual rows 4 lq + i, 16 + 4 lq + i
         float wx[8];
 #pragma unroll
@@ -818,18 +821,19 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
           const int v = 16 * (i >> 2) + 4 * lq + (i & 3);
           wx[i] = Xl[v * xs + p0 + l16] * sc_w[v >> rsl];
         }
-        uintx4 bh, bl;
-        split8_bf16(wx, bh, bl);
+        uintx4 bh, bm, bl;
+        split8_bf16x3(wx, bh, bm, bl);
 #pragma unroll
         for (int j = 0; j < JMAX; ++j) {
           const int n = (nb0 + j) * 16 + l16;
           const int blk = 4 * (lq ^ ((n >> 2) & 3));
           const uintx4 ah = *reinterpret_cast<const uintx4*>(KTh + n * kKTw + blk);
+          const uintx4 am = *reinterpret_cast<const uintx4*>(KTm + n * kKTw + blk);
           const uintx4 al = *reinterpret_cast<const uintx4*>(KTl + n * kKTw + blk);
-          Hacc[j] = mfma_bf16x3(ah, al, bh, bl, Hacc[j]);
+          Hacc[j] = mfma_bf16x6(ah, am, al, bh, bm, bl, Hacc[j]);
         }
       }
-      for (int sb = 0; sb < (BF3 ? 0 : TB); ++sb) {
+      for (int sb = 0; sb < (SPLIT ? 0 : TB); ++sb) {
         const int v0 = sb * 16 + 4 * lq;
         const float* xc = Xl + v0 * xs + p0 + l16;
         const float xw0 = xc[0] * sc_w[(v0 + 0) >> rsl];
@@ -970,22 +974,22 @@ ScanPlan make_plan(const ScanGeom& g) {
 // LDS layout of one pass; the summary pass needs no Q, M or Y buffers.  Rows
 // are padded by four floats so that rows 4 apart start 16 banks apart.
 //
-// With the bf16 state update (bf3) the keys are also kept split and
+// With the split state update the keys are also kept split (three bf16 planes) and
 // transposed (o_kt); the summary pass keeps no fp32 keys, and in the main
 // pass the two raw y buffers overlay the fp32 keys, whose last reader is
 // S = Q K^T (a barrier separates it from the y writes); the key buffer is
 // enlarged where the two do not fit in it.
-void layout(ScanKParams& kp, bool full, bool mimo, bool bf3) {
+void layout(ScanKParams& kp, bool full, bool mimo, bool split) {
   const int QV = kQV;
   kp.ks = kp.NT * 16 + 4;
   kp.xs = kp.PT * 16 + 4;
   kp.ms = QV + 4;
   kp.ys = kp.PT * 16 + 4;
-  const bool y_over_k = full && bf3 && kp.NH > 1;
+  const bool y_over_k = full && split && kp.NH > 1;
   int off = 0;
   kp.o_ql = off; off += full ? QV * kp.ks : 0;
-  kp.o_kl = off; off += (full || !bf3) ? (y_over_k ? std::max(QV * kp.ks, 2 * QV * kp.ys) : QV * kp.ks) : 0;
-  kp.o_kt = off; off += bf3 ? 2 * kp.NT * 16 * kKTw : 0;
+  kp.o_kl = off; off += (full || !split) ? (y_over_k ? std::max(QV * kp.ks, 2 * QV * kp.ys) : QV * kp.ks) : 0;
+  kp.o_kt = off; off += split ? 3 * kp.NT * 16 * kKTw : 0;
   kp.o_xl = off; off += QV * kp.xs;
   kp.o_ml = off; off += full ? QV * kp.ms : 0;
   kp.o_ml2 = off; off += (full && kp.NH > 1) ? QV * kp.ms : 0;
@@ -1028,15 +1032,18 @@ hipError_t launch_one(const ScanKParams& kp, unsigned grid, unsigned block, hipS
 template <int VEC, bool MIMO, int NTC, int PTC, int NWC, int RSC, bool STR = false>
 hipError_t launch_passes(ScanKParams kp, const ScanPlan& plan, unsigned bhn, unsigned block,
                          hipStream_t stream) {
-  constexpr bool kBf3 = merged_variant(NTC, PTC, NWC, RSC) && !MIMO;  // as in the kernel
+  // as in the kernel: the split update in the summary pass of the merged
+  // layout, and in its main pass for SISO (the MIMO main pass has no LDS for it)
+  constexpr bool kSplitA = merged_variant(NTC, PTC, NWC, RSC);
+  constexpr bool kSplit = kSplitA && !MIMO;
   if (plan.nseg > 1) {
     ScanKParams ka = kp;
-    layout(ka, false, MIMO, kBf3);
+    layout(ka, false, MIMO, kSplitA);
     hipError_t e = launch_one<VEC, false, MIMO, NTC, PTC, NWC, RSC, STR>(ka, bhn * (unsigned)(plan.nseg - 1), block,
                                                                        stream);
     if (e != hipSuccess) return e;
   }
-  layout(kp, true, MIMO, kBf3);
+  layout(kp, true, MIMO, kSplit);
   const ProfileEvents& pe = profile_events();
   if (pe.start) {
     hipError_t e = hipEventRecord(pe.start, stream);
