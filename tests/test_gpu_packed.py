@@ -62,10 +62,9 @@ def test_packed_equals_preprocess_then_scan(d):
     if _same_variant(d):
         np.testing.assert_array_equal(fused.cpu().numpy(), twostep.cpu().numpy())
     else:
-        # different kernel variants: the fixed-geometry one takes its segment
-        # summaries on the split-bf16 update (about 2^-16 per product), so the
-        # two agree to the parity bar rather than to fp32 rounding
-        assert_parity(fused.cpu().numpy(), twostep.cpu().numpy().astype(np.float64), "packed vs two calls")
+        # different kernel variants (the fixed-geometry one with its split-bf16
+        # state update, fp32-level): they agree to fp32 rounding
+        assert_parity(fused.cpu().numpy(), twostep.cpu().numpy().astype(np.float64), "packed vs two calls", tol=1e-5)
     ref = O.preprocess(pk["projected"], pk["dt_bias"], op)
     oi = {k: ref[src].reshape(shape[k]) for k, src in PRE_KEYS}
     oi.update({k: pk[k] for k in ("c_bias", "b_bias", "d")})
