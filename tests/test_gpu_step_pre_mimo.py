@@ -185,6 +185,12 @@ MIMO_SMALL = [
     ("R5_many_segments", Dims(1, 200, 1, 1, 32, 64, 16, R=5, has_output_norm=True), 5007),
     ("R6_G2_H2", Dims(2, 77, 2, 2, 16, 48, 8, R=6), 5008),
     ("R7_P128_N128_A64", Dims(1, 60, 1, 1, 128, 128, 64, R=7, has_output_norm=True), 5009),
+    # the head-geometry kernels at every rank stride (1, 2, 4 via rank 3, 8),
+    # long enough for sequence segments, so both passes of each run
+    ("R1_P64_N128_A32_L200", Dims(1, 200, 2, 1, 64, 128, 32, R=1, has_output_norm=True), 5010),
+    ("R2_P64_N128_A32_L160_nonorm", Dims(2, 160, 2, 1, 64, 128, 32, R=2), 5011),
+    ("R3_P64_N128_A16_L150", Dims(1, 150, 3, 1, 64, 128, 16, R=3, has_output_norm=True), 5012),
+    ("R8_P64_N128_A32_L96", Dims(1, 96, 2, 1, 64, 128, 32, R=8, has_output_norm=True), 5013),
 ]
 
 
