@@ -581,27 +581,30 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         // word pos(mt & ~1) / 2 of the row: block (mt >> 2) & 3, swizzled by
         // the row (the same for the four rows col..col + 3), word 2 (mt >> 4) + ((mt >> 1) & 1)
         const int wd = 4 * (((mt >> 2) & 3) ^ ((col >> 2) & 3)) + 2 * (mt >> 4) + ((mt >> 1) & 1);
-        float res[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};  // running remainders
+        // The even lane keeps its columns mc0.. and takes the odd lane's values
+        // there; the odd lane keeps mc1.. and takes the even lane's: after one
+        // exchange each lane holds rows mt & ~1 (ra) and mt | 1 (rb) of its
+        // four columns, and each converted pair is one word of the plane.
+        float ra[4], rb[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float own = odd ? k1[c] : k0[c];
+          const float other = __uint_as_float(swap_pair_u(__float_as_uint(odd ? k0[c] : k1[c])));
+          ra[c] = odd ? other : own;
+          rb[c] = odd ? own : other;
+        }
 #pragma unroll
         for (int part = 0; part < 3; ++part) {
-          unsigned v4[4];
+          unsigned* dst = KTh + part * N * kKTw + col * kKTw + wd;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v4[i] = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){res[2 * i], res[2 * i + 1]}, bf16x2));
-            if (part < 2) {
-              res[2 * i] -= __uint_as_float(v4[i] << 16);
-              res[2 * i + 1] -= __uint_as_float(v4[i] & 0xffff0000u);
+          for (int c = 0; c < 4; ++c) {
+            const unsigned w = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){ra[c], rb[c]}, bf16x2));
+            dst[c * kKTw] = w;
+            if (part < 2) {  // the remainders for the next plane
+              ra[c] -= __uint_as_float(w << 16);
+              rb[c] -= __uint_as_float(w & 0xffff0000u);
             }
           }
-          unsigned* dst = KTh + part * N * kKTw + col * kKTw + wd;
-          const unsigned r0 = swap_pair_u(odd ? v4[0] : v4[2]);
-          const unsigned r1 = swap_pair_u(odd ? v4[1] : v4[3]);
-          const unsigned a0 = odd ? r0 : v4[0], a1 = odd ? r1 : v4[1];      // row mt & ~1
-          const unsigned b0 = odd ? v4[2] : r0, b1 = odd ? v4[3] : r1;      // row mt | 1
-          dst[0 * kKTw] = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
-          dst[1 * kKTw] = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
-          dst[2 * kKTw] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
-          dst[3 * kKTw] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
         }
       }
       if (FULL) {
