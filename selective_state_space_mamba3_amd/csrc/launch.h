@@ -56,6 +56,8 @@ struct ScanPlan {
   int chunk;
   int nseg;
   int seg_len;
+  int npc;   // summary pieces per segment before the last
+  int plen;  // tokens per summary piece (whole chunks)
   size_t ws_state_floats;
   size_t ws_aux_floats;
 };

@@ -41,10 +41,11 @@
 //     the chunk that uses it.  (The bf16-update variant issues the next x
 //     and this chunk's z after S, where its registers allow.)  The
 //     cumulative angle is a 32-lane scan.
-//   * Sequence segments: a first pass computes each segment's end state
-//     from a zero entry (plus its decay product and angle increment) into
-//     the workspace; the main pass folds the earlier segments' summaries
-//     into its entry state, so segments of one sequence run in parallel.
+//   * Sequence segments: a first pass computes the end state of each piece
+//     (two per segment before the last) from a zero entry, plus its decay
+//     product and angle increment, into the workspace; the main pass folds
+//     the earlier pieces' summaries, in order, into its entry state, so the
+//     segments of one sequence run in parallel.
 #include "common.h"
 #include "launch.h"
 
@@ -69,8 +70,8 @@ struct ScanKParams {
   const float *c, *b, *x, *z, *adt, *dt, *trap, *angle, *c_bias, *b_bias, *d;
   const float *mimo_x, *mimo_z, *mimo_o, *norm_weight;
   float* out;
-  float* ws_state;  // [B*H][nseg-1][PT*NT tiles][64 lanes][4]
-  float* ws_aux;    // [B*H][nseg-1][kAux]
+  float* ws_state;  // [B*H][(nseg-1) npc][PT*NT tiles][64 lanes][4]
+  float* ws_aux;    // [B*H][(nseg-1) npc][kAux]
   int B, L, H, G, P, N, A, R;
   int has_z, has_d, has_norm;
   int NT, PT;       // 16-wide blocks of N and P
@@ -79,6 +80,7 @@ struct ScanKParams {
   int Qt;           // tokens per chunk (QV / RS)
   int xstr, tstr, astr;  // per-token strides of x / z, trap and angle (packed rows share one)
   int seg_len, nseg;
+  int npc, plen;    // summary pieces per segment before the last, and their length (tokens)
   // LDS layout (float offsets) and row strides
   int o_ql, o_kl, o_kt, o_xl, o_ml, o_ml2, o_yl, o_yl2, o_cs, o_bias, o_mimo, o_sc, o_run, lds_floats;
   int ks, xs, ms, ys;
@@ -165,7 +167,10 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   const int l16 = lane & 15;
   const int lq = lane >> 4;
 
-  const int nseg_run = FULL ? p.nseg : p.nseg - 1;
+  // the main pass runs (b, h, segment); the summary pass (b, h, piece), each
+  // of the first nseg - 1 segments cut into npc pieces of plen tokens
+  const int nsum_all = (p.nseg - 1) * p.npc;  // summaries per (b, h)
+  const int nseg_run = FULL ? p.nseg : nsum_all;
   const uint32_t unit = xcd_remap(blockIdx.x, gridDim.x);
   const int h = unit % p.H;
   const int rest = unit / p.H;
@@ -173,8 +178,11 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   const int b = rest / nseg_run;
   const int g = h / (p.H / p.G);
   const int bh = b * p.H + h;
-  const int t_begin = seg * p.seg_len;
-  const int t_end = min(t_begin + p.seg_len, p.L);
+  const int seg_base = (FULL ? seg : seg / p.npc) * p.seg_len;
+  const int piece = FULL ? 0 : seg - (seg / p.npc) * p.npc;
+  const int t_begin = min(seg_base + piece * p.plen, p.L);
+  const int t_end = FULL ? min(seg_base + p.seg_len, p.L) : min(seg_base + min((piece + 1) * p.plen, p.seg_len), p.L);
+  const int nsum = FULL ? seg * p.npc : 0;  // summaries folded into the entry state
   const int R = MIMO ? p.R : 1;
   const int RG = R * p.G;
   const int Qt = MIMO ? p.Qt : QV;
@@ -273,12 +281,12 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   // and a / 16 + A / 16), so the fold rotates in registers, with all
   // summaries loaded at once and cos / sin of every theta_i from an LDS table.
   // Otherwise U_i passes through LDS in [p][n] layout for the pair rotation.
-  const bool reg_fold = FIXED && NTC == 8 && !MIMO && (A == 0 || A == 16 || A == 32) && p.nseg <= 64;
+  const bool reg_fold = FIXED && NTC == 8 && !MIMO && (A == 0 || A == 16 || A == 32) && nsum_all <= 128;
   if (FULL && seg > 0 && reg_fold) {
-    const size_t sbase = (size_t)bh * (p.nseg - 1);
-    float* CSt = lds;  // [seg][A] cos, then [seg][A] sin; overlays the chunk buffers (unused yet)
-    float* SNt = CSt + seg * A;
-    for (int idx = tid; idx < seg * A; idx += nthreads) {
+    const size_t sbase = (size_t)bh * nsum_all;
+    float* CSt = lds;  // [nsum][A] cos, then [nsum][A] sin; overlays the chunk buffers (unused yet)
+    float* SNt = CSt + nsum * A;
+    for (int idx = tid; idx < nsum * A; idx += nthreads) {
       const int i = idx / A, a = idx - i * A;
       float th = 0.f;
       for (int k = 0; k < i; ++k) th += p.ws_aux[(sbase + k) * kAux + a];
@@ -289,11 +297,11 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
     }
     for (int a = tid; a < A; a += nthreads) {
       float th = 0.f;
-      for (int k = 0; k < seg; ++k) th += p.ws_aux[(sbase + k) * kAux + a];
+      for (int k = 0; k < nsum; ++k) th += p.ws_aux[(sbase + k) * kAux + a];
       run[a] = th;
     }
     __syncthreads();
-    for (int i = 0; i < seg; ++i) {
+    for (int i = 0; i < nsum; ++i) {
       const float* st = p.ws_state + (sbase + i) * (size_t)(PT * NT) * 256;
       floatx4 u[JMAX];
 #pragma unroll
@@ -326,13 +334,13 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       for (int j = 0; j < JMAX; ++j) Hacc[j] = dec * Hacc[j] + u[j];
     }
     __syncthreads();
-    for (int i = tid; i < 2 * seg * A; i += nthreads) CSt[i] = 0.f;  // restore the zeroed chunk buffers
+    for (int i = tid; i < 2 * nsum * A; i += nthreads) CSt[i] = 0.f;  // restore the zeroed chunk buffers
   } else if (FULL && seg > 0) {
     __syncthreads();
     float* Ub = lds;  // [PT*16][NT*16 + 4], overlays the chunk buffers (unused yet)
     const int us = NT * 16 + 4;
-    for (int i = 0; i < seg; ++i) {
-      const size_t si = (size_t)bh * (p.nseg - 1) + i;
+    for (int i = 0; i < nsum; ++i) {
+      const size_t si = (size_t)bh * nsum_all + i;
       const float* aux = p.ws_aux + si * kAux;
       const float* st = p.ws_state + si * (size_t)(PT * NT) * 256;
       if (mma_wave) {
@@ -922,7 +930,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   }
 
   if constexpr (!FULL) {
-    const size_t si = (size_t)bh * (p.nseg - 1) + seg;
+    const size_t si = (size_t)bh * nsum_all + seg;  // this piece
     float* st = p.ws_state + si * (size_t)(PT * NT) * 256;
     if (mma_wave) {
 #pragma unroll
@@ -969,8 +977,16 @@ ScanPlan make_plan(const ScanGeom& g) {
   nseg = ((long)g.L + seg_len - 1) / seg_len;
   pl.nseg = (int)nseg;
   pl.seg_len = (int)seg_len;
-  pl.ws_state_floats = nseg > 1 ? (size_t)bhn * (nseg - 1) * PT * NT * 256 : 0;
-  pl.ws_aux_floats = nseg > 1 ? (size_t)bhn * (nseg - 1) * kAux : 0;
+  // The summary pass cuts each segment before the last into two pieces of
+  // whole chunks: twice the workgroups over the same tokens, so that it
+  // fills the CUs' second workgroup slots (one summary segment per chain
+  // would leave them idle wherever B*H is near the CU count); the main pass
+  // folds the pieces' summaries in order.
+  pl.npc = nseg > 1 ? 2 : 1;
+  pl.plen = (int)(((seg_len / Qt + pl.npc - 1) / pl.npc) * Qt);
+  const long nsum = (nseg - 1) * pl.npc;
+  pl.ws_state_floats = nseg > 1 ? (size_t)bhn * nsum * PT * NT * 256 : 0;
+  pl.ws_aux_floats = nseg > 1 ? (size_t)bhn * nsum * kAux : 0;
   return pl;
 }
 
@@ -1042,7 +1058,7 @@ hipError_t launch_passes(ScanKParams kp, const ScanPlan& plan, unsigned bhn, uns
   if (plan.nseg > 1) {
     ScanKParams ka = kp;
     layout(ka, false, MIMO, kSplitA);
-    hipError_t e = launch_one<VEC, false, MIMO, NTC, PTC, NWC, RSC, STR>(ka, bhn * (unsigned)(plan.nseg - 1), block,
+    hipError_t e = launch_one<VEC, false, MIMO, NTC, PTC, NWC, RSC, STR>(ka, bhn * (unsigned)((plan.nseg - 1) * plan.npc), block,
                                                                        stream);
     if (e != hipSuccess) return e;
   }
@@ -1084,6 +1100,8 @@ hipError_t launch_scan(const ScanGeom& g, const ScanOperands& o, const ScanPlan&
   kp.astr = o.as ? (int)o.as : (int)g.A;
   kp.seg_len = plan.seg_len;
   kp.nseg = plan.nseg;
+  kp.npc = plan.npc;
+  kp.plen = plan.plen;
   float* ws = static_cast<float*>(workspace);
   kp.ws_state = ws;
   kp.ws_aux = ws ? ws + plan.ws_state_floats : nullptr;
