@@ -2,10 +2,11 @@
 """One-GPU benchmark of the Mamba-3 SISO forward path on MI355X.
 
 A step is one pass of the whole SISO hot path over one batch of the
-B4 L2048 H24 P64 N128 A32 layer: m3_preprocess on the packed projection
-[8192, 3432], then m3_siso_fwd on its outputs.  Inputs for three
-independent batches are resident in HBM before timing and are rotated so
-the 256 MB last-level cache cannot hold a whole step's working set.
+B4 L2048 H24 P64 N128 A32 layer: m3_siso_fwd_packed, the preprocess of the
+packed projection [8192, 3432] fused into the scan.  The same pass as two
+calls (m3_preprocess, then m3_siso_fwd) is timed beside it.  Inputs for
+three independent batches are resident in HBM before timing and are rotated
+so the 256 MB last-level cache cannot hold a whole step's working set.
 
 Prints one JSON line: tokens/s of the step, the scan kernel's roofline
 (algorithmic bytes / live HIP-event duration against 8 TB/s), and the float64
@@ -18,7 +19,7 @@ geometry, the MIMO backward at the MIMO scan's geometry, the preprocess
 backward over the step's packed projection, and the step's preprocess and
 scan fused into one call on the packed rows.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 200]
 """
 
 from __future__ import annotations
