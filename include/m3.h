@@ -2,7 +2,7 @@
  * m3.h -- C ABI of the MI355X (gfx950) Mamba-3 selective-state path.
  *
  * Nine operations, named after the public functions of the oarust 0.8.6
- * source page src/rs/ml/matrix/mamba3.rs ("Public API" section) and the
+ * source page src/rs/ml/matrix/mamba3.rs (its Public API section) and the
  * ml::matrix API index:
  *
  *   m3_preprocess   mamba3_preprocess   split + transform one packed projection
@@ -64,8 +64,8 @@ typedef enum m3_status {
 } m3_status;
 
 /*
- * Scan geometry and flags: mirror of SsmConfig (mamba3.rs, "Explicit tensor
- * geometry and optional paths for a selective-state scan").  Passed by value.
+ * Scan geometry and flags: mirror of the SsmConfig struct (mamba3.rs, Public
+ * API section).  Passed by value.
  *   batch_size B, sequence_length L, num_heads H,
  *   num_groups G  (0 means G = H: one Q/K group per head),
  *   head_dim P, state_size N, num_rope_angles A (rotary pairs in the state
@@ -89,9 +89,8 @@ typedef struct m3_ssm_config {
 } m3_ssm_config;
 
 /*
- * Preprocess geometry and bounds: mirror of Mamba3PreprocessConfig
- * (mamba3.rs, "Geometry and numerical bounds for the fused Mamba-3
- * projection preprocess").  inner_size I (width of the z and x slices),
+ * Preprocess geometry and bounds: mirror of the Mamba3PreprocessConfig struct
+ * (mamba3.rs, Public API section).  inner_size I (width of the z and x slices),
  * state_size N, num_heads H, num_rope_angles A, num_groups G (>= 1 here),
  * mimo_rank R, RMS epsilon, inclusive dt bounds [dt_min, dt_max], and
  * a_floor, the positive floor of the A magnitude.
@@ -110,8 +109,7 @@ typedef struct m3_preprocess_config {
 } m3_preprocess_config;
 
 /*
- * m3_preprocess -- mamba3_preprocess ("Split and transform one packed
- * Mamba-3 input projection"; PreprocessGeometry::resolve for the rules;
+ * m3_preprocess -- mamba3_preprocess (PreprocessGeometry::resolve for the rules;
  * Mamba3PreprocessResult for the outputs).
  *
  * In:  projected [rows, W] with W = 2I + 2*G*R*N + 3H + A, columns in the
@@ -133,9 +131,8 @@ int m3_preprocess(const float* projected, const float* dt_bias, uint32_t rows,
                   void* stream);
 
 /*
- * m3_siso_fwd -- mamba3_siso ("Run the Mamba-3 SISO selective-state
- * recurrence"; Geometry::resolve for the rules).  Operands in the pages'
- * order, C before B:
+ * m3_siso_fwd -- mamba3_siso (Geometry::resolve for the rules).  Operands in
+ * the pages' order, C before B:
  *   c, b [B,L,G,N];  x, z [B,L,H,P];  adt, dt, trap [B,L,H];  angle [B,L,A];
  *   c_bias, b_bias [H,N];  d [H]   ->   out [B,L,H,P].
  * Per (batch, head), from a zero state, for t = 0..L-1:
@@ -187,8 +184,7 @@ int m3_siso_fwd_packed(const float* projected, const float* dt_bias, const float
                        void* stream);
 
 /*
- * m3_mimo_fwd -- mamba3_mimo ("Run the shared-state Mamba-3 MIMO selective
- * scan"; MimoGeometry::resolve for the rules).  Operands:
+ * m3_mimo_fwd -- mamba3_mimo (MimoGeometry::resolve for the rules).  Operands:
  *   c, b [B,L,R*G,N] (row r*G + g is rank r of group g);  x, z [B,L,H,P];
  *   adt, dt, trap [B,L,H];  angle [B,L,A];  c_bias, b_bias [H,R,N];  d [H];
  *   mimo_x, mimo_z, mimo_o [H,R,P];  norm_weight [H,P]  ->  out [B,L,H,P].
@@ -215,8 +211,7 @@ int m3_mimo_fwd(const float* c, const float* b, const float* x, const float* z,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * m3_siso_step -- mamba3_siso_step ("Advance one Mamba-3 SISO token and
- * update four explicit recurrent states"; dispatch_mamba3_siso_step for the
+ * m3_siso_step -- mamba3_siso_step (dispatch_mamba3_siso_step for the
  * state shapes).  The eleven operands take their L == 1 shapes
  * (c, b [B,1,G,N]; x, z [B,1,H,P]; adt, dt, trap [B,1,H]; angle [B,1,A];
  * biases [H,N]; d [H]).  States, read and written in place:
@@ -238,8 +233,7 @@ int m3_siso_step(const float* c, const float* b, const float* x, const float* z,
                  m3_ssm_config cfg, float* out, void* stream);
 
 /*
- * m3_mimo_step -- mamba3_mimo_step ("Advance one Mamba-3 MIMO token";
- * dispatch_mamba3_mimo_step for the state shapes).  The fifteen operands of
+ * m3_mimo_step -- mamba3_mimo_step (dispatch_mamba3_mimo_step for the state shapes).  The fifteen operands of
  * m3_mimo_fwd take their L == 1 shapes (c, b [B,1,R*G,N]; x, z [B,1,H,P];
  * adt, dt, trap [B,1,H]; angle [B,1,A]; biases [H,R,N]; d [H];
  * mimo_x, mimo_z, mimo_o [H,R,P]; norm_weight [H,P]).  States, read and
@@ -264,8 +258,8 @@ int m3_mimo_step(const float* c, const float* b, const float* x, const float* z,
                  m3_ssm_config cfg, float* out, void* stream);
 
 /*
- * m3_siso_bwd -- mamba3_siso_backward ("Compute all explicit Mamba-3 SISO
- * adjoints"; SsmBackward for the eleven gradients).  Given the upstream
+ * m3_siso_bwd -- mamba3_siso_backward (SsmBackward for the eleven
+ * gradients).  Given the upstream
  * gradient dout [B,L,H,P] of m3_siso_fwd's output and the same eleven
  * operands and config as the forward call, writes the gradient of
  * sum(dout * out) with respect to every operand, each in its operand's
@@ -300,9 +294,8 @@ int m3_siso_bwd(const float* dout, const float* c, const float* b, const float* 
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * m3_mimo_bwd -- mamba3_mimo_backward ("deterministic prepare, post,
- * reverse-core, inverse-rotation, and reduction stages"; Mamba3MimoBackward
- * for the fifteen gradients).  Given dout [B,L,H,P] and the fifteen
+ * m3_mimo_bwd -- mamba3_mimo_backward (Mamba3MimoBackward for the fifteen
+ * gradients).  Given dout [B,L,H,P] and the fifteen
  * operands and config of the m3_mimo_fwd call, writes the gradient of
  * sum(dout * out) for every operand in its layout: d_c, d_b [B,L,R*G,N]
  * (row r*G + g, summed over the group's heads); d_x, d_z [B,L,H,P];
@@ -365,7 +358,19 @@ int m3_preprocess_bwd(const float* projected, const float* dt_bias, uint32_t row
  */
 void m3_set_profile_events(void* start_event, void* stop_event);
 
-/* Thread-local message of the last failed call on this thread ("" if none). */
+/*
+ * Scan plan override (testing and tuning).  The scan cuts each sequence
+ * into segments that run in parallel, after a first pass that summarises
+ * every segment but the last; by default the count fills two workgroups per
+ * compute unit of the current device.  m3_set_scan_segments(n) with n > 0
+ * makes later m3_siso_fwd, m3_siso_fwd_packed and m3_mimo_fwd calls (and
+ * their workspace queries) on this thread use n segments, fewer when the
+ * sequence has fewer whole chunks; n = 0 restores the default.  Results
+ * agree to float32 rounding whatever the count.
+ */
+void m3_set_scan_segments(uint32_t segments);
+
+/* Thread-local message of the last failed call on this thread (empty if none). */
 const char* m3_last_error(void);
 
 /* Library version string. */

@@ -26,6 +26,8 @@ from ._binding import (  # noqa: F401
     m3_siso_step,
     mimo_bwd_workspace_bytes,
     mimo_fwd_workspace_bytes,
+    scan_segments,
+    set_scan_segments,
     siso_bwd_workspace_bytes,
     siso_fwd_packed_workspace_bytes,
     siso_fwd_workspace_bytes,

@@ -129,10 +129,32 @@ def lib() -> ctypes.CDLL:
     L.m3_siso_bwd_workspace_bytes.argtypes = [_CSsm]
     L.m3_siso_bwd.restype = ctypes.c_int
     L.m3_siso_bwd.argtypes = [_P] * 12 + [_CSsm] + [_P] * 11 + [_P, ctypes.c_size_t, _P]
+    L.m3_set_scan_segments.restype = None
+    L.m3_set_scan_segments.argtypes = [ctypes.c_uint32]
     L.m3_preprocess_bwd.restype = ctypes.c_int
     L.m3_preprocess_bwd.argtypes = [_P, _P, ctypes.c_uint32, _CPre] + [_P] * 8 + [_P, _P, _P]
     _LIB = L
     return L
+
+
+def set_scan_segments(segments: int) -> None:
+    """Force the scan plan's segment count on this thread (0 = automatic)."""
+    lib().m3_set_scan_segments(int(segments))
+
+
+class scan_segments:
+    """Context manager: run the scans inside it with a forced segment count."""
+
+    def __init__(self, segments: int):
+        self.segments = int(segments)
+
+    def __enter__(self):
+        set_scan_segments(self.segments)
+        return self
+
+    def __exit__(self, *exc):
+        set_scan_segments(0)
+        return False
 
 
 def header_functions() -> list:

@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 
 namespace {
 
@@ -48,39 +49,61 @@ struct Resolved {
   m3::ScanGeom g;
 };
 
-// Shared rule set of the scan geometry.  `mimo` selects the MIMO rules.
+// Shared rule set of the scan geometry, one rule at a time, so that the
+// message names the rule that failed.  `mimo` selects the multi-input rules
+// (rank 1..8 and an optional output norm) instead of the single-input ones
+// (rank exactly 1, no output norm).
 int resolve_scan(const char* op, const m3_ssm_config& cfg, bool mimo, m3::ScanGeom* out) {
   const uint32_t G = cfg.num_groups == 0 ? cfg.num_heads : cfg.num_groups;
-  const bool flags_ok = cfg.has_z <= 1 && cfg.has_d <= 1 && cfg.has_output_norm <= 1;
-  if (!flags_ok)
-    return fail(M3_ERR_INVALID_ARGUMENT, "%s: has_z, has_d and has_output_norm must be 0 or 1", op);
-  bool bad = cfg.batch_size == 0 || cfg.sequence_length == 0 || cfg.num_heads == 0 || G == 0 ||
-             cfg.num_heads % G != 0 || cfg.head_dim == 0 || cfg.head_dim > 128 ||
-             cfg.state_size == 0 || cfg.state_size > 128 || cfg.num_rope_angles > 64 ||
-             2ull * cfg.num_rope_angles > cfg.state_size;
+  const struct {
+    const char* name;
+    uint32_t v;
+  } flags[] = {{"has_z", cfg.has_z}, {"has_d", cfg.has_d}, {"has_output_norm", cfg.has_output_norm}};
+  for (const auto& f : flags)
+    if (f.v > 1) return fail(M3_ERR_INVALID_ARGUMENT, "%s: flag %s is %u; a flag is 0 or 1", op, f.name, f.v);
+  const struct {
+    const char* name;
+    uint32_t v;
+  } extents[] = {{"batch_size", cfg.batch_size}, {"sequence_length", cfg.sequence_length},
+                 {"num_heads", cfg.num_heads}, {"head_dim", cfg.head_dim}, {"state_size", cfg.state_size}};
+  for (const auto& e : extents)
+    if (e.v == 0) return fail(M3_ERR_INVALID_ARGUMENT, "%s: %s is 0; every extent must be at least 1", op, e.name);
+  if (cfg.num_heads % G != 0)
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: num_groups %u does not divide num_heads %u", op, G, cfg.num_heads);
+  if (cfg.head_dim > 128)
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: head_dim %u is above the limit of 128", op, cfg.head_dim);
+  if (cfg.state_size > 128)
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: state_size %u is above the limit of 128", op, cfg.state_size);
+  if (cfg.num_rope_angles > 64)
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: num_rope_angles %u is above the limit of 64", op,
+                cfg.num_rope_angles);
+  if (2ull * cfg.num_rope_angles > cfg.state_size)
+    return fail(M3_ERR_INVALID_ARGUMENT,
+                "%s: the %u rotary pairs need 2 * num_rope_angles = %u state coordinates, but state_size is %u",
+                op, cfg.num_rope_angles, 2 * cfg.num_rope_angles, cfg.state_size);
   if (mimo) {
-    bad = bad || cfg.mimo_rank < 1 || cfg.mimo_rank > 8;
-    if (bad)
-      return fail(M3_ERR_INVALID_ARGUMENT,
-                  "%s requires B/L/H/G/P/N > 0, H divisible by G, P/N <= 128, A <= 64, 2A <= N, "
-                  "and MIMO rank in 1..=8",
-                  op);
+    if (cfg.mimo_rank < 1 || cfg.mimo_rank > 8)
+      return fail(M3_ERR_INVALID_ARGUMENT, "%s: mimo_rank %u is outside 1..8", op, cfg.mimo_rank);
   } else {
-    bad = bad || cfg.mimo_rank != 1 || cfg.has_output_norm != 0;
-    if (bad)
+    if (cfg.mimo_rank != 1)
+      return fail(M3_ERR_INVALID_ARGUMENT, "%s: mimo_rank is %u; the single-input scan takes rank 1 only", op,
+                  cfg.mimo_rank);
+    if (cfg.has_output_norm != 0)
       return fail(M3_ERR_INVALID_ARGUMENT,
-                  "%s requires B/L/H/G/P/N > 0, H divisible by G, P/N <= 128, A <= 64, 2A <= N, "
-                  "MIMO rank one, and no MIMO output normalization",
-                  op);
+                  "%s: has_output_norm is set; the output norm belongs to the multi-input scan only", op);
   }
   const uint64_t B = cfg.batch_size, L = cfg.sequence_length, H = cfg.num_heads, P = cfg.head_dim,
                  N = cfg.state_size, A = cfg.num_rope_angles, R = mimo ? cfg.mimo_rank : 1;
-  const bool counts_ok = count_u32({B, L, R * G, N}) && count_u32({B, L, H, P}) &&
-                         count_u32({B, L, H}) && count_u32({B, L, A}) && count_u32({H, R, N}) &&
-                         count_u32({H, R, P}) && count_u32({B, H});
-  if (!counts_ok)
-    return fail(M3_ERR_INVALID_ARGUMENT, "%s: a tensor element count or the batch-head count exceeds u32",
-                op);
+  const struct {
+    const char* name;
+    bool ok;
+  } counts[] = {{"c / b", count_u32({B, L, R * G, N})}, {"x / z / out", count_u32({B, L, H, P})},
+                {"adt / dt / trap", count_u32({B, L, H})}, {"angle", count_u32({B, L, A})},
+                {"c_bias / b_bias", count_u32({H, R, N})}, {"mimo weight", count_u32({H, R, P})},
+                {"batch * heads", count_u32({B, H})}};
+  for (const auto& c : counts)
+    if (!c.ok)
+      return fail(M3_ERR_INVALID_ARGUMENT, "%s: the %s element count does not fit in u32", op, c.name);
   out->B = cfg.batch_size;
   out->L = cfg.sequence_length;
   out->H = cfg.num_heads;
@@ -119,24 +142,41 @@ void m3_set_profile_events(void* start_event, void* stop_event) {
   pe.stop = on ? static_cast<hipEvent_t>(stop_event) : nullptr;
 }
 
-const char* m3_version(void) { return "m3 0.1.0 gfx950"; }
+const char* m3_version(void) { return "m3 0.2.0 gfx950"; }
+
+void m3_set_scan_segments(uint32_t segments) { m3::set_forced_segments(segments); }
 
 }  // extern "C"
 
 namespace {
 
-// Preprocess geometry rules shared by the forward and the backward.
+// Preprocess geometry rules shared by the forward and the backward, checked
+// one at a time so that the message names the rule that failed.
 int resolve_pre(const char* op, uint32_t rows, const m3_preprocess_config& cfg, m3::PreGeom* out) {
-  if (rows == 0 || cfg.inner_size == 0 || cfg.state_size == 0 || cfg.num_heads == 0 ||
-      cfg.num_groups == 0 || cfg.mimo_rank == 0 ||
-      2ull * cfg.num_rope_angles > cfg.state_size || !std::isfinite(cfg.epsilon) ||
-      cfg.epsilon <= 0.f || !std::isfinite(cfg.dt_min) || !std::isfinite(cfg.dt_max) ||
-      cfg.dt_min <= 0.f || cfg.dt_min > cfg.dt_max || !std::isfinite(cfg.a_floor) ||
-      cfg.a_floor <= 0.f)
+  const struct {
+    const char* name;
+    uint32_t v;
+  } extents[] = {{"rows", rows}, {"inner_size", cfg.inner_size}, {"state_size", cfg.state_size},
+                 {"num_heads", cfg.num_heads}, {"num_groups", cfg.num_groups}, {"mimo_rank", cfg.mimo_rank}};
+  for (const auto& e : extents)
+    if (e.v == 0) return fail(M3_ERR_INVALID_ARGUMENT, "%s: %s is 0; every extent must be at least 1", op, e.name);
+  if (2ull * cfg.num_rope_angles > cfg.state_size)
     return fail(M3_ERR_INVALID_ARGUMENT,
-                "%s requires positive geometry, 2*rope_angles <= state_size, finite epsilon/dt/A bounds, "
-                "epsilon/dt_min/A floor > 0, and dt_min <= dt_max",
-                op);
+                "%s: the %u rotary pairs need 2 * num_rope_angles = %u state coordinates, but state_size is %u",
+                op, cfg.num_rope_angles, 2 * cfg.num_rope_angles, cfg.state_size);
+  const struct {
+    const char* name;
+    float v;
+  } bounds[] = {{"epsilon", cfg.epsilon}, {"dt_min", cfg.dt_min}, {"dt_max", cfg.dt_max}, {"a_floor", cfg.a_floor}};
+  for (const auto& b : bounds)
+    if (!std::isfinite(b.v)) return fail(M3_ERR_INVALID_ARGUMENT, "%s: %s is not a finite number", op, b.name);
+  // dt_max needs no sign rule of its own: it is at least dt_min
+  for (const auto& b : {bounds[0], bounds[1], bounds[3]})
+    if (b.v <= 0.f)
+      return fail(M3_ERR_INVALID_ARGUMENT, "%s: %s is %g; it must be above zero", op, b.name, (double)b.v);
+  if (cfg.dt_min > cfg.dt_max)
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: dt_min %g is above dt_max %g", op, (double)cfg.dt_min,
+                (double)cfg.dt_max);
   const uint64_t I = cfg.inner_size, N = cfg.state_size, H = cfg.num_heads,
                  A = cfg.num_rope_angles, GR = (uint64_t)cfg.num_groups * cfg.mimo_rank;
   const uint64_t M = GR * N;
@@ -244,12 +284,21 @@ int resolve_packed(const char* op, const m3_preprocess_config& pcfg, const m3_ss
   if (!count_u32({g.B, g.L})) return fail(M3_ERR_INVALID_ARGUMENT, "%s: batch_size * sequence_length exceeds u32", op);
   st = resolve_pre(op, g.B * g.L, pcfg, &pp->pg);
   if (st) return st;
-  if ((uint64_t)pcfg.inner_size != (uint64_t)g.H * g.P || pcfg.state_size != g.N || pcfg.num_heads != g.H ||
-      pcfg.num_rope_angles != g.A || pcfg.num_groups != g.G || pcfg.mimo_rank != 1)
-    return fail(M3_ERR_INVALID_ARGUMENT,
-                "%s requires inner_size == num_heads * head_dim and equal state_size, num_heads, "
-                "num_rope_angles and num_groups (resolved) in both configs, and mimo_rank 1",
-                op);
+  if ((uint64_t)pcfg.inner_size != (uint64_t)g.H * g.P)
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: inner_size %u differs from num_heads * head_dim = %u", op,
+                pcfg.inner_size, g.H * g.P);
+  const struct {
+    const char* name;
+    uint32_t pre, scan;
+  } same[] = {{"state_size", pcfg.state_size, g.N}, {"num_heads", pcfg.num_heads, g.H},
+              {"num_rope_angles", pcfg.num_rope_angles, g.A}, {"num_groups", pcfg.num_groups, g.G}};
+  for (const auto& m : same)
+    if (m.pre != m.scan)
+      return fail(M3_ERR_INVALID_ARGUMENT, "%s: %s is %u in the preprocess config but %u in the scan config", op,
+                  m.name, m.pre, m.scan);
+  if (pcfg.mimo_rank != 1)
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: the preprocess config has mimo_rank %u; the fused call is rank 1",
+                op, pcfg.mimo_rank);
   pp->I = pcfg.inner_size;
   pp->M = g.G * g.N;
   pp->W = 2 * pp->I + 2 * pp->M + 3 * g.H + g.A;
@@ -425,7 +474,8 @@ int m3_siso_step(const float* c, const float* b, const float* x, const float* z,
   int st = resolve_scan(op, cfg, false, &g);
   if (st) return st;
   if (cfg.sequence_length != 1)
-    return fail(M3_ERR_INVALID_ARGUMENT, "%s requires sequence_length == 1", op);
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: sequence_length is %u; a decode step takes exactly one token", op,
+                cfg.sequence_length);
   if (!count_u32({g.B, g.H, g.P, g.N}))
     return fail(M3_ERR_INVALID_ARGUMENT, "%s: state element count exceeds u32", op);
   st = check_ptrs(op, {{"c", c}, {"b", b}, {"x", x}, {"z", z}, {"adt", adt}, {"dt", dt},
@@ -452,7 +502,8 @@ int m3_mimo_step(const float* c, const float* b, const float* x, const float* z,
   int st = resolve_scan(op, cfg, true, &g);
   if (st) return st;
   if (cfg.sequence_length != 1)
-    return fail(M3_ERR_INVALID_ARGUMENT, "%s requires sequence_length == 1", op);
+    return fail(M3_ERR_INVALID_ARGUMENT, "%s: sequence_length is %u; a decode step takes exactly one token", op,
+                cfg.sequence_length);
   if (!count_u32({g.B, g.H, g.P, g.N}) || !count_u32({g.B, g.H, g.R, g.N}) || !count_u32({g.B, g.H, g.R, g.P}))
     return fail(M3_ERR_INVALID_ARGUMENT, "%s: state element count exceeds u32", op);
   st = check_ptrs(op, {{"c", c}, {"b", b}, {"x", x}, {"z", z}, {"adt", adt}, {"dt", dt},

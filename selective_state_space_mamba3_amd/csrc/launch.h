@@ -68,6 +68,16 @@ struct ProfileEvents {
 };
 ProfileEvents& profile_events();
 
+// Compute units of the current HIP device, queried once per device (256, the
+// MI355X count, when no device answers).  The scan plan sizes its sequence
+// segments by it, so a workspace query and the call it sizes must run with
+// the same device current.
+int device_cu_count();
+// Thread-local override of the scan plan's sequence-segment count: 0 is the
+// automatic choice; n > 0 asks for n segments (fewer when the sequence has
+// fewer whole chunks).
+void set_forced_segments(uint32_t nseg);
+
 ScanPlan plan_siso(const ScanGeom& g);
 ScanPlan plan_mimo(const ScanGeom& g);
 inline size_t plan_workspace_bytes(const ScanPlan& p) {

@@ -49,9 +49,9 @@
 #include "common.h"
 #include "launch.h"
 
-#include <stdlib.h>
-
 #include <algorithm>
+#include <map>
+#include <mutex>
 
 namespace m3 {
 namespace {
@@ -943,11 +943,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   }
 }
 
-int env_int(const char* name, int dflt) {
-  const char* s = getenv(name);
-  if (!s || !*s) return dflt;
-  return atoi(s);
-}
+thread_local uint32_t g_forced_segments = 0;
 
 int rank_stride(int R) {
   int RS = 1;
@@ -962,15 +958,14 @@ ScanPlan make_plan(const ScanGeom& g) {
   const int NT = ((int)g.N + 15) / 16, PT = ((int)g.P + 15) / 16;
   const long bhn = (long)g.B * g.H;
   // Split the sequence into as many segments as keep every workgroup resident
-  // at once (two per CU on 256 CUs), so no CU runs a second round; each
-  // segment keeps at least four chunks.
-  const int target = env_int("M3_SCAN_TARGET_WG", 512);
+  // at once (two per CU), so no CU runs a second round; each segment keeps at
+  // least four chunks.
+  const long target = 2L * device_cu_count();
   long nseg = 1;
   if (bhn < target) nseg = target / bhn;
   const long max_seg = ((long)g.L + 4L * Qt - 1) / (4L * Qt);
   if (nseg > max_seg) nseg = max_seg;
-  const int forced = env_int("M3_SCAN_NSEG", 0);
-  if (forced > 0) nseg = forced;
+  if (g_forced_segments > 0) nseg = (long)g_forced_segments;
   if (nseg < 1) nseg = 1;
   long seg_len = ((long)g.L + nseg - 1) / nseg;
   seg_len = (seg_len + Qt - 1) / Qt * Qt;
@@ -1030,18 +1025,29 @@ void layout(ScanKParams& kp, bool full, bool mimo, bool split) {
   kp.lds_floats = off;
 }
 
+// Raise a kernel's dynamic-LDS limit to one CU's 160 KiB, once per kernel
+// (thread-safe); later calls return the first call's status.
+hipError_t set_max_lds_once(const void* fn) {
+  static std::mutex mu;
+  static std::map<const void*, hipError_t> done;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = done.find(fn);
+  if (it != done.end()) return it->second;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e != hipSuccess) (void)hipGetLastError();
+  done.emplace(fn, e);
+  return e;
+}
+
 template <int VEC, bool FULL, bool MIMO, int NTC, int PTC, int NWC, int RSC, bool STR>
 hipError_t launch_one(const ScanKParams& kp, unsigned grid, unsigned block, hipStream_t stream) {
   const size_t lds_bytes = (size_t)kp.lds_floats * sizeof(float);
-  // Dynamic LDS above 64 KiB needs the opt-in attribute on some runtimes;
-  // raise it when a larger layout first appears, and keep going if the
-  // runtime does not know the attribute.
-  static size_t attr_bytes = 64 * 1024;
-  if (lds_bytes > attr_bytes) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC, RSC, STR>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) != hipSuccess)
-      (void)hipGetLastError();
-    attr_bytes = lds_bytes;
+  // Dynamic LDS above 64 KiB needs the opt-in attribute; set it once per
+  // kernel instantiation to the largest layout it can take (the CU's 160 KiB)
+  // and report a failure instead of launching.
+  if (lds_bytes > 64 * 1024) {
+    hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(&scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC, RSC, STR>));
+    if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC, RSC, STR>), dim3(grid), dim3(block), lds_bytes,
                      stream, kp);
@@ -1150,6 +1156,28 @@ ProfileEvents& profile_events() {
   static thread_local ProfileEvents pe{nullptr, nullptr};
   return pe;
 }
+
+int device_cu_count() {
+  constexpr int kMaxDev = 64;
+  static std::once_flag once[kMaxDev];
+  static int cus[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  std::call_once(once[dev], [dev] {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
+      (void)hipGetLastError();
+      v = 256;
+    }
+    cus[dev] = v;
+  });
+  return cus[dev];
+}
+
+void set_forced_segments(uint32_t nseg) { g_forced_segments = nseg; }
 
 ScanPlan plan_siso(const ScanGeom& g) { return make_plan(g); }
 ScanPlan plan_mimo(const ScanGeom& g) { return make_plan(g); }

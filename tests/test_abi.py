@@ -24,7 +24,7 @@ def _lib():
 
 def test_library_exports_every_header_function():
     names = m3.header_functions()
-    assert set(names) >= {"m3_preprocess", "m3_siso_fwd", "m3_mimo_fwd", "m3_siso_step",
+    assert set(names) >= {"m3_preprocess", "m3_siso_fwd", "m3_mimo_fwd", "m3_siso_step", "m3_set_scan_segments",
                           "m3_mimo_step", "m3_siso_bwd", "m3_preprocess_bwd", "m3_siso_fwd_packed",
                           "m3_mimo_bwd", "m3_mimo_bwd_workspace_bytes",
                           "m3_siso_bwd_workspace_bytes", "m3_last_error", "m3_siso_fwd_workspace_bytes",
@@ -52,18 +52,25 @@ def _siso_call(cfg, ptrs=None, ws=FAKE, ws_bytes=1 << 40):
     return L.m3_siso_fwd(*p, bd.c_ssm(cfg), FAKE, ws, ws_bytes, None)
 
 
+# each broken rule, with the words the error message must use to name it
 SISO_BAD = [
-    dict(batch_size=0), dict(sequence_length=0), dict(num_heads=0), dict(num_groups=3),
-    dict(head_dim=0), dict(head_dim=129), dict(state_size=0), dict(state_size=129),
-    dict(num_rope_angles=65, state_size=128), dict(num_rope_angles=17), dict(mimo_rank=2),
-    dict(has_output_norm=True), dict(num_heads=4, num_groups=8),
+    (dict(batch_size=0), "batch_size is 0"), (dict(sequence_length=0), "sequence_length is 0"),
+    (dict(num_heads=0), "num_heads is 0"), (dict(num_groups=3), "num_groups 3 does not divide num_heads 4"),
+    (dict(head_dim=0), "head_dim is 0"), (dict(head_dim=129), "head_dim 129 is above the limit of 128"),
+    (dict(state_size=0), "state_size is 0"), (dict(state_size=129), "state_size 129 is above the limit of 128"),
+    (dict(num_rope_angles=65, state_size=128), "num_rope_angles 65 is above the limit of 64"),
+    (dict(num_rope_angles=17), "2 * num_rope_angles = 34 state coordinates, but state_size is 32"),
+    (dict(mimo_rank=2), "mimo_rank is 2; the single-input scan takes rank 1 only"),
+    (dict(has_output_norm=True), "has_output_norm is set"),
+    (dict(num_heads=4, num_groups=8), "num_groups 8 does not divide num_heads 4"),
 ]
 
 
-@pytest.mark.parametrize("bad", SISO_BAD)
-def test_siso_rejects_broken_geometry(bad):
+@pytest.mark.parametrize("bad,rule", SISO_BAD)
+def test_siso_rejects_broken_geometry(bad, rule):
     assert _siso_call(_ssm(**bad)) == INVALID
-    assert "m3_siso_fwd" in m3.last_error()
+    msg = m3.last_error()
+    assert msg.startswith("m3_siso_fwd: ") and rule in msg, msg
 
 
 def test_siso_rejects_flags_and_null_operands():
@@ -71,6 +78,7 @@ def test_siso_rejects_flags_and_null_operands():
     c = bd.c_ssm(_ssm())
     c.has_z = 2
     assert L.m3_siso_fwd(*[FAKE] * 11, c, FAKE, FAKE, 1 << 40, None) == INVALID
+    assert "flag has_z is 2" in m3.last_error()
     for i in range(11):
         p = [FAKE] * 11
         p[i] = None
@@ -89,7 +97,7 @@ def test_u32_element_count_limit():
     cfg = _ssm(batch_size=1 << 12, sequence_length=1 << 12, num_heads=2, num_groups=1,
                head_dim=128, state_size=16, num_rope_angles=0)
     assert _siso_call(cfg) == INVALID
-    assert "u32" in m3.last_error()
+    assert "the x / z / out element count does not fit in u32" in m3.last_error()
 
 
 def test_workspace_rule():
@@ -104,18 +112,43 @@ def test_workspace_rule():
     assert m3.siso_fwd_workspace_bytes(_ssm(batch_size=0)) == 0
 
 
-MIMO_BAD = [dict(mimo_rank=0), dict(mimo_rank=9), dict(head_dim=129), dict(num_groups=3),
-            dict(num_rope_angles=17), dict(has_output_norm=2)]
+def test_scan_segment_override():
+    # the plan override changes the segment count, and with it the summary
+    # workspace, on this thread only; 0 restores the automatic plan
+    cfg = _ssm(batch_size=1, num_heads=1, num_groups=1, sequence_length=4096, head_dim=64,
+               state_size=128, num_rope_angles=32)
+    auto = m3.siso_fwd_workspace_bytes(cfg)
+    with m3.scan_segments(1):
+        assert m3.siso_fwd_workspace_bytes(cfg) == 0
+    with m3.scan_segments(3):
+        three = m3.siso_fwd_workspace_bytes(cfg)
+    with m3.scan_segments(5):
+        five = m3.siso_fwd_workspace_bytes(cfg)
+    assert 0 < three < five
+    assert m3.siso_fwd_workspace_bytes(cfg) == auto
+    import threading
+    seen = {}
+    with m3.scan_segments(1):
+        th = threading.Thread(target=lambda: seen.setdefault("ws", m3.siso_fwd_workspace_bytes(cfg)))
+        th.start()
+        th.join()
+    assert seen["ws"] == auto
 
 
-@pytest.mark.parametrize("bad", MIMO_BAD)
-def test_mimo_rejects_broken_geometry(bad):
+MIMO_BAD = [(dict(mimo_rank=0), "mimo_rank 0 is outside 1..8"), (dict(mimo_rank=9), "mimo_rank 9 is outside 1..8"),
+            (dict(head_dim=129), "head_dim 129 is above"), (dict(num_groups=3), "does not divide"),
+            (dict(num_rope_angles=17), "2 * num_rope_angles = 34"), (dict(has_output_norm=2), "flag has_output_norm is 2")]
+
+
+@pytest.mark.parametrize("bad,rule", MIMO_BAD)
+def test_mimo_rejects_broken_geometry(bad, rule):
     L = _lib()
     c = bd.c_ssm(_ssm(mimo_rank=2))
     for k, v in bad.items():
         setattr(c, k, int(v))
     assert L.m3_mimo_fwd(*[FAKE] * 15, c, FAKE, FAKE, 1 << 40, None) == INVALID
-    assert "m3_mimo_fwd" in m3.last_error()
+    msg = m3.last_error()
+    assert msg.startswith("m3_mimo_fwd: ") and rule in msg, msg
 
 
 def test_mimo_lifts_the_pn_cap_and_checks_pointers():
@@ -133,7 +166,7 @@ def test_step_rules():
     cfg = _ssm(sequence_length=2)
     args = [FAKE] * 15
     assert L.m3_siso_step(*args, bd.c_ssm(cfg), FAKE, None) == INVALID
-    assert "sequence_length == 1" in m3.last_error()
+    assert "sequence_length is 2; a decode step takes exactly one token" in m3.last_error()
     for i in (11, 13, 14):  # ssm_state, k_state, v_state
         a = list(args)
         a[i] = None
@@ -149,7 +182,7 @@ def test_mimo_step_rules():
     args = [FAKE] * 19
     one = _ssm(sequence_length=1, mimo_rank=2)
     assert L.m3_mimo_step(*args, bd.c_ssm(_ssm(sequence_length=2, mimo_rank=2)), FAKE, None) == INVALID
-    assert "sequence_length == 1" in m3.last_error()
+    assert "sequence_length is 2; a decode step takes exactly one token" in m3.last_error()
     for i in (15, 17, 18):  # ssm_state, k_state, v_state
         a = list(args)
         a[i] = None
@@ -172,34 +205,41 @@ def _pre(**kw):
     return bd.PreprocessConfig(**base)
 
 
-PRE_BAD = [dict(inner_size=0), dict(state_size=0), dict(num_heads=0), dict(num_groups=0),
-           dict(mimo_rank=0), dict(num_rope_angles=9), dict(epsilon=0.0), dict(epsilon=float("nan")),
-           dict(dt_min=0.0), dict(dt_min=0.2), dict(dt_max=float("inf")), dict(a_floor=0.0),
-           dict(a_floor=-1.0)]
+PRE_BAD = [(dict(inner_size=0), "inner_size is 0"), (dict(state_size=0), "state_size is 0"),
+           (dict(num_heads=0), "num_heads is 0"), (dict(num_groups=0), "num_groups is 0"),
+           (dict(mimo_rank=0), "mimo_rank is 0"), (dict(num_rope_angles=9), "2 * num_rope_angles = 18"),
+           (dict(epsilon=0.0), "epsilon is 0; it must be above zero"),
+           (dict(epsilon=float("nan")), "epsilon is not a finite number"),
+           (dict(dt_min=0.0), "dt_min is 0; it must be above zero"), (dict(dt_min=0.2), "dt_min 0.2 is above dt_max 0.1"),
+           (dict(dt_max=float("inf")), "dt_max is not a finite number"),
+           (dict(a_floor=0.0), "a_floor is 0; it must be above zero"), (dict(a_floor=-1.0), "a_floor is -1")]
 
 
-@pytest.mark.parametrize("bad", PRE_BAD)
-def test_preprocess_rejects_broken_config(bad):
+@pytest.mark.parametrize("bad,rule", PRE_BAD)
+def test_preprocess_rejects_broken_config(bad, rule):
     L = _lib()
     assert L.m3_preprocess(FAKE, FAKE, 16, bd.c_pre(_pre(**bad)), *[FAKE] * 8, None) == INVALID
-    assert "m3_preprocess" in m3.last_error()
+    msg = m3.last_error()
+    assert msg.startswith("m3_preprocess: ") and rule in msg, msg
 
 
 def test_preprocess_rejects_empty_rows_and_nulls():
     L = _lib()
     assert L.m3_preprocess(FAKE, FAKE, 0, bd.c_pre(_pre()), *[FAKE] * 8, None) == INVALID
+    assert "rows is 0" in m3.last_error()
     for i in range(10):
         p = [FAKE] * 10
         p[i] = None
         assert L.m3_preprocess(p[0], p[1], 16, bd.c_pre(_pre()), *p[2:], None) == INVALID
 
 
-@pytest.mark.parametrize("bad", SISO_BAD)
-def test_siso_bwd_rejects_broken_geometry(bad):
+@pytest.mark.parametrize("bad,rule", SISO_BAD)
+def test_siso_bwd_rejects_broken_geometry(bad, rule):
     L = _lib()
     cfg = bd.c_ssm(_ssm(**bad))
     assert L.m3_siso_bwd(*[FAKE] * 12, cfg, *[FAKE] * 11, FAKE, 1 << 40, None) == INVALID
-    assert "m3_siso_bwd" in m3.last_error()
+    msg = m3.last_error()
+    assert msg.startswith("m3_siso_bwd: ") and rule in msg, msg
     assert L.m3_siso_bwd_workspace_bytes(cfg) == 0
 
 
@@ -248,18 +288,20 @@ def test_mimo_bwd_rules():
     assert call([FAKE] * 31, cfg, nb=need - 1) == INVALID
     assert "workspace" in m3.last_error()
     assert call([FAKE] * 31, cfg, ws=None) == INVALID
-    for bad in (dict(mimo_rank=0), dict(mimo_rank=9), dict(head_dim=129), dict(num_groups=3)):
+    for bad, rule in MIMO_BAD[:4]:
         assert call([FAKE] * 31, bd.c_ssm(_ssm(**bad))) == INVALID, bad
+        assert rule in m3.last_error()
         assert L.m3_mimo_bwd_workspace_bytes(bd.c_ssm(_ssm(**bad))) == 0
     big = bd.c_ssm(_ssm(num_heads=256, num_groups=1, state_size=128, mimo_rank=4))
     assert call([FAKE] * 31, big, nb=1 << 40) == bd.M3_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("bad", PRE_BAD)
-def test_preprocess_bwd_rejects_broken_config(bad):
+@pytest.mark.parametrize("bad,rule", PRE_BAD)
+def test_preprocess_bwd_rejects_broken_config(bad, rule):
     L = _lib()
     assert L.m3_preprocess_bwd(FAKE, FAKE, 16, bd.c_pre(_pre(**bad)), *[FAKE] * 8, FAKE, FAKE, None) == INVALID
-    assert "m3_preprocess_bwd" in m3.last_error()
+    msg = m3.last_error()
+    assert msg.startswith("m3_preprocess_bwd: ") and rule in msg, msg
 
 
 def test_preprocess_bwd_null_rules():
@@ -287,13 +329,19 @@ def test_siso_fwd_packed_rules():
     rows = cfg.batch_size * cfg.sequence_length
     assert need >= 4 * rows * (2 * cfg.num_groups * cfg.state_size + 2 * cfg.num_heads)
     call = lambda p, c, s, ws=FAKE, nb=need: L.m3_siso_fwd_packed(*p, bd.c_pre(c), bd.c_ssm(s), FAKE, ws, nb, None)
-    for bad in (dict(inner_size=cfg.num_heads * cfg.head_dim + 4), dict(state_size=16), dict(num_heads=2),
-                dict(num_rope_angles=4), dict(num_groups=1), dict(mimo_rank=2), dict(epsilon=0.0)):
+    for bad, rule in ((dict(inner_size=cfg.num_heads * cfg.head_dim + 4), "inner_size 68 differs from num_heads * head_dim = 64"),
+                      (dict(state_size=16), "state_size is 16 in the preprocess config but 32 in the scan config"),
+                      (dict(num_heads=2), "num_heads is 2 in the preprocess config but 4"),
+                      (dict(num_rope_angles=4), "num_rope_angles is 4 in the preprocess config but 8"),
+                      (dict(num_groups=1), "num_groups is 1 in the preprocess config but 2"),
+                      (dict(mimo_rank=2), "the preprocess config has mimo_rank 2"), (dict(epsilon=0.0), "epsilon is 0")):
         assert call([FAKE] * 5, _packed_pre(cfg, **bad), cfg) == INVALID, bad
-        assert "m3_siso_fwd_packed" in m3.last_error()
+        msg = m3.last_error()
+        assert msg.startswith("m3_siso_fwd_packed: ") and rule in msg, msg
         assert L.m3_siso_fwd_packed_workspace_bytes(bd.c_pre(_packed_pre(cfg, **bad)), bd.c_ssm(cfg)) == 0
-    for bad in SISO_BAD:
+    for bad, rule in SISO_BAD:
         assert call([FAKE] * 5, pc, _ssm(**bad)) == INVALID
+        assert rule in m3.last_error()
     for i in range(5):
         p = [FAKE] * 5
         p[i] = None

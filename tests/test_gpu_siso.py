@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+import selective_state_space_mamba3_amd as m3
 from _gpu import assert_parity, gpu_siso, oracle_siso, to_dev
 from workloads import WORKLOADS, Dims, ssm_inputs
 
@@ -49,45 +50,45 @@ def test_siso_trap_extremes(sign):
 
 
 @pytest.mark.parametrize("nseg", [1, 3])
-def test_siso_wide_dynamic_range(nseg, monkeypatch):
+def test_siso_wide_dynamic_range(nseg):
     """x spread over eight decades per token and fast decay (dt up to 0.2):
     the head-geometry kernels split their state-update operands into bf16
     heads and remainders, whose error is relative to each product, so the
     bar holds at any mix of scales."""
-    monkeypatch.setenv("M3_SCAN_NSEG", str(nseg))
     d = Dims(2, 300, 3, 1, 64, 128, 32)
     inp = ssm_inputs(d, seed=2030, dt_range=(1e-3, 0.2))
     rng = np.random.default_rng(2031)
     inp["x"] = (inp["x"] * 10.0 ** rng.uniform(-4.0, 4.0, size=(d.B, d.L, 1, 1))).astype(np.float32)
-    got = gpu_siso(to_dev(inp), d).cpu().numpy()
+    with m3.scan_segments(nseg):
+        got = gpu_siso(to_dev(inp), d).cpu().numpy()
     assert_parity(got, oracle_siso(inp, d), f"wide_range_segments_{nseg}")
 
 
 @pytest.mark.parametrize("nseg", [1, 2, 3, 7])
-def test_siso_forced_segments(nseg, monkeypatch):
+def test_siso_forced_segments(nseg):
     # the same answer whatever the number of sequence segments
-    monkeypatch.setenv("M3_SCAN_NSEG", str(nseg))
     d = Dims(2, 300, 3, 1, 64, 128, 32)
     inp = ssm_inputs(d, seed=2020)
-    got = gpu_siso(to_dev(inp), d).cpu().numpy()
+    with m3.scan_segments(nseg):
+        got = gpu_siso(to_dev(inp), d).cpu().numpy()
     assert_parity(got, oracle_siso(inp, d), f"segments_{nseg}")
 
 
 @pytest.mark.parametrize("nseg", [4, 10])
-def test_siso_forced_segments_a16(nseg, monkeypatch):
-    monkeypatch.setenv("M3_SCAN_NSEG", str(nseg))
+def test_siso_forced_segments_a16(nseg):
     d = Dims(2, 300, 3, 1, 64, 128, 16, has_z=False)
     inp = ssm_inputs(d, seed=2021)
-    got = gpu_siso(to_dev(inp), d).cpu().numpy()
+    with m3.scan_segments(nseg):
+        got = gpu_siso(to_dev(inp), d).cpu().numpy()
     assert_parity(got, oracle_siso(inp, d), f"segments_a16_{nseg}")
 
 
-def test_siso_sixty_four_segments(monkeypatch):
-    # one 32-token chunk per segment: the entry state folds up to 63 summaries
-    monkeypatch.setenv("M3_SCAN_NSEG", "64")
+def test_siso_sixty_four_segments():
+    # one 32-token chunk per segment: the entry state composes up to 126 summaries
     d = Dims(1, 2048, 2, 1, 64, 128, 32)
     inp = ssm_inputs(d, seed=2022)
-    got = gpu_siso(to_dev(inp), d).cpu().numpy()
+    with m3.scan_segments(64):
+        got = gpu_siso(to_dev(inp), d).cpu().numpy()
     assert_parity(got, oracle_siso(inp, d), "segments_64")
 
 
