@@ -158,6 +158,25 @@ int m3_siso_fwd(const float* c, const float* b, const float* x, const float* z,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * m3_siso_fwd_noalloc -- m3_siso_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same operands, layouts, rules and
+ * result as m3_siso_fwd (the same kernels run), but no workspace argument:
+ * the segment summaries go to a fixed 64 MiB scratch array in device memory
+ * that the library holds on every GPU it runs on until the process ends.
+ * The call allocates nothing.  Returns M3_ERR_UNSUPPORTED when
+ * m3_siso_fwd_workspace_bytes(cfg) exceeds 64 MiB (not reached at
+ * head_dim 64 / state_size 128 for any batch, heads or length).  Every call
+ * on one GPU shares that GPU's scratch: calls that overlap on one GPU (two
+ * streams, two threads) race and must be ordered by the caller.  The
+ * scratch needs no clearing: each call writes every part it reads.
+ */
+int m3_siso_fwd_noalloc(const float* c, const float* b, const float* x, const float* z,
+                        const float* adt, const float* dt, const float* trap, const float* angle,
+                        const float* c_bias, const float* b_bias, const float* d,
+                        m3_ssm_config cfg, float* out, void* stream);
+
+/*
  * m3_siso_fwd_packed -- mamba3_preprocess followed by mamba3_siso in one
  * call that reads the packed projection rows directly.  projected [B*L, W]
  * (W = 2I + 2GN + 3H + A, columns z | x | B | C | dt | A | trap | angle) and

@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     m3_preprocess_bwd,
     m3_siso_bwd,
     m3_siso_fwd,
+    m3_siso_fwd_noalloc,
     m3_siso_fwd_packed,
     m3_siso_step,
     mimo_bwd_workspace_bytes,

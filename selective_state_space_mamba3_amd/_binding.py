@@ -129,6 +129,8 @@ def lib() -> ctypes.CDLL:
     L.m3_siso_bwd_workspace_bytes.argtypes = [_CSsm]
     L.m3_siso_bwd.restype = ctypes.c_int
     L.m3_siso_bwd.argtypes = [_P] * 12 + [_CSsm] + [_P] * 11 + [_P, ctypes.c_size_t, _P]
+    L.m3_siso_fwd_noalloc.restype = ctypes.c_int
+    L.m3_siso_fwd_noalloc.argtypes = [_P] * 11 + [_CSsm, _P, _P]
     L.m3_set_scan_segments.restype = None
     L.m3_set_scan_segments.argtypes = [ctypes.c_uint32]
     L.m3_preprocess_bwd.restype = ctypes.c_int
@@ -248,6 +250,24 @@ def m3_siso_fwd(c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d, cfg: SsmCon
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(L_.m3_siso_fwd(*[_ptr(ops[k]) for k in _OPS11], c_ssm(cfg), _ptr(out),
                           _ptr(workspace), ws_bytes, _stream(dev, stream)))
+    return out
+
+
+def m3_siso_fwd_noalloc(c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d, cfg: SsmConfig,
+                        out=None, stream=None) -> torch.Tensor:
+    """m3_siso_fwd with the library's fixed scratch in place of a workspace
+    (the C call allocates nothing); returns out [B, L, H, P]."""
+    L_ = lib()
+    dev = x.device
+    ops = dict(zip(_OPS11, (c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d)))
+    for k, shp in _scan_shapes(cfg, cfg.groups, (cfg.num_heads, cfg.state_size)).items():
+        _expect(k, ops[k], shp, dev)
+    oshape = (cfg.batch_size, cfg.sequence_length, cfg.num_heads, cfg.head_dim)
+    if out is None:
+        out = torch.empty(oshape, dtype=torch.float32, device=dev)
+    _expect("out", out, oshape, dev)
+    _check(L_.m3_siso_fwd_noalloc(*[_ptr(ops[k]) for k in _OPS11], c_ssm(cfg), _ptr(out),
+                                  _stream(dev, stream)))
     return out
 
 

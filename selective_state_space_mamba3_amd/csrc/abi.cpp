@@ -521,3 +521,62 @@ int m3_mimo_step(const float* c, const float* b, const float* x, const float* z,
 }
 
 }  // extern "C"
+
+// ---- m3_siso_fwd_noalloc: the scan's workspace in a fixed device array ------
+//
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops): the segment summaries live in `scratch`, a file-scope
+// device array that every GPU the library runs on holds until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in for the symbol): on the first call on a device, with
+// that device current, hipGetSymbolAddress gives that device's own copy,
+// and every later call on the device uses the kept pointer.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(64) << 20;  // 64 MiB per device
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+}  // namespace
+
+extern "C" {
+
+int m3_siso_fwd_noalloc(const float* c, const float* b, const float* x, const float* z, const float* adt,
+                        const float* dt, const float* trap, const float* angle, const float* c_bias,
+                        const float* b_bias, const float* d, m3_ssm_config cfg, float* out, void* stream) {
+  const char* op = "m3_siso_fwd_noalloc";
+  clear_error();
+  m3::ScanGeom g{};
+  int st = resolve_scan(op, cfg, false, &g);
+  if (st) return st;
+  st = check_ptrs(op, {{"c", c}, {"b", b}, {"x", x}, {"z", z}, {"adt", adt}, {"dt", dt},
+                       {"trap", trap}, {"c_bias", c_bias}, {"b_bias", b_bias}, {"d", d}, {"out", out}});
+  if (st) return st;
+  if (g.A > 0 && angle == nullptr) return fail(M3_ERR_INVALID_ARGUMENT, "%s: operand angle is NULL", op);
+  const m3::ScanPlan plan = m3::plan_siso(g);
+  const size_t need = m3::plan_workspace_bytes(plan);
+  if (need > kScratchBytes)
+    return fail(M3_ERR_UNSUPPORTED, "%s: this geometry needs %zu bytes of scan workspace; the fixed scratch holds %zu",
+                op, need, kScratchBytes);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(op, e);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(M3_ERR_UNSUPPORTED, "%s: device %d is beyond the %d devices the scratch table covers", op, dev,
+                kMaxDevices);
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+    if (g_scratch_err[dev] != hipSuccess) (void)hipGetLastError();
+  });
+  if (g_scratch_err[dev] != hipSuccess) return hip_status(op, g_scratch_err[dev]);
+  m3::ScanOperands o{c, b, x, z, adt, dt, trap, angle, c_bias, b_bias, d,
+                     nullptr, nullptr, nullptr, nullptr, out};
+  void* ws = need > 0 ? g_scratch_ptr[dev] : nullptr;
+  return hip_status(op, m3::launch_siso_fwd(g, o, plan, ws, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+

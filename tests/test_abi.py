@@ -135,6 +135,23 @@ def test_scan_segment_override():
     assert seen["ws"] == auto
 
 
+def test_noalloc_rules():
+    # same validation as m3_siso_fwd, and a clear refusal (before any HIP
+    # call) when the plan's workspace exceeds the fixed 64 MiB scratch
+    L = _lib()
+    for bad, rule in SISO_BAD:
+        assert L.m3_siso_fwd_noalloc(*[FAKE] * 11, bd.c_ssm(_ssm(**bad)), FAKE, None) == INVALID
+        msg = m3.last_error()
+        assert msg.startswith("m3_siso_fwd_noalloc: ") and rule in msg, msg
+    big = _ssm(batch_size=1, num_heads=1, num_groups=1, sequence_length=64000, head_dim=128,
+               state_size=128, num_rope_angles=32)
+    with m3.scan_segments(2000):
+        need = m3.siso_fwd_workspace_bytes(big)
+        assert need > 64 << 20
+        assert L.m3_siso_fwd_noalloc(*[FAKE] * 11, bd.c_ssm(big), FAKE, None) == bd.M3_ERR_UNSUPPORTED
+    assert "fixed scratch holds 67108864" in m3.last_error()
+
+
 MIMO_BAD = [(dict(mimo_rank=0), "mimo_rank 0 is outside 1..8"), (dict(mimo_rank=9), "mimo_rank 9 is outside 1..8"),
             (dict(head_dim=129), "head_dim 129 is above"), (dict(num_groups=3), "does not divide"),
             (dict(num_rope_angles=17), "2 * num_rope_angles = 34"), (dict(has_output_norm=2), "flag has_output_norm is 2")]
