@@ -80,6 +80,54 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     return LIB_PATH
 
 
+ASAN_DIR = os.path.join(BUILD_DIR, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libm3_asan.so")
+
+
+def asan_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime that hipcc's host pass links against."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = shutil.which("clang") or clang
+    res = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError(f"AddressSanitizer runtime not found (clang printed {path!r})")
+    return path
+
+
+def build_asan(verbose: bool = False) -> str:
+    """Host-side AddressSanitizer build of the C ABI layer, for CPU tests.
+
+    abi.cpp (argument validation, plans, error text, the scratch set-up) is
+    compiled with -fsanitize=address on the host pass only (the device code
+    is unchanged) and linked with the kernels' regular objects into
+    _build/asan/libm3_asan.so.  The library carries no sanitizer runtime: a
+    process loads it with asan_runtime() preloaded."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    others = []
+    for src in SOURCES:
+        if src == "abi.cpp":
+            continue
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        others.append(obj if os.path.exists(obj) else _compile(src, verbose))
+    obj = os.path.join(ASAN_DIR, "abi.o")
+    cmd = [hipcc(), "-x", "hip", *COMMON_FLAGS, "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+           "-fno-omit-frame-pointer", "-I", os.path.join(REPO, "include"), "-c", os.path.join(CSRC, "abi.cpp"),
+           "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc (asan) failed for abi.cpp:\n{res.stdout}{res.stderr}")
+    tmp = ASAN_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address", obj, *others,
+           "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"asan link failed:\n{res.stdout}{res.stderr}")
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("-j", "--jobs", type=int, default=min(8, os.cpu_count() or 4))
