@@ -121,29 +121,10 @@ __device__ __forceinline__ float softplusf_acc(float u) {
   return fmaxf(u, 0.f) + log1pf(expf(-fabsf(u)));
 }
 
-// sin and cos of x, accurate to a few ulp.  The argument is reduced by pi/2
-// (k = rint(x 2/pi), r = x - k pi/2) with pi/2 split into three float32
-// pieces applied by fused multiply-adds (Cody-Waite), or in float64 for
-// |x| >= 8192; then Taylor polynomials on |r| <= pi/4, whose truncation error
-// (below 1e-12) is far under float32 rounding.  The pieces of pi/2 come from
-// Machin's formula evaluated to 60 digits.
-__device__ __forceinline__ void sincos_acc(float x, float* s_out, float* c_out) {
-  float r;
-  int q;
-  if (fabsf(x) < 8192.f) {
-    const float k = rintf(x * 0x1.45f306p-1f);
-    r = fmaf(-k, 0x1.921fb6p+0f, x);
-    r = fmaf(-k, -0x1.777a5cp-25f, r);
-    r = fmaf(-k, -0x1.ee59dap-50f, r);
-    q = (int)k;
-  } else {
-    const double xd = (double)x;
-    const double kd = rint(xd * 0x1.45f306dc9c883p-1);
-    double rd = fma(-kd, 0x1.921fb54442d18p+0, xd);
-    rd = fma(-kd, 0x1.1a62633145c07p-54, rd);
-    r = (float)rd;
-    q = (int)(kd - 4.0 * floor(kd * 0.25));  // k mod 4 without integer overflow
-  }
+// sin and cos of the reduced argument r (|r| <= pi/4) in quadrant q: Taylor
+// polynomials whose truncation error (below 1e-12) is far under float32
+// rounding, then the quadrant's swap and signs.
+__device__ __forceinline__ void sincos_poly(float r, int q, float* s_out, float* c_out) {
   const float r2 = r * r;
   // sin r = r - r^3/3! + r^5/5! - ... ; cos r = 1 - r^2/2! + r^4/4! - ...
   float sp = fmaf(r2, -1.f / 39916800.f, 1.f / 362880.f);
@@ -163,6 +144,43 @@ __device__ __forceinline__ void sincos_acc(float x, float* s_out, float* c_out) 
     case 2: *s_out = -sn; *c_out = -cs; break;
     default: *s_out = -cs; *c_out = sn; break;
   }
+}
+
+// sin and cos of x, accurate to a few ulp.  The argument is reduced by pi/2
+// (k = rint(x 2/pi), r = x - k pi/2) with pi/2 split into three float32
+// pieces applied by fused multiply-adds (Cody-Waite), or in float64 for
+// |x| >= 8192; then sincos_poly.  The pieces of pi/2 come from Machin's
+// formula evaluated to 60 digits.
+__device__ __forceinline__ void sincos_acc(float x, float* s_out, float* c_out) {
+  float r;
+  int q;
+  if (fabsf(x) < 8192.f) {
+    const float k = rintf(x * 0x1.45f306p-1f);
+    r = fmaf(-k, 0x1.921fb6p+0f, x);
+    r = fmaf(-k, -0x1.777a5cp-25f, r);
+    r = fmaf(-k, -0x1.ee59dap-50f, r);
+    q = (int)k;
+  } else {
+    const double xd = (double)x;
+    const double kd = rint(xd * 0x1.45f306dc9c883p-1);
+    double rd = fma(-kd, 0x1.921fb54442d18p+0, xd);
+    rd = fma(-kd, 0x1.1a62633145c07p-54, rd);
+    r = (float)rd;
+    q = (int)(kd - 4.0 * floor(kd * 0.25));  // k mod 4 without integer overflow
+  }
+  sincos_poly(r, q, s_out, c_out);
+}
+
+// The same for an argument held in float64, reduced in float64 whatever its
+// size.  The decode steps form theta = angle_state + dt angle exactly in
+// float64 from its float32 parts, so that an accumulated angle of large
+// magnitude (|theta| of 1e4 has a float32 spacing of 1e-3) loses nothing to
+// a float32 rounding of the sum before its sine is taken.
+__device__ __forceinline__ void sincos_acc_d(double x, float* s_out, float* c_out) {
+  const double kd = rint(x * 0x1.45f306dc9c883p-1);
+  double rd = fma(-kd, 0x1.921fb54442d18p+0, x);
+  rd = fma(-kd, 0x1.1a62633145c07p-54, rd);
+  sincos_poly((float)rd, (int)(kd - 4.0 * floor(kd * 0.25)), s_out, c_out);
 }
 
 // Workgroup barrier for hand-offs through LDS only.  It waits for this wave's

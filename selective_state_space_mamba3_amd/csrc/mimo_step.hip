@@ -57,7 +57,10 @@ __device__ __forceinline__ StepScalars mimo_step_setup(const MimoStepParams& p, 
   // column j < A: the pair (j, j + A); A <= j < N - A: the plain column j + A
   for (int j = tid; j < N - A; j += nthreads) {
     float sn = 0.f, co = 1.f;
-    if (j < A) sincos_acc(fmaf(s.dtv, p.angle[(size_t)b * A + j], p.ang_state[(size_t)bh * A + j]), &sn, &co);
+    // theta exact in float64 (the stored state is its float32 rounding)
+    if (j < A)
+      sincos_acc_d(fma((double)s.dtv, (double)p.angle[(size_t)b * A + j], (double)p.ang_state[(size_t)bh * A + j]),
+                   &sn, &co);
     for (int r = 0; r < R; ++r) {
       const float* brow = p.b + ((size_t)b * R * p.G + (size_t)r * p.G + g) * N;
       const float* crow = p.c + ((size_t)b * R * p.G + (size_t)r * p.G + g) * N;
@@ -230,11 +233,11 @@ __global__ __launch_bounds__(256) void mimo_step_n128p64_kernel(MimoStepParams p
       vp[tid + 256 * k] = vpl[k];
       xr[tid + 256 * k] = xl[k] * mxl[k];
     }
-  const float th = fmaf(dtv, ang, ast);
+  const float th = fmaf(dtv, ang, ast);  // the stored state: float32 rounding of the exact theta
   if (tid < N - A) {
     if (j < A) {
       float sn, co;
-      sincos_acc(th, &sn, &co);
+      sincos_acc_d(fma((double)dtv, (double)ang, (double)ast), &sn, &co);  // theta exact in float64
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float k0 = bl0[r] + bb0[r], k1 = bl1[r] + bb1[r];

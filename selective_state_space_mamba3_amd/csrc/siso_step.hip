@@ -62,9 +62,10 @@ __global__ __launch_bounds__(256) void siso_step_kernel(StepKParams p) {
   const size_t brow = (size_t)h * N;
   for (int j = tid; j < N - A; j += nthreads) {
     if (j < A) {
-      const float th = fmaf(dtv, p.angle[(size_t)b * A + j], p.ang_state[sidx * A + j]);
+      // theta exact in float64 (the stored state is its float32 rounding)
+      const double th = fma((double)dtv, (double)p.angle[(size_t)b * A + j], (double)p.ang_state[sidx * A + j]);
       float s, co;
-      sincos_acc(th, &s, &co);
+      sincos_acc_d(th, &s, &co);
       const float b0 = p.b[row + j] + p.b_bias[brow + j];
       const float b1 = p.b[row + j + A] + p.b_bias[brow + j + A];
       const float c0 = p.c[row + j] + p.c_bias[brow + j];
@@ -180,9 +181,10 @@ __global__ __launch_bounds__(256) void siso_step_n128p64_kernel(StepKParams p) {
   if (tid < N - A) {
     const int j = tid;
     if (j < A) {
-      const float th = fmaf(dtv, p.angle[(size_t)b * A + j], p.ang_state[sidx * A + j]);
+      // theta exact in float64 (the stored state is its float32 rounding)
+      const double th = fma((double)dtv, (double)p.angle[(size_t)b * A + j], (double)p.ang_state[sidx * A + j]);
       float s, co;
-      sincos_acc(th, &s, &co);
+      sincos_acc_d(th, &s, &co);
       const float b0 = p.b[row + j] + p.b_bias[brow + j];
       const float b1 = p.b[row + j + A] + p.b_bias[brow + j + A];
       const float c0 = p.c[row + j] + p.c_bias[brow + j];

@@ -1,6 +1,7 @@
 """GPU parity of m3_siso_fwd against the float64 oracle on seeded inputs."""
 
 import os
+import time
 
 import numpy as np
 import pytest
@@ -8,6 +9,7 @@ import torch
 
 import selective_state_space_mamba3_amd as m3
 from _gpu import assert_parity, gpu_siso, oracle_siso, to_dev
+from oracle_pool import oracle_heads, pool_size
 from workloads import WORKLOADS, Dims, ssm_inputs
 
 pytestmark = pytest.mark.gpu
@@ -109,26 +111,32 @@ def test_siso_does_not_touch_inputs():
         np.testing.assert_array_equal(di[k].cpu().numpy(), v)
 
 
-def test_siso_full_b4_l2048_sampled():
-    """The 1.3B-class layer B4 L2048 H24 P64 N128 A32, every batch row of three heads."""
+def test_siso_full_b4_l2048_all_heads():
+    """The 1.3B-class layer B4 L2048 H24 P64 N128 A32: every output element
+    against the oracle (all 24 heads, the oracle sharded over host cores)."""
     w = WORKLOADS["siso_b4_l2048"]
     d = w.dims
     inp = ssm_inputs(d, seed=w.seed, dt_range=w.dt_range)
     got = gpu_siso(to_dev(inp), d).cpu().numpy()
     assert got.shape == (4, 2048, 24, 64)
     assert np.isfinite(got).all()
-    heads = [0, 11, 23]
-    ref = oracle_siso(inp, d, heads=heads)
-    assert_parity(got[:, :, heads], ref, "siso_b4_l2048 heads 0,11,23")
+    t0 = time.time()
+    ref = oracle_heads("siso_b4_l2048")
+    print(f"[oracle] siso_b4_l2048 all heads on {pool_size(d.H)} processes: {time.time() - t0:.1f} s", flush=True)
+    assert_parity(got, ref, "siso_b4_l2048 all heads")
 
 
-def test_siso_full_long_l65536_sampled():
-    """B1 L65536 H32 with dt in [1e-3, 0.01]: two heads over the whole sequence."""
+def test_siso_full_long_l65536_all_heads():
+    """B1 L65536 H32 with dt in [1e-3, 0.01]: every head over the whole
+    sequence (the oracle sharded over host cores)."""
     w = WORKLOADS["siso_long_l65536"]
     d = w.dims
     inp = ssm_inputs(d, seed=w.seed, dt_range=w.dt_range)
     got = gpu_siso(to_dev(inp), d).cpu().numpy()
+    del inp
     assert np.isfinite(got).all()
-    heads = [0, 31]
-    ref = oracle_siso(inp, d, heads=heads)
-    assert_parity(got[:, :, heads], ref, "siso_long_l65536 heads 0,31")
+    t0 = time.time()
+    ref = oracle_heads("siso_long_l65536")
+    print(f"[oracle] siso_long_l65536 all heads on {pool_size(d.H)} processes: {time.time() - t0:.1f} s",
+          flush=True)
+    assert_parity(got, ref, "siso_long_l65536 all heads")
