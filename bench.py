@@ -9,17 +9,19 @@ three independent batches are resident in HBM before timing and are rotated
 so the 256 MB last-level cache cannot hold a whole step's working set.
 
 Prints one JSON line: tokens/s of the step, the scan kernel's roofline
-(algorithmic bytes / live HIP-event duration against 8 TB/s), and the float64
-CPU oracle timed on a bounded sample on the host cores.  After the timed
-region it also measures the other rows of the path at their own workloads
-("rows"): the decode step at B256 H32 (1 token per step, HBM-bound), the
-rank-4 MIMO decode step at the same geometry, the MIMO scan at
-B8 L4096 H32 R4 (FP32-matrix-bound), the SISO backward at the step's
-geometry, the MIMO backward at the MIMO scan's geometry, the preprocess
-backward over the step's packed projection, and the step's preprocess and
-scan fused into one call on the packed rows.
+(algorithmic bytes / live HIP-event duration against 8 TB/s) beside the same
+bytes over the whole scan call (summary pass + main pass) and over the whole
+step, and the float64 CPU oracle timed on the host cores (all cores, and one
+thread).  Before the warmup it measures the other rows of the path at their
+own workloads ("rows"), which also brings the GPU to the clocks it holds
+under load before the step is timed: the long-sequence scan at
+B1 L65536 H32 (dt in [1e-3, 0.01]), the decode step at B256 H32 (1 token per
+step, HBM-bound), the rank-4 MIMO decode step at the same geometry, the MIMO
+scan at B8 L4096 H32 R4 (FP32-matrix-bound), the SISO backward at the step's
+geometry, the MIMO backward at the MIMO scan's geometry and the preprocess
+backward over the step's packed projection.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 200]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 """
 
 from __future__ import annotations
@@ -58,12 +60,13 @@ def kernel_source_hash() -> str:
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first: the GPU reaches its steady clocks after some tens of ms of work")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5,
+                    help="untimed steps right before the timed ones (the rows, measured first, already "
+                         "bring the GPU to its steady clocks)")
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated through the timed loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=24, help="heads in the oracle's timed sample")
+    ap.add_argument("--cpu-heads", type=int, default=24, help="heads in the one-thread oracle's timed sample")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run plain device copies of this many MiB (counter calibration)")
@@ -72,6 +75,71 @@ def parse():
     ap.add_argument("--calib-mib", type=int, default=256, help="copy size used in the calibrated runs")
     ap.add_argument("--no-rows", action="store_true", help="skip the decode-step and MIMO measurements")
     return ap.parse_args()
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_pass(hs, heads):
+    """The float64 oracle over the step's packed projection: preprocess of
+    every row, then the scan of `heads` over every batch row and token.
+    Returns (preprocess seconds, scan seconds)."""
+    import oracle as O
+    from workloads import WORKLOADS
+    d = WORKLOADS["siso_b4_l2048"].dims
+    B, L, H, G, P, N, A = d.B, d.L, d.H, d.groups, d.P, d.N, d.A
+    ocfg = O.PreprocessConfig(H * P, N, H, A, G, 1, 1e-5, 1e-3, 0.1, 1e-4)
+    c0 = time.perf_counter()
+    pre = O.preprocess(hs["projected"], hs["dt_bias"], ocfg)
+    t_pre = time.perf_counter() - c0
+    shp = {"x": (B, L, H, P), "z": (B, L, H, P), "bh": (B, L, G, N), "ch": (B, L, G, N),
+           "dt": (B, L, H), "adt": (B, L, H), "trap": (B, L, H), "angle": (B, L, A)}
+    oi = {k: pre[k].reshape(shp[k]) for k in shp}
+    c0 = time.perf_counter()
+    O.siso_scan(oi["ch"], oi["bh"], oi["x"], oi["z"], oi["adt"], oi["dt"], oi["trap"], oi["angle"],
+                hs["c_bias"], hs["b_bias"], hs["d"], O.SsmConfig(B, L, H, G, P, N, A), heads=list(heads))
+    return t_pre, time.perf_counter() - c0
+
+
+def _oracle_shard(heads):
+    """One process of the multi-core baseline: its own copy of the seeded
+    packed projection (not timed), the whole preprocess, its heads' scan."""
+    from workloads import WORKLOADS, packed_projection
+    w = WORKLOADS["siso_b4_l2048"]
+    return _oracle_pass(packed_projection(w.dims, seed=w.seed, dt_range=w.dt_range), heads)
+
+
+def oracle_all_cores(H: int):
+    """The oracle over all H heads sharded across min(16, cores) spawned
+    processes (one thread each).  The job's time is its slowest shard:
+    every shard repeats the preprocess, which a shared run would split."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    n = max(1, min(16, os.cpu_count() or 1, H))
+    shards = [list(range(H))[i::n] for i in range(n)]
+    keys = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    saved = {k: os.environ.get(k) for k in keys}
+    for k in keys:
+        os.environ[k] = "1"
+    try:
+        with ProcessPoolExecutor(n, mp_context=mp.get_context("spawn")) as pool:
+            res = list(pool.map(_oracle_shard, shards))
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    crit = max(tp + ts for tp, ts in res)
+    return n, crit, float(np.median([tp for tp, _ in res])), max(len(s) for s in shards)
 
 
 def decode_algorithmic_bytes(B, H, G, P, N, A) -> int:
@@ -87,6 +155,45 @@ def measure_rows(torch, m3, lib, hip, new_event, dev):
     from workloads import WORKLOADS, decode_states, mimo_decode_states, ssm_inputs, step_inputs
     ops11 = ("c", "b", "x", "z", "adt", "dt", "trap", "angle", "c_bias", "b_bias", "d")
     rows = {}
+    f = ctypes.c_float()
+
+    # long-sequence SISO scan: B1 L65536 H32, dt in [1e-3, 0.01] (m3_siso_fwd on dense operands)
+    w = WORKLOADS["siso_long_l65536"]
+    d = w.dims
+    inp = {k: torch.from_numpy(v).to(dev) for k, v in ssm_inputs(d, seed=w.seed, dt_range=w.dt_range).items()}
+    cfg = m3.SsmConfig(d.B, d.L, d.H, d.G, d.P, d.N, d.A)
+    ws = torch.empty(max(1, m3.siso_fwd_workspace_bytes(cfg)), dtype=torch.uint8, device=dev)
+    out = torch.empty(d.B, d.L, d.H, d.P, device=dev)
+    ops = [inp[k] for k in ops11]
+    for _ in range(5):
+        m3.m3_siso_fwd(*ops, cfg, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    kms, cms = [], []
+    for _ in range(20):
+        e0, e1 = new_event(), new_event()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        lib.m3_set_profile_events(e0, e1)
+        a.record()
+        m3.m3_siso_fwd(*ops, cfg, out=out, workspace=ws)
+        b.record()
+        torch.cuda.synchronize()
+        lib.m3_set_profile_events(None, None)
+        hip.hipEventElapsedTime(ctypes.byref(f), e0, e1)
+        kms.append(f.value)
+        cms.append(a.elapsed_time(b))
+        hip.hipEventDestroy(e0)
+        hip.hipEventDestroy(e1)
+    km, cm = float(np.mean(kms)), float(np.mean(cms))
+    byt = scan_algorithmic_bytes(d.B, d.L, d.H, d.groups, d.P, d.N, d.A)
+    rows["siso_long_scan"] = {
+        "workload": "siso_long_l65536: B1 L65536 H32 G1 P64 N128 A32, dt in [1e-3, 0.01], m3_siso_fwd",
+        "call_ms": cm, "main_kernel_ms": km, "tokens_per_s": d.B * d.L / (cm * 1e-3),
+        "algorithmic_bytes": byt, "bound": "hbm",
+        "main_kernel": DENSE_KERNEL, "main_kernel_gbs": byt / (km * 1e-3) / 1e9,
+        "main_kernel_hbm_frac": byt / (km * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "call_gbs": byt / (cm * 1e-3) / 1e9, "call_hbm_frac": byt / (cm * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "workspace_bytes": ws.numel(), "calls_timed": len(cms)}
+    del inp, ops, ws, out
 
     # decode: 256 x 32 heads, state [256, 32, 64, 128]; eight staged token sets
     w = WORKLOADS["decode_b256"]
@@ -166,7 +273,6 @@ def measure_rows(torch, m3, lib, hip, new_event, dev):
         m3.m3_mimo_fwd(*ops, cfg, out=out, workspace=ws)
     torch.cuda.synchronize()
     kms, cms = [], []
-    f = ctypes.c_float()
     for _ in range(10):
         e0, e1 = new_event(), new_event()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -462,13 +568,6 @@ def main():
             print(json.dumps({"parity_failed": parity}), file=sys.stderr)
             return 4
 
-    # ---- warmup ------------------------------------------------------------
-    for i in range(args.warmup):
-        step(sets[i % len(sets)])
-        two_call(sets[i % len(sets)])
-    torch.cuda.synchronize()
-
-    # ---- timed region ------------------------------------------------------
     hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
     hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
     hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
@@ -481,6 +580,21 @@ def main():
             raise RuntimeError("hipEventCreate failed")
         return e
 
+    # ---- the other rows, each at its own workload --------------------------
+    # (measured first: seconds of GPU work that leave the GPU at the clocks it
+    # holds under load, so that a short warmup suffices before the timed steps)
+    rows_out = None
+    if not args.no_rows:
+        rows_out = measure_rows(torch, m3, lib, hip, new_event, dev)
+        torch.cuda.empty_cache()
+
+    # ---- warmup ------------------------------------------------------------
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+        two_call(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    # ---- timed region ------------------------------------------------------
     K = args.steps
     kern_ev = [(new_event(), new_event()) for _ in range(K)]
     t_begin = torch.cuda.Event(enable_timing=True)
@@ -519,12 +633,6 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    rows_out = None
-    if not args.no_rows:
-        del sets, ws, fws
-        torch.cuda.empty_cache()
-        rows_out = measure_rows(torch, m3, lib, hip, new_event, dev)
-
     ms_total = t_begin.elapsed_time(t_end)
     ms_step = ms_total / K
     f = ctypes.c_float()
@@ -545,38 +653,36 @@ def main():
     tokens = B * L
     scan_bytes = scan_algorithmic_bytes(B, L, H, G, P, N, A)
     pre_bytes = preprocess_algorithmic_bytes(rows, W, I, M, H, A)
+    # the fused step: packed rows and dt_bias read once, biases and D read, out written once
+    step_bytes = 4 * (rows * W + H + 2 * H * N + H + B * L * H * P)
     min_flops = 4 * N * P * B * L * H  # state read-out and state update, per token-head
     kern_gbs = scan_bytes / (kern_avg * 1e-3) / 1e9
     scan_call_ms = float(np.mean(scan_ms))
     pre_avg = float(np.mean(pre_ms))
 
-    # ---- CPU baseline: the oracle on a bounded sample ---------------------
+    # ---- CPU baseline: the float64 oracle on the host cores ---------------
     cpu = None
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits
 
-        import oracle as O
-        single = threadpool_limits(limits=1)  # numpy's BLAS on one thread: cores == 1 below
-        hs = host_sets[0]
-        ocfg = O.PreprocessConfig(I, N, H, A, G, 1, 1e-5, 1e-3, 0.1, 1e-4)
-        c0 = time.perf_counter()
-        pre = O.preprocess(hs["projected"], hs["dt_bias"], ocfg)
-        t_pre = time.perf_counter() - c0
-        shp = {"x": (B, L, H, P), "z": (B, L, H, P), "bh": (B, L, G, N), "ch": (B, L, G, N),
-               "dt": (B, L, H), "adt": (B, L, H), "trap": (B, L, H), "angle": (B, L, A)}
-        oi = {k: pre[k].reshape(shp[k]) for k in shp}
+        # every core: the 24 heads sharded over processes, each with the preprocess
+        n_proc, crit, t_pre_med, per_shard = oracle_all_cores(H)
+        # one thread: the preprocess and a sample of heads, scaled to all heads
         hsel = list(range(min(args.cpu_heads, H)))
-        c0 = time.perf_counter()
-        O.siso_scan(oi["ch"], oi["bh"], oi["x"], oi["z"], oi["adt"], oi["dt"], oi["trap"], oi["angle"],
-                    hs["c_bias"], hs["b_bias"], hs["d"], O.SsmConfig(B, L, H, G, P, N, A), heads=hsel)
-        t_scan = time.perf_counter() - c0
-        single.restore_original_limits()
+        with threadpool_limits(limits=1):
+            t_pre, t_scan = _oracle_pass(host_sets[0], hsel)
         est = t_pre + t_scan * H / len(hsel)
-        cpu = {"value": tokens / est, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": (f"float64 oracle, one thread: preprocess of all {rows} packed rows "
-                          f"({t_pre:.2f} s) + scan of {len(hsel)} of {H} heads over all {B} batch rows "
-                          f"and {L} tokens ({t_scan:.2f} s), scan time scaled by {H}/{len(hsel)}"),
-               "host_cpus": os.cpu_count()}
+        cpu = {"value": tokens / crit, "unit": "tokens/s", "cores": n_proc, "kind": "oracle",
+               "sample": (f"float64 oracle on the whole step's work: preprocess of all {rows} packed rows and "
+                          f"the scan of all {H} heads over all {B} batch rows and {L} tokens, heads sharded "
+                          f"over {n_proc} processes of one thread (at most {per_shard} heads each; every "
+                          f"process repeats the preprocess, median {t_pre_med:.2f} s); time = slowest "
+                          f"process, {crit:.2f} s"),
+               "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
+               "one_thread": {"value": tokens / est, "unit": "tokens/s", "cores": 1,
+                              "sample": (f"preprocess of all {rows} rows ({t_pre:.2f} s) + scan of "
+                                         f"{len(hsel)} of {H} heads ({t_scan:.2f} s), scan time scaled by "
+                                         f"{H}/{len(hsel)}")}}
 
     result = {
         "metric": "scan fwd tokens/s + HBM GB/s (% roofline), SISO B4 L2048 H24 P64 N128",
@@ -603,7 +709,16 @@ def main():
                      "kernel": MAIN_KERNEL + " (main scan pass on the packed rows)",
                      "kernel_ms": kern_avg, "algorithmic_bytes": scan_bytes,
                      "fp32_tflops_min_work": min_flops / (kern_avg * 1e-3) / 1e12,
-                     "fp32_frac": min_flops / (kern_avg * 1e-3) / 1e12 / FP32_PEAK_TFLOPS},
+                     "fp32_frac": min_flops / (kern_avg * 1e-3) / 1e12 / FP32_PEAK_TFLOPS,
+                     # the same bytes over the whole scan call (summary pass, fold and
+                     # main pass; the two-call form's m3_siso_fwd) and over the whole step
+                     "scan_level": {"ms": scan_call_ms, "gbs": scan_bytes / (scan_call_ms * 1e-3) / 1e9,
+                                    "frac": scan_bytes / (scan_call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                    "what": "m3_siso_fwd call on dense operands: summary pass + main pass"},
+                     "step_level": {"ms": ms_step, "algorithmic_bytes": step_bytes,
+                                    "gbs": step_bytes / (ms_step * 1e-3) / 1e9,
+                                    "frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                    "what": "the timed step: packed rows read once, out written once"}},
         "two_call_step": {"ms": two_ms, "tokens_per_s": tokens / (two_ms * 1e-3),
                           "calls": "m3_preprocess then m3_siso_fwd", "main_kernel": DENSE_KERNEL,
                           "main_kernel_ms": dense_avg, "main_kernel_gbs": scan_bytes / (dense_avg * 1e-3) / 1e9,
