@@ -60,6 +60,7 @@ constexpr int kAux = 68;        // per segment summary: angle increment [<=64], 
 constexpr int kAuxDecay = 64;
 constexpr float kNormEps = 1.0e-5f;  // MIMO output-norm epsilon of the MIMO push constants
 constexpr int kQV = 32;         // virtual rows per chunk
+constexpr long kMaxAutoSegments = 65;  // automatic plan: at most 2 * 64 = 128 summary pieces per chain
 // Key buffer of the bf16 state update, transposed: per state coordinate n one
 // row of 32 bf16 (16 words), its four 16-byte blocks stored in the order
 // q ^ ((n >> 2) & 3), so that the 16 rows read by one lane group hit 16
@@ -965,6 +966,11 @@ ScanPlan make_plan(const ScanGeom& g) {
   if (bhn < target) nseg = target / bhn;
   const long max_seg = ((long)g.L + 4L * Qt - 1) / (4L * Qt);
   if (nseg > max_seg) nseg = max_seg;
+  // Segment s folds the 2s summary pieces before it, so the fold's work grows
+  // with the square of the segment count.  At most 65 segments (128 pieces,
+  // the register fold's limit) keep the last segment's fold within a few
+  // chunks' time where few chains would otherwise ask for hundreds.
+  if (nseg > kMaxAutoSegments) nseg = kMaxAutoSegments;
   if (g_forced_segments > 0) nseg = (long)g_forced_segments;
   if (nseg < 1) nseg = 1;
   long seg_len = ((long)g.L + nseg - 1) / nseg;

@@ -94,6 +94,19 @@ def test_siso_sixty_four_segments():
     assert_parity(got, oracle_siso(inp, d), "segments_64")
 
 
+def test_siso_few_chains_long_sequence_automatic_plan():
+    # two chains over 16384 tokens: the automatic plan would take 128 segments
+    # and is held at 65 (the last segment folds 128 summary pieces)
+    d = Dims(1, 16384, 2, 1, 64, 128, 32)
+    inp = ssm_inputs(d, seed=2023, dt_range=(1e-3, 0.01))
+    cfg = m3.SsmConfig(d.B, d.L, d.H, d.G, d.P, d.N, d.A)
+    with m3.scan_segments(65):
+        capped = m3.siso_fwd_workspace_bytes(cfg)
+    assert m3.siso_fwd_workspace_bytes(cfg) == capped
+    got = gpu_siso(to_dev(inp), d).cpu().numpy()
+    assert_parity(got, oracle_siso(inp, d), "few chains, 65 segments")
+
+
 def test_siso_deterministic():
     d = Dims(2, 200, 4, 1, 64, 128, 32)
     inp = to_dev(ssm_inputs(d, seed=2030))
