@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated through the timed loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=24, help="heads in the one-thread oracle's timed sample")
+    ap.add_argument("--cpu-decode-steps", type=int, default=32,
+                    help="decode steps in the decode row's oracle baseline (0: skip the rows' baselines)")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run plain device copies of this many MiB (counter calibration)")
@@ -117,29 +119,94 @@ def _oracle_shard(heads):
     return _oracle_pass(packed_projection(w.dims, seed=w.seed, dt_range=w.dt_range), heads)
 
 
-def oracle_all_cores(H: int):
-    """The oracle over all H heads sharded across min(16, cores) spawned
-    processes (one thread each).  The job's time is its slowest shard:
-    every shard repeats the preprocess, which a shared run would split."""
+def _spawn_pool_map(fn, tasks):
+    """map fn over tasks in min(16, cores) spawned processes of one thread each."""
     import multiprocessing as mp
     from concurrent.futures import ProcessPoolExecutor
-    n = max(1, min(16, os.cpu_count() or 1, H))
-    shards = [list(range(H))[i::n] for i in range(n)]
+    n = max(1, min(16, os.cpu_count() or 1, len(tasks)))
     keys = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
     saved = {k: os.environ.get(k) for k in keys}
     for k in keys:
         os.environ[k] = "1"
     try:
         with ProcessPoolExecutor(n, mp_context=mp.get_context("spawn")) as pool:
-            res = list(pool.map(_oracle_shard, shards))
+            return n, list(pool.map(fn, tasks))
     finally:
         for k, v in saved.items():
             if v is None:
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
+
+
+def oracle_all_cores(H: int):
+    """The oracle over all H heads sharded across min(16, cores) spawned
+    processes (one thread each).  The job's time is its slowest shard:
+    every shard repeats the preprocess, which a shared run would split."""
+    n = max(1, min(16, os.cpu_count() or 1, H))
+    shards = [list(range(H))[i::n] for i in range(n)]
+    n, res = _spawn_pool_map(_oracle_shard, shards)
     crit = max(tp + ts for tp, ts in res)
     return n, crit, float(np.median([tp for tp, _ in res])), max(len(s) for s in shards)
+
+
+def _row_shard(task):
+    """One process of a row's oracle baseline: the workload's seeded inputs
+    (not timed), then the oracle over this shard's heads (scans) or batch
+    rows (decode).  Returns the oracle's own seconds."""
+    import oracle as O
+    from workloads import WORKLOADS, Dims, decode_states, ssm_inputs, step_inputs
+    name, part, steps = task
+    w = WORKLOADS[name]
+    d = w.dims
+    ops = ("c", "b", "x", "z", "adt", "dt", "trap", "angle", "c_bias", "b_bias", "d")
+    cfg = O.SsmConfig(d.B, d.L, d.H, d.G, d.P, d.N, d.A, d.R, d.has_z, d.has_d, d.has_output_norm)
+    if w.kind in ("siso", "mimo"):
+        inp = ssm_inputs(d, seed=w.seed, dt_range=w.dt_range, mimo=w.kind == "mimo")
+        c0 = time.perf_counter()
+        if w.kind == "mimo":
+            O.mimo_scan(*[inp[k] for k in ops + ("mimo_x", "mimo_z", "mimo_o", "norm_weight")], cfg, heads=part)
+        else:
+            O.siso_scan(*[inp[k] for k in ops], cfg, heads=part)
+        return time.perf_counter() - c0
+    rows = np.asarray(part)
+    keys = ("ssm_state", "angle_state", "k_state", "v_state")
+    st = {k: v[rows].astype(np.float64) for k, v in decode_states(d, seed=w.seed).items()}
+    sub = O.SsmConfig(len(rows), 1, d.H, d.G, d.P, d.N, d.A)
+    t = 0.0
+    for s in range(steps):
+        tok = {k: (v[rows] if v.ndim >= 3 else v) for k, v in step_inputs(d, w.seed, s).items()}
+        c0 = time.perf_counter()
+        _, st = O.siso_step(*[tok[k] for k in ops], *[st[k] for k in keys], sub)
+        t += time.perf_counter() - c0
+    return t
+
+
+def oracle_rows_all_cores(decode_steps: int):
+    """The oracle baselines of the other scan and decode rows, each over all
+    host cores: the long-sequence SISO scan and the MIMO scan sharded by head
+    (all heads), the decode step sharded by batch row over its first
+    `decode_steps` steps.  Each row's time is its slowest process."""
+    from workloads import WORKLOADS
+    out = {}
+    for row, name in (("siso_long_scan", "siso_long_l65536"), ("mimo_scan", "mimo_b8_l4096_r4")):
+        d = WORKLOADS[name].dims
+        n = max(1, min(16, os.cpu_count() or 1, d.H))
+        n, res = _spawn_pool_map(_row_shard, [(name, list(range(d.H))[i::n], 0) for i in range(n)])
+        crit = max(res)
+        out[row] = {"value": d.B * d.L / crit, "unit": "tokens/s", "cores": n, "kind": "oracle",
+                    "sample": f"float64 oracle, all {d.H} heads of {name} sharded over {n} processes; "
+                              f"time = slowest process, {crit:.2f} s (input generation not timed)"}
+    w = WORKLOADS["decode_b256"]
+    d = w.dims
+    n = max(1, min(16, os.cpu_count() or 1, d.B))
+    n, res = _spawn_pool_map(_row_shard, [("decode_b256", list(range(d.B))[i::n], decode_steps) for i in range(n)])
+    crit = max(res)
+    out["decode_step"] = {"value": d.B * decode_steps / crit, "unit": "tokens/s", "cores": n, "kind": "oracle",
+                          "sample": f"float64 oracle, the first {decode_steps} of the {w.steps} decode_b256 steps "
+                                    f"over all {d.B} batch rows sharded over {n} processes; time = slowest "
+                                    f"process, {crit:.2f} s (input generation not timed)"}
+    return out
 
 
 def decode_algorithmic_bytes(B, H, G, P, N, A) -> int:
@@ -683,6 +750,8 @@ def main():
                               "sample": (f"preprocess of all {rows} rows ({t_pre:.2f} s) + scan of "
                                          f"{len(hsel)} of {H} heads ({t_scan:.2f} s), scan time scaled by "
                                          f"{H}/{len(hsel)}")}}
+        if args.cpu_decode_steps > 0 and not args.no_rows:
+            cpu["rows"] = oracle_rows_all_cores(args.cpu_decode_steps)
 
     result = {
         "metric": "scan fwd tokens/s + HBM GB/s (% roofline), SISO B4 L2048 H24 P64 N128",
