@@ -25,6 +25,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef unsigned int uintx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int uintx2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ floatx4 mfma_bf16(uintx4 a, uintx4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
@@ -181,6 +182,67 @@ __device__ __forceinline__ void sincos_acc_d(double x, float* s_out, float* c_ou
   double rd = fma(-kd, 0x1.921fb54442d18p+0, x);
   rd = fma(-kd, 0x1.1a62633145c07p-54, rd);
   sincos_poly((float)rd, (int)(kd - 4.0 * floor(kd * 0.25)), s_out, c_out);
+}
+
+// fp16 matrix products of split fp32 operands (v_mfma_f32_16x16x32_f16; the
+// operand layout is that of mfma_bf16).  A value v, first scaled by a power
+// of two so that the block's largest magnitude lies in [2^14, 2^15), is
+// held as a head h = fp16(v) and a tail l = fp16(v - h) (the remainder v - h
+// is exact in fp32 before its one rounding to fp16); v - h - l is
+// below 2^-22 |v| for normal heads, and h h' + h l' + l h' leaves out
+// l l' < 2^-22 |v v'|: about 2^-21 relative per product, at the level of an
+// fp32 dot product's own rounding.
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ floatx4 mfma_f16(uintx4 a, uintx4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, a), __builtin_bit_cast(halfx8, b), c, 0,
+                                                0, 0);
+}
+// Split two fp32 values x0 s, x1 s (s a power of two) into fp16 head and
+// tail words (x0 in the low half of each word), the scaling folded into
+// v_fma_mix{lo,hi}_f16, which round a fused x s + c to fp16 in one half of
+// the word and keep the other half: the heads fp16(x s) and the tails
+// fp16(x s - h).
+__device__ __forceinline__ void split2_f16s(float x0, float x1, float s, unsigned& h, unsigned& l) {
+  unsigned hw, lw;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0" : "=v"(hw) : "v"(x0), "v"(s));
+  asm("v_fma_mixhi_f16 %0, %1, %2, 0" : "+v"(hw) : "v"(x1), "v"(s));
+  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,0,1]" : "=v"(lw) : "v"(x0), "v"(s), "v"(hw));
+  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(lw) : "v"(x1), "v"(s), "v"(hw));
+  h = hw;
+  l = lw;
+}
+// Exponent e such that 2^e m lies in [2^14, 2^15) for m > 0 (0 for m = 0 or
+// non-finite m), at most 120 (so that 2^e is a finite float; for finite m
+// the frexp exponent is at most 128, so e >= -113 without a lower clamp).
+__device__ __forceinline__ int f16_scale_exp(float m) {
+  const int e = min(15 - __builtin_amdgcn_frexp_expf(m), 120);
+  return (m > 0.f && m <= 3.0e38f) ? e : 0;
+}
+// max(|a|, |b|, m) for m >= 0 in one v_max3_f32 with absolute-value
+// modifiers (a NaN operand may be dropped; the NaN itself still reaches the
+// products it belongs to).
+__device__ __forceinline__ float max3_abs(float a, float b, float m) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(a), "v"(b), "v"(m));
+  return r;
+}
+// Maximum of non-negative v over lanes l, l ^ 16, l ^ 32, l ^ 48 (v_permlane16/32_swap).
+__device__ __forceinline__ float max_xor16_32(float v) {
+  const unsigned u = __float_as_uint(v);
+  auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned w = max(s16[0], s16[1]);
+  auto s32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(max(s32[0], s32[1]));
+}
+// Maximum of non-negative v over the 64 lanes of a wave (in every lane).
+__device__ __forceinline__ float wave_max_nn(float v) {
+  unsigned u = __float_as_uint(v);
+  u = max(u, (unsigned)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xf, 0xf, false));  // quad_perm 1,0,3,2
+  u = max(u, (unsigned)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xf, 0xf, false));  // quad_perm 2,3,0,1
+  u = max(u, (unsigned)__builtin_amdgcn_ds_swizzle((int)u, 0x101F));                      // xor 4
+  u = max(u, (unsigned)__builtin_amdgcn_ds_swizzle((int)u, 0x201F));                      // xor 8
+  return max_xor16_32(__uint_as_float(u));
 }
 
 // Workgroup barrier for hand-offs through LDS only.  It waits for this wave's

@@ -66,6 +66,17 @@ constexpr long kMaxAutoSegments = 65;  // automatic plan: at most 2 * 64 = 128 s
 // q ^ ((n >> 2) & 3), so that the 16 rows read by one lane group hit 16
 // different bank groups.
 constexpr int kKTw = 16;
+// fp16 query / key planes of the SISO main pass (HALF below): rows of 136
+// halves (128 + 8 pad, 272 bytes), head plane then tail plane
+constexpr int kPQK = 136;
+// Column of state coordinate n in a plane row: within each group of 32,
+// n = 16 u + 4 q + e (e < 4) goes to 8 q + 4 u + e, so that the eight
+// coordinates lane group q holds of two adjacent 16-row state blocks
+// (4 q .. 4 q + 3 of each) are contiguous: one 16-byte read per MFMA
+// operand in the read-out.  S contracts over the same order on both sides.
+__device__ __forceinline__ int colp(int n) {
+  return (n & ~31) | (((n >> 2) & 3) << 3) | (((n >> 4) & 1) << 2) | (n & 3);
+}
 
 struct ScanKParams {
   const float *c, *b, *x, *z, *adt, *dt, *trap, *angle, *c_bias, *b_bias, *d;
@@ -95,6 +106,19 @@ __host__ __device__ constexpr bool fixed_variant(int NTC, int PTC, int NWC) {
 }
 __host__ __device__ constexpr bool merged_variant(int NTC, int PTC, int NWC, int RSC) {
   return fixed_variant(NTC, PTC, NWC) && NTC * 16 == 16 * NWC && RSC > 0;
+}
+
+// Two workgroups share a CU, and the wave arbiter, at equal priority,
+// favours the older one, so the workgroup dispatched second runs its chunks
+// markedly slower and finishes alone, at one workgroup's rate.  Each
+// workgroup sets its waves' priority from the chunks it has left (more left,
+// higher priority, in bins that narrow towards the end), so the one behind
+// takes the issue slots and the two finish close together.
+__device__ __forceinline__ void set_progress_priority(int left) {
+  if (left > 6) __builtin_amdgcn_s_setprio(3);
+  else if (left > 3) __builtin_amdgcn_s_setprio(2);
+  else if (left > 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
 }
 
 template <int VEC>
@@ -221,9 +245,21 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   //     pos(v) = 8 ((v >> 2) & 3) + 4 (v >> 4) + (v & 3)
   // of its key row, and the x rows a lane reads are 4 apart (16 banks apart).
   constexpr bool SPLIT = MERGED && (!MIMO || !FULL);
+  // The SISO main pass of the merged layout keeps its queries and keys as fp16
+  // head / tail planes, split once by the lanes that rotate them, and forms
+  // S = Q K^T and the read-out Q h'^T on v_mfma_f32_16x16x32_f16 from them
+  // (three products per k = 32 step, about 2^-21 relative each).  The scales
+  // are powers of two from a bound known before the rotation: the largest
+  // raw B / C entry of the chunk plus the largest bias entry, times sqrt(2)
+  // (a rotation keeps each pair's norm).
+  constexpr bool HALF = FULL && MERGED && !MIMO;
 
   float* Ql = lds + p.o_ql;   // [QV][ks] C (+bias), pairs rotated in place   (main pass)
   float* Kl = lds + p.o_kl;   // [QV][ks] B (+bias), pairs rotated in place
+  // HALF: the same regions as fp16 planes [head, tail][QV][kPQK]
+  _Float16* const Qp = reinterpret_cast<_Float16*>(Ql);
+  _Float16* const Kp = reinterpret_cast<_Float16*>(Kl);
+  constexpr int QPL = QV * kPQK;  // halves per plane
   float* Xl = lds + p.o_xl;   // [QV][xs] per-rank x
   float* Ml = lds + p.o_ml;   // [QV][ms] masked S (N-half 0 when S is split)  (main pass)
   float* Ml2 = lds + p.o_ml2;  // [QV][ms] masked S, N-half 1 (split S only)
@@ -243,7 +279,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   float* sc_scl = sc_gam + QV;
   float* sc_w = sc_scl + QV;
   float* sc_dt = sc_w + QV;
-  float* run = lds + p.o_run;  // [0,64) running theta, [64] chunk decay
+  float* run = lds + p.o_run;  // [0,64) running theta, [64] chunk decay, [68,84) raw B / C maxima per wave (HALF)
   unsigned* KTh = reinterpret_cast<unsigned*>(lds + p.o_kt);  // [N][kKTw] bf16 pairs of K, head parts (SPLIT)
   unsigned* KTm = KTh + N * kKTw;                     // middle parts
   unsigned* KTl = KTm + N * kKTw;                     // tail parts
@@ -253,6 +289,17 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   for (int i = tid; i < R * N; i += nthreads) {
     bbL[i] = p.b_bias[(size_t)h * R * N + i];
     if (FULL) cbL[i] = p.c_bias[(size_t)h * R * N + i];
+  }
+  // HALF: the largest bias magnitudes of this head (with the raw-row maxima,
+  // the bound behind the fp16 scales)
+  float bmax_b = 0.f, bmax_c = 0.f;
+  if constexpr (HALF) {
+    for (int i = lane; i < N; i += 64) {
+      bmax_b = max3_abs(p.b_bias[(size_t)h * N + i], 0.f, bmax_b);
+      bmax_c = max3_abs(p.c_bias[(size_t)h * N + i], 0.f, bmax_c);
+    }
+    bmax_b = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_nn(bmax_b))));
+    bmax_c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_nn(bmax_c))));
   }
   if constexpr (FULL && MIMO) {
     for (int i = tid; i < R * P; i += nthreads) {
@@ -285,57 +332,83 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   const bool reg_fold = FIXED && NTC == 8 && !MIMO && (A == 0 || A == 16 || A == 32) && nsum_all <= 128;
   if (FULL && seg > 0 && reg_fold) {
     const size_t sbase = (size_t)bh * nsum_all;
-    float* CSt = lds;  // [nsum][A] cos, then [nsum][A] sin; overlays the chunk buffers (unused yet)
-    float* SNt = CSt + nsum * A;
+    // LDS (overlaying the chunk buffers, unused yet): the summaries' angle
+    // increments and decays, loaded at once; then per angle the running sums
+    // theta_i (in summary order), and cos / sin of each
+    float* CSt = lds;  // [nsum][A] theta_i, then cos theta_i
+    float* SNt = CSt + nsum * A;  // [nsum][A] sin theta_i
+    float* AXt = SNt + nsum * A;  // [nsum][A] angle increment of summary i
+    float* DCt = AXt + nsum * A;  // [nsum] decay of summary i
     for (int idx = tid; idx < nsum * A; idx += nthreads) {
       const int i = idx / A, a = idx - i * A;
-      float th = 0.f;
-      for (int k = 0; k < i; ++k) th += p.ws_aux[(sbase + k) * kAux + a];
-      float sn, cs;
-      sincos_acc(th, &sn, &cs);
-      CSt[idx] = cs;
-      SNt[idx] = sn;
+      AXt[idx] = p.ws_aux[(sbase + i) * kAux + a];
     }
+    for (int i = tid; i < nsum; i += nthreads) DCt[i] = p.ws_aux[(sbase + i) * kAux + kAuxDecay];
+    __syncthreads();
     for (int a = tid; a < A; a += nthreads) {
       float th = 0.f;
-      for (int k = 0; k < nsum; ++k) th += p.ws_aux[(sbase + k) * kAux + a];
+      for (int i = 0; i < nsum; ++i) {
+        CSt[i * A + a] = th;
+        th += AXt[i * A + a];
+      }
       run[a] = th;
     }
     __syncthreads();
-    for (int i = 0; i < nsum; ++i) {
-      const float* st = p.ws_state + (sbase + i) * (size_t)(PT * NT) * 256;
-      floatx4 u[JMAX];
-#pragma unroll
-      for (int j = 0; j < JMAX; ++j) u[j] = *reinterpret_cast<const floatx4*>(st + ((pt * NT + nb0 + j) * 64 + lane) * 4);
-      if (nb0 == 0 && A > 0) {
-        const float* ci = CSt + i * A;
-        const float* si = SNt + i * A;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (A == 32) {
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-              const int a = 16 * jb + 4 * lq + r;
-              const float c = ci[a], sv = si[a];
-              const float u0 = u[jb][r], u1 = u[jb + 2][r];
-              u[jb][r] = u0 * c - u1 * sv;
-              u[jb + 2][r] = u0 * sv + u1 * c;
-            }
-          } else {  // A == 16
-            const int a = 4 * lq + r;
-            const float c = ci[a], sv = si[a];
-            const float u0 = u[0][r], u1 = u[1][r];
-            u[0][r] = u0 * c - u1 * sv;
-            u[1][r] = u0 * sv + u1 * c;
-          }
-        }
-      }
-      const float dec = p.ws_aux[(sbase + i) * kAux + kAuxDecay];
-#pragma unroll
-      for (int j = 0; j < JMAX; ++j) Hacc[j] = dec * Hacc[j] + u[j];
+    for (int idx = tid; idx < nsum * A; idx += nthreads) {
+      float sn, cs;
+      sincos_acc(CSt[idx], &sn, &cs);
+      CSt[idx] = cs;
+      SNt[idx] = sn;
     }
     __syncthreads();
-    for (int i = tid; i < 2 * nsum * A; i += nthreads) CSt[i] = 0.f;  // restore the zeroed chunk buffers
+    // the summary states, four in flight at a time
+    constexpr int FB = 4;
+    for (int i0 = 0; i0 < nsum; i0 += FB) {
+      floatx4 u[FB][JMAX];
+#pragma unroll
+      for (int k = 0; k < FB; ++k) {
+        if (i0 + k < nsum) {
+          const float* st = p.ws_state + (sbase + i0 + k) * (size_t)(PT * NT) * 256;
+#pragma unroll
+          for (int j = 0; j < JMAX; ++j)
+            u[k][j] = *reinterpret_cast<const floatx4*>(st + ((pt * NT + nb0 + j) * 64 + lane) * 4);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < FB; ++k) {
+        const int i = i0 + k;
+        if (i < nsum) {
+          if (nb0 == 0 && A > 0) {
+            const float* ci = CSt + i * A;
+            const float* si = SNt + i * A;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (A == 32) {
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb) {
+                  const int a = 16 * jb + 4 * lq + r;
+                  const float c = ci[a], sv = si[a];
+                  const float u0 = u[k][jb][r], u1 = u[k][jb + 2][r];
+                  u[k][jb][r] = u0 * c - u1 * sv;
+                  u[k][jb + 2][r] = u0 * sv + u1 * c;
+                }
+              } else {  // A == 16
+                const int a = 4 * lq + r;
+                const float c = ci[a], sv = si[a];
+                const float u0 = u[k][0][r], u1 = u[k][1][r];
+                u[k][0][r] = u0 * c - u1 * sv;
+                u[k][1][r] = u0 * sv + u1 * c;
+              }
+            }
+          }
+          const float dec = DCt[i];
+#pragma unroll
+          for (int j = 0; j < JMAX; ++j) Hacc[j] = dec * Hacc[j] + u[k][j];
+        }
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < 3 * nsum * A + nsum; i += nthreads) CSt[i] = 0.f;  // restore the zeroed chunk buffers
   } else if (FULL && seg > 0) {
     __syncthreads();
     float* Ub = lds;  // [PT*16][NT*16 + 4], overlays the chunk buffers (unused yet)
@@ -481,12 +554,42 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
     }
   };
 
+  // HALF: per-wave maxima of the prefetched raw B / C rows of a chunk, in
+  // LDS for the staging of that chunk (all waves take the largest)
+  auto raw_maxima = [&]() {
+    if constexpr (HALF) {
+      float mk = 0.f, mq = 0.f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        mk = max3_abs(br[i][0], br[i][1], mk);
+        mk = max3_abs(br[i][2], br[i][3], mk);
+        mq = max3_abs(cr[i][0], cr[i][1], mq);
+        mq = max3_abs(cr[i][2], cr[i][3], mq);
+      }
+      mk = wave_max_nn(mk);
+      mq = wave_max_nn(mq);
+      if (lane == 0) {
+        run[68 + wave] = mk;
+        run[76 + wave] = mq;
+      }
+    }
+  };
+  auto slot_max = [&](const float* sl) {
+    const floatx4 a = lds_read4(sl), c = lds_read4(sl + 4);
+    const float m = fmaxf(fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w)), fmaxf(fmaxf(c.x, c.y), fmaxf(c.z, c.w)));
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(m)));
+  };
+  // fp16 scale exponents of the staged chunk's keys and queries (uniform)
+  int eK = 0, eQ = 0;
+
   prefetch(t_begin);
   if constexpr (LATE_X) prefetch_x(t_begin);
+  raw_maxima();
   __syncthreads();
 
   for (int c0 = t_begin; c0 < t_end; c0 += Qt) {
     const int nvalid = min(Qt, t_end - c0);
+    if constexpr (FULL) set_progress_priority((t_end - c0 + Qt - 1) / Qt);
 
     // ---- P0: scalars (one wave, lane = token); x, B, C rows into LDS; z loads --
     if (wave == (MERGED ? sw : 0)) {
@@ -538,6 +641,11 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       // every rank of a token sees that token's angle), then the rotation in
       // registers
       const bool tok_ok = mtok < nvalid && mr < R;
+      if constexpr (HALF) {
+        // |rotated entry| <= sqrt(2) max |raw + bias| (a rotation keeps each pair's norm)
+        eK = __builtin_amdgcn_readfirstlane(f16_scale_exp(1.4143f * (slot_max(run + 68) + bmax_b)));
+        eQ = __builtin_amdgcn_readfirstlane(f16_scale_exp(1.4143f * (slot_max(run + 76) + bmax_c)));
+      }
       float th[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < 4; ++e) th[e] = scan32_f((mpair && tok_ok && mr == 0) ? mdt * angr[e] : 0.f);
@@ -576,7 +684,29 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         q0 = k0;
         q1 = k0;
       }
-      if (FULL || !SPLIT) {
+      if constexpr (HALF) {
+        // fp16 head / tail words of the four columns at mc0 and at mc1, in
+        // the plane column order colp
+        const float sK = ldexpf(1.f, eK), sQ = ldexpf(1.f, eQ);
+        const int r0 = mt * kPQK + colp(mc0), r1 = mt * kPQK + colp(mc1);
+        unsigned h0, h1, t0, t1;
+        split2_f16s(k0[0], k0[1], sK, h0, t0);
+        split2_f16s(k0[2], k0[3], sK, h1, t1);
+        *reinterpret_cast<uintx2*>(Kp + r0) = uintx2{h0, h1};
+        *reinterpret_cast<uintx2*>(Kp + QPL + r0) = uintx2{t0, t1};
+        split2_f16s(k1[0], k1[1], sK, h0, t0);
+        split2_f16s(k1[2], k1[3], sK, h1, t1);
+        *reinterpret_cast<uintx2*>(Kp + r1) = uintx2{h0, h1};
+        *reinterpret_cast<uintx2*>(Kp + QPL + r1) = uintx2{t0, t1};
+        split2_f16s(q0[0], q0[1], sQ, h0, t0);
+        split2_f16s(q0[2], q0[3], sQ, h1, t1);
+        *reinterpret_cast<uintx2*>(Qp + r0) = uintx2{h0, h1};
+        *reinterpret_cast<uintx2*>(Qp + QPL + r0) = uintx2{t0, t1};
+        split2_f16s(q1[0], q1[1], sQ, h0, t0);
+        split2_f16s(q1[2], q1[3], sQ, h1, t1);
+        *reinterpret_cast<uintx2*>(Qp + r1) = uintx2{h0, h1};
+        *reinterpret_cast<uintx2*>(Qp + QPL + r1) = uintx2{t0, t1};
+      } else if (FULL || !SPLIT) {
         vstore<VEC>(Kl + mt * ks + mc0, k0);
         vstore<VEC>(Kl + mt * ks + mc1, k1);
       }
@@ -616,7 +746,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
           }
         }
       }
-      if (FULL) {
+      if (FULL && !HALF) {
         vstore<VEC>(Ql + mt * ks + mc0, q0);
         vstore<VEC>(Ql + mt * ks + mc1, q1);
       }
@@ -710,23 +840,44 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         const int pr = un / SPL, half = un - pr * SPL;
         int tb = 0, sb = pr;
         while (sb > tb) { sb -= tb + 1; ++tb; }
-        floatx4 accs[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-        const float* qa = Ql + (tb * 16 + l16) * ks + 4 * lq + half * (NT / SPL) * 16;
-        const float* kb = Kl + (sb * 16 + l16) * ks + 4 * lq + half * (NT / SPL) * 16;
         float* Mdst = half ? Ml2 : Ml;
+        floatx4 acc;
+        if constexpr (HALF) {
+          // the N-half's 64 plane columns in two k = 32 steps, each the two
+          // tail products, then the head product
+          floatx4 a16 = floatx4{0.f, 0.f, 0.f, 0.f};
+          const _Float16* qa = Qp + (tb * 16 + l16) * kPQK + half * 64 + 8 * lq;
+          const _Float16* kb = Kp + (sb * 16 + l16) * kPQK + half * 64 + 8 * lq;
 #pragma unroll
-        for (int nb = 0; nb < 8 / SPL; ++nb) {
-          if (nb < NT / SPL) {
-            const floatx4 a4 = lds_read4(qa + nb * 16);
-            const floatx4 b4 = lds_read4(kb + nb * 16);
-            floatx4& acc = accs[nb & 1];
-            acc = mfma16(a4.x, b4.x, acc);
-            acc = mfma16(a4.y, b4.y, acc);
-            acc = mfma16(a4.z, b4.z, acc);
-            acc = mfma16(a4.w, b4.w, acc);
+          for (int i = 0; i < 2; ++i) {
+            const uintx4 qh = *reinterpret_cast<const uintx4*>(qa + 32 * i);
+            const uintx4 ql = *reinterpret_cast<const uintx4*>(qa + QPL + 32 * i);
+            const uintx4 kh = *reinterpret_cast<const uintx4*>(kb + 32 * i);
+            const uintx4 kl = *reinterpret_cast<const uintx4*>(kb + QPL + 32 * i);
+            a16 = mfma_f16(ql, kh, a16);
+            a16 = mfma_f16(qh, kl, a16);
+            a16 = mfma_f16(qh, kh, a16);
           }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] = ldexpf(a16[r], -(eQ + eK));
+        } else {
+          floatx4 accs[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+          const float* qa = Ql + (tb * 16 + l16) * ks + 4 * lq + half * (NT / SPL) * 16;
+          const float* kb = Kl + (sb * 16 + l16) * ks + 4 * lq + half * (NT / SPL) * 16;
+#pragma unroll
+          for (int nb = 0; nb < 8 / SPL; ++nb) {
+            if (nb < NT / SPL) {
+              const floatx4 a4 = lds_read4(qa + nb * 16);
+              const floatx4 b4 = lds_read4(kb + nb * 16);
+              floatx4& ac = accs[nb & 1];
+              ac = mfma16(a4.x, b4.x, ac);
+              ac = mfma16(a4.y, b4.y, ac);
+              ac = mfma16(a4.z, b4.z, ac);
+              ac = mfma16(a4.w, b4.w, ac);
+            }
+          }
+          acc = accs[0] + accs[1];
         }
-        const floatx4 acc = accs[0] + accs[1];
         const int vs = sb * 16 + l16;
         const int ts_ = vs >> rsl;
         const float cum_s = sc_cum[ts_], scl_s = sc_scl[ts_];
@@ -744,9 +895,6 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
     }
 
     if constexpr (FULL && !MIMO && SPLIT) load_z();
-    if constexpr (LATE_X) {
-      if (c0 + Qt < t_end) prefetch_x(c0 + Qt);
-    }
     if (mma_wave) {
       if constexpr (FULL) {
         // ---- P5a: Y = M X + diag(exp(cum)) Q h'^T over this wave's state
@@ -790,11 +938,49 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
           floatx4 acc[TB];
 #pragma unroll
           for (int tb = 0; tb < TB; ++tb) acc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-          add_qh(acc);
+          if constexpr (HALF) {
+            // the state to fp16 head / tail, one scale per head_dim column
+            // over this wave's state blocks; per pair of blocks (one k = 32
+            // step, plane columns 32 i' .. 32 i' + 31 hold exactly their rows)
+            // the two tail products, then the head product
+            float hm = 0.f;
 #pragma unroll
-          for (int tb = 0; tb < TB; ++tb)
+            for (int j = 0; j < JMAX; ++j) {
+              hm = max3_abs(Hacc[j][0], Hacc[j][1], hm);
+              hm = max3_abs(Hacc[j][2], Hacc[j][3], hm);
+            }
+            const int eH = f16_scale_exp(max_xor16_32(hm));
+            const float sH = ldexpf(1.f, eH);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[tb][r] *= sc_ecum[(tb * 16 + 4 * lq + r) >> rsl];
+            for (int i = 0; i < JMAX / 2; ++i) {
+              unsigned h0, h1, h2, h3, t0, t1, t2, t3;
+              split2_f16s(Hacc[2 * i][0], Hacc[2 * i][1], sH, h0, t0);
+              split2_f16s(Hacc[2 * i][2], Hacc[2 * i][3], sH, h1, t1);
+              split2_f16s(Hacc[2 * i + 1][0], Hacc[2 * i + 1][1], sH, h2, t2);
+              split2_f16s(Hacc[2 * i + 1][2], Hacc[2 * i + 1][3], sH, h3, t3);
+              const uintx4 hh = uintx4{h0, h1, h2, h3}, hl = uintx4{t0, t1, t2, t3};
+#pragma unroll
+              for (int tb = 0; tb < TB; ++tb) {
+                const _Float16* qr = Qp + (tb * 16 + l16) * kPQK + (nb0 + 2 * i) * 16 + 8 * lq;
+                const uintx4 qh = *reinterpret_cast<const uintx4*>(qr);
+                const uintx4 ql = *reinterpret_cast<const uintx4*>(qr + QPL);
+                acc[tb] = mfma_f16(ql, hh, acc[tb]);
+                acc[tb] = mfma_f16(qh, hl, acc[tb]);
+                acc[tb] = mfma_f16(qh, hh, acc[tb]);
+              }
+            }
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                acc[tb][r] = ldexpf(acc[tb][r], -(eQ + eH)) * sc_ecum[(tb * 16 + 4 * lq + r) >> rsl];
+          } else {
+            add_qh(acc);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[tb][r] *= sc_ecum[(tb * 16 + 4 * lq + r) >> rsl];
+          }
           if (nb0 == 0) add_mx(acc);
 #pragma unroll
           for (int tb = 0; tb < TB; ++tb)
@@ -820,6 +1006,11 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
               Yd[v * ys + p0 + l16] = fmaf(sc_ecum[v >> rsl], aci[tb][r], acc[tb][r]);
             }
         }
+      }
+      // the next chunk's x rows land during the update and the epilogue (every
+      // wave is an MFMA wave where they load late)
+      if constexpr (LATE_X) {
+        if (c0 + Qt < t_end) prefetch_x(c0 + Qt);
       }
       // ---- P5b: state update h' = decay h' + K^T (w X) ------------------------
       const float dec = run[64];
@@ -888,6 +1079,9 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
           bstore<VEC>(ores, (uint32_t)(t * tokx + pv * VEC), y);
         }
       }
+      // the next chunk's raw maxima (its rows were prefetched before S;
+      // this chunk's staging has read the slots)
+      raw_maxima();
       lds_barrier();
     }
     if constexpr (FULL && MIMO) {
@@ -1007,8 +1201,13 @@ void layout(ScanKParams& kp, bool full, bool mimo, bool split) {
   kp.ys = kp.PT * 16 + 4;
   const bool y_over_k = full && split && kp.NH > 1;
   int off = 0;
-  kp.o_ql = off; off += full ? QV * kp.ks : 0;
-  kp.o_kl = off; off += (full || !split) ? (y_over_k ? std::max(QV * kp.ks, 2 * QV * kp.ys) : QV * kp.ks) : 0;
+  // the SISO main pass of the split layout keeps Q and K as fp16 planes
+  // [2][QV][kPQK] halves in these two regions
+  const bool half = full && split && !mimo;
+  const int planes = half ? QV * kPQK : 0;  // floats of two fp16 planes
+  kp.o_ql = off; off += full ? std::max(QV * kp.ks, planes) : 0;
+  kp.o_kl = off;
+  off += (full || !split) ? std::max(y_over_k ? std::max(QV * kp.ks, 2 * QV * kp.ys) : QV * kp.ks, planes) : 0;
   kp.o_kt = off; off += split ? 3 * kp.NT * 16 * kKTw : 0;
   kp.o_xl = off; off += QV * kp.xs;
   kp.o_ml = off; off += full ? QV * kp.ms : 0;
@@ -1020,14 +1219,17 @@ void layout(ScanKParams& kp, bool full, bool mimo, bool split) {
     kp.o_yl = off; off += full ? QV * kp.ys : 0;
     kp.o_yl2 = off; off += (full && kp.NH > 1) ? QV * kp.ys : 0;
   }
-  // the entry-state fold overlays [PT*16][NT*16+4] floats on the chunk buffers
+  // the entry-state fold overlays [PT*16][NT*16+4] floats on the chunk buffers,
+  // or (the register fold, at most 128 summaries of 32 angles) three
+  // [128][32] tables and 128 decays
   if (full && off < kp.PT * 16 * (kp.NT * 16 + 4)) off = kp.PT * 16 * (kp.NT * 16 + 4);
+  if (full && off < 3 * 128 * 32 + 128) off = 3 * 128 * 32 + 128;
   kp.o_cs = off; off += 2 * 64;
   kp.o_bias = off; off += 2 * kp.R * kp.N;
   kp.o_mimo = off; off += mimo ? 3 * kp.R * kp.P + kp.P : 0;
   off = (off + 3) / 4 * 4;
   kp.o_sc = off; off += 6 * QV;
-  kp.o_run = off; off += 68;
+  kp.o_run = off; off += 84;
   kp.lds_floats = off;
 }
 
