@@ -881,14 +881,29 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         const int vs = sb * 16 + l16;
         const int ts_ = vs >> rsl;
         const float cum_s = sc_cum[ts_], scl_s = sc_scl[ts_];
+        if constexpr (HALF) {
+          // one virtual row per token: the weights of the lane's four rows
+          // by selects (every lane computes the decay term; no branches)
+          const floatx4 cum_t = lds_read4(sc_cum + tb * 16 + 4 * lq);
+          const floatx4 gam_t = lds_read4(sc_gam + tb * 16 + 4 * lq);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int vt = tb * 16 + 4 * lq + r;
-          const int tt = vt >> rsl;
-          float m = 0.f;
-          if (ts_ < tt) m = acc[r] * (exp_fast(sc_cum[tt] - cum_s) * scl_s);
-          else if (ts_ == tt) m = acc[r] * sc_gam[tt];
-          Mdst[vt * ms + vs] = m;
+          for (int r = 0; r < 4; ++r) {
+            const int tt = tb * 16 + 4 * lq + r;
+            float wdec = exp_fast(cum_t[r] - cum_s) * scl_s;
+            asm volatile("" : "+v"(wdec));
+            const float wt = ts_ < tt ? wdec : (ts_ == tt ? gam_t[r] : 0.f);
+            Mdst[tt * ms + vs] = acc[r] * wt;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int vt = tb * 16 + 4 * lq + r;
+            const int tt = vt >> rsl;
+            float m = 0.f;
+            if (ts_ < tt) m = acc[r] * (exp_fast(sc_cum[tt] - cum_s) * scl_s);
+            else if (ts_ == tt) m = acc[r] * sc_gam[tt];
+            Mdst[vt * ms + vs] = m;
+          }
         }
       }
       lds_barrier();
