@@ -768,7 +768,9 @@ def main():
         "dtype": "f32",
         "arithmetic": "fp32 storage, accumulation and element-wise work; the chunk state update K^T (w x) "
                       "as bf16 matrix products of six-term splits (three bf16 pieces per fp32 operand, "
-                      "about 2^-23 per product)",
+                      "about 2^-23 per product); S = Q K^T and the read-out Q h'^T as fp16 matrix "
+                      "products of power-of-two-scaled head/tail splits (about 2^-21 per product); "
+                      "M X in fp32",
         "data": "synthetic",
         "config": {"workload": "siso_b4_l2048: m3_siso_fwd_packed on the [8192 x 3432] packed projection "
                                "(preprocess fused into the scan)",
