@@ -172,6 +172,25 @@ __device__ __forceinline__ void sincos_acc(float x, float* s_out, float* c_out) 
   sincos_poly(r, q, s_out, c_out);
 }
 
+// sin and cos of x from the hardware sine and cosine (v_sin_f32 / v_cos_f32,
+// arguments in revolutions) after the same three-part fused reduction by
+// 2 pi (the pi/2 pieces times four), for |x| < 8192; sincos_acc beyond.
+// Measured on gfx950 over 4M arguments in |x| < 8192: at most 3.9e-7 from
+// the float64 sine and cosine (sincos_acc: 7e-8).
+__device__ __forceinline__ void sincos_hw(float x, float* s_out, float* c_out) {
+  if (fabsf(x) < 8192.f) {
+    const float k = rintf(x * 0x1.45f306p-3f);
+    float r = fmaf(-k, 0x1.921fb6p+2f, x);
+    r = fmaf(-k, -0x1.777a5cp-23f, r);
+    r = fmaf(-k, -0x1.ee59dap-48f, r);
+    const float rev = r * 0x1.45f306p-3f;
+    *s_out = __builtin_amdgcn_sinf(rev);
+    *c_out = __builtin_amdgcn_cosf(rev);
+  } else {
+    sincos_acc(x, s_out, c_out);
+  }
+}
+
 // The same for an argument held in float64, reduced in float64 whatever its
 // size.  The decode steps form theta = angle_state + dt angle exactly in
 // float64 from its float32 parts, so that an accumulated angle of large

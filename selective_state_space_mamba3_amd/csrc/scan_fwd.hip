@@ -666,7 +666,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         for (int e = 0; e < 4; ++e) {
           thv[e] = r4[e] + th[e];
           float sn, co;
-          sincos_acc(thv[e], &sn, &co);
+          sincos_hw(thv[e], &sn, &co);
           const float u0 = k0[e], u1 = k1[e];
           k0[e] = u0 * co - u1 * sn;
           k1[e] = u0 * sn + u1 * co;
