@@ -647,8 +647,10 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         eQ = __builtin_amdgcn_readfirstlane(f16_scale_exp(1.4143f * (slot_max(run + 76) + bmax_c)));
       }
       float th[4] = {0.f, 0.f, 0.f, 0.f};
+      if (2 * wave < A / 4) {  // the wave holds rotated pair groups (uniform)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) th[e] = scan32_f((mpair && tok_ok && mr == 0) ? mdt * angr[e] : 0.f);
+        for (int e = 0; e < 4; ++e) th[e] = scan32_f((mpair && tok_ok && mr == 0) ? mdt * angr[e] : 0.f);
+      }
       vec_t k0 = br[0], k1 = br[1], q0 = cr[0], q1 = cr[1];
       const float* bbr = bbL + mrc * N;
       const floatx4 bb0 = lds_read4(bbr + mc0), bb1 = lds_read4(bbr + mc1);
@@ -678,7 +680,9 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         }
         if (mt == ((nvalid - 1) << rsl)) *reinterpret_cast<floatx4*>(run + mc0) = floatx4{thv[0], thv[1], thv[2], thv[3]};
       }
-      if (!tok_ok) {
+      // rows past the chunk's last token, or of padding ranks (a full SISO
+      // chunk has none: uniform test first)
+      if ((nvalid < Qt || R < (1 << rsl)) && !tok_ok) {
         k0 = floatx4{0.f, 0.f, 0.f, 0.f};
         k1 = k0;
         q0 = k0;
