@@ -284,180 +284,6 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   unsigned* KTm = KTh + N * kKTw;                     // middle parts
   unsigned* KTl = KTm + N * kKTw;                     // tail parts
 
-  for (int i = tid; i < p.lds_floats; i += nthreads) lds[i] = 0.f;
-  __syncthreads();
-  for (int i = tid; i < R * N; i += nthreads) {
-    bbL[i] = p.b_bias[(size_t)h * R * N + i];
-    if (FULL) cbL[i] = p.c_bias[(size_t)h * R * N + i];
-  }
-  // HALF: the largest bias magnitudes of this head (with the raw-row maxima,
-  // the bound behind the fp16 scales)
-  float bmax_b = 0.f, bmax_c = 0.f;
-  if constexpr (HALF) {
-    for (int i = lane; i < N; i += 64) {
-      bmax_b = max3_abs(p.b_bias[(size_t)h * N + i], 0.f, bmax_b);
-      bmax_c = max3_abs(p.c_bias[(size_t)h * N + i], 0.f, bmax_c);
-    }
-    bmax_b = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_nn(bmax_b))));
-    bmax_c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_nn(bmax_c))));
-  }
-  if constexpr (FULL && MIMO) {
-    for (int i = tid; i < R * P; i += nthreads) {
-      mxL[i] = p.mimo_x[(size_t)h * R * P + i];
-      mzL[i] = p.mimo_z[(size_t)h * R * P + i];
-      moL[i] = p.mimo_o[(size_t)h * R * P + i];
-    }
-    for (int i = tid; i < P; i += nthreads) nwL[i] = p.norm_weight[(size_t)h * P + i];
-  } else if constexpr (MIMO) {
-    for (int i = tid; i < R * P; i += nthreads) mxL[i] = p.mimo_x[(size_t)h * R * P + i];
-  }
-
-  const int p0 = pt * 16;
-  floatx4 Hacc[4];  // state blocks nb0 .. nb0 + ntw - 1 of columns p0 .. p0 + 15
-#pragma unroll
-  for (int j = 0; j < JMAX; ++j) Hacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  // Entry state: fold the summaries of the earlier segments, in order,
-  //   h' <- decay_i h' + rot(theta_i) U_i,
-  // where U_i was built with the angle restarted at zero inside segment i, so
-  // its state axis is turned by theta_i = the summed angle of the segments
-  // before i (the keys it holds are rot(theta_i + local) = rot(theta_i) rot(local)).
-  //
-  // With N = 128 split into two halves of 64 state rows per wave and A a
-  // multiple of 16 with 2A <= 64, both members of every rotated pair
-  // (a, a + A) sit in the same lane and register of one wave (blocks a / 16
-  // and a / 16 + A / 16), so the fold rotates in registers, with all
-  // summaries loaded at once and cos / sin of every theta_i from an LDS table.
-  // Otherwise U_i passes through LDS in [p][n] layout for the pair rotation.
-  const bool reg_fold = FIXED && NTC == 8 && !MIMO && (A == 0 || A == 16 || A == 32) && nsum_all <= 128;
-  if (FULL && seg > 0 && reg_fold) {
-    const size_t sbase = (size_t)bh * nsum_all;
-    // LDS (overlaying the chunk buffers, unused yet): the summaries' angle
-    // increments and decays, loaded at once; then per angle the running sums
-    // theta_i (in summary order), and cos / sin of each
-    float* CSt = lds;  // [nsum][A] theta_i, then cos theta_i
-    float* SNt = CSt + nsum * A;  // [nsum][A] sin theta_i
-    float* AXt = SNt + nsum * A;  // [nsum][A] angle increment of summary i
-    float* DCt = AXt + nsum * A;  // [nsum] decay of summary i
-    for (int idx = tid; idx < nsum * A; idx += nthreads) {
-      const int i = idx / A, a = idx - i * A;
-      AXt[idx] = p.ws_aux[(sbase + i) * kAux + a];
-    }
-    for (int i = tid; i < nsum; i += nthreads) DCt[i] = p.ws_aux[(sbase + i) * kAux + kAuxDecay];
-    __syncthreads();
-    for (int a = tid; a < A; a += nthreads) {
-      float th = 0.f;
-      for (int i = 0; i < nsum; ++i) {
-        CSt[i * A + a] = th;
-        th += AXt[i * A + a];
-      }
-      run[a] = th;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < nsum * A; idx += nthreads) {
-      float sn, cs;
-      sincos_acc(CSt[idx], &sn, &cs);
-      CSt[idx] = cs;
-      SNt[idx] = sn;
-    }
-    __syncthreads();
-    // the summary states, four in flight at a time
-    constexpr int FB = 4;
-    for (int i0 = 0; i0 < nsum; i0 += FB) {
-      floatx4 u[FB][JMAX];
-#pragma unroll
-      for (int k = 0; k < FB; ++k) {
-        if (i0 + k < nsum) {
-          const float* st = p.ws_state + (sbase + i0 + k) * (size_t)(PT * NT) * 256;
-#pragma unroll
-          for (int j = 0; j < JMAX; ++j)
-            u[k][j] = *reinterpret_cast<const floatx4*>(st + ((pt * NT + nb0 + j) * 64 + lane) * 4);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < FB; ++k) {
-        const int i = i0 + k;
-        if (i < nsum) {
-          if (nb0 == 0 && A > 0) {
-            const float* ci = CSt + i * A;
-            const float* si = SNt + i * A;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (A == 32) {
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb) {
-                  const int a = 16 * jb + 4 * lq + r;
-                  const float c = ci[a], sv = si[a];
-                  const float u0 = u[k][jb][r], u1 = u[k][jb + 2][r];
-                  u[k][jb][r] = u0 * c - u1 * sv;
-                  u[k][jb + 2][r] = u0 * sv + u1 * c;
-                }
-              } else {  // A == 16
-                const int a = 4 * lq + r;
-                const float c = ci[a], sv = si[a];
-                const float u0 = u[k][0][r], u1 = u[k][1][r];
-                u[k][0][r] = u0 * c - u1 * sv;
-                u[k][1][r] = u0 * sv + u1 * c;
-              }
-            }
-          }
-          const float dec = DCt[i];
-#pragma unroll
-          for (int j = 0; j < JMAX; ++j) Hacc[j] = dec * Hacc[j] + u[k][j];
-        }
-      }
-    }
-    __syncthreads();
-    for (int i = tid; i < 3 * nsum * A + nsum; i += nthreads) CSt[i] = 0.f;  // restore the zeroed chunk buffers
-  } else if (FULL && seg > 0) {
-    __syncthreads();
-    float* Ub = lds;  // [PT*16][NT*16 + 4], overlays the chunk buffers (unused yet)
-    const int us = NT * 16 + 4;
-    for (int i = 0; i < nsum; ++i) {
-      const size_t si = (size_t)bh * nsum_all + i;
-      const float* aux = p.ws_aux + si * kAux;
-      const float* st = p.ws_state + si * (size_t)(PT * NT) * 256;
-      if (mma_wave) {
-#pragma unroll
-        for (int j = 0; j < JMAX; ++j) {
-          if (FIXED || j < ntw) {
-            const int nb = nb0 + j;
-            const floatx4 u = *reinterpret_cast<const floatx4*>(st + ((pt * NT + nb) * 64 + lane) * 4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Ub[(p0 + l16) * us + nb * 16 + 4 * lq + r] = u[r];
-          }
-        }
-      }
-      if (tid < A) {
-        float sn, cs;
-        sincos_acc(run[tid], &sn, &cs);
-        CS[tid] = cs;
-        SN[tid] = sn;
-      }
-      __syncthreads();
-      for (int e = tid; e < PT * 16 * A; e += nthreads) {
-        const int pp = e / A, a = e - pp * A;
-        const float u0 = Ub[pp * us + a], u1 = Ub[pp * us + a + A];
-        Ub[pp * us + a] = u0 * CS[a] - u1 * SN[a];
-        Ub[pp * us + a + A] = u0 * SN[a] + u1 * CS[a];
-      }
-      __syncthreads();
-      const float dec = aux[kAuxDecay];
-      if (mma_wave) {
-#pragma unroll
-        for (int j = 0; j < JMAX; ++j) {
-          if (FIXED || j < ntw) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              Hacc[j][r] = fmaf(dec, Hacc[j][r], Ub[(p0 + l16) * us + (nb0 + j) * 16 + 4 * lq + r]);
-          }
-        }
-      }
-      if (tid < A) run[tid] += aux[tid];
-      __syncthreads();
-    }
-    for (int i = tid; i < PT * 16 * us; i += nthreads) Ub[i] = 0.f;  // restore the zero padding
-  }
   float seg_decay = 1.f;  // lane 0 of the scalar wave: product of chunk decays (summary pass)
 
   // ---- register prefetch of one chunk's global operands -------------------
@@ -554,6 +380,186 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
     }
   };
 
+  // The first chunk's loads go out before the set-up below (LDS clearing, biases,
+  // the entry-state fold), whose own loads and waits they overlap.
+  prefetch(t_begin);
+  if constexpr (LATE_X) prefetch_x(t_begin);
+
+  for (int i = tid; i < p.lds_floats; i += nthreads) lds[i] = 0.f;
+  __syncthreads();
+  for (int i = tid; i < R * N; i += nthreads) {
+    bbL[i] = p.b_bias[(size_t)h * R * N + i];
+    if (FULL) cbL[i] = p.c_bias[(size_t)h * R * N + i];
+  }
+  // HALF: the largest bias magnitudes of this head (with the raw-row maxima,
+  // the bound behind the fp16 scales)
+  float bmax_b = 0.f, bmax_c = 0.f;
+  if constexpr (HALF) {
+    for (int i = lane; i < N; i += 64) {
+      bmax_b = max3_abs(p.b_bias[(size_t)h * N + i], 0.f, bmax_b);
+      bmax_c = max3_abs(p.c_bias[(size_t)h * N + i], 0.f, bmax_c);
+    }
+    bmax_b = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_nn(bmax_b))));
+    bmax_c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_nn(bmax_c))));
+  }
+  if constexpr (FULL && MIMO) {
+    for (int i = tid; i < R * P; i += nthreads) {
+      mxL[i] = p.mimo_x[(size_t)h * R * P + i];
+      mzL[i] = p.mimo_z[(size_t)h * R * P + i];
+      moL[i] = p.mimo_o[(size_t)h * R * P + i];
+    }
+    for (int i = tid; i < P; i += nthreads) nwL[i] = p.norm_weight[(size_t)h * P + i];
+  } else if constexpr (MIMO) {
+    for (int i = tid; i < R * P; i += nthreads) mxL[i] = p.mimo_x[(size_t)h * R * P + i];
+  }
+
+  const int p0 = pt * 16;
+  floatx4 Hacc[4];  // state blocks nb0 .. nb0 + ntw - 1 of columns p0 .. p0 + 15
+#pragma unroll
+  for (int j = 0; j < JMAX; ++j) Hacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // Entry state: fold the summaries of the earlier segments, in order,
+  //   h' <- decay_i h' + rot(theta_i) U_i,
+  // where U_i was built with the angle restarted at zero inside segment i, so
+  // its state axis is turned by theta_i = the summed angle of the segments
+  // before i (the keys it holds are rot(theta_i + local) = rot(theta_i) rot(local)).
+  //
+  // With N = 128 split into two halves of 64 state rows per wave and A a
+  // multiple of 16 with 2A <= 64, both members of every rotated pair
+  // (a, a + A) sit in the same lane and register of one wave (blocks a / 16
+  // and a / 16 + A / 16), so the fold rotates in registers, with all
+  // summaries loaded at once and cos / sin of every theta_i from an LDS table.
+  // Otherwise U_i passes through LDS in [p][n] layout for the pair rotation.
+  const bool reg_fold = FIXED && NTC == 8 && !MIMO && (A == 0 || A == 16 || A == 32) && nsum_all <= 128;
+  if (FULL && seg > 0 && reg_fold) {
+    const size_t sbase = (size_t)bh * nsum_all;
+    // LDS (overlaying the chunk buffers, unused yet): the summaries' angle
+    // increments and decays, loaded at once; then per angle the running sums
+    // theta_i (in summary order), and cos / sin of each
+    float* CSt = lds;  // [nsum][A] theta_i, then cos theta_i
+    float* SNt = CSt + nsum * A;  // [nsum][A] sin theta_i
+    float* AXt = SNt + nsum * A;  // [nsum][A] angle increment of summary i
+    float* DCt = AXt + nsum * A;  // [nsum] decay of summary i
+    for (int idx = tid; idx < nsum * A; idx += nthreads) {
+      const int i = idx / A, a = idx - i * A;
+      AXt[idx] = p.ws_aux[(sbase + i) * kAux + a];
+    }
+    for (int i = tid; i < nsum; i += nthreads) DCt[i] = p.ws_aux[(sbase + i) * kAux + kAuxDecay];
+    __syncthreads();
+    for (int a = tid; a < A; a += nthreads) {
+      float th = 0.f;
+      for (int i = 0; i < nsum; ++i) {
+        CSt[i * A + a] = th;
+        th += AXt[i * A + a];
+      }
+      run[a] = th;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < nsum * A; idx += nthreads) {
+      float sn, cs;
+      sincos_acc(CSt[idx], &sn, &cs);
+      CSt[idx] = cs;
+      SNt[idx] = sn;
+    }
+    __syncthreads();
+    // the summary states, two in flight at a time (with the first chunk's
+    // loads already in flight, four spill registers)
+    constexpr int FB = 2;
+    for (int i0 = 0; i0 < nsum; i0 += FB) {
+      floatx4 u[FB][JMAX];
+#pragma unroll
+      for (int k = 0; k < FB; ++k) {
+        if (i0 + k < nsum) {
+          const float* st = p.ws_state + (sbase + i0 + k) * (size_t)(PT * NT) * 256;
+#pragma unroll
+          for (int j = 0; j < JMAX; ++j)
+            u[k][j] = *reinterpret_cast<const floatx4*>(st + ((pt * NT + nb0 + j) * 64 + lane) * 4);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < FB; ++k) {
+        const int i = i0 + k;
+        if (i < nsum) {
+          if (nb0 == 0 && A > 0) {
+            const float* ci = CSt + i * A;
+            const float* si = SNt + i * A;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (A == 32) {
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb) {
+                  const int a = 16 * jb + 4 * lq + r;
+                  const float c = ci[a], sv = si[a];
+                  const float u0 = u[k][jb][r], u1 = u[k][jb + 2][r];
+                  u[k][jb][r] = u0 * c - u1 * sv;
+                  u[k][jb + 2][r] = u0 * sv + u1 * c;
+                }
+              } else {  // A == 16
+                const int a = 4 * lq + r;
+                const float c = ci[a], sv = si[a];
+                const float u0 = u[k][0][r], u1 = u[k][1][r];
+                u[k][0][r] = u0 * c - u1 * sv;
+                u[k][1][r] = u0 * sv + u1 * c;
+              }
+            }
+          }
+          const float dec = DCt[i];
+#pragma unroll
+          for (int j = 0; j < JMAX; ++j) Hacc[j] = dec * Hacc[j] + u[k][j];
+        }
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < 3 * nsum * A + nsum; i += nthreads) CSt[i] = 0.f;  // restore the zeroed chunk buffers
+  } else if (FULL && seg > 0) {
+    __syncthreads();
+    float* Ub = lds;  // [PT*16][NT*16 + 4], overlays the chunk buffers (unused yet)
+    const int us = NT * 16 + 4;
+    for (int i = 0; i < nsum; ++i) {
+      const size_t si = (size_t)bh * nsum_all + i;
+      const float* aux = p.ws_aux + si * kAux;
+      const float* st = p.ws_state + si * (size_t)(PT * NT) * 256;
+      if (mma_wave) {
+#pragma unroll
+        for (int j = 0; j < JMAX; ++j) {
+          if (FIXED || j < ntw) {
+            const int nb = nb0 + j;
+            const floatx4 u = *reinterpret_cast<const floatx4*>(st + ((pt * NT + nb) * 64 + lane) * 4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Ub[(p0 + l16) * us + nb * 16 + 4 * lq + r] = u[r];
+          }
+        }
+      }
+      if (tid < A) {
+        float sn, cs;
+        sincos_acc(run[tid], &sn, &cs);
+        CS[tid] = cs;
+        SN[tid] = sn;
+      }
+      __syncthreads();
+      for (int e = tid; e < PT * 16 * A; e += nthreads) {
+        const int pp = e / A, a = e - pp * A;
+        const float u0 = Ub[pp * us + a], u1 = Ub[pp * us + a + A];
+        Ub[pp * us + a] = u0 * CS[a] - u1 * SN[a];
+        Ub[pp * us + a + A] = u0 * SN[a] + u1 * CS[a];
+      }
+      __syncthreads();
+      const float dec = aux[kAuxDecay];
+      if (mma_wave) {
+#pragma unroll
+        for (int j = 0; j < JMAX; ++j) {
+          if (FIXED || j < ntw) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              Hacc[j][r] = fmaf(dec, Hacc[j][r], Ub[(p0 + l16) * us + (nb0 + j) * 16 + 4 * lq + r]);
+          }
+        }
+      }
+      if (tid < A) run[tid] += aux[tid];
+      __syncthreads();
+    }
+    for (int i = tid; i < PT * 16 * us; i += nthreads) Ub[i] = 0.f;  // restore the zero padding
+  }
   // HALF: per-wave maxima of the prefetched raw B / C rows of a chunk, in
   // LDS for the staging of that chunk (all waves take the largest)
   auto raw_maxima = [&]() {
@@ -582,8 +588,6 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   // fp16 scale exponents of the staged chunk's keys and queries (uniform)
   int eK = 0, eQ = 0;
 
-  prefetch(t_begin);
-  if constexpr (LATE_X) prefetch_x(t_begin);
   raw_maxima();
   __syncthreads();
 
