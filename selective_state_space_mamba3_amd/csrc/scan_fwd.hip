@@ -279,7 +279,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   float* sc_scl = sc_gam + QV;
   float* sc_w = sc_scl + QV;
   float* sc_dt = sc_w + QV;
-  float* run = lds + p.o_run;  // [0,64) running theta, [64] chunk decay, [68,84) raw B / C maxima per wave (HALF)
+  float* run = lds + p.o_run;  // [0,64) running theta, [64] chunk decay, [68] / [69] raw B / C maxima (HALF)
   unsigned* KTh = reinterpret_cast<unsigned*>(lds + p.o_kt);  // [N][kKTw] bf16 pairs of K, head parts (SPLIT)
   unsigned* KTm = KTh + N * kKTw;                     // middle parts
   unsigned* KTl = KTm + N * kKTw;                     // tail parts
@@ -560,8 +560,11 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
     }
     for (int i = tid; i < PT * 16 * us; i += nthreads) Ub[i] = 0.f;  // restore the zero padding
   }
-  // HALF: per-wave maxima of the prefetched raw B / C rows of a chunk, in
-  // LDS for the staging of that chunk (all waves take the largest)
+  // HALF: the largest raw B / C entries of the prefetched rows of a chunk,
+  // for the staging of that chunk: each wave's maximum goes into one LDS
+  // slot per operand by an integer atomic max (the values are non-negative,
+  // so their bit patterns order as the floats do); the scalar wave clears
+  // the slots during S, after the staging has read them
   auto raw_maxima = [&]() {
     if constexpr (HALF) {
       float mk = 0.f, mq = 0.f;
@@ -575,15 +578,13 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       mk = wave_max_nn(mk);
       mq = wave_max_nn(mq);
       if (lane == 0) {
-        run[68 + wave] = mk;
-        run[76 + wave] = mq;
+        atomicMax(reinterpret_cast<unsigned*>(run + 68), __float_as_uint(mk));
+        atomicMax(reinterpret_cast<unsigned*>(run + 69), __float_as_uint(mq));
       }
     }
   };
   auto slot_max = [&](const float* sl) {
-    const floatx4 a = lds_read4(sl), c = lds_read4(sl + 4);
-    const float m = fmaxf(fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w)), fmaxf(fmaxf(c.x, c.y), fmaxf(c.z, c.w)));
-    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(m)));
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(*sl)));
   };
   // fp16 scale exponents of the staged chunk's keys and queries (uniform)
   int eK = 0, eQ = 0;
@@ -648,7 +649,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       if constexpr (HALF) {
         // |rotated entry| <= sqrt(2) max |raw + bias| (a rotation keeps each pair's norm)
         eK = __builtin_amdgcn_readfirstlane(f16_scale_exp(1.4143f * (slot_max(run + 68) + bmax_b)));
-        eQ = __builtin_amdgcn_readfirstlane(f16_scale_exp(1.4143f * (slot_max(run + 76) + bmax_c)));
+        eQ = __builtin_amdgcn_readfirstlane(f16_scale_exp(1.4143f * (slot_max(run + 69) + bmax_c)));
       }
       float th[4] = {0.f, 0.f, 0.f, 0.f};
       if (2 * wave < A / 4) {  // the wave holds rotated pair groups (uniform)
@@ -913,6 +914,9 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
             Mdst[vt * ms + vs] = m;
           }
         }
+      }
+      if constexpr (HALF) {
+        if (tid == sw * 64) *reinterpret_cast<floatx2*>(run + 68) = floatx2{0.f, 0.f};  // the staging has read them
       }
       lds_barrier();
     }
@@ -1252,7 +1256,7 @@ void layout(ScanKParams& kp, bool full, bool mimo, bool split) {
   kp.o_mimo = off; off += mimo ? 3 * kp.R * kp.P + kp.P : 0;
   off = (off + 3) / 4 * 4;
   kp.o_sc = off; off += 6 * QV;
-  kp.o_run = off; off += 84;
+  kp.o_run = off; off += 72;
   kp.lds_floats = off;
 }
 
