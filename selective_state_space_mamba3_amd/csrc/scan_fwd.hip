@@ -60,7 +60,7 @@ constexpr int kAux = 68;        // per segment summary: angle increment [<=64], 
 constexpr int kAuxDecay = 64;
 constexpr float kNormEps = 1.0e-5f;  // MIMO output-norm epsilon of the MIMO push constants
 constexpr int kQV = 32;         // virtual rows per chunk
-constexpr long kMaxAutoSegments = 65;  // automatic plan: at most 2 * 64 = 128 summary pieces per chain
+constexpr long kMaxAutoSegments = 65;  // automatic plan: at most 64 summaries per chain (one per segment)
 // Key buffer of the bf16 state update, transposed: per state coordinate n one
 // row of 32 bf16 (16 words), its four 16-byte blocks stored in the order
 // q ^ ((n >> 2) & 3), so that the 16 rows read by one lane group hit 16
@@ -1187,10 +1187,10 @@ ScanPlan make_plan(const ScanGeom& g) {
   if (bhn < target) nseg = target / bhn;
   const long max_seg = ((long)g.L + 4L * Qt - 1) / (4L * Qt);
   if (nseg > max_seg) nseg = max_seg;
-  // Segment s folds the 2s summary pieces before it, so the fold's work grows
-  // with the square of the segment count.  At most 65 segments (128 pieces,
-  // the register fold's limit) keep the last segment's fold within a few
-  // chunks' time where few chains would otherwise ask for hundreds.
+  // Segment s folds the summaries before it, so the fold's work grows with
+  // the square of the segment count.  At most 65 segments keep the last
+  // segment's fold within a few chunks' time where few chains would
+  // otherwise ask for hundreds.
   if (nseg > kMaxAutoSegments) nseg = kMaxAutoSegments;
   if (g_forced_segments > 0) nseg = (long)g_forced_segments;
   if (nseg < 1) nseg = 1;
@@ -1199,12 +1199,15 @@ ScanPlan make_plan(const ScanGeom& g) {
   nseg = ((long)g.L + seg_len - 1) / seg_len;
   pl.nseg = (int)nseg;
   pl.seg_len = (int)seg_len;
-  // The summary pass cuts each segment before the last into two pieces of
-  // whole chunks: twice the workgroups over the same tokens, so that it
-  // fills the CUs' second workgroup slots (one summary segment per chain
-  // would leave them idle wherever B*H is near the CU count); the main pass
-  // folds the pieces' summaries in order.
-  pl.npc = nseg > 1 ? 2 : 1;
+  // With few segments the summary pass cuts each segment before the last
+  // into two pieces of whole chunks: twice the workgroups over the same
+  // tokens, where one summary per segment would leave CUs' second slots
+  // idle (B4 H24: 384 workgroups; 768 in pieces ran the pass 4 us faster).
+  // The main pass folds every earlier piece, so with many segments, or when
+  // the pieces would take more than one and a half rounds of the slots, one
+  // summary per segment is faster (the fold halves; B1 L65536 H32 / H4 / H1
+  // 2% / 9% / 5% faster per call).
+  pl.npc = (nseg > 1 && nseg <= 8 && 2L * bhn * (nseg - 1) <= 3L * device_cu_count()) ? 2 : 1;
   pl.plen = (int)(((seg_len / Qt + pl.npc - 1) / pl.npc) * Qt);
   const long nsum = (nseg - 1) * pl.npc;
   pl.ws_state_floats = nseg > 1 ? (size_t)bhn * nsum * PT * NT * 256 : 0;

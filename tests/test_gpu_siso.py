@@ -86,7 +86,7 @@ def test_siso_forced_segments_a16(nseg):
 
 
 def test_siso_sixty_four_segments():
-    # one 32-token chunk per segment: the entry state composes up to 126 summaries
+    # one 32-token chunk per segment: the entry state composes up to 63 summaries
     d = Dims(1, 2048, 2, 1, 64, 128, 32)
     inp = ssm_inputs(d, seed=2022)
     with m3.scan_segments(64):
@@ -94,9 +94,19 @@ def test_siso_sixty_four_segments():
     assert_parity(got, oracle_siso(inp, d), "segments_64")
 
 
+def test_siso_register_fold_limit():
+    # 128 one-chunk segments: the last folds 127 summaries, next to the
+    # register fold's limit of 128
+    d = Dims(1, 4096, 2, 1, 64, 128, 32)
+    inp = ssm_inputs(d, seed=2024, dt_range=(1e-3, 0.01))
+    with m3.scan_segments(128):
+        got = gpu_siso(to_dev(inp), d).cpu().numpy()
+    assert_parity(got, oracle_siso(inp, d), "segments_128")
+
+
 def test_siso_few_chains_long_sequence_automatic_plan():
     # two chains over 16384 tokens: the automatic plan would take 128 segments
-    # and is held at 65 (the last segment folds 128 summary pieces)
+    # and is held at 65 (the last segment folds 64 summaries)
     d = Dims(1, 16384, 2, 1, 64, 128, 32)
     inp = ssm_inputs(d, seed=2023, dt_range=(1e-3, 0.01))
     cfg = m3.SsmConfig(d.B, d.L, d.H, d.G, d.P, d.N, d.A)
