@@ -637,16 +637,39 @@ def main():
             return 4
 
     hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
-    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
     hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
     hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     lib.m3_set_profile_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    # Events for timing only: without the system-scope fence that a default
+    # event adds when it is recorded (an L2 writeback and invalidate between
+    # the kernels it separates); the elapsed times are read after a device
+    # synchronisation.
+    HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
     def new_event():
         e = ctypes.c_void_p()
-        if hip.hipEventCreate(ctypes.byref(e)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        if hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(HIP_EVENT_DISABLE_SYSTEM_FENCE)) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
         return e
+
+    class FenceFreeEvent:
+        """A timing event of that kind recorded on torch's current stream."""
+
+        def __init__(self):
+            self.e = new_event()
+
+        def record(self):
+            if hip.hipEventRecord(self.e, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) != 0:
+                raise RuntimeError("hipEventRecord failed")
+
+        def elapsed_time(self, other):
+            f = ctypes.c_float()
+            if hip.hipEventElapsedTime(ctypes.byref(f), self.e, other.e) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            return f.value
 
     # ---- the other rows, each at its own workload --------------------------
     # (measured first: seconds of GPU work that leave the GPU at the clocks it
@@ -663,32 +686,45 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region ------------------------------------------------------
+    # The library records the main pass's events on every KERN_EVERY-th timed
+    # step only: each recorded event leaves the GPU idle for about 4.5 us
+    # between the kernels it separates (kernel trace), which would otherwise
+    # add about 9 us to every step.
     K = args.steps
-    kern_ev = [(new_event(), new_event()) for _ in range(K)]
+    KERN_EVERY = 4
+    kern_steps = [i for i in range(K) if i % KERN_EVERY == KERN_EVERY - 1] or [K - 1]
+    kern_ev = {i: (new_event(), new_event()) for i in kern_steps}
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_begin.record()
     for i in range(K):
-        lib.m3_set_profile_events(kern_ev[i][0], kern_ev[i][1])
+        if i in kern_ev:
+            lib.m3_set_profile_events(kern_ev[i][0], kern_ev[i][1])
+        else:
+            lib.m3_set_profile_events(None, None)
         step(sets[i % len(sets)])
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     lib.m3_set_profile_events(None, None)
 
-    # the two-call form of the same pass, after the timed region: its own
-    # breakdown and the dense main pass's time
-    dense_ev = [(new_event(), new_event()) for _ in range(K)]
-    step_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # the two-call form of the same pass, after the timed region: timed as a
+    # whole with no events between its calls, then once more with events
+    # for its breakdown and the dense main pass's time
     t2_begin = torch.cuda.Event(enable_timing=True)
     t2_end = torch.cuda.Event(enable_timing=True)
     t2_begin.record()
     for i in range(K):
+        two_call(sets[i % len(sets)])
+    t2_end.record()
+    torch.cuda.synchronize()
+    dense_ev = [(new_event(), new_event()) for _ in range(K)]
+    step_ev = [[FenceFreeEvent() for _ in range(3)] for _ in range(K)]
+    for i in range(K):
         lib.m3_set_profile_events(dense_ev[i][0], dense_ev[i][1])
         two_call(sets[i % len(sets)], step_ev[i])
-    t2_end.record()
     torch.cuda.synchronize()
     lib.m3_set_profile_events(None, None)
 
@@ -713,7 +749,7 @@ def main():
             hip.hipEventDestroy(a)
             hip.hipEventDestroy(b)
         return float(np.mean(out))
-    kern_avg = event_ms(kern_ev)
+    kern_avg = event_ms(kern_ev.values())
     dense_avg = event_ms(dense_ev)
     pre_ms = [ev[0].elapsed_time(ev[1]) for ev in step_ev]
     scan_ms = [ev[1].elapsed_time(ev[2]) for ev in step_ev]
@@ -779,7 +815,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": kern_gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(),
                      "kernel": MAIN_KERNEL + " (main scan pass on the packed rows)",
-                     "kernel_ms": kern_avg, "algorithmic_bytes": scan_bytes,
+                     "kernel_ms": kern_avg, "kernel_launches_timed": len(kern_steps), "algorithmic_bytes": scan_bytes,
                      "fp32_tflops_min_work": min_flops / (kern_avg * 1e-3) / 1e12,
                      "fp32_frac": min_flops / (kern_avg * 1e-3) / 1e12 / FP32_PEAK_TFLOPS,
                      # the same bytes over the whole scan call (summary pass, fold and
