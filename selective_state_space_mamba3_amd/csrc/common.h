@@ -221,13 +221,19 @@ __device__ __forceinline__ floatx4 mfma_f16(uintx4 a, uintx4 b, floatx4 c) {
 // tail words (x0 in the low half of each word), the scaling folded into
 // v_fma_mix{lo,hi}_f16, which round a fused x s + c to fp16 in one half of
 // the word and keep the other half: the heads fp16(x s) and the tails
-// fp16(x s - h).
+// fp16(x s - h).  The compiler's hazard tracking does not see inside an asm
+// statement, and an MFMA that reads a VGPR needs two wait states after a VALU
+// instruction writes it, so the block ends with them (s_nop 1) before either
+// word can reach an MFMA operand.
 __device__ __forceinline__ void split2_f16s(float x0, float x1, float s, unsigned& h, unsigned& l) {
   unsigned hw, lw;
-  asm("v_fma_mixlo_f16 %0, %1, %2, 0" : "=v"(hw) : "v"(x0), "v"(s));
-  asm("v_fma_mixhi_f16 %0, %1, %2, 0" : "+v"(hw) : "v"(x1), "v"(s));
-  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,0,1]" : "=v"(lw) : "v"(x0), "v"(s), "v"(hw));
-  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(lw) : "v"(x1), "v"(s), "v"(hw));
+  asm("v_fma_mixlo_f16 %0, %2, %4, 0\n\t"
+      "v_fma_mixhi_f16 %0, %3, %4, 0\n\t"
+      "v_fma_mixlo_f16 %1, %2, %4, -%0 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %1, %3, %4, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "s_nop 1"
+      : "=&v"(hw), "=&v"(lw)
+      : "v"(x0), "v"(x1), "v"(s));
   h = hw;
   l = lw;
 }
@@ -238,13 +244,11 @@ __device__ __forceinline__ int f16_scale_exp(float m) {
   const int e = min(15 - __builtin_amdgcn_frexp_expf(m), 120);
   return (m > 0.f && m <= 3.0e38f) ? e : 0;
 }
-// max(|a|, |b|, m) for m >= 0 in one v_max3_f32 with absolute-value
-// modifiers (a NaN operand may be dropped; the NaN itself still reaches the
+// max(|a|, |b|, m) for m >= 0 (one v_max3_f32 with absolute-value
+// modifiers; a NaN operand may be dropped, the NaN itself still reaches the
 // products it belongs to).
 __device__ __forceinline__ float max3_abs(float a, float b, float m) {
-  float r;
-  asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(a), "v"(b), "v"(m));
-  return r;
+  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(a), __builtin_fabsf(b)), m);
 }
 // Maximum of non-negative v over lanes l, l ^ 16, l ^ 32, l ^ 48 (v_permlane16/32_swap).
 __device__ __forceinline__ float max_xor16_32(float v) {
