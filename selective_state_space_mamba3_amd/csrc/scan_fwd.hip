@@ -66,7 +66,7 @@ constexpr long kMaxAutoSegments = 65;  // automatic plan: at most 64 summaries p
 // q ^ ((n >> 2) & 3), so that the 16 rows read by one lane group hit 16
 // different bank groups.
 constexpr int kKTw = 16;
-// fp16 query / key planes of the SISO main pass (HALF below): rows of 136
+// fp16 query / key planes of the main pass (HALF below): rows of 136
 // halves (128 + 8 pad, 272 bytes), head plane then tail plane
 constexpr int kPQK = 136;
 // Column of state coordinate n in a plane row: within each group of 32,
@@ -233,26 +233,32 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   // S is split over six waves (three tile pairs x two N-halves).
   constexpr bool MERGED = merged_variant(NTC, PTC, NWC, RSC);
   const int sw = nwaves - 1;  // wave that computes the per-token scalars
-  // The merged layout runs its state update on bf16 MFMA with the six-term
-  // split (v_mfma_f32_16x16x32_bf16, k = the chunk's 32 virtual rows; fp32
-  // accuracy) in the summary pass, and for SISO in the main pass too (the
-  // MIMO main pass has no LDS left for it).  Its keys go to LDS split into
-  // three bf16 planes and transposed, [n][slot].  In the main pass they sit
-  // beside the fp32 keys that S = Q K^T reads, and the raw y buffers overlay
-  // those fp32 keys, which are dead once S is formed.  Lane
+  // The merged layout runs its state update on split matrix products with k
+  // = the chunk's 32 virtual rows at fp32-level accuracy: in the summary
+  // pass and the SISO main pass on bf16 MFMA with the six-term split
+  // (v_mfma_f32_16x16x32_bf16), in the MIMO main pass, short of LDS for a
+  // third key plane, on fp16 MFMA with head / tail splits (KT16 below).  Its
+  // keys go to LDS split into planes and transposed, [n][slot].  In the main
+  // pass they sit beside the fp16 query / key planes that S = Q K^T reads,
+  // and the raw y buffers overlay the key planes, which are dead once S is
+  // formed.  Lane
   // group q of an MFMA operand holds virtual rows 4q..4q+3 and 16+4q..16+4q+3
   // in its eight k-slots, so row v sits in slot position
   //     pos(v) = 8 ((v >> 2) & 3) + 4 (v >> 4) + (v & 3)
   // of its key row, and the x rows a lane reads are 4 apart (16 banks apart).
-  constexpr bool SPLIT = MERGED && (!MIMO || !FULL);
-  // The SISO main pass of the merged layout keeps its queries and keys as fp16
+  constexpr bool SPLIT = MERGED;
+  // The main pass of the merged layout keeps its queries and keys as fp16
   // head / tail planes, split once by the lanes that rotate them, and forms
   // S = Q K^T and the read-out Q h'^T on v_mfma_f32_16x16x32_f16 from them
   // (three products per k = 32 step, about 2^-21 relative each).  The scales
   // are powers of two from a bound known before the rotation: the largest
   // raw B / C entry of the chunk plus the largest bias entry, times sqrt(2)
   // (a rotation keeps each pair's norm).
-  constexpr bool HALF = FULL && MERGED && !MIMO;
+  constexpr bool HALF = FULL && MERGED;
+  // MIMO main pass: the transposed keys as two fp16 planes (head / tail at
+  // the chunk's key scale), w x split per head_dim column, three fp16
+  // products per state tile
+  constexpr bool KT16 = HALF && MIMO;
 
   float* Ql = lds + p.o_ql;   // [QV][ks] C (+bias), pairs rotated in place   (main pass)
   float* Kl = lds + p.o_kl;   // [QV][ks] B (+bias), pairs rotated in place
@@ -395,9 +401,9 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   // the bound behind the fp16 scales)
   float bmax_b = 0.f, bmax_c = 0.f;
   if constexpr (HALF) {
-    for (int i = lane; i < N; i += 64) {
-      bmax_b = max3_abs(p.b_bias[(size_t)h * N + i], 0.f, bmax_b);
-      bmax_c = max3_abs(p.c_bias[(size_t)h * N + i], 0.f, bmax_c);
+    for (int i = lane; i < R * N; i += 64) {
+      bmax_b = max3_abs(p.b_bias[(size_t)h * R * N + i], 0.f, bmax_b);
+      bmax_c = max3_abs(p.c_bias[(size_t)h * R * N + i], 0.f, bmax_c);
     }
     bmax_b = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_nn(bmax_b))));
     bmax_c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_nn(bmax_c))));
@@ -741,16 +747,28 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
           ra[c] = odd ? other : own;
           rb[c] = odd ? own : other;
         }
-#pragma unroll
-        for (int part = 0; part < 3; ++part) {
-          unsigned* dst = KTh + part * N * kKTw + col * kKTw + wd;
+        if constexpr (KT16) {
+          // fp16 head / tail planes at the chunk's key scale
+          const float sK = ldexpf(1.f, eK);
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const unsigned w = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){ra[c], rb[c]}, bf16x2));
-            dst[c * kKTw] = w;
-            if (part < 2) {  // the remainders for the next plane
-              ra[c] -= __uint_as_float(w << 16);
-              rb[c] -= __uint_as_float(w & 0xffff0000u);
+            unsigned hw, lw;
+            split2_f16s(ra[c], rb[c], sK, hw, lw);
+            KTh[(col + c) * kKTw + wd] = hw;
+            KTm[(col + c) * kKTw + wd] = lw;
+          }
+        } else {
+#pragma unroll
+          for (int part = 0; part < 3; ++part) {
+            unsigned* dst = KTh + part * N * kKTw + col * kKTw + wd;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const unsigned w = __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){ra[c], rb[c]}, bf16x2));
+              dst[c * kKTw] = w;
+              if (part < 2) {  // the remainders for the next plane
+                ra[c] -= __uint_as_float(w << 16);
+                rb[c] -= __uint_as_float(w & 0xffff0000u);
+              }
             }
           }
         }
@@ -793,10 +811,8 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         zr[k] = bload<VEC>(zres, (uint32_t)(t * tokxs + pv * VEC));
       }
     };
-    // With the bf16 update the z loads wait until S is formed (the registers
-    // are short across S); they land during the read-out and update.
-    if constexpr (FULL && !MIMO && !SPLIT) load_z();
-    if constexpr (FULL && MIMO) {
+    // MIMO: z of the tokens this wave finishes in the epilogue
+    auto load_zm = [&]() {
 #pragma unroll
       for (int i = 0; i < KZM; ++i) {
         const int t = wave + i * nwaves;
@@ -804,7 +820,11 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         zm[i][0] = lane < P ? buf_load1(zres, (ob + lane) * 4u) : 0.f;
         zm[i][1] = lane + 64 < P ? buf_load1(zres, (ob + lane + 64) * 4u) : 0.f;
       }
-    }
+    };
+    // With the split update the z loads wait until S is formed (the registers
+    // are short across S); they land during the read-out and update.
+    if constexpr (FULL && !MIMO && !SPLIT) load_z();
+    if constexpr (FULL && MIMO && !SPLIT) load_zm();
     if constexpr (!MERGED) lds_barrier();
 
     // ---- P2: cumulative angle (32-lane scans), cos / sin, and the rotation of
@@ -891,17 +911,27 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         const int ts_ = vs >> rsl;
         const float cum_s = sc_cum[ts_], scl_s = sc_scl[ts_];
         if constexpr (HALF) {
-          // one virtual row per token: the weights of the lane's four rows
-          // by selects (every lane computes the decay term; no branches)
-          const floatx4 cum_t = lds_read4(sc_cum + tb * 16 + 4 * lq);
-          const floatx4 gam_t = lds_read4(sc_gam + tb * 16 + 4 * lq);
+          // the weights of the lane's four rows by selects (every lane
+          // computes the decay term; no branches)
+          floatx4 cum_t, gam_t;
+          if constexpr (RSC == 1) {  // one virtual row per token
+            cum_t = lds_read4(sc_cum + tb * 16 + 4 * lq);
+            gam_t = lds_read4(sc_gam + tb * 16 + 4 * lq);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              cum_t[r] = sc_cum[(tb * 16 + 4 * lq + r) >> rsl];
+              gam_t[r] = sc_gam[(tb * 16 + 4 * lq + r) >> rsl];
+            }
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int tt = tb * 16 + 4 * lq + r;
+            const int vt = tb * 16 + 4 * lq + r;
+            const int tt = vt >> rsl;
             float wdec = exp_fast(cum_t[r] - cum_s) * scl_s;
             asm volatile("" : "+v"(wdec));
             const float wt = ts_ < tt ? wdec : (ts_ == tt ? gam_t[r] : 0.f);
-            Mdst[tt * ms + vs] = acc[r] * wt;
+            Mdst[vt * ms + vs] = acc[r] * wt;
           }
         } else {
 #pragma unroll
@@ -922,6 +952,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
     }
 
     if constexpr (FULL && !MIMO && SPLIT) load_z();
+    if constexpr (FULL && MIMO && SPLIT) load_zm();
     if (mma_wave) {
       if constexpr (FULL) {
         // ---- P5a: Y = M X + diag(exp(cum)) Q h'^T over this wave's state
@@ -1051,16 +1082,45 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
           const int v = 16 * (i >> 2) + 4 * lq + (i & 3);
           wx[i] = Xl[v * xs + p0 + l16] * sc_w[v >> rsl];
         }
-        uintx4 bh, bm, bl;
-        split8_bf16x3(wx, bh, bm, bl);
+        if constexpr (KT16) {
+          // w x to fp16 head / tail, one scale per head_dim column; the
+          // product of the two scales comes off each tile's three products
+          float wm = 0.f;
 #pragma unroll
-        for (int j = 0; j < JMAX; ++j) {
-          const int n = (nb0 + j) * 16 + l16;
-          const int blk = 4 * (lq ^ ((n >> 2) & 3));
-          const uintx4 ah = *reinterpret_cast<const uintx4*>(KTh + n * kKTw + blk);
-          const uintx4 am = *reinterpret_cast<const uintx4*>(KTm + n * kKTw + blk);
-          const uintx4 al = *reinterpret_cast<const uintx4*>(KTl + n * kKTw + blk);
-          Hacc[j] = mfma_bf16x6(ah, am, al, bh, bm, bl, Hacc[j]);
+          for (int i = 0; i < 8; i += 2) wm = max3_abs(wx[i], wx[i + 1], wm);
+          const int eW = f16_scale_exp(max_xor16_32(wm));
+          const float sW = ldexpf(1.f, eW);
+          unsigned h0, h1, h2, h3, t0, t1, t2, t3;
+          split2_f16s(wx[0], wx[1], sW, h0, t0);
+          split2_f16s(wx[2], wx[3], sW, h1, t1);
+          split2_f16s(wx[4], wx[5], sW, h2, t2);
+          split2_f16s(wx[6], wx[7], sW, h3, t3);
+          const uintx4 bh = uintx4{h0, h1, h2, h3}, bl = uintx4{t0, t1, t2, t3};
+          const int esh = -(eK + eW);
+#pragma unroll
+          for (int j = 0; j < JMAX; ++j) {
+            const int n = (nb0 + j) * 16 + l16;
+            const int blk = 4 * (lq ^ ((n >> 2) & 3));
+            const uintx4 ah = *reinterpret_cast<const uintx4*>(KTh + n * kKTw + blk);
+            const uintx4 al = *reinterpret_cast<const uintx4*>(KTm + n * kKTw + blk);
+            floatx4 d = mfma_f16(al, bh, floatx4{0.f, 0.f, 0.f, 0.f});
+            d = mfma_f16(ah, bl, d);
+            d = mfma_f16(ah, bh, d);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Hacc[j][r] += ldexpf(d[r], esh);
+          }
+        } else {
+          uintx4 bh, bm, bl;
+          split8_bf16x3(wx, bh, bm, bl);
+#pragma unroll
+          for (int j = 0; j < JMAX; ++j) {
+            const int n = (nb0 + j) * 16 + l16;
+            const int blk = 4 * (lq ^ ((n >> 2) & 3));
+            const uintx4 ah = *reinterpret_cast<const uintx4*>(KTh + n * kKTw + blk);
+            const uintx4 am = *reinterpret_cast<const uintx4*>(KTm + n * kKTw + blk);
+            const uintx4 al = *reinterpret_cast<const uintx4*>(KTl + n * kKTw + blk);
+            Hacc[j] = mfma_bf16x6(ah, am, al, bh, bm, bl, Hacc[j]);
+          }
         }
       }
       for (int sb = 0; sb < (SPLIT ? 0 : TB); ++sb) {
@@ -1147,6 +1207,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         if (pa < P) buf_store1(ores, (ob + pa) * 4u, o0);
         if (pb < P) buf_store1(ores, (ob + pb) * 4u, o1);
       }
+      raw_maxima();  // the next chunk's (see the SISO epilogue)
       lds_barrier();
     }
   }
@@ -1218,8 +1279,8 @@ ScanPlan make_plan(const ScanGeom& g) {
 // LDS layout of one pass; the summary pass needs no Q, M or Y buffers.  Rows
 // are padded by four floats so that rows 4 apart start 16 banks apart.
 //
-// With the split state update the keys are also kept split (three bf16 planes) and
-// transposed (o_kt); the summary pass keeps no fp32 keys, and in the main
+// With the split state update the keys are also kept split and transposed
+// (o_kt: three bf16 planes, two fp16 planes in the MIMO main pass); the summary pass keeps no fp32 keys, and in the main
 // pass the two raw y buffers overlay the fp32 keys, whose last reader is
 // S = Q K^T (a barrier separates it from the y writes); the key buffer is
 // enlarged where the two do not fit in it.
@@ -1231,14 +1292,14 @@ void layout(ScanKParams& kp, bool full, bool mimo, bool split) {
   kp.ys = kp.PT * 16 + 4;
   const bool y_over_k = full && split && kp.NH > 1;
   int off = 0;
-  // the SISO main pass of the split layout keeps Q and K as fp16 planes
+  // the main pass of the split layout keeps Q and K as fp16 planes
   // [2][QV][kPQK] halves in these two regions
-  const bool half = full && split && !mimo;
+  const bool half = full && split;
   const int planes = half ? QV * kPQK : 0;  // floats of two fp16 planes
   kp.o_ql = off; off += full ? std::max(QV * kp.ks, planes) : 0;
   kp.o_kl = off;
   off += (full || !split) ? std::max(y_over_k ? std::max(QV * kp.ks, 2 * QV * kp.ys) : QV * kp.ks, planes) : 0;
-  kp.o_kt = off; off += split ? 3 * kp.NT * 16 * kKTw : 0;
+  kp.o_kt = off; off += split ? (half && mimo ? 2 : 3) * kp.NT * 16 * kKTw : 0;  // MIMO main pass: two fp16 planes
   kp.o_xl = off; off += QV * kp.xs;
   kp.o_ml = off; off += full ? QV * kp.ms : 0;
   kp.o_ml2 = off; off += (full && kp.NH > 1) ? QV * kp.ms : 0;
@@ -1295,13 +1356,11 @@ hipError_t launch_one(const ScanKParams& kp, unsigned grid, unsigned block, hipS
 template <int VEC, bool MIMO, int NTC, int PTC, int NWC, int RSC, bool STR = false>
 hipError_t launch_passes(ScanKParams kp, const ScanPlan& plan, unsigned bhn, unsigned block,
                          hipStream_t stream) {
-  // as in the kernel: the split update in the summary pass of the merged
-  // layout, and in its main pass for SISO (the MIMO main pass has no LDS for it)
-  constexpr bool kSplitA = merged_variant(NTC, PTC, NWC, RSC);
-  constexpr bool kSplit = kSplitA && !MIMO;
+  // as in the kernel: both passes of the merged layout run the split update
+  constexpr bool kSplit = merged_variant(NTC, PTC, NWC, RSC);
   if (plan.nseg > 1) {
     ScanKParams ka = kp;
-    layout(ka, false, MIMO, kSplitA);
+    layout(ka, false, MIMO, kSplit);
     hipError_t e = launch_one<VEC, false, MIMO, NTC, PTC, NWC, RSC, STR>(ka, bhn * (unsigned)((plan.nseg - 1) * plan.npc), block,
                                                                        stream);
     if (e != hipSuccess) return e;
