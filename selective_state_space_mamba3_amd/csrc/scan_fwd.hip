@@ -235,9 +235,8 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   const int sw = nwaves - 1;  // wave that computes the per-token scalars
   // The merged layout runs its state update on split matrix products with k
   // = the chunk's 32 virtual rows at fp32-level accuracy: in the summary
-  // pass and the SISO main pass on bf16 MFMA with the six-term split
-  // (v_mfma_f32_16x16x32_bf16), in the MIMO main pass, short of LDS for a
-  // third key plane, on fp16 MFMA with head / tail splits (KT16 below).  Its
+  // pass on bf16 MFMA with the six-term split (v_mfma_f32_16x16x32_bf16), in
+  // the main pass on fp16 MFMA with head / tail splits (KT16 below).  Its
   // keys go to LDS split into planes and transposed, [n][slot].  In the main
   // pass they sit beside the fp16 query / key planes that S = Q K^T reads,
   // and the raw y buffers overlay the key planes, which are dead once S is
@@ -255,10 +254,11 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   // raw B / C entry of the chunk plus the largest bias entry, times sqrt(2)
   // (a rotation keeps each pair's norm).
   constexpr bool HALF = FULL && MERGED;
-  // MIMO main pass: the transposed keys as two fp16 planes (head / tail at
-  // the chunk's key scale), w x split per head_dim column, three fp16
-  // products per state tile
-  constexpr bool KT16 = HALF && MIMO;
+  // The main pass keeps the transposed keys as two fp16 planes (head / tail
+  // at the chunk's key scale) and splits w x per head_dim column: three fp16
+  // products per state tile, their sum scaled back by a power of two and
+  // added to the decayed state in one fused multiply-add
+  constexpr bool KT16 = HALF;
 
   float* Ql = lds + p.o_ql;   // [QV][ks] C (+bias), pairs rotated in place   (main pass)
   float* Kl = lds + p.o_kl;   // [QV][ks] B (+bias), pairs rotated in place
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       xr[k] = bload<VEC>(xres, (uint32_t)(t * tokxs + pv * VEC));
     }
   };
-  // The main pass with the bf16 update is short of registers across S, so it
+  // The main pass with the split update is short of registers across S, so it
   // issues the next chunk's x loads after S (they land during the read-out,
   // the update and the epilogue); the other variants load x with the rest.
   constexpr bool LATE_X = FULL && SPLIT;
@@ -1073,7 +1073,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       // ---- P5b: state update h' = decay h' + K^T (w X) ------------------------
       const float dec = run[64];
 #pragma unroll
-      for (int j = 0; j < JMAX; ++j) Hacc[j] *= dec;
+      for (int j = 0; j < (KT16 ? 0 : JMAX); ++j) Hacc[j] *= dec;
       if constexpr (SPLIT) {
         // B operand: w x of column p0 + l16 at virtual rows 4 lq + i, 16 + 4 lq + i
         float wx[8];
@@ -1107,7 +1107,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
             d = mfma_f16(ah, bl, d);
             d = mfma_f16(ah, bh, d);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Hacc[j][r] += ldexpf(d[r], esh);
+            for (int r = 0; r < 4; ++r) Hacc[j][r] = fmaf(Hacc[j][r], dec, ldexpf(d[r], esh));
           }
         } else {
           uintx4 bh, bm, bl;
@@ -1280,10 +1280,11 @@ ScanPlan make_plan(const ScanGeom& g) {
 // are padded by four floats so that rows 4 apart start 16 banks apart.
 //
 // With the split state update the keys are also kept split and transposed
-// (o_kt: three bf16 planes, two fp16 planes in the MIMO main pass); the summary pass keeps no fp32 keys, and in the main
-// pass the two raw y buffers overlay the fp32 keys, whose last reader is
-// S = Q K^T (a barrier separates it from the y writes); the key buffer is
-// enlarged where the two do not fit in it.
+// (o_kt: three bf16 planes in the summary pass, two fp16 planes in the main
+// pass); the summary pass keeps no fp32 keys, and in the main pass the two raw
+// y buffers overlay the fp32 keys (the fp16 query / key planes of the merged
+// layout), whose last reader is S = Q K^T (a barrier separates it from the y
+// writes); the key buffer is enlarged where the two do not fit in it.
 void layout(ScanKParams& kp, bool full, bool mimo, bool split) {
   const int QV = kQV;
   kp.ks = kp.NT * 16 + 4;
@@ -1299,7 +1300,7 @@ void layout(ScanKParams& kp, bool full, bool mimo, bool split) {
   kp.o_ql = off; off += full ? std::max(QV * kp.ks, planes) : 0;
   kp.o_kl = off;
   off += (full || !split) ? std::max(y_over_k ? std::max(QV * kp.ks, 2 * QV * kp.ys) : QV * kp.ks, planes) : 0;
-  kp.o_kt = off; off += split ? (half && mimo ? 2 : 3) * kp.NT * 16 * kKTw : 0;  // MIMO main pass: two fp16 planes
+  kp.o_kt = off; off += split ? (half ? 2 : 3) * kp.NT * 16 * kKTw : 0;  // main pass: two fp16 planes
   kp.o_xl = off; off += QV * kp.xs;
   kp.o_ml = off; off += full ? QV * kp.ms : 0;
   kp.o_ml2 = off; off += (full && kp.NH > 1) ? QV * kp.ms : 0;
