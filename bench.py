@@ -802,11 +802,11 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "arithmetic": "fp32 storage, accumulation and element-wise work; the chunk state update K^T (w x) "
-                      "as bf16 matrix products of six-term splits (three bf16 pieces per fp32 operand, "
-                      "about 2^-23 per product); S = Q K^T and the read-out Q h'^T as fp16 matrix "
-                      "products of power-of-two-scaled head/tail splits (about 2^-21 per product); "
-                      "M X in fp32",
+        "arithmetic": "fp32 storage, accumulation and element-wise work; in the main pass S = Q K^T, the "
+                      "read-out Q h'^T and the state update K^T (w x) as fp16 matrix products of "
+                      "power-of-two-scaled head/tail splits (about 2^-21 per product), M X in fp32; in the "
+                      "segment-summary pass the state update as bf16 matrix products of six-term splits "
+                      "(about 2^-23 per product)",
         "data": "synthetic",
         "config": {"workload": "siso_b4_l2048: m3_siso_fwd_packed on the [8192 x 3432] packed projection "
                                "(preprocess fused into the scan)",
