@@ -319,7 +319,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
 
   // x rows of the chunk at token cs
   auto prefetch_x = [&](int cs) {
-    const int nv = min(Qt, t_end - cs);
+    const int nv = max(0, min(Qt, t_end - cs));  // 0 past the end: every load returns zero
     const rsrc_t xres = make_rsrc(STR ? p.x + ((size_t)b * p.L + cs) * tokxs + (size_t)h * P
                                       : p.x + (((size_t)b * p.L + cs) * p.H + h) * P,
                                   (uint32_t)(nv * tokxs * 4));
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   // the update and the epilogue); the other variants load x with the rest.
   constexpr bool LATE_X = FULL && SPLIT;
   auto prefetch = [&](int cs) {
-    const int nv = min(Qt, t_end - cs);
+    const int nv = max(0, min(Qt, t_end - cs));  // 0 past the end: every load returns zero
     const rsrc_t bres = make_rsrc(p.b + ((size_t)b * p.L + cs) * tokb, (uint32_t)(nv * tokb * 4));
     const rsrc_t cres = make_rsrc(p.c + ((size_t)b * p.L + cs) * tokb, (uint32_t)(nv * tokb * 4));
     const rsrc_t ares = make_rsrc(p.angle + ((size_t)b * p.L + cs) * astr, (uint32_t)(nv * astr * 4));
@@ -349,7 +349,12 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         cr[1] = bload<VEC>(cres, row + mc1);
       }
       if (mpair) {
-        const floatx4 a4 = buf_load4(ares, (uint32_t)(mtok * astr + mc0) * 4u);
+        // the offset is formed here each time rather than kept in a register
+        // across the chunk loop (kept, it was spilled, and its reload waited
+        // for every load in flight, the prefetch just issued included)
+        int arow = mtok;
+        asm volatile("" : "+v"(arow));
+        const floatx4 a4 = buf_load4(ares, (uint32_t)(arow * astr + mc0) * 4u);
         angr[0] = a4.x; angr[1] = a4.y; angr[2] = a4.z; angr[3] = a4.w;
       }
       const size_t sbase = ((size_t)b * p.L + cs) * p.H + h;
@@ -374,14 +379,16 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
     if (wave == (MERGED ? sw : 0)) {
       // tokens cs .. cs + Qt (one past the chunk, for the trapezoid look-ahead)
       const size_t sbase = ((size_t)b * p.L + cs) * p.H + h;
-      const uint32_t nl = (uint32_t)min(Qt + 1, p.L - cs);
+      const uint32_t nl = (uint32_t)max(0, min(Qt + 1, p.L - cs));
       const rsrc_t dres = make_rsrc(p.dt + sbase, nl * p.H * 4);
       const rsrc_t tres = STR ? make_rsrc(p.trap + ((size_t)b * p.L + cs) * p.tstr + h, nl * p.tstr * 4)
                               : make_rsrc(p.trap + sbase, nl * p.H * 4);
       const rsrc_t adres = make_rsrc(p.adt + sbase, (uint32_t)(nv * p.H * 4));
       const uint32_t so = (uint32_t)(lane * p.H) * 4u;
       s_dt = buf_load1(dres, so);
-      s_trap = buf_load1(tres, STR ? (uint32_t)(lane * p.tstr) * 4u : so);
+      int tl = lane;  // (formed here each time, as the angle offset above)
+      asm volatile("" : "+v"(tl));
+      s_trap = buf_load1(tres, STR ? (uint32_t)(tl * p.tstr) * 4u : so);
       s_adt = buf_load1(adres, so);
     }
   };
@@ -594,6 +601,9 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
   };
   // fp16 scale exponents of the staged chunk's keys and queries (uniform)
   int eK = 0, eQ = 0;
+  // the D skip of this head, read once (read in the chunk loop, its load
+  // came after the prefetches in flight and waited for all of them)
+  const float dh = (FULL && p.has_d) ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(p.d[h]))) : 0.f;
 
   raw_maxima();
   __syncthreads();
@@ -857,7 +867,10 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       }
     }
     // The next chunk's loads go out now and land during this chunk's MFMA work.
-    if (c0 + Qt < t_end) prefetch(c0 + Qt);
+    // Issued after the last chunk too (on empty ranges: no memory access,
+    // zeros): with no branch around the loads the compiler counts them
+    // through the loop and waits for exactly the ones it needs.
+    prefetch(c0 + Qt);
     lds_barrier();
 
     if constexpr (FULL) {
@@ -1068,7 +1081,7 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       // the next chunk's x rows land during the update and the epilogue (every
       // wave is an MFMA wave where they load late)
       if constexpr (LATE_X) {
-        if (c0 + Qt < t_end) prefetch_x(c0 + Qt);
+        prefetch_x(c0 + Qt);
       }
       // ---- P5b: state update h' = decay h' + K^T (w X) ------------------------
       const float dec = run[64];
@@ -1147,7 +1160,6 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
     // ---- P6: epilogue ---------------------------------------------------------
     if constexpr (FULL && !MIMO) {
       // out = (y + D x) * silu(z), VEC-wide and coalesced along head_dim
-      const float dh = p.has_d ? p.d[h] : 0.f;
 #pragma unroll
       for (int k = 0; k < KX; ++k) {
         const int idx = tid + k * nthreads;
@@ -1174,7 +1186,6 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
     if constexpr (FULL && MIMO) {
       // per rank: D skip, gate silu(z * mimo_z), optional RMS norm over P,
       // then the mimo_o-weighted sum over ranks; one wave per token
-      const float dh = p.has_d ? p.d[h] : 0.f;
       const int pa = lane, pb = lane + 64;
 #pragma unroll
       for (int i = 0; i < KZM; ++i) {
