@@ -1192,7 +1192,11 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
         const int t = wave + i * nwaves;
         if (t >= nvalid) break;  // wave-uniform
         float o0 = 0.f, o1 = 0.f;
-        for (int r = 0; r < R; ++r) {
+        // ranks unrolled to the rank stride where it is known, so that their
+        // norm reductions overlap
+#pragma unroll
+        for (int r = 0; r < (RSC > 0 ? RSC : R); ++r) {
+          if (RSC > 0 && r >= R) break;  // uniform
           const int v = (t << rsl) + r;
           float y0 = 0.f, y1 = 0.f;
           if (pa < P) {
