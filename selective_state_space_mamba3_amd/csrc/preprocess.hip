@@ -91,6 +91,13 @@ __global__ __launch_bounds__(256) void preprocess_derived_kernel(PreKParams p) {
   if (r >= p.rows) return;
   const float* row = p.projected + (size_t)r * p.W;
   const int nb = p.M / p.N;  // B rows (and C rows) per packed row
+  // the dt / A columns of the first 64 heads load with the rows (loaded after
+  // the row stores, they were a second round trip)
+  const float* sc = row + 2 * p.I + 2 * p.M;
+  const bool hv = lane < p.H;
+  const float dt_raw = hv ? sc[lane] : 0.f;
+  const float a_raw = hv ? sc[p.H + lane] : 0.f;
+  const float dt_b = hv ? p.dt_bias[lane] : 0.f;
   for (int k = 0; k < nb; ++k) {
     const float* sb = row + 2 * p.I + k * p.N;
     const float* scc = sb + p.M;
@@ -134,8 +141,13 @@ __global__ __launch_bounds__(256) void preprocess_derived_kernel(PreKParams p) {
       dc[i] = scc[i] * ic;
     }
   }
-  const float* sc = row + 2 * p.I + 2 * p.M;
-  for (int h = lane; h < p.H; h += 64) {
+  if (hv) {
+    const float dtv = fminf(fmaxf(softplusf_acc(dt_raw + dt_b), p.dt_min), p.dt_max);
+    const float amag = fmaxf(softplusf_acc(a_raw), p.a_floor);
+    p.dt[(size_t)r * p.H + lane] = dtv;
+    p.adt[(size_t)r * p.H + lane] = -amag * dtv;
+  }
+  for (int h = lane + 64; h < p.H; h += 64) {
     const float dtv = fminf(fmaxf(softplusf_acc(sc[h] + p.dt_bias[h]), p.dt_min), p.dt_max);
     const float amag = fmaxf(softplusf_acc(sc[p.H + h]), p.a_floor);
     p.dt[(size_t)r * p.H + h] = dtv;
