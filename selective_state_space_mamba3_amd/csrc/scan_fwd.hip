@@ -1164,7 +1164,11 @@ __global__ __launch_bounds__(NWC ? NWC * 64 : 1024, NWC ? NWC / 2 : 1) void scan
       for (int k = 0; k < KX; ++k) {
         const int idx = tid + k * nthreads;
         const int t = idx / xrow, pv = idx - t * xrow;
-        if (idx < Qt * xrow && t < nvalid) {
+        // fixed-size variant: one item per thread, and rows past the chunk's
+        // last token fall outside the store's buffer range, so the store
+        // needs no branch (the compiler then counts it and the next
+        // chunk's staging does not wait for it)
+        if (FIXED || (idx < Qt * xrow && t < nvalid)) {
           vec_t y = vload<VEC>(Yl + t * ys + pv * VEC);
           if (NH > 1) y += vload<VEC>(Yl2 + t * ys + pv * VEC);
           const vec_t xv = vload<VEC>(Xl + t * xs + pv * VEC);
