@@ -703,9 +703,17 @@ __global__ __launch_bounds__(512, 4) void bwd_chunk_kernel(BwdK p) {
     load_kq(p, b, h, g, t0, nv, Kc, Qc, NS, CS, SN, tid);
     load_xg(p, b, h, t0, nv, X, GY, PS, nullptr, nullptr, tid);
   }
+  const int r = lane & 15, q = lane >> 4;
+  // fixed geometry: this wave's state tile (read by the y / G K products
+  // below) loads now, during the staging and the chunk-square products
+  floatx4 sv[FIX ? NC / 16 : 1];
+  if constexpr (FIX) {
+    const float* Sg = (wave >= 4 ? GXg : HEg) + ((wave & 3) * 16 + r) * N + 4 * q;  // B[k][n] = S[pt 16 + n][k]
+#pragma unroll
+    for (int j = 0; j < NC / 16; ++j) sv[j] = ldg4(Sg + 16 * j);
+  }
   __syncthreads();
   const float Dh = p.has_d ? p.d[h] : 0.f;
-  const int r = lane & 15, q = lane >> 4;
 
   // ---- chunk-square products, masked: waves 0-3 Q K^T, waves 4-7 gy x^T
   {
@@ -742,10 +750,6 @@ __global__ __launch_bounds__(512, 4) void bwd_chunk_kernel(BwdK p) {
     // token halves, so each state tile is read from global memory once
     const bool isgk = wave >= 4;
     const int pt = wave & 3;
-    const float* Sg = (isgk ? GXg : HEg) + (pt * 16 + r) * N + 4 * q;  // B[k][n] = S[pt 16 + n][k]
-    floatx4 sv[NC / 16];
-#pragma unroll
-    for (int j = 0; j < NC / 16; ++j) sv[j] = ldg4(Sg + 16 * j);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
