@@ -263,8 +263,8 @@ __device__ __forceinline__ float wave_max_nn(float v) {
   unsigned u = __float_as_uint(v);
   u = max(u, (unsigned)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xf, 0xf, false));  // quad_perm 1,0,3,2
   u = max(u, (unsigned)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xf, 0xf, false));  // quad_perm 2,3,0,1
-  u = max(u, (unsigned)__builtin_amdgcn_ds_swizzle((int)u, 0x101F));                      // xor 4
-  u = max(u, (unsigned)__builtin_amdgcn_ds_swizzle((int)u, 0x201F));                      // xor 8
+  u = max(u, (unsigned)__builtin_amdgcn_update_dpp(0, (int)u, 0x124, 0xf, 0xf, false));  // row_ror 4
+  u = max(u, (unsigned)__builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xf, 0xf, false));  // row_ror 8
   return max_xor16_32(__uint_as_float(u));
 }
 
