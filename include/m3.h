@@ -369,11 +369,13 @@ int m3_preprocess_bwd(const float* projected, const float* dt_bias, uint32_t row
 
 /*
  * Measurement hook.  After m3_set_profile_events(start, stop) with two
- * hipEvent_t handles, later m3_siso_fwd / m3_mimo_fwd calls on this thread
- * record `start` just before and `stop` just after their main scan kernel,
- * on the call's stream, so hipEventElapsedTime(start, stop) is that
- * kernel's duration.  Passing NULL, NULL turns the hook off.  The caller
- * owns the events.
+ * hipEvent_t handles, later m3_siso_fwd / m3_siso_fwd_packed / m3_mimo_fwd
+ * calls on this thread launch their main scan kernel with the two events
+ * attached (hipExtLaunchKernelGGL): `start` is recorded as the kernel
+ * begins and `stop` as it ends, on the call's stream, so
+ * hipEventElapsedTime(start, stop) is that kernel's duration with no event
+ * command of its own in the stream.  Both handles must be non-NULL; a NULL
+ * in either turns the hook off.  The caller owns the events.
  */
 void m3_set_profile_events(void* start_event, void* stop_event);
 

@@ -49,6 +49,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <map>
 #include <mutex>
@@ -1358,8 +1360,12 @@ hipError_t set_max_lds_once(const void* fn) {
   return e;
 }
 
+// start / stop (optional): events the launch itself records around the
+// kernel's execution (hipExtLaunchKernel), with no event commands of their
+// own between the kernels in the stream
 template <int VEC, bool FULL, bool MIMO, int NTC, int PTC, int NWC, int RSC, bool STR>
-hipError_t launch_one(const ScanKParams& kp, unsigned grid, unsigned block, hipStream_t stream) {
+hipError_t launch_one(const ScanKParams& kp, unsigned grid, unsigned block, hipStream_t stream,
+                      hipEvent_t start = nullptr, hipEvent_t stop = nullptr) {
   const size_t lds_bytes = (size_t)kp.lds_floats * sizeof(float);
   // Dynamic LDS above 64 KiB needs the opt-in attribute; set it once per
   // kernel instantiation to the largest layout it can take (the CU's 160 KiB)
@@ -1368,8 +1374,12 @@ hipError_t launch_one(const ScanKParams& kp, unsigned grid, unsigned block, hipS
     hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(&scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC, RSC, STR>));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC, RSC, STR>), dim3(grid), dim3(block), lds_bytes,
-                     stream, kp);
+  if (start != nullptr && stop != nullptr)
+    hipExtLaunchKernelGGL((scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC, RSC, STR>), dim3(grid), dim3(block),
+                          (std::uint32_t)lds_bytes, stream, start, stop, 0u, kp);
+  else
+    hipLaunchKernelGGL((scan_chunk_kernel<VEC, FULL, MIMO, NTC, PTC, NWC, RSC, STR>), dim3(grid), dim3(block), lds_bytes,
+                       stream, kp);
   return hipGetLastError();
 }
 
@@ -1387,13 +1397,8 @@ hipError_t launch_passes(ScanKParams kp, const ScanPlan& plan, unsigned bhn, uns
   }
   layout(kp, true, MIMO, kSplit);
   const ProfileEvents& pe = profile_events();
-  if (pe.start) {
-    hipError_t e = hipEventRecord(pe.start, stream);
-    if (e != hipSuccess) return e;
-  }
-  hipError_t e = launch_one<VEC, true, MIMO, NTC, PTC, NWC, RSC, STR>(kp, bhn * (unsigned)plan.nseg, block, stream);
-  if (e == hipSuccess && pe.stop) e = hipEventRecord(pe.stop, stream);
-  return e;
+  return launch_one<VEC, true, MIMO, NTC, PTC, NWC, RSC, STR>(kp, bhn * (unsigned)plan.nseg, block, stream, pe.start,
+                                                              pe.stop);
 }
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0u; }
