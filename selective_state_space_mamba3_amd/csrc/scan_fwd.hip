@@ -54,6 +54,7 @@
 #include <algorithm>
 #include <map>
 #include <mutex>
+#include <utility>
 
 namespace m3 {
 namespace {
@@ -1346,17 +1347,21 @@ void layout(ScanKParams& kp, bool full, bool mimo, bool split) {
   kp.lds_floats = off;
 }
 
-// Raise a kernel's dynamic-LDS limit to one CU's 160 KiB, once per kernel
-// (thread-safe); later calls return the first call's status.
+// Raise a kernel's dynamic-LDS limit to one CU's 160 KiB, once per kernel and
+// device (thread-safe; the attribute is set with that device current); later
+// calls return the first call's status.
 hipError_t set_max_lds_once(const void* fn) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
   static std::mutex mu;
-  static std::map<const void*, hipError_t> done;
+  static std::map<std::pair<int, const void*>, hipError_t> done;
   std::lock_guard<std::mutex> lock(mu);
-  auto it = done.find(fn);
+  auto it = done.find({dev, fn});
   if (it != done.end()) return it->second;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (e != hipSuccess) (void)hipGetLastError();
-  done.emplace(fn, e);
+  done.emplace(std::make_pair(dev, fn), e);
   return e;
 }
 
